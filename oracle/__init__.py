@@ -1,0 +1,21 @@
+"""fp64 CPU oracle for the ARL2 hybrid attention step.
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. It shares no code
+with the HIP path and imports nothing from it.
+"""
+from .arl2_oracle import (  # noqa: F401
+    L2_EPS,
+    attention_weights,
+    commit,
+    commit_inputs,
+    default_scale,
+    feature_map,
+    fullkv_attention,
+    inter_read,
+    intra_attention,
+    l2_normalize_rows,
+    read,
+    rollout,
+    state_commit,
+)

@@ -1,0 +1,397 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Source: "Attend Locally, Remember Linearly" technical summary (gist.science),
+§2.1 (hybrid decomposition: intra-frame softmax, feature maps, update and read
+equations) and §2.2 (frame-level access, clean-pass update). The pages print no
+numerical example, so the pins are closed forms, invariants, hand-derived
+rational examples (tests/golden/), special cases and a scalar brute-force
+unroll (tests/bruteforce.py). Each test names the mistake it is meant to catch.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import bruteforce as bf
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            key, r, c = parts[0], int(parts[1]), int(parts[2])
+            vals = []
+            for tok in parts[3:]:
+                vals.append(math.log(3.0) if tok == "ln3" else Fraction(tok))
+            out[key] = (r, c, vals)
+    return out
+
+
+def _as_array(entry):
+    r, c, vals = entry
+    return np.array([float(v) for v in vals], dtype=np.float64).reshape(r, c)
+
+
+def _rs(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- softmax (a2)
+
+def test_p1_softmax_rows_sum_to_one():
+    """P1: attention weights are a probability distribution per query row."""
+    g = _rs(1)
+    q = g.standard_normal((2, 3, 17, 8)) * 3
+    k = g.standard_normal((2, 3, 29, 8)) * 3
+    w = oracle.attention_weights(q, k)
+    assert w.shape == (2, 3, 17, 29)
+    assert np.all(w >= 0)
+    np.testing.assert_allclose(w.sum(-1), 1.0, rtol=0, atol=1e-15)
+
+
+def test_golden_softmax_ln3():
+    """Hand-derived weights (1/4, 3/4): catches a wrong exp base, a missing
+    normalisation or weights applied to the wrong value rows."""
+    gd = _load_golden("softmax_ln3.txt")
+    q, k, v = _as_array(gd["q"]), _as_array(gd["k"]), _as_array(gd["v"])
+    w = oracle.attention_weights(q[None, None], k[None, None], scale=1.0)[0, 0]
+    np.testing.assert_allclose(w, _as_array(gd["weights"]), rtol=0, atol=1e-15)
+    o = oracle.intra_attention(q[None, None], k[None, None], v[None, None], scale=1.0)[0, 0]
+    np.testing.assert_allclose(o, _as_array(gd["o"]), rtol=0, atol=1e-14)
+
+
+def test_p2_closed_forms():
+    """P2: Q = 0 gives the column mean of V; T = 1 gives V; equal keys give
+    uniform weights whatever the query."""
+    g = _rs(2)
+    v = g.standard_normal((1, 2, 11, 4))
+    k = g.standard_normal((1, 2, 11, 4))
+    o = oracle.intra_attention(np.zeros((1, 2, 5, 4)), k, v)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape),
+                               rtol=0, atol=1e-15)
+    o1 = oracle.intra_attention(g.standard_normal((1, 2, 1, 4)), k[:, :, :1], v[:, :, :1])
+    np.testing.assert_allclose(o1, v[:, :, :1], rtol=0, atol=1e-15)
+    keq = np.broadcast_to(g.standard_normal((1, 2, 1, 4)), (1, 2, 11, 4))
+    w = oracle.attention_weights(g.standard_normal((1, 2, 3, 4)), keq)
+    np.testing.assert_allclose(w, 1.0 / 11, rtol=0, atol=1e-15)
+
+
+def test_default_scale_is_inverse_sqrt_d():
+    """Reading A8: temperature 1/sqrt(d). Two keys differing by a logit gap:
+    the weight ratio is exp(gap / sqrt(d))."""
+    d = 16
+    q = np.zeros((1, 1, 1, d)); q[..., 0] = 2.0
+    k = np.zeros((1, 1, 2, d)); k[..., 1, 0] = 1.5
+    w = oracle.attention_weights(q, k)[0, 0, 0]
+    assert w[1] / w[0] == pytest.approx(math.exp(3.0 / 4.0), rel=1e-14)
+
+
+def test_p3_bruteforce_attention():
+    """P3: the matrix form equals scalar loops on T <= 8 (catches K vs K^T and
+    softmax over the wrong axis)."""
+    g = _rs(3)
+    q = g.standard_normal((6, 5)) * 2
+    k = g.standard_normal((8, 5)) * 2
+    v = g.standard_normal((8, 3))
+    ref = bf.softmax_attention(q.tolist(), k.tolist(), v.tolist(), 0.37)
+    got = oracle.intra_attention(q[None, None], k[None, None], v[None, None], 0.37)[0, 0]
+    np.testing.assert_allclose(got, np.array(ref), rtol=0, atol=1e-13)
+
+
+def test_softmax_shift_invariance_large_logits():
+    """Adding a constant to every logit of a row leaves the weights unchanged,
+    also far beyond exp's range (max subtraction)."""
+    g = _rs(4)
+    q = g.standard_normal((1, 1, 3, 4))
+    k = g.standard_normal((1, 1, 7, 4))
+    w = oracle.attention_weights(q, k, 1.0)
+    shift = np.zeros((1, 1, 1, 5)); shift[..., 4] = 1.0
+    q2 = np.concatenate([q, np.full((1, 1, 3, 1), 1.0)], -1)
+    k2 = np.concatenate([k, np.full((1, 1, 7, 1), 900.0)], -1)
+    w2 = oracle.attention_weights(q2, k2, 1.0)
+    np.testing.assert_allclose(w2, w, rtol=1e-12, atol=0)
+
+
+# ----------------------------------------------------------- feature maps (a1)
+
+def test_feature_map_orientation_and_heads():
+    """Reading A7: X' = X Phi[h] with Phi[h] indexed [d_in, d_out]. A unit row
+    e_i picks row i of Phi[h]; each head uses its own Phi (catches Phi^T and a
+    head-index mix-up)."""
+    g = _rs(5)
+    phi = g.standard_normal((3, 4, 4))
+    x = np.zeros((2, 3, 4, 4))
+    for b in range(2):
+        for h in range(3):
+            x[b, h] = np.eye(4)
+    y = oracle.feature_map(x, phi)
+    for b in range(2):
+        for h in range(3):
+            np.testing.assert_array_equal(y[b, h], phi[h])
+    xr = g.standard_normal((1, 3, 6, 4))
+    yr = oracle.feature_map(xr, phi)
+    for h in range(3):
+        ref = bf.feature_map(xr[0, h].tolist(), phi[h].tolist())
+        np.testing.assert_allclose(yr[0, h], np.array(ref), rtol=0, atol=1e-13)
+
+
+def test_l2_normalize_rows():
+    """Reading A6: unit rows, direction kept, the zero row stays zero."""
+    g = _rs(6)
+    x = g.standard_normal((5, 7)) * 10
+    x[2] = 0.0
+    y = oracle.l2_normalize_rows(x)
+    n = np.linalg.norm(y, axis=-1)
+    np.testing.assert_allclose(np.delete(n, 2), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(y[2], 0.0)
+    np.testing.assert_allclose(y[0] * np.linalg.norm(x[0]), x[0], rtol=1e-14)
+    assert oracle.l2_normalize_rows(np.array([[3.0, 4.0]])).tolist() == [[0.6, 0.8]]
+
+
+# ------------------------------------------------------------ commit (a5)
+
+def test_golden_delta_rule_2x2():
+    """Hand-derived rational example: catches the residual taken against
+    alpha*S (reading A2), beta applied per column instead of per token, S K'
+    instead of K' S, and a missing alpha*S term."""
+    gd = _load_golden("delta_rule_2x2.txt")
+    S = _as_array(gd["S_prev"])[None, None]
+    K = _as_array(gd["K"])[None, None]
+    V = _as_array(gd["V"])[None, None]
+    beta = _as_array(gd["beta"])[None]            # [1, 1, T]
+    alpha = _as_array(gd["alpha"])[0]             # [1, 1]
+    got = oracle.state_commit(K, V, beta, alpha, S)[0, 0]
+    np.testing.assert_allclose(got, _as_array(gd["S_next"]), rtol=0, atol=1e-15)
+    # through the full commit with identity maps and the same (unit) keys
+    eye = np.eye(2)[None]
+    got2 = oracle.commit(K, V, eye, eye, beta, alpha, S)[0, 0]
+    np.testing.assert_allclose(got2, _as_array(gd["S_next"]), rtol=0, atol=1e-15)
+
+
+def test_p4_identity_and_pure_decay():
+    """P4: alpha=1, beta=0 leaves S unchanged exactly; beta=0 gives alpha*S and
+    after k frames prod(alpha)*S."""
+    g = _rs(7)
+    B, H, T, d = 2, 3, 9, 5
+    S = g.standard_normal((B, H, d, d))
+    kp = oracle.l2_normalize_rows(g.standard_normal((B, H, T, d)))
+    vp = g.standard_normal((B, H, T, d))
+    zero = np.zeros((B, H, T))
+    out = oracle.state_commit(kp, vp, zero, np.ones((B, H)), S)
+    np.testing.assert_array_equal(out, S)
+    cur = S
+    prod = np.ones((B, H))
+    for _ in range(4):
+        a = g.uniform(0.2, 0.99, (B, H))
+        cur = oracle.state_commit(kp, vp, zero, a, cur)
+        prod = prod * a
+    np.testing.assert_allclose(cur, prod[..., None, None] * S, rtol=1e-14, atol=0)
+
+
+def test_p5_exact_write_single_key():
+    """P5 (delta-rule exact write): alpha=1, beta=1, one unit key k, identity
+    maps: afterwards k S_n = v, whatever S_{n-1} held. Catches a wrong sign in
+    the residual and the missing transpose."""
+    g = _rs(8)
+    d = 6
+    S = g.standard_normal((1, 1, d, d))
+    k = g.standard_normal((1, 1, 1, d)) * 3.0     # not unit: commit normalises
+    v = g.standard_normal((1, 1, 1, d))
+    eye = np.eye(d)[None]
+    Sn = oracle.commit(k, v, eye, eye, np.ones((1, 1, 1)), np.ones((1, 1)), S)
+    ku = k / np.linalg.norm(k)
+    np.testing.assert_allclose(ku[0, 0] @ Sn[0, 0], v[0, 0], rtol=0, atol=1e-14)
+
+
+def test_p6_exact_write_orthonormal_keys():
+    """P6: T <= d orthonormal keys, alpha = beta = 1, identity maps:
+    K' S_n = V' for every key at once (frame-level batched write)."""
+    g = _rs(9)
+    d, T = 8, 5
+    Qm, _ = np.linalg.qr(g.standard_normal((d, d)))
+    K = Qm[:T][None, None]
+    V = g.standard_normal((1, 1, T, d))
+    S = g.standard_normal((1, 1, d, d))
+    eye = np.eye(d)[None]
+    Sn = oracle.commit(K, V, eye, eye, np.ones((1, 1, T)), np.ones((1, 1)), S)
+    np.testing.assert_allclose(K[0, 0] @ Sn[0, 0], V[0, 0], rtol=0, atol=1e-13)
+
+
+def test_p7_token_loop_and_gram_form():
+    """P7: the matrix form equals the loop of rank-1 terms against the same
+    S_{n-1}, and the independent Gram form
+    S_n = (alpha I - K'^T B K') S_{n-1} + K'^T B V'."""
+    g = _rs(10)
+    B, H, T, d = 1, 2, 7, 4
+    kp = oracle.l2_normalize_rows(g.standard_normal((B, H, T, d)))
+    vp = g.standard_normal((B, H, T, d))
+    beta = g.uniform(0, 1, (B, H, T))
+    alpha = g.uniform(0.5, 1, (B, H))
+    S = g.standard_normal((B, H, d, d))
+    got = oracle.state_commit(kp, vp, beta, alpha, S)
+    for h in range(H):
+        ref = bf.commit_tokens(kp[0, h].tolist(), vp[0, h].tolist(), beta[0, h].tolist(),
+                               alpha[0, h], S[0, h].tolist())
+        np.testing.assert_allclose(got[0, h], np.array(ref), rtol=0, atol=1e-13)
+        Bm = np.diag(beta[0, h])
+        K, V = kp[0, h], vp[0, h]
+        gram = (alpha[0, h] * np.eye(d) - K.T @ Bm @ K) @ S[0, h] + K.T @ Bm @ V
+        np.testing.assert_allclose(got[0, h], gram, rtol=0, atol=1e-13)
+
+
+def test_p12_first_frame():
+    """P12: S_0 = 0 gives S_1 = K'^T diag(beta) V' and a zero inter read."""
+    g = _rs(11)
+    B, H, T, d = 1, 1, 6, 4
+    q = g.standard_normal((B, H, T, d))
+    k = g.standard_normal((B, H, T, d))
+    v = g.standard_normal((B, H, T, d))
+    phis = [g.standard_normal((H, d, d)) for _ in range(3)]
+    beta = g.uniform(0, 0.2, (B, H, T))
+    alpha = g.uniform(0.5, 1, (B, H))
+    frames = [{"passes": [(q, k, v)], "beta": beta, "alpha": alpha}]
+    outs, states = oracle.rollout(frames, *phis)
+    np.testing.assert_array_equal(outs[(0, 0)]["o_inter"], 0.0)
+    kp, vp = oracle.commit_inputs(k, v, phis[1], phis[2])
+    ref = kp[0, 0].T @ np.diag(beta[0, 0]) @ vp[0, 0]
+    np.testing.assert_allclose(states[1][0, 0], ref, rtol=0, atol=1e-14)
+
+
+def test_p11_stability_bound():
+    """P11: with the workloads' gates (sum of beta < 1), the linear part
+    A = alpha I - K'^T diag(beta) K' has eigenvalues in [alpha - sum(beta),
+    alpha], and ||S|| stays bounded over a long rollout."""
+    g = _rs(12)
+    T, d = 64, 16
+    kp = oracle.l2_normalize_rows(g.standard_normal((T, d)))
+    beta = 1.0 / (1.0 + np.exp(-g.standard_normal(T))) / T
+    alpha = 0.9
+    A = alpha * np.eye(d) - kp.T @ np.diag(beta) @ kp
+    ev = np.linalg.eigvalsh(A)
+    assert ev.min() >= alpha - beta.sum() - 1e-12 and ev.max() <= alpha + 1e-12
+    S = np.zeros((1, 1, d, d))
+    norms = []
+    for f in range(240):
+        kf = oracle.l2_normalize_rows(g.standard_normal((1, 1, T, d)))
+        vf = g.standard_normal((1, 1, T, d))
+        bf_ = (1.0 / (1.0 + np.exp(-g.standard_normal((1, 1, T)))) / T)
+        af = 1.0 / (1.0 + np.exp(-g.normal(3.0, 0.5, (1, 1))))
+        S = oracle.state_commit(kf, vf, bf_, af, S)
+        norms.append(np.linalg.norm(S))
+    assert max(norms[120:]) < 3 * max(norms[:120]) + 1e-9
+    assert np.isfinite(norms).all()
+
+
+# ------------------------------------------------ read and sequencing (a3-a6)
+
+def test_p9_frame_level_access():
+    """P9: identical query rows in a frame get identical O_inter (and O) rows,
+    because every row reads the same S_{N-1}."""
+    g = _rs(13)
+    B, H, T, d = 1, 2, 10, 8
+    q = g.standard_normal((B, H, T, d))
+    q[:, :, 7] = q[:, :, 2]
+    k = g.standard_normal((B, H, T, d))
+    v = g.standard_normal((B, H, T, d))
+    S = g.standard_normal((B, H, d, d))
+    phi = g.standard_normal((H, d, d))
+    out = oracle.read(q, k, v, phi, S)
+    np.testing.assert_allclose(out["o_inter"][:, :, 7], out["o_inter"][:, :, 2], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out["o"][:, :, 7], out["o"][:, :, 2], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out["o"], out["o_intra"] + out["o_inter"], rtol=0, atol=0)
+
+
+def test_p10_reads_never_mutate_state():
+    """P10: a read leaves S untouched, and S_n does not depend on how many
+    denoising reads preceded the clean pass."""
+    g = _rs(14)
+    B, H, T, d = 1, 2, 6, 4
+    phis = [g.standard_normal((H, d, d)) for _ in range(3)]
+    S = g.standard_normal((B, H, d, d))
+    S_copy = S.copy()
+    oracle.read(g.standard_normal((B, H, T, d)), g.standard_normal((B, H, T, d)),
+                g.standard_normal((B, H, T, d)), phis[0], S)
+    np.testing.assert_array_equal(S, S_copy)
+
+    clean = [(g.standard_normal((B, H, T, d)) for _ in range(3)) for _ in range(3)]
+    clean = [tuple(c) for c in clean]
+    gates_ = [(g.uniform(0, 0.1, (B, H, T)), g.uniform(0.5, 1, (B, H))) for _ in range(3)]
+    finals = []
+    for n_denoise in (0, 1, 4):
+        frames = []
+        for f in range(3):
+            noisy = [tuple(g.standard_normal((B, H, T, d)) for _ in range(3))
+                     for _ in range(n_denoise)]
+            frames.append({"passes": noisy + [clean[f]], "beta": gates_[f][0],
+                           "alpha": gates_[f][1]})
+        _, states = oracle.rollout(frames, *phis)
+        finals.append(states)
+    for f in range(4):
+        np.testing.assert_array_equal(finals[0][f], finals[1][f])
+        np.testing.assert_array_equal(finals[0][f], finals[2][f])
+
+
+def test_p8_bruteforce_rollout():
+    """P8: the oracle's whole rollout (reads on every pass, clean-pass commits,
+    frame-level access) equals explicit scalar loops on tiny inputs, with
+    distinct denoise and clean inputs so that committing a noisy pass, reading
+    the post-commit state, or mixing frames all fail."""
+    g = _rs(15)
+    B, H, T, d, F, P = 1, 2, 5, 4, 4, 3
+    phis = [g.standard_normal((H, d, d)) for _ in range(3)]
+    frames = []
+    for f in range(F):
+        passes = [tuple(g.standard_normal((B, H, T, d)) for _ in range(3)) for _ in range(P)]
+        frames.append({"passes": passes, "beta": g.uniform(0, 0.3, (B, H, T)),
+                       "alpha": g.uniform(0.5, 1, (B, H))})
+    scale = 1.0 / math.sqrt(d)
+    outs, states = oracle.rollout(frames, *phis)
+    for h in range(H):
+        bframes = []
+        for fr in frames:
+            bframes.append({
+                "passes": [tuple(x[0, h].tolist() for x in p) for p in fr["passes"]],
+                "beta": fr["beta"][0, h].tolist(), "alpha": float(fr["alpha"][0, h])})
+        bouts, bstates = bf.rollout(bframes, phis[0][h].tolist(), phis[1][h].tolist(),
+                                    phis[2][h].tolist(), scale)
+        for f in range(F + 1):
+            np.testing.assert_allclose(states[f][0, h], np.array(bstates[f]), rtol=0, atol=1e-12)
+        for key, val in bouts.items():
+            for name in ("o", "o_intra", "o_inter"):
+                np.testing.assert_allclose(outs[key][name][0, h], np.array(val[name]),
+                                           rtol=0, atol=1e-12)
+
+
+def test_fullkv_comparator_is_softmax_over_all_keys():
+    """The comparator is plain softmax attention over the concatenated keys;
+    with a single frame in the cache it equals the intra-frame branch."""
+    g = _rs(16)
+    q = g.standard_normal((1, 1, 4, 8))
+    ks = [g.standard_normal((1, 1, 6, 8)) for _ in range(3)]
+    vs = [g.standard_normal((1, 1, 6, 8)) for _ in range(3)]
+    o = oracle.fullkv_attention(q, np.concatenate(ks, 2), np.concatenate(vs, 2))
+    ref = bf.softmax_attention(q[0, 0].tolist(), np.concatenate(ks, 2)[0, 0].tolist(),
+                               np.concatenate(vs, 2)[0, 0].tolist(), 1 / math.sqrt(8))
+    np.testing.assert_allclose(o[0, 0], np.array(ref), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.fullkv_attention(q, ks[0], vs[0]),
+                               oracle.intra_attention(q, ks[0], vs[0]), rtol=0, atol=0)
+
+
+def test_planted_mistakes_are_caught():
+    """A mistake planted in a copy of the commit (residual against alpha*S,
+    the reading the pages do not print) changes the golden example, so the
+    golden pin can tell the two readings apart."""
+    gd = _load_golden("delta_rule_2x2.txt")
+    S = _as_array(gd["S_prev"]); K = _as_array(gd["K"]); V = _as_array(gd["V"])
+    beta = _as_array(gd["beta"])[0]; alpha = float(_as_array(gd["alpha"])[0, 0])
+    decay_first = alpha * S + K.T @ np.diag(beta) @ (V - K @ (alpha * S))
+    assert np.abs(decay_first - _as_array(gd["S_next"])).max() > 0.1
