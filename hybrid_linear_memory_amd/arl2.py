@@ -1,0 +1,225 @@
+"""Thin ctypes binding of libarl2.so (include/arl2.h).
+
+Argument marshalling only: every step of the hybrid attention layer runs in
+the library's HIP kernels. torch provides device memory (tensor data
+pointers) and streams (torch.cuda.current_stream() unless one is given).
+There is no fallback: if libarl2.so is missing or fails to load, importing
+this module raises.
+
+Function names mirror the C entry points without the ``arl2_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch  # loaded first: libarl2 then binds to the HIP runtime torch carries
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so")
+
+F32 = 0
+BF16 = 1
+OP_READ, OP_CLEAN_PASS, OP_COMMIT, OP_STATE_COMMIT = 0, 1, 2, 3
+
+STATUS_NAMES = {
+    0: "ARL2_OK", 1: "ARL2_E_NULL", 2: "ARL2_E_SHAPE", 3: "ARL2_E_DTYPE",
+    4: "ARL2_E_LAYOUT", 5: "ARL2_E_ALIAS", 6: "ARL2_E_WORKSPACE", 7: "ARL2_E_HIP",
+}
+
+# Every entry point the header declares, with its ctypes signature.
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("B", _i32), ("H", _i32), ("T", _i32), ("D", _i32),
+                ("act_dtype", _i32), ("softmax_scale", ctypes.c_float)]
+
+
+_SP = ctypes.POINTER(_Shape)
+SIGNATURES = {
+    "arl2_feature_map": (_i32, [_SP, _vp, _vp, _vp, _i32, _vp]),
+    "arl2_intra_attn": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp]),
+    "arl2_inter_read": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp]),
+    "arl2_state_commit": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "arl2_read": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "arl2_commit": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "arl2_clean_pass": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _sz, _vp]),
+    "arl2_fullkv_attn": (_i32, [_SP, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "arl2_workspace_bytes": (_sz, [_SP, _i32]),
+    "arl2_status_string": (ctypes.c_char_p, [_i32]),
+    "arl2_last_error": (ctypes.c_char_p, []),
+    "arl2_abi_version": (_i32, []),
+}
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m hybrid_linear_memory_amd.build` "
+            "(the ARL2 path has no non-HIP fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+class Arl2Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, f"status {status}")
+        super().__init__(f"{self.name}: {detail}")
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    B: int
+    H: int
+    T: int
+    D: int
+    act_dtype: int = BF16
+    softmax_scale: float = 0.0
+
+    def c(self) -> _Shape:
+        return _Shape(self.B, self.H, self.T, self.D, self.act_dtype, self.softmax_scale)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.act_dtype == BF16 else torch.float32
+
+
+def _check(status: int):
+    if status != 0:
+        raise Arl2Error(status, _lib.arl2_last_error().decode())
+
+
+def _ptr(t, name, dtype=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def abi_version() -> int:
+    return _lib.arl2_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.arl2_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _lib.arl2_last_error().decode()
+
+
+def workspace_bytes(shape: Shape, op: int) -> int:
+    return _lib.arl2_workspace_bytes(ctypes.byref(shape.c()), op)
+
+
+def alloc_workspace(shape: Shape, op: int, device=None) -> torch.Tensor:
+    n = max(workspace_bytes(shape, op), 16)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def feature_map(shape: Shape, x, phi, x_out, normalize_rows=False, stream=None):
+    a = shape.torch_dtype
+    _check(_lib.arl2_feature_map(ctypes.byref(shape.c()), _ptr(x, "x", a), _ptr(phi, "phi", a),
+                                 _ptr(x_out, "x_out", a), int(bool(normalize_rows)),
+                                 _stream(stream)))
+
+
+def intra_attn(shape: Shape, q, k, v, o_intra, stream=None):
+    a = shape.torch_dtype
+    _check(_lib.arl2_intra_attn(ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a),
+                                _ptr(v, "v", a), _ptr(o_intra, "o_intra", a), _stream(stream)))
+
+
+def inter_read(shape: Shape, q_prime, S, o_intra, o, stream=None):
+    a = shape.torch_dtype
+    _check(_lib.arl2_inter_read(ctypes.byref(shape.c()), _ptr(q_prime, "q_prime", a),
+                                _ptr(S, "S", torch.float32),
+                                _ptr(o_intra, "o_intra", a, optional=True), _ptr(o, "o", a),
+                                _stream(stream)))
+
+
+def state_commit(shape: Shape, k_prime, v_prime, beta, alpha, S_prev, S_next, ws, stream=None):
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_state_commit(
+        ctypes.byref(shape.c()), _ptr(k_prime, "k_prime", a), _ptr(v_prime, "v_prime", a),
+        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
+        _ptr(S_next, "S_next", f), _ptr(ws, "ws", optional=True),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def read(shape: Shape, q, k, v, phi_q, S, o, o_intra=None, o_inter=None, ws=None, stream=None):
+    a = shape.torch_dtype
+    _check(_lib.arl2_read(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(phi_q, "phi_q", a), _ptr(S, "S", torch.float32), _ptr(o, "o", a),
+        _ptr(o_intra, "o_intra", a, optional=True), _ptr(o_inter, "o_inter", a, optional=True),
+        _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(stream)))
+
+
+def commit(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, stream=None):
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_commit(
+        ctypes.byref(shape.c()), _ptr(k, "k", a), _ptr(v, "v", a), _ptr(phi_k, "phi_k", a),
+        _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f), _ptr(alpha, "alpha", f),
+        _ptr(S_prev, "S_prev", f), _ptr(S_next, "S_next", f), _ptr(ws, "ws", optional=True),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def clean_pass(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, S_next, o,
+               o_intra=None, o_inter=None, ws=None, stream=None):
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_clean_pass(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(phi_q, "phi_q", a), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
+        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
+        _ptr(S_next, "S_next", f), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
+        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def fullkv_attn(shape: Shape, q, k_cache, v_cache, n_kv: int, o, stream=None):
+    a = shape.torch_dtype
+    cap = k_cache.shape[2]
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache shapes differ")
+    _check(_lib.arl2_fullkv_attn(ctypes.byref(shape.c()), _ptr(q, "q", a),
+                                 _ptr(k_cache, "k_cache", a), _ptr(v_cache, "v_cache", a),
+                                 int(n_kv), int(cap), _ptr(o, "o", a), _stream(stream)))
+
+
+def raw_call(name: str, *args):
+    """Call an entry point with raw ctypes arguments and return its status
+    (used by the ABI error-path tests)."""
+    return getattr(_lib, name)(*args)
+
+
+def c_shape(shape: Shape):
+    return ctypes.byref(shape.c())

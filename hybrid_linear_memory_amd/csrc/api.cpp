@@ -1,0 +1,392 @@
+// C-ABI layer of libarl2: host-side validation, workspace carving and
+// dispatch to the HIP kernels. Every check runs before anything is enqueued;
+// on error nothing is launched and the detail text is kept per thread.
+//
+// The pass-level calls follow "Attend Locally, Remember Linearly" technical
+// summary §2.2: a denoising read takes the state as const; only the clean
+// pass (or arl2_commit) writes the next state, into a separate buffer.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/arl2.h"
+#include "arl2_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+arl2_status fail(arl2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+arl2_status ok() {
+  g_err.clear();
+  return ARL2_OK;
+}
+
+arl2_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ARL2_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+arl2_status check_shape(const arl2_shape* sh, arl2::Dims* d) {
+  if (!sh) return fail(ARL2_E_NULL, "shape is NULL");
+  if (sh->act_dtype != ARL2_F32 && sh->act_dtype != ARL2_BF16)
+    return fail(ARL2_E_DTYPE, "act_dtype %d is neither ARL2_F32 (0) nor ARL2_BF16 (1)",
+                sh->act_dtype);
+  if (sh->B < 1 || sh->H < 1 || sh->T < 1)
+    return fail(ARL2_E_SHAPE, "B, H, T must be >= 1 (got %d, %d, %d)", sh->B, sh->H, sh->T);
+  const bool bf16 = sh->act_dtype == ARL2_BF16;
+  if (bf16 && sh->D != 128)
+    return fail(ARL2_E_SHAPE, "bf16 activations need D = 128 (got %d)", sh->D);
+  if (!bf16 && sh->D != 16 && sh->D != 32 && sh->D != 64 && sh->D != 128)
+    return fail(ARL2_E_SHAPE, "float32 activations need D in {16, 32, 64, 128} (got %d)", sh->D);
+  const double elems = (double)sh->B * sh->H * sh->T * sh->D;
+  if (elems >= 2147483648.0)
+    return fail(ARL2_E_SHAPE, "B*H*T*D = %.0f exceeds 2^31 - 1", elems);
+  if (!(sh->softmax_scale >= 0.f) || isinf(sh->softmax_scale))
+    return fail(ARL2_E_SHAPE, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(D))");
+  d->B = sh->B;
+  d->H = sh->H;
+  d->T = sh->T;
+  d->D = sh->D;
+  d->bf16 = bf16;
+  d->scale = sh->softmax_scale > 0.f ? sh->softmax_scale : 1.0f / sqrtf((float)sh->D);
+  return ARL2_OK;
+}
+
+#define REQUIRE_PTR(p)                                                          \
+  do {                                                                          \
+    if (!(p)) return fail(ARL2_E_NULL, "argument '%s' is NULL", #p);            \
+    if (!aligned16(p)) return fail(ARL2_E_LAYOUT, "argument '%s' is not 16-byte aligned", #p); \
+  } while (0)
+
+#define OPTIONAL_PTR(p)                                                         \
+  do {                                                                          \
+    if ((p) && !aligned16(p))                                                   \
+      return fail(ARL2_E_LAYOUT, "argument '%s' is not 16-byte aligned", #p);   \
+  } while (0)
+
+size_t state_bytes(const arl2::Dims& d) { return (size_t)d.B * d.H * d.D * d.D * sizeof(float); }
+size_t phi_bytes(const arl2::Dims& d) { return (size_t)d.H * d.D * d.D * (d.bf16 ? 2 : 4); }
+size_t commit_ws(const arl2::Dims& d) {
+  return arl2::use_mfma(d) ? arl2::mfma_state_commit_ws_bytes(d)
+                           : arl2::generic_state_commit_ws_bytes(d);
+}
+
+size_t ws_read(const arl2::Dims& d) { return 2 * arl2::round_up(arl2::act_bytes(d), 256); }
+size_t ws_commit(const arl2::Dims& d) {
+  return 2 * arl2::round_up(arl2::act_bytes(d), 256) + arl2::round_up(commit_ws(d), 256);
+}
+
+arl2_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return ARL2_OK;
+  if (!ws) return fail(ARL2_E_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (!aligned16(ws)) return fail(ARL2_E_LAYOUT, "workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(ARL2_E_WORKSPACE, "workspace has %zu bytes, %zu are needed", ws_bytes, need);
+  return ARL2_OK;
+}
+
+// ---------------------------------------------------------------- dispatch
+hipError_t run_feature_map(const arl2::Dims& d, const void* x, const void* phi, void* out,
+                           bool norm, hipStream_t s) {
+  return arl2::use_mfma(d) ? arl2::mfma_feature_map(d, x, phi, out, norm, s)
+                           : arl2::generic_feature_map(d, x, phi, out, norm, s);
+}
+hipError_t run_attention(const arl2::Dims& d, const void* q, const void* k, const void* v,
+                         void* o, int64_t n_kv, int64_t cap, hipStream_t s) {
+  return arl2::use_mfma(d) ? arl2::mfma_attention(d, q, k, v, o, n_kv, cap, s)
+                           : arl2::generic_attention(d, q, k, v, o, n_kv, cap, s);
+}
+hipError_t run_inter_read(const arl2::Dims& d, const void* qp, const float* S, const void* oi,
+                          void* o, void* oe, hipStream_t s) {
+  return arl2::use_mfma(d) ? arl2::mfma_inter_read(d, qp, S, oi, o, oe, s)
+                           : arl2::generic_inter_read(d, qp, S, oi, o, oe, s);
+}
+hipError_t run_state_commit(const arl2::Dims& d, const void* kp, const void* vp,
+                            const float* beta, const float* alpha, const float* Sp, float* Sn,
+                            void* ws, hipStream_t s) {
+  return arl2::use_mfma(d) ? arl2::mfma_state_commit(d, kp, vp, beta, alpha, Sp, Sn, ws, s)
+                           : arl2::generic_state_commit(d, kp, vp, beta, alpha, Sp, Sn, ws, s);
+}
+
+// Read = feature map of Q, intra attention, inter read + combine.
+arl2_status do_read(const arl2::Dims& d, const void* q, const void* k, const void* v,
+                    const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
+                    void* ws, hipStream_t s) {
+  const size_t ab = arl2::round_up(arl2::act_bytes(d), 256);
+  char* w = static_cast<char*>(ws);
+  void* q_prime = w;
+  void* oi = o_intra ? o_intra : (void*)(w + ab);
+  hipError_t e = run_feature_map(d, q, phi_q, q_prime, false, s);
+  if (e != hipSuccess) return hip_status(e, "feature map (phi_q)");
+  e = run_attention(d, q, k, v, oi, d.T, d.T, s);
+  if (e != hipSuccess) return hip_status(e, "intra-frame attention");
+  e = run_inter_read(d, q_prime, S, oi, o, o_inter, s);
+  if (e != hipSuccess) return hip_status(e, "inter-frame read");
+  return ok();
+}
+
+arl2_status do_commit(const arl2::Dims& d, const void* k, const void* v, const void* phi_k,
+                      const void* phi_v, const float* beta, const float* alpha,
+                      const float* S_prev, float* S_next, void* ws, hipStream_t s) {
+  const size_t ab = arl2::round_up(arl2::act_bytes(d), 256);
+  char* w = static_cast<char*>(ws);
+  void* kp = w;
+  void* vp = w + ab;
+  void* cws = w + 2 * ab;
+  hipError_t e = run_feature_map(d, k, phi_k, kp, true, s);
+  if (e != hipSuccess) return hip_status(e, "feature map (phi_k)");
+  e = run_feature_map(d, v, phi_v, vp, false, s);
+  if (e != hipSuccess) return hip_status(e, "feature map (phi_v)");
+  e = run_state_commit(d, kp, vp, beta, alpha, S_prev, S_next, cws, s);
+  if (e != hipSuccess) return hip_status(e, "state commit");
+  return ok();
+}
+
+arl2_status check_state_pair(const arl2::Dims& d, const float* S_prev, const float* S_next) {
+  if (overlap({S_prev, state_bytes(d)}, {S_next, state_bytes(d)}))
+    return fail(ARL2_E_ALIAS, "S_prev and S_next overlap; the state must be double-buffered");
+  return ARL2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t arl2_abi_version(void) { return ARL2_ABI_VERSION; }
+
+const char* arl2_last_error(void) { return g_err.c_str(); }
+
+const char* arl2_status_string(arl2_status st) {
+  switch (st) {
+    case ARL2_OK: return "ARL2_OK";
+    case ARL2_E_NULL: return "ARL2_E_NULL";
+    case ARL2_E_SHAPE: return "ARL2_E_SHAPE";
+    case ARL2_E_DTYPE: return "ARL2_E_DTYPE";
+    case ARL2_E_LAYOUT: return "ARL2_E_LAYOUT";
+    case ARL2_E_ALIAS: return "ARL2_E_ALIAS";
+    case ARL2_E_WORKSPACE: return "ARL2_E_WORKSPACE";
+    case ARL2_E_HIP: return "ARL2_E_HIP";
+  }
+  return "ARL2_E_UNKNOWN";
+}
+
+size_t arl2_workspace_bytes(const arl2_shape* shape, int32_t op) {
+  arl2::Dims d;
+  if (check_shape(shape, &d) != ARL2_OK) return 0;
+  switch (op) {
+    case ARL2_OP_READ: return ws_read(d);
+    case ARL2_OP_COMMIT: return ws_commit(d);
+    case ARL2_OP_CLEAN_PASS: return std::max(ws_read(d), ws_commit(d));
+    case ARL2_OP_STATE_COMMIT: return commit_ws(d);
+    default: return 0;
+  }
+}
+
+arl2_status arl2_feature_map(const arl2_shape* shape, const void* x, const void* phi, void* x_out,
+                             int32_t normalize_rows, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(phi);
+  REQUIRE_PTR(x_out);
+  const size_t ab = arl2::act_bytes(d);
+  if (overlap({x, ab}, {x_out, ab}) || overlap({phi, phi_bytes(d)}, {x_out, ab}))
+    return fail(ARL2_E_ALIAS, "x_out overlaps an input");
+  return hip_status(run_feature_map(d, x, phi, x_out, normalize_rows != 0, (hipStream_t)stream),
+                    "feature map");
+}
+
+arl2_status arl2_intra_attn(const arl2_shape* shape, const void* q, const void* k, const void* v,
+                            void* o_intra, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o_intra);
+  const size_t ab = arl2::act_bytes(d);
+  if (overlap({q, ab}, {o_intra, ab}) || overlap({k, ab}, {o_intra, ab}) ||
+      overlap({v, ab}, {o_intra, ab}))
+    return fail(ARL2_E_ALIAS, "o_intra overlaps an input");
+  return hip_status(run_attention(d, q, k, v, o_intra, d.T, d.T, (hipStream_t)stream),
+                    "intra-frame attention");
+}
+
+arl2_status arl2_inter_read(const arl2_shape* shape, const void* q_prime, const float* S,
+                            const void* o_intra, void* o, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q_prime);
+  REQUIRE_PTR(S);
+  REQUIRE_PTR(o);
+  OPTIONAL_PTR(o_intra);
+  const size_t ab = arl2::act_bytes(d);
+  if (overlap({q_prime, ab}, {o, ab}) || overlap({S, state_bytes(d)}, {o, ab}))
+    return fail(ARL2_E_ALIAS, "o overlaps q_prime or S");
+  if (o_intra && o_intra != o && overlap({o_intra, ab}, {o, ab}))
+    return fail(ARL2_E_ALIAS, "o partially overlaps o_intra (only o == o_intra is allowed)");
+  return hip_status(run_inter_read(d, q_prime, S, o_intra, o, nullptr, (hipStream_t)stream),
+                    "inter-frame read");
+}
+
+arl2_status arl2_state_commit(const arl2_shape* shape, const void* k_prime, const void* v_prime,
+                              const float* beta, const float* alpha, const float* S_prev,
+                              float* S_next, void* ws, size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(k_prime);
+  REQUIRE_PTR(v_prime);
+  REQUIRE_PTR(beta);
+  REQUIRE_PTR(alpha);
+  REQUIRE_PTR(S_prev);
+  REQUIRE_PTR(S_next);
+  if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, commit_ws(d))) != ARL2_OK) return st;
+  return hip_status(run_state_commit(d, k_prime, v_prime, beta, alpha, S_prev, S_next, ws,
+                                     (hipStream_t)stream),
+                    "state commit");
+}
+
+arl2_status arl2_read(const arl2_shape* shape, const void* q, const void* k, const void* v,
+                      const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
+                      void* ws, size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_q);
+  REQUIRE_PTR(S);
+  REQUIRE_PTR(o);
+  OPTIONAL_PTR(o_intra);
+  OPTIONAL_PTR(o_inter);
+  if ((st = check_ws(ws, ws_bytes, ws_read(d))) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d);
+  const Range outs[3] = {{o, ab}, {o_intra, ab}, {o_inter, ab}};
+  const Range ins[6] = {{q, ab}, {k, ab}, {v, ab}, {phi_q, phi_bytes(d)}, {S, state_bytes(d)},
+                        {ws, ws_read(d)}};
+  for (const Range& a : outs) {
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
+  }
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return fail(ARL2_E_ALIAS, "outputs o, o_intra, o_inter overlap");
+  return do_read(d, q, k, v, phi_q, S, o, o_intra, o_inter, ws, (hipStream_t)stream);
+}
+
+arl2_status arl2_commit(const arl2_shape* shape, const void* k, const void* v, const void* phi_k,
+                        const void* phi_v, const float* beta, const float* alpha,
+                        const float* S_prev, float* S_next, void* ws, size_t ws_bytes,
+                        void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_k);
+  REQUIRE_PTR(phi_v);
+  REQUIRE_PTR(beta);
+  REQUIRE_PTR(alpha);
+  REQUIRE_PTR(S_prev);
+  REQUIRE_PTR(S_next);
+  if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, ws_commit(d))) != ARL2_OK) return st;
+  if (overlap({S_next, state_bytes(d)}, {ws, ws_commit(d)}))
+    return fail(ARL2_E_ALIAS, "S_next overlaps the workspace");
+  return do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, (hipStream_t)stream);
+}
+
+arl2_status arl2_clean_pass(const arl2_shape* shape, const void* q, const void* k, const void* v,
+                            const void* phi_q, const void* phi_k, const void* phi_v,
+                            const float* beta, const float* alpha, const float* S_prev,
+                            float* S_next, void* o, void* o_intra, void* o_inter, void* ws,
+                            size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_q);
+  REQUIRE_PTR(phi_k);
+  REQUIRE_PTR(phi_v);
+  REQUIRE_PTR(beta);
+  REQUIRE_PTR(alpha);
+  REQUIRE_PTR(S_prev);
+  REQUIRE_PTR(S_next);
+  REQUIRE_PTR(o);
+  OPTIONAL_PTR(o_intra);
+  OPTIONAL_PTR(o_inter);
+  if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
+  const size_t need = std::max(ws_read(d), ws_commit(d));
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d);
+  const Range outs[4] = {{o, ab}, {o_intra, ab}, {o_inter, ab}, {S_next, state_bytes(d)}};
+  const Range ins[7] = {{q, ab}, {k, ab}, {v, ab}, {phi_q, phi_bytes(d)}, {S_prev, state_bytes(d)},
+                        {ws, need}, {beta, (size_t)d.B * d.H * d.T * 4}};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ARL2_E_ALIAS, "two outputs overlap");
+  st = do_read(d, q, k, v, phi_q, S_prev, o, o_intra, o_inter, ws, (hipStream_t)stream);
+  if (st != ARL2_OK) return st;
+  return do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, (hipStream_t)stream);
+}
+
+arl2_status arl2_fullkv_attn(const arl2_shape* shape, const void* q, const void* k_cache,
+                             const void* v_cache, int64_t n_kv, int64_t kv_capacity, void* o,
+                             void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(o);
+  if (n_kv < 1 || n_kv > kv_capacity)
+    return fail(ARL2_E_SHAPE, "need 1 <= n_kv <= kv_capacity (got %lld, %lld)", (long long)n_kv,
+                (long long)kv_capacity);
+  const double cache_elems = (double)d.B * d.H * (double)kv_capacity * d.D;
+  if (cache_elems >= 2147483648.0 * 64.0 || n_kv >= 2147483647LL)
+    return fail(ARL2_E_SHAPE, "KV cache too large");
+  const size_t ab = arl2::act_bytes(d);
+  const size_t cb = (size_t)cache_elems * (d.bf16 ? 2 : 4);
+  if (overlap({o, ab}, {q, ab}) || overlap({o, ab}, {k_cache, cb}) || overlap({o, ab}, {v_cache, cb}))
+    return fail(ARL2_E_ALIAS, "o overlaps an input");
+  return hip_status(run_attention(d, q, k_cache, v_cache, o, n_kv, kv_capacity, (hipStream_t)stream),
+                    "full-KV attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+"""Streaming driver of one ARL2 hybrid attention layer.
+
+Holds the double-buffered fp32 state, the feature maps and the workspace,
+and enforces the pass order of the memory-state management rules
+("Attend Locally, Remember Linearly" technical summary, §2.2): within a
+frame every denoising read and the clean pass see the same S_{N-1}; the
+state is written once, by the clean pass, into the other buffer; the
+buffers swap and the frame index advances only then.
+
+The pass order itself (``PassSequencer``) is plain host logic with no device
+dependency.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import arl2
+
+
+class SequenceError(RuntimeError):
+    """A pass was issued out of the read* -> clean pass order."""
+
+
+class PassSequencer:
+    """Frame / pass bookkeeping. With ``n_denoise`` set (strict mode) each
+    frame must have exactly that many reads before its clean pass."""
+
+    def __init__(self, n_denoise: int | None = None):
+        if n_denoise is not None and n_denoise < 0:
+            raise ValueError("n_denoise must be >= 0")
+        self.n_denoise = n_denoise
+        self.frame = 0
+        self.reads = 0
+
+    def before_read(self):
+        if self.n_denoise is not None and self.reads >= self.n_denoise:
+            raise SequenceError(
+                f"frame {self.frame}: {self.reads} denoising reads already issued; the next "
+                "pass of this frame must be the clean pass")
+
+    def after_read(self):
+        self.reads += 1
+
+    def before_clean_pass(self):
+        if self.n_denoise is not None and self.reads != self.n_denoise:
+            raise SequenceError(
+                f"frame {self.frame}: clean pass after {self.reads} reads, expected "
+                f"{self.n_denoise}")
+
+    def after_clean_pass(self):
+        self.frame += 1
+        self.reads = 0
+
+    def restore(self, frame: int):
+        if frame < 0:
+            raise ValueError("frame index must be >= 0")
+        self.frame = frame
+        self.reads = 0
+
+
+class Arl2Layer:
+    """One hybrid attention layer over B streams on the current device.
+
+    phi_q, phi_k, phi_v: [H, D, D] tensors of the activation dtype.
+    """
+
+    def __init__(self, shape: arl2.Shape, phi_q, phi_k, phi_v, n_denoise: int | None = None,
+                 device=None):
+        self.shape = shape
+        self.device = torch.device(device or "cuda")
+        dt = shape.torch_dtype
+        self.phi = [p.to(self.device, dt).contiguous() for p in (phi_q, phi_k, phi_v)]
+        st = (shape.B, shape.H, shape.D, shape.D)
+        self._S = [torch.zeros(st, dtype=torch.float32, device=self.device),
+                   torch.zeros(st, dtype=torch.float32, device=self.device)]
+        self._cur = 0
+        self.ws = arl2.alloc_workspace(shape, arl2.OP_CLEAN_PASS, self.device)
+        self.seq = PassSequencer(n_denoise)
+
+    @property
+    def S(self) -> torch.Tensor:
+        """The state every pass of the current frame reads (S_{N-1})."""
+        return self._S[self._cur]
+
+    @property
+    def frame(self) -> int:
+        return self.seq.frame
+
+    def reset(self):
+        for s in self._S:
+            s.zero_()
+        self._cur = 0
+        self.seq.restore(0)
+
+    def new_output(self):
+        s = self.shape
+        return torch.empty((s.B, s.H, s.T, s.D), dtype=s.torch_dtype, device=self.device)
+
+    def read(self, q, k, v, o=None, o_intra=None, o_inter=None, stream=None):
+        """Denoising read against S_{N-1}; never writes the state."""
+        self.seq.before_read()
+        o = self.new_output() if o is None else o
+        arl2.read(self.shape, q, k, v, self.phi[0], self.S, o, o_intra, o_inter, self.ws, stream)
+        self.seq.after_read()
+        return o
+
+    def clean_pass(self, q, k, v, beta, alpha, o=None, o_intra=None, o_inter=None, stream=None):
+        """Read against S_{N-1}, commit S_N into the other buffer, swap."""
+        self.seq.before_clean_pass()
+        o = self.new_output() if o is None else o
+        nxt = 1 - self._cur
+        arl2.clean_pass(self.shape, q, k, v, self.phi[0], self.phi[1], self.phi[2], beta, alpha,
+                        self._S[self._cur], self._S[nxt], o, o_intra, o_inter, self.ws, stream)
+        self._cur = nxt
+        self.seq.after_clean_pass()
+        return o
+
+    def commit(self, k, v, beta, alpha, stream=None):
+        """State write of the clean pass without its read."""
+        self.seq.before_clean_pass()
+        nxt = 1 - self._cur
+        arl2.commit(self.shape, k, v, self.phi[1], self.phi[2], beta, alpha, self._S[self._cur],
+                    self._S[nxt], self.ws, stream)
+        self._cur = nxt
+        self.seq.after_clean_pass()
+
+    # checkpoint / resume: the whole cross-frame memory is S plus the frame index
+    def state_dict(self) -> dict:
+        return {"S": self.S.detach().clone(), "frame": self.frame}
+
+    def load_state_dict(self, sd: dict):
+        S = sd["S"]
+        if tuple(S.shape) != tuple(self.S.shape) or S.dtype != torch.float32:
+            raise ValueError("state shape or dtype mismatch")
+        self._S[0].copy_(S)
+        self._cur = 0
+        self.seq.restore(int(sd["frame"]))

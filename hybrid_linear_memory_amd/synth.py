@@ -72,9 +72,10 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32
     holding exactly bf16-representable values. Finite inputs only."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (u << 16).astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    # finite values never carry out of 32 bits here (max 0xFF7FFFFF + 0x8000)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(x.shape)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -98,8 +99,8 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
 
 
 def _unit_rows(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (x / np.maximum(n, 1e-30)).astype(np.float32)
+    n = np.sqrt(np.einsum("...i,...i->...", x, x))[..., None]
+    return (x / np.maximum(n, np.float32(1e-30))).astype(np.float32)
 
 
 def qkv(w: Workload, frame: int, pass_: int, rows=None):

@@ -1,0 +1,206 @@
+/*
+ * arl2.h - C ABI of the ARL2 hybrid attention step on MI355X (gfx950).
+ *
+ * The step follows "Attend Locally, Remember Linearly: Linear Attention as
+ * Cross-Frame Memory for Autoregressive Video Diffusion" (Li, Shah, Shang),
+ * technical summary on gist.science (Chinese, Portuguese and French versions):
+ *
+ *   §2.1 Hybrid attention decomposition
+ *        intra-frame branch: bidirectional softmax over the frame's T tokens
+ *          with the frozen Q, K, V (no mask);
+ *        inter-frame branch: per-head grouped 1x1 feature maps
+ *          Q' = Q Phi_q[h], K' = rownorm(K Phi_k[h]), V' = V Phi_v[h];
+ *          read   O_inter = Q' S_{N-1};
+ *          update S_N = alpha_N S_{N-1} + K'^T diag(beta_N) (V' - K' S_{N-1}).
+ *   §2.2 Memory state management
+ *        frame-level access: every token of frame N reads the same S_{N-1};
+ *        clean-pass update: denoising reads never write S; S is written once
+ *          per frame, after the frame's clean pass.
+ *
+ * The printed update lacks the transpose on the first K'; the row-vector read
+ * Q'S fixes it as written above. The residual uses the undecayed S_{N-1} as
+ * printed; alpha is one scalar per (video, head, frame), beta one per (video,
+ * head, token); K' rows are normalised as x / max(||x||_2, 1e-12) after
+ * Phi_k; O = O_intra + O_inter.
+ *
+ * Conventions shared by every entry point
+ *   - Activations Q, K, V, Q', K', V', O are contiguous [B, H, T, D] tensors
+ *     of the shape's act_dtype (float32 or bfloat16), D contiguous.
+ *   - Phi maps are contiguous [H, D_in, D_out] of act_dtype: X' = X Phi[h].
+ *   - The state S is always float32, contiguous [B, H, D_k, D_v], D_v
+ *     contiguous.
+ *   - beta is float32 [B, H, T]; alpha is float32 [B, H].
+ *   - Every pointer is a device pointer, 16-byte aligned, owned by the
+ *     caller. The library allocates no memory and keeps no state between
+ *     calls. Scratch memory comes from the caller's workspace (ws, ws_bytes),
+ *     sized by arl2_workspace_bytes().
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued asynchronously on it; stream order alone makes a
+ *     read of frame N+1 see the S_N written by frame N's commit.
+ *   - Each call validates every argument on the host first; on error nothing
+ *     is enqueued and a status other than ARL2_OK is returned, with detail
+ *     text available from arl2_last_error() on the calling thread.
+ *     ARL2_E_HIP reports a launch failure (hipGetLastError after launch).
+ *   - Supported shapes: act_dtype ARL2_F32 with D in {16, 32, 64, 128};
+ *     ARL2_BF16 with D = 128. Any T >= 1, B >= 1, H >= 1 with
+ *     B*H*T*D < 2^31.
+ *   - Results are deterministic: no floating-point atomics, fixed reduction
+ *     order, so identical inputs give bit-identical outputs.
+ */
+#ifndef ARL2_H
+#define ARL2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ARL2_ABI_VERSION 1
+
+typedef enum arl2_status {
+  ARL2_OK = 0,
+  ARL2_E_NULL = 1,      /* a required pointer is NULL                        */
+  ARL2_E_SHAPE = 2,     /* B, H, T, D out of range or unsupported            */
+  ARL2_E_DTYPE = 3,     /* act_dtype not ARL2_F32 / ARL2_BF16                */
+  ARL2_E_LAYOUT = 4,    /* a pointer is not 16-byte aligned                  */
+  ARL2_E_ALIAS = 5,     /* S_prev and S_next overlap, or an output aliases   */
+  ARL2_E_WORKSPACE = 6, /* workspace NULL or smaller than required           */
+  ARL2_E_HIP = 7        /* the HIP runtime reported an error                 */
+} arl2_status;
+
+typedef enum arl2_dtype { ARL2_F32 = 0, ARL2_BF16 = 1 } arl2_dtype;
+
+typedef struct arl2_shape {
+  int32_t B;            /* videos (independent streams)                      */
+  int32_t H;            /* heads                                             */
+  int32_t T;            /* tokens per frame                                  */
+  int32_t D;            /* head dimension (d_k = d_v = D)                    */
+  int32_t act_dtype;    /* arl2_dtype of activations and Phi maps            */
+  float softmax_scale;  /* intra-frame softmax temperature; 0 => 1/sqrt(D)   */
+} arl2_shape;
+
+/* Operations whose workspace size arl2_workspace_bytes() reports. */
+typedef enum arl2_op {
+  ARL2_OP_READ = 0,
+  ARL2_OP_CLEAN_PASS = 1,
+  ARL2_OP_COMMIT = 2,
+  ARL2_OP_STATE_COMMIT = 3
+} arl2_op;
+
+/* ------------------------------------------------------------------------
+ * Steps of the hybrid attention layer, one entry point each.
+ * ------------------------------------------------------------------------ */
+
+/* Per-head grouped 1x1 feature map (§2.1, "adaptation" of Q, K, V):
+ *   x_out[b,h,t,:] = x[b,h,t,:] Phi[h]          (Phi [H, D_in, D_out])
+ * and, when normalize_rows != 0, each output row is divided by
+ * max(||row||_2, 1e-12) (the key map). x and x_out are [B,H,T,D] act_dtype
+ * and must not overlap. */
+arl2_status arl2_feature_map(const arl2_shape* shape, const void* x,
+                             const void* phi, void* x_out,
+                             int32_t normalize_rows, void* stream);
+
+/* Intra-frame branch (§2.1): per (b,h), the bidirectional softmax over the
+ * frame's T tokens, no mask:
+ *   o_intra = softmax(Q K^T * scale) V
+ * q, k, v, o_intra are [B,H,T,D] act_dtype; o_intra must not overlap the
+ * inputs. Accumulation in float32. */
+arl2_status arl2_intra_attn(const arl2_shape* shape, const void* q,
+                            const void* k, const void* v, void* o_intra,
+                            void* stream);
+
+/* Inter-frame read (§2.1 output equation, §2.2 frame-level access):
+ *   o = o_intra + Q' S            (o = Q' S when o_intra is NULL)
+ * q_prime, o_intra and o are [B,H,T,D] act_dtype; S is float32 [B,H,D,D]
+ * and is only read. o may equal o_intra (in-place add); it must not overlap
+ * q_prime or S. */
+arl2_status arl2_inter_read(const arl2_shape* shape, const void* q_prime,
+                            const float* S, const void* o_intra, void* o,
+                            void* stream);
+
+/* State commit (§2.1 update equation), from already mapped K', V':
+ *   R      = V' - K' S_prev
+ *   S_next = alpha * S_prev + K'^T diag(beta) R
+ * k_prime, v_prime [B,H,T,D] act_dtype (K' rows expected unit length),
+ * beta float32 [B,H,T], alpha float32 [B,H], S_prev and S_next float32
+ * [B,H,D,D]. S_prev and S_next must not overlap (ARL2_E_ALIAS): the state is
+ * double-buffered and S_prev is left untouched. Needs
+ * arl2_workspace_bytes(shape, ARL2_OP_STATE_COMMIT) bytes of workspace. */
+arl2_status arl2_state_commit(const arl2_shape* shape, const void* k_prime,
+                              const void* v_prime, const float* beta,
+                              const float* alpha, const float* S_prev,
+                              float* S_next, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * The pass-level API: denoising reads versus the clean-pass commit (§2.2).
+ * ------------------------------------------------------------------------ */
+
+/* Denoising-step read: Q' = Q Phi_q[h], o_intra = softmax(QK^T*scale)V,
+ * o = o_intra + Q' S. S is const: a read never writes the state.
+ * o_intra and o_inter are optional extra outputs (NULL to skip) holding the
+ * two branches separately. Needs arl2_workspace_bytes(shape, ARL2_OP_READ). */
+arl2_status arl2_read(const arl2_shape* shape, const void* q, const void* k,
+                      const void* v, const void* phi_q, const float* S,
+                      void* o, void* o_intra, void* o_inter, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Commit only (the clean pass's state write without its read):
+ * K' = rownorm(K Phi_k[h]), V' = V Phi_v[h], then arl2_state_commit.
+ * Needs arl2_workspace_bytes(shape, ARL2_OP_COMMIT). */
+arl2_status arl2_commit(const arl2_shape* shape, const void* k, const void* v,
+                        const void* phi_k, const void* phi_v,
+                        const float* beta, const float* alpha,
+                        const float* S_prev, float* S_next, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Clean pass: the read of arl2_read against S_prev, then the commit of
+ * arl2_commit from the same K, V into S_next. Needs
+ * arl2_workspace_bytes(shape, ARL2_OP_CLEAN_PASS). */
+arl2_status arl2_clean_pass(const arl2_shape* shape, const void* q,
+                            const void* k, const void* v, const void* phi_q,
+                            const void* phi_k, const void* phi_v,
+                            const float* beta, const float* alpha,
+                            const float* S_prev, float* S_next, void* o,
+                            void* o_intra, void* o_inter, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Comparator: the cross-frame softmax over a growing KV cache that the
+ * recurrent state replaces (§1 of the summary: the cache grows with every
+ * generated block).
+ * ------------------------------------------------------------------------ */
+
+/* o[b,h,t,:] = softmax(q[b,h,t,:] K_c^T * scale) V_c over the first n_kv
+ * cached tokens of head (b,h). q, o: [B,H,T,D] act_dtype; k_cache, v_cache:
+ * [B,H,kv_capacity,D] act_dtype; 1 <= n_kv <= kv_capacity. The caller appends
+ * each frame's keys and values to the cache. */
+arl2_status arl2_fullkv_attn(const arl2_shape* shape, const void* q,
+                             const void* k_cache, const void* v_cache,
+                             int64_t n_kv, int64_t kv_capacity, void* o,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * Support calls.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes needed by `op` (an arl2_op) for this shape; 0 for an
+ * invalid shape or op. */
+size_t arl2_workspace_bytes(const arl2_shape* shape, int32_t op);
+
+/* Static text naming a status code. */
+const char* arl2_status_string(arl2_status status);
+
+/* Detail text of the last error on the calling thread ("" if none). */
+const char* arl2_last_error(void);
+
+/* ARL2_ABI_VERSION of the built library. */
+int32_t arl2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARL2_H */

@@ -1,0 +1,124 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point
+that include/arl2.h declares, and rejects bad arguments before launching
+anything. None of these calls reaches the GPU (validation fails first), so
+they run without one. Also covers the pass sequencer's host logic."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arl2.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(arl2_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def arl2():
+    from hybrid_linear_memory_amd import arl2 as mod
+    return mod
+
+
+def test_every_declared_symbol_is_exported(arl2):
+    names = _declared()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(arl2._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in arl2.h but not exported"
+    assert set(names) == set(arl2.SIGNATURES), "binding signatures out of sync with arl2.h"
+
+
+def test_version_and_status_strings(arl2):
+    assert arl2.abi_version() == 1
+    for code, name in arl2.STATUS_NAMES.items():
+        assert arl2.status_string(code) == name
+    assert arl2.status_string(99) == "ARL2_E_UNKNOWN"
+
+
+def test_workspace_sizes(arl2):
+    s = arl2.Shape(1, 12, 1560, 128, arl2.BF16)
+    act = 1 * 12 * 1560 * 128 * 2
+    assert arl2.workspace_bytes(s, arl2.OP_READ) >= 2 * act
+    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) >= 2 * act
+    assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS) == max(
+        arl2.workspace_bytes(s, arl2.OP_READ), arl2.workspace_bytes(s, arl2.OP_COMMIT))
+    assert arl2.workspace_bytes(s, 17) == 0
+    assert arl2.workspace_bytes(arl2.Shape(0, 1, 1, 128), arl2.OP_READ) == 0
+    f = arl2.Shape(1, 1, 64, 16, arl2.F32)
+    assert arl2.workspace_bytes(f, arl2.OP_STATE_COMMIT) == 64 * 16 * 4
+
+
+A = 1 << 20     # fake, 16-byte aligned "device" addresses: validation fails before any use
+B = 2 << 20
+
+
+def _st(arl2, name, *args):
+    return arl2.raw_call(name, *args)
+
+
+def test_null_shape_dtype_layout_errors(arl2):
+    good = arl2.Shape(1, 2, 64, 128, arl2.BF16)
+    cs = arl2.c_shape
+    assert _st(arl2, "arl2_intra_attn", None, A, A, A, B, None) == 1
+    assert _st(arl2, "arl2_intra_attn", cs(good), None, A, A, B, None) == 1
+    assert "'q'" in arl2.last_error()
+    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, 64, arl2.BF16)), A, A, A, B,
+               None) == 2
+    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 0, 128, arl2.BF16)), A, A, A, B,
+               None) == 2
+    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, 48, arl2.F32)), A, A, A, B,
+               None) == 2
+    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, 128, 7)), A, A, A, B, None) == 3
+    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, 128, arl2.BF16, -1.0)), A, A, A,
+               B, None) == 2
+    assert _st(arl2, "arl2_intra_attn", cs(good), A + 2, A, A, B, None) == 4
+    assert _st(arl2, "arl2_intra_attn", cs(good), A, A, A, A + 64, None) == 5
+    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(4096, 64, 4096, 128)), A, A, A, B,
+               None) == 2
+
+
+def test_alias_and_workspace_errors(arl2):
+    s = arl2.Shape(1, 2, 64, 128, arl2.BF16)
+    cs = arl2.c_shape
+    S1, S2, WS = 8 << 20, 16 << 20, 32 << 20
+    need = arl2.workspace_bytes(s, arl2.OP_COMMIT)
+    # S_prev == S_next
+    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S1, WS, need, None) == 5
+    # overlapping by one element
+    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S1 + 16, WS, need, None) == 5
+    # workspace missing / too small
+    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S2, None, 0, None) == 6
+    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S2, WS, need - 1, None) == 6
+    assert "needed" in arl2.last_error()
+    # read outputs overlapping inputs
+    rneed = arl2.workspace_bytes(s, arl2.OP_READ)
+    assert _st(arl2, "arl2_read", cs(s), A, B, B, B, S1, A, None, None, WS, rneed, None) == 5
+    # fullkv: n_kv beyond capacity
+    assert _st(arl2, "arl2_fullkv_attn", cs(s), A, B, S1, 200, 100, WS, None) == 2
+
+
+def test_sequencer_host_logic():
+    from hybrid_linear_memory_amd.layer import PassSequencer, SequenceError
+    seq = PassSequencer(n_denoise=2)
+    for f in range(3):
+        seq.before_read(); seq.after_read()
+        seq.before_read(); seq.after_read()
+        with pytest.raises(SequenceError):
+            seq.before_read()
+        seq.before_clean_pass(); seq.after_clean_pass()
+        assert seq.frame == f + 1
+    with pytest.raises(SequenceError):
+        seq.before_clean_pass()          # clean pass before the frame's reads
+    seq.restore(7)
+    assert seq.frame == 7 and seq.reads == 0
+    free = PassSequencer(None)
+    free.before_clean_pass(); free.after_clean_pass()
+    for _ in range(10):
+        free.before_read(); free.after_read()
+    with pytest.raises(ValueError):
+        PassSequencer(-1)

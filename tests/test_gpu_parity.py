@@ -1,0 +1,179 @@
+"""Parity of the HIP path (through the C-ABI) with the fp64 oracle.
+
+Tolerance: max |gpu - oracle| <= 1e-4 * max|oracle| for float32 workloads and
+<= 2e-2 * max|oracle| for bf16 workloads, per tensor (each output of each
+compared pass, the state after every commit). Inputs come from the seeded
+generator, identical on both sides (bf16 values upcast exactly by the oracle).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (TOL, assert_close, dev, dev32, host, lockstep_rollout, log,
+                         shape_of)
+from hybrid_linear_memory_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import hybrid_linear_memory_amd.arl2  # noqa: F401  (fails loudly if not built)
+
+
+def _w(dtype, B, H, T, D, frames=2, n_denoise=1):
+    base = synth.WORKLOADS[0] if dtype == "f32" else synth.WORKLOADS[1]
+    return base.replace(B=B, H=H, T=T, D=D, frames=frames, n_denoise=n_denoise)
+
+
+STEP_CASES = [
+    ("f32", 1, 1, 64, 16), ("f32", 2, 3, 100, 32), ("f32", 1, 2, 37, 64), ("f32", 1, 2, 130, 128),
+    ("f32", 1, 1, 1, 16),
+    ("bf16", 1, 2, 200, 128), ("bf16", 2, 3, 1, 128), ("bf16", 1, 1, 37, 128),
+    ("bf16", 1, 2, 513, 128), ("bf16", 1, 12, 1560, 128),
+]
+
+
+def _ids(c):
+    return "{}-B{}H{}T{}D{}".format(*c)
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
+@pytest.mark.parametrize("normalize", [False, True])
+def test_feature_map(case, normalize):
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"feature_map {_ids(case)} normalize={normalize}")
+    x, _, _ = synth.qkv(w, 0, 0)
+    phi = synth.phi_maps(w)[1]
+    out = dev(np.zeros_like(x), w.dtype)
+    arl2.feature_map(shape_of(w), dev(x, w.dtype), dev(phi, w.dtype), out, normalize)
+    ref = oracle.feature_map(x, phi)
+    if normalize:
+        ref = oracle.l2_normalize_rows(ref)
+    assert_close(host(out), ref, TOL[w.dtype], "feature map")
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
+@pytest.mark.parametrize("stress", [False, True])
+def test_intra_attn(case, stress):
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"intra_attn {_ids(case)} stress={stress}")
+    q, k, v = synth.stress_qkv(w, 0, 1) if stress else synth.qkv(w, 0, 1)
+    o = dev(np.zeros_like(q), w.dtype)
+    arl2.intra_attn(shape_of(w), dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), o)
+    rows = slice(None) if w.T <= 600 else np.r_[0:40, 700:740, w.T - 40:w.T]
+    ref = oracle.intra_attention(q[:, :, rows], k, v)
+    assert_close(host(o)[:, :, rows], ref, TOL[w.dtype], "o_intra")
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
+def test_inter_read(case):
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"inter_read {_ids(case)}")
+    qp, oi, _ = synth.qkv(w, 1, 0)
+    g = np.random.default_rng(5)
+    S = (g.standard_normal((w.B, w.H, w.D, w.D)) * 0.05).astype(np.float32)
+    o = dev(np.zeros_like(qp), w.dtype)
+    arl2.inter_read(shape_of(w), dev(qp, w.dtype), dev32(S), dev(oi, w.dtype), o)
+    ref = oi.astype(np.float64) + oracle.inter_read(qp, S)
+    assert_close(host(o), ref, TOL[w.dtype], "o")
+    # without o_intra, and in place (o == o_intra)
+    o2 = dev(np.zeros_like(qp), w.dtype)
+    arl2.inter_read(shape_of(w), dev(qp, w.dtype), dev32(S), None, o2)
+    assert_close(host(o2), oracle.inter_read(qp, S), TOL[w.dtype], "o_inter only")
+    o3 = dev(oi, w.dtype)
+    arl2.inter_read(shape_of(w), dev(qp, w.dtype), dev32(S), o3, o3)
+    assert_close(host(o3), ref, TOL[w.dtype], "in place")
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
+def test_state_commit(case):
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"state_commit {_ids(case)}")
+    k, v = synth.kv(w, 0, 0)                      # unit rows, cast to the activation type
+    beta, alpha = synth.gates(w, 0)
+    g = np.random.default_rng(6)
+    S = (g.standard_normal((w.B, w.H, w.D, w.D)) * 0.05).astype(np.float32)
+    Sn = dev32(np.zeros_like(S))
+    sh = shape_of(w)
+    ws = arl2.alloc_workspace(sh, arl2.OP_STATE_COMMIT)
+    arl2.state_commit(sh, dev(k, w.dtype), dev(v, w.dtype), dev32(beta), dev32(alpha), dev32(S),
+                      Sn, ws)
+    ref = oracle.state_commit(k, v, beta, alpha, S)
+    assert_close(host(Sn), ref, TOL[w.dtype], "S_next")
+
+
+def test_rollout_tiny_fp32_all_passes():
+    """Workload 0: every pass of every frame, every row, and the state."""
+    w = synth.WORKLOADS[0]
+    log("rollout tiny fp32")
+    worst = lockstep_rollout(w, read_frames=set(range(w.frames)))
+    log(f"worst relative errors {worst}")
+
+
+def _rows(T):
+    return np.unique(np.r_[0:16, T // 2 - 8:T // 2 + 8, T - 16:T])
+
+
+def test_rollout_wan13b_layer():
+    """Workload 1 (1 x 12 x 128, T = 1560, 21 frames, 4 reads + clean pass):
+    state after every commit; every output of every pass on frames 0, 1, 10,
+    20 on sampled rows (head, middle, ragged tail)."""
+    w = synth.WORKLOADS[1]
+    log("rollout wan13b layer")
+    worst = lockstep_rollout(w, read_frames={0, 1, 10, 20}, row_sample=_rows(w.T))
+    log(f"worst relative errors {worst}")
+
+
+def test_rollout_long_240_frames():
+    """Workload 2: 240 frames; state after every commit, outputs on 3 frames."""
+    w = synth.WORKLOADS[2]
+    log("rollout long 240 frames")
+    worst = lockstep_rollout(w, read_frames={0, 120, 239}, row_sample=_rows(w.T))
+    log(f"worst relative errors {worst}")
+
+
+def test_rollout_batched_streams():
+    """Workload 3: 8 independent videos."""
+    w = synth.WORKLOADS[3]
+    log("rollout batched streams")
+    worst = lockstep_rollout(w, read_frames={0, 20}, row_sample=_rows(w.T))
+    log(f"worst relative errors {worst}")
+
+
+def test_rollout_large_model():
+    """Workload 4: 40 heads, 81 frames."""
+    w = synth.WORKLOADS[4]
+    log("rollout large model")
+    worst = lockstep_rollout(w, read_frames={0, 40, 80}, row_sample=_rows(w.T))
+    log(f"worst relative errors {worst}")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_fullkv_comparator(dtype, D):
+    """The full-KV comparator equals softmax over every cached key (three
+    frames in a larger cache, ragged total)."""
+    import torch
+    from hybrid_linear_memory_amd import arl2
+    T = 300 if dtype == "bf16" else 70
+    w = _w(dtype, 1, 2, T, D)
+    log(f"fullkv {dtype} D={D}")
+    frames = [synth.qkv(w, f, 0) for f in range(3)]
+    cap = 4 * T + 5
+    kc = torch.zeros((1, 2, cap, D), dtype=shape_of(w).torch_dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    for f, (_, k, v) in enumerate(frames):
+        kc[:, :, f * T:(f + 1) * T] = dev(k, dtype)
+        vc[:, :, f * T:(f + 1) * T] = dev(v, dtype)
+    q = frames[2][0]
+    o = dev(np.zeros_like(q), dtype)
+    arl2.fullkv_attn(shape_of(w), dev(q, dtype), kc, vc, 3 * T, o)
+    K = np.concatenate([f[1] for f in frames], 2)
+    V = np.concatenate([f[2] for f in frames], 2)
+    assert_close(host(o), oracle.fullkv_attention(q, K, V), TOL[dtype], "fullkv")
