@@ -1,0 +1,413 @@
+#!/usr/bin/env python3
+"""Throughput of the ARL2 hybrid attention layer on one MI355X.
+
+A step is one frame of the streaming loop of the Wan-1.3B-shaped layer
+(1 video x 12 heads x 128, T = 1560 tokens per frame, bf16 activations, fp32
+state): 4 denoising reads and the clean pass (its read plus the state commit),
+i.e. every step of the hot path: feature maps, intra-frame softmax, inter-frame
+read, combine, state commit. Inputs are seeded synthetic tensors resident in
+HBM before timing starts (a pool of frames is cycled); the state carries over
+from frame to frame. By default each frame's launches are replayed from a HIP
+graph.
+
+Printed (one JSON line): frames/s (value) and tokens/s, the roofline of the
+dominant kernel (intra-frame attention, bf16 MFMA) measured with HIP events on
+the launch stream, per-kernel times, the fp64 CPU oracle timed on this host on
+a bounded sample, and the flatness of per-frame time and memory over a long
+rollout beside the full-KV-cache softmax comparator.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_MFMA = 2.5e15        # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12              # HBM3E, B/s
+COMMIT_BYTES_PER_HEAD = None   # filled from the shape: 2*T*D*2 + 4*T + 2*D*D*4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed frames")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed frames")
+    ap.add_argument("--pool", type=int, default=4, help="distinct resident input frames")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly, no HIP graph")
+    ap.add_argument("--kernel-iters", type=int, default=50)
+    ap.add_argument("--rollout-frames", type=int, default=240)
+    ap.add_argument("--skip-rollout", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hybrid_linear_memory_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+
+        from hybrid_linear_memory_amd import arl2, synth
+        from hybrid_linear_memory_amd.layer import Arl2Layer
+
+        self.torch, self.arl2, self.synth = torch, arl2, synth
+        self.args = args
+        self.w = synth.WORKLOADS[1]
+        w = self.w
+        self.shape = arl2.Shape(w.B, w.H, w.T, w.D, arl2.BF16)
+        self.stream = torch.cuda.current_stream()
+        bf = torch.bfloat16
+
+        def dev(x, dt=bf):
+            return torch.from_numpy(x).to("cuda").to(dt).contiguous()
+
+        self.dev = dev
+        phis = synth.phi_maps(w)
+        self.layer = Arl2Layer(self.shape, *[dev(p) for p in phis])
+        # pool of resident frames: passes[p] = (q, k, v), plus gates
+        self.pool = []
+        for f in range(args.pool):
+            passes = [tuple(dev(x) for x in synth.qkv(w, f, p)) for p in range(w.passes)]
+            beta, alpha = synth.gates(w, f)
+            self.pool.append((passes, dev(beta, torch.float32), dev(alpha, torch.float32)))
+        self.out = [self.layer.new_output() for _ in range(w.passes)]
+        torch.cuda.synchronize()
+
+    def frame(self, i):
+        passes, beta, alpha = self.pool[i % len(self.pool)]
+        L = self.layer
+        for p in range(self.w.n_denoise):
+            L.read(*passes[p], o=self.out[p])
+        L.clean_pass(*passes[-1], beta, alpha, o=self.out[-1])
+
+    def run_frames(self, n_frames, start=0):
+        for i in range(n_frames):
+            self.frame(start + i)
+
+    def make_graphs(self):
+        """One graph per pair of pool frames: the state ping-pongs between
+        the layer's two buffers, so a pair returns it to the same buffer."""
+        torch = self.torch
+        assert len(self.pool) % 2 == 0
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(0, len(self.pool), 2):
+                self.layer.seq.restore(self.layer.frame)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    self.frame(i)
+                    self.frame(i + 1)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        return graphs
+
+    def timed(self, steps, warmup, use_graph):
+        torch = self.torch
+        if use_graph:
+            graphs = self.make_graphs()
+            n_pairs = (steps + 1) // 2
+            for i in range(max(1, warmup // 2)):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            w0 = time.perf_counter()
+            for i in range(n_pairs):
+                graphs[i % len(graphs)].replay()
+            t1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - w0
+            frames = 2 * n_pairs
+        else:
+            self.run_frames(warmup)
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            w0 = time.perf_counter()
+            self.run_frames(steps)
+            t1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - w0
+            frames = steps
+        gpu_ms = t0.elapsed_time(t1)
+        return frames, max(gpu_ms / 1e3, wall), gpu_ms / 1e3
+
+    def kernel_times(self, iters):
+        """Average launch duration of each kernel of the path, from HIP events
+        around back-to-back launches on the launch stream."""
+        torch, arl2, sh = self.torch, self.arl2, self.shape
+        passes, beta, alpha = self.pool[0]
+        q, k, v = passes[-1]
+        L = self.layer
+        tmp = [L.new_output() for _ in range(3)]
+        S_next = torch.empty_like(L.S)
+        ws = arl2.alloc_workspace(sh, arl2.OP_STATE_COMMIT)
+        arl2.feature_map(sh, k, L.phi[1], tmp[1], True)
+        arl2.feature_map(sh, v, L.phi[2], tmp[2], False)
+        cases = {
+            "intra_attn": lambda: arl2.intra_attn(sh, q, k, v, tmp[0]),
+            "feature_map": lambda: arl2.feature_map(sh, q, L.phi[0], tmp[0], False),
+            "inter_read": lambda: arl2.inter_read(sh, tmp[1], L.S, tmp[2], tmp[0]),
+            "state_commit": lambda: arl2.state_commit(sh, tmp[1], tmp[2], beta, alpha, L.S,
+                                                      S_next, ws),
+        }
+        res = {}
+        for name, fn in cases.items():
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / iters * 1e3   # microseconds
+        return res
+
+    def copy_calibration(self, nbytes=1 << 30):
+        """A plain device copy of known size, so rocprofv3 counter runs of this
+        script can scale FETCH_SIZE / WRITE_SIZE against known bytes."""
+        torch = self.torch
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        del a, b
+        return {"bytes_read": nbytes, "bytes_written": nbytes,
+                "GBps": 2 * nbytes / (ms / 1e3) / 1e9}
+
+    def rollout_flatness(self, n_frames):
+        """Per-frame time and device memory over a long rollout of the layer,
+        beside the full-KV-cache softmax comparator at the same shapes."""
+        import numpy as np
+        torch, arl2, sh, w = self.torch, self.arl2, self.shape, self.w
+        L = self.layer
+        L.reset()
+        torch.cuda.synchronize()
+        mem0 = torch.cuda.memory_allocated()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_frames + 1)]
+        ev[0].record()
+        for f in range(n_frames):
+            self.frame(f)
+            ev[f + 1].record()
+        torch.cuda.synchronize()
+        mem1 = torch.cuda.memory_allocated()
+        t_arl2 = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n_frames)])
+        # comparator: the cache grows by one frame of K and V per clean pass
+        cap = n_frames * w.T
+        kc = torch.empty((w.B, w.H, cap, w.D), dtype=torch.bfloat16, device="cuda")
+        vc = torch.empty_like(kc)
+        o = L.new_output()
+        ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(n_frames + 1)]
+        mem_cache = []
+        ev2[0].record()
+        for f in range(n_frames):
+            passes, _, _ = self.pool[f % len(self.pool)]
+            sl = slice(f * w.T, (f + 1) * w.T)
+            for (q, k, v) in passes:
+                kc[:, :, sl].copy_(k)
+                vc[:, :, sl].copy_(v)
+                arl2.fullkv_attn(sh, q, kc, vc, (f + 1) * w.T, o)
+            ev2[f + 1].record()
+            mem_cache.append(2 * (f + 1) * w.T * w.D * 2 * w.B * w.H)
+        torch.cuda.synchronize()
+        t_full = np.array([ev2[i].elapsed_time(ev2[i + 1]) for i in range(n_frames)])
+        del kc, vc
+        lo = min(20, n_frames // 4)
+        x = np.arange(lo, n_frames)
+        slope = float(np.polyfit(x, t_arl2[lo:], 1)[0]) if n_frames - lo > 2 else 0.0
+        slope_full = float(np.polyfit(x, t_full[lo:], 1)[0]) if n_frames - lo > 2 else 0.0
+        mean = float(t_arl2[lo:].mean())
+        return {
+            "frames": n_frames,
+            "arl2_ms_per_frame_mean": mean,
+            "arl2_ms_first_last": [float(t_arl2[lo]), float(t_arl2[-1])],
+            "arl2_slope_ms_per_frame": slope,
+            "arl2_flat": abs(slope * n_frames) < 0.05 * mean,
+            "arl2_state_bytes": 2 * w.B * w.H * w.D * w.D * 4,
+            "arl2_device_mem_delta_bytes": int(mem1 - mem0),
+            "fullkv_ms_first_last": [float(t_full[lo]), float(t_full[-1])],
+            "fullkv_slope_ms_per_frame": slope_full,
+            "fullkv_cache_bytes_last": int(mem_cache[-1]),
+            "fullkv_total_ms": float(t_full.sum()),
+            "arl2_total_ms": float(t_arl2.sum()),
+            "speedup_total": float(t_full.sum() / t_arl2.sum()),
+        }
+
+
+def cpu_baseline(seconds: float):
+    """The fp64 oracle, as it stands, on this host: whole frames of the same
+    workload (4 reads + clean pass, all heads) until ~`seconds` of CPU time,
+    at least 2 frames. Input generation is outside the timed part."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    from hybrid_linear_memory_amd import synth
+    cores = len(os.sched_getaffinity(0))
+    w = synth.WORKLOADS[1]
+    phis = synth.phi_maps(w)
+    with threadpool_limits(limits=cores):
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+        S = np.zeros((w.B, w.H, w.D, w.D))
+        frames, busy = 0, 0.0
+        est = None
+        while frames < 2 or (busy < seconds and frames < w.frames):
+            fr = synth.oracle_frame(w, frames)
+            t0 = time.perf_counter()
+            _, states = oracle.rollout([fr], *phis, S0=S)
+            busy += time.perf_counter() - t0
+            S = states[-1]
+            frames += 1
+            est = busy / frames
+            if busy + est > 2.5 * seconds:
+                break
+    threads = max((n for _, n in blas if n), default=1)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": frames / busy,
+        "unit": "frames/s",
+        "cores": int(min(threads, cores)),
+        "kind": "oracle",
+        "sample": f"{frames} whole frames of the 1x12x128, T=1560 layer (4 reads + clean pass "
+                  f"each), fp64 numpy, {busy:.1f} s",
+        "tokens_per_s": frames * w.T / busy,
+        "cpu_model": cpu_model,
+        "blas": blas,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer shards "
+              "by (video, head) with no exchange inside the step, and this build measures "
+              "the one-GPU share.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print(f"[bench] building pool of {args.pool} frames", file=sys.stderr, flush=True)
+    b = Bench(args)
+    w = b.w
+    calib = b.copy_calibration()
+    print("[bench] timing frames", file=sys.stderr, flush=True)
+    frames, secs, gpu_secs = b.timed(args.steps, args.warmup, use_graph=not args.no_graph)
+    fps = w.B * frames / secs
+    eager = None
+    if not args.no_graph:
+        ef, es, _ = b.timed(max(20, args.steps // 4), 5, use_graph=False)
+        eager = w.B * ef / es
+    print("[bench] timing kernels", file=sys.stderr, flush=True)
+    kt = b.kernel_times(args.kernel_iters)
+    flops = 4.0 * w.T * w.T * w.D * w.B * w.H
+    attn_s = kt["intra_attn"] * 1e-6
+    achieved = flops / attn_s
+    src_hash = kernel_source_hash()
+    traffic = load_traffic("attn_mfma_k", src_hash)
+    commit_bytes = w.B * w.H * (2 * w.T * w.D * 2 + 4 * w.T + 2 * w.D * w.D * 4)
+    kernels = {
+        "intra_attn_us": kt["intra_attn"],
+        "feature_map_us": kt["feature_map"],
+        "inter_read_us": kt["inter_read"],
+        "state_commit_us": kt["state_commit"],
+        "state_commit_hbm_frac": commit_bytes / (kt["state_commit"] * 1e-6) / PEAK_HBM,
+        "state_commit_algorithmic_bytes": commit_bytes,
+        "copy_calibration": calib,
+    }
+    flat = None
+    if not args.skip_rollout:
+        print("[bench] rollout flatness", file=sys.stderr, flush=True)
+        flat = b.rollout_flatness(args.rollout_frames)
+    cpu = None
+    if not args.skip_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.cpu_seconds)
+    res = {
+        "metric": "ARL2 layer frames/sec (12x128 heads, 1560 tok/frame)",
+        "value": fps,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": frames,
+        "warmup": args.warmup,
+        "ms_per_step": secs / frames * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "wan13b_layer: 1 video x 12 heads x d128, T=1560 tokens/frame, "
+                               "4 denoising reads + clean pass (read + state commit) per frame, "
+                               "bf16 activations, fp32 state",
+                   "B": w.B, "H": w.H, "D": w.D, "T": w.T, "passes_per_frame": w.passes,
+                   "hip_graph": not args.no_graph},
+        "tokens_per_s": fps * w.T,
+        "frames_per_s_eager": eager,
+        "roofline": {"bound": "mfma", "kernel": "attn_mfma_k (intra-frame softmax)",
+                     "achieved": achieved / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_MFMA,
+                     "traffic": traffic, "flop_per_launch": flops,
+                     "avg_launch_us": kt["intra_attn"]},
+        "kernels": kernels,
+        "flatness": flat,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -71,47 +71,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
 }
 
-// ===========================================================================
-// Intra-frame softmax attention (and the full-KV comparator).
-//
-// One workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
-// queries. Keys stream through LDS in tiles of 64 (K row-major, V transposed),
-// double-buffered. Scores are computed transposed, S^T = K Q^T, so that each
-// lane holds one query's scores: the row max and sum need one cross-half
-// exchange, and P^T feeds O^T = V^T P^T directly from registers.
-// ===========================================================================
-constexpr int AQ = 128;               // queries per workgroup
-constexpr int AKT = 64;               // keys per tile
-constexpr int AKS = HD + 8;           // K row stride in LDS (bf16)
-constexpr int AVS = AKT + 8;          // V^T row stride in LDS (bf16)
-constexpr int AKBUF = AKT * AKS;
-constexpr int AVBUF = HD * AVS;
-constexpr int ASTAGE = AKBUF + AVBUF;
-
-struct KVRegs {
-  uint4 k[4];
-  uint4 v[4];
-};
-
-__device__ __forceinline__ void attn_load_tile(KVRegs& r, const __bf16* kh, const __bf16* vh,
-                                               int k0, int n_kv, int tid) {
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int c = tid + 256 * it;
-    const int row = c >> 4, col = (c & 15) * 8;
-    const int key = k0 + row;
-    r.k[it] = key < n_kv ? *reinterpret_cast<const uint4*>(kh + (size_t)key * HD + col)
-                         : make_uint4(0, 0, 0, 0);
-  }
-  const int kg = tid & 15, dg = tid >> 4;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int key = k0 + 4 * kg + rr;
-    r.v[rr] = key < n_kv ? *reinterpret_cast<const uint4*>(vh + (size_t)key * HD + 8 * dg)
-                         : make_uint4(0, 0, 0, 0);
-  }
-}
-
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 
@@ -121,137 +80,287 @@ __device__ __forceinline__ uint32_t elem(const uint4& x, int e) {
   return (e & 1) ? hi16(w) : lo16(w);
 }
 
-__device__ __forceinline__ void attn_store_tile(const KVRegs& r, __bf16* stage, int tid) {
-  __bf16* Ks = stage;
-  __bf16* Vt = stage + AKBUF;
+// ===========================================================================
+// Intra-frame softmax attention (and the full-KV comparator).
+//
+// One workgroup = 4 waves = 128 query rows of one (b, h). The keys are dealt
+// to two streams (even and odd tiles of 64 keys); waves 0-1 run stream A and
+// waves 2-3 stream B, each wave owning 64 queries (two 32-query MFMA blocks
+// that share every K and V operand read). The two streams' partial results
+// are merged through LDS at the end.
+//
+// Tiles reach LDS by direct global->LDS loads (no staging registers), stored
+// unpadded with an XOR swizzle of their 16-byte chunks so that the operand
+// reads are free of bank conflicts: K is read as the A operand of
+// S^T = K Q^T with plain 16-byte reads, V is kept row-major and read as the
+// A operand of O^T = V^T P^T with transposing reads (ds_read_b64_tr_b16). Each
+// lane therefore holds one query's scores, the row max and sum need a single
+// cross-half exchange, and P^T feeds the second product straight from
+// registers.
+//
+// Pipeline per iteration j: loads of K(j+2), V(j+1) are in flight while the
+// matrix cores compute the scores of tile j+1 and the vector ALUs run the
+// softmax of tile j, then O^T += V(j)^T P(j)^T. The running maximum moves
+// lazily: exponents use a reference maximum that is raised only when a score
+// exceeds it by more than 2^8 in the exponent, so the accumulator rescale is
+// rare.
+// ===========================================================================
+constexpr int AQ = 128;                     // queries per workgroup
+constexpr int AKT = 64;                     // keys per tile
+constexpr int TILE_B = AKT * HD * 2;        // one 64 x 128 bf16 tile (16 KB)
+constexpr float kLazyLimit = 8.0f;          // log2 of the largest unscaled p
+// LDS: [stream][K buf 0, K buf 1, V buf 0, V buf 1] = 2 x 4 x 16 KB
+constexpr int ALDS = 2 * 4 * TILE_B;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz_k(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
+
+// Wave-wide load of one 64 x 128 bf16 tile (rows clamped to the last key:
+// their scores are masked and their values meet p = 0) into `dst`, 16-byte
+// chunk p of row r holding global chunk p ^ swz(r).
+template <bool IS_V>
+__device__ __forceinline__ void tile_load(char* dst, const __bf16* src, int tile, int n_kv,
+                                          int lane) {
+  const int p = lane & 15;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int c = tid + 256 * it;
-    const int row = c >> 4, col = (c & 15) * 8;
-    *reinterpret_cast<uint4*>(Ks + row * AKS + col) = r.k[it];
-  }
-  const int kg = tid & 15, dg = tid >> 4;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint2 w;
-    w.x = elem(r.v[0], e) | (elem(r.v[1], e) << 16);
-    w.y = elem(r.v[2], e) | (elem(r.v[3], e) << 16);
-    *reinterpret_cast<uint2*>(Vt + (8 * dg + e) * AVS + 4 * kg) = w;
+  for (int i = 0; i < 16; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int key = min(tile * AKT + r, n_kv - 1);
+    const int c16 = p ^ (IS_V ? swz_v(r) : swz_k(r));
+    const __bf16* g = src + (size_t)key * HD + c16 * 8;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
   }
 }
 
-__global__ void __launch_bounds__(256)
+__device__ __forceinline__ bf16x8 k_operand(const char* Kb, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(Kb + row * 256 + ((chunk ^ swz_k(row)) << 4));
+}
+
+// A operand of O^T = V^T P^T for d-block db and keys kb*32 + 16*h2 + 8*cc + u
+// (u = 0..7) at column d = 32*db + (lane % 32), by two transposing reads.
+__device__ __forceinline__ bf16x8 v_operand(const char* Vb, int db, int kb, int cc, int lane) {
+  const int G = lane >> 4;
+  const int s = lane & 15, c = s >> 2, j = s & 3;
+  const int d = 32 * db + 16 * (G & 1) + 4 * j;
+  const int c16 = d >> 3, sub = (d & 7) * 2;
+  v4i16 r[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = kb * 32 + 16 * (G >> 1) + 8 * cc + 4 * half + c;
+    const char* a = Vb + row * 256 + ((c16 ^ swz_v(row)) << 4) + sub;
+    r[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
+  }
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, r[0]);
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, r[1]);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// max / sum of x over lanes l and l ^ 32.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct AttnState {
+  f32x16 acc[2][4];     // [query block][d block] of O^T
+  float m_ref[2];
+  float l[2];
+};
+
+// S^T for both query blocks: s[qi][kb][r] = q_qi . k[kb*32 + 16*h2 + r], masked
+// past `valid` keys.
+__device__ __forceinline__ void attn_scores(f32x16 s[2][2], const char* Kb, int lane,
+                                            const bf16x8 (&qreg)[2][8], int valid) {
+  const int n = lane & 31, h2 = lane >> 5;
+  const int krow = perm32(n);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[0][kb] = zero16();
+    s[1][kb] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8 a = k_operand(Kb, kb * 32 + krow, 2 * kc + h2);
+      s[0][kb] = mfma32(a, qreg[0][kc], s[0][kb]);
+      s[1][kb] = mfma32(a, qreg[1][kc], s[1][kb]);
+    }
+  }
+  if (valid < AKT) {
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 16 * h2 + r >= valid) s[qi][kb][r] = -INFINITY;
+  }
+}
+
+// Softmax of one tile against the lazily moved reference maximum, then
+// O^T += V^T P^T.
+__device__ __forceinline__ void attn_softmax_pv(AttnState& st, const f32x16 (&s)[2][2],
+                                                const char* Vb, int lane, float sl2) {
+  bf16x8 pb[2][2][2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qi][kb][r]);
+    mt = halves_max(mt);
+    if (__any((mt - st.m_ref[qi]) * sl2 > kLazyLimit)) {
+      const float m_new = fmaxf(st.m_ref[qi], mt);
+      const float corr = __builtin_amdgcn_exp2f((st.m_ref[qi] - m_new) * sl2);
+      st.m_ref[qi] = m_new;
+      st.l[qi] *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[qi][db][r] *= corr;
+    }
+    const float mc = st.m_ref[qi] * sl2;
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[qi][kb][r], sl2, -mc));
+        if (r & 1) ls1 += p; else ls0 += p;
+        pb[qi][kb][r >> 3][r & 7] = (__bf16)p;
+      }
+    st.l[qi] += ls0 + ls1;
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 a = v_operand(Vb, db, kb, cc, lane);
+        st.acc[0][db] = mfma32(a, pb[0][kb][cc], st.acc[0][db]);
+        st.acc[1][db] = mfma32(a, pb[1][kb][cc], st.acc[1][db]);
+      }
+}
+
+__global__ void __launch_bounds__(256, 1)
 attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
             long kv_cap, float sl2, int n_qblk) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * ASTAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[ALDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const long bh = blk / n_qblk;
   const int qblk = blk % n_qblk;
-  const int t = qblk * AQ + wave * 32 + n;
+  const int stream = wave >> 1;
+  const int tq0 = qblk * AQ + (wave & 1) * 64;
   const __bf16* kh = k + (size_t)bh * kv_cap * HD;
   const __bf16* vh = v + (size_t)bh * kv_cap * HD;
 
-  // Q^T as the B operand of S^T = K Q^T: column n = query t, k = head dim.
-  bf16x8 qreg[8];
-  {
-    const __bf16* qrow = q + ((size_t)bh * T + t) * HD + 8 * h2;
+  bf16x8 qreg[2][8];
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) qreg[kc] = t < T ? ld8(qrow + 16 * kc) : zero8();
+  for (int qi = 0; qi < 2; ++qi) {
+    const int t = tq0 + 32 * qi + n;
+    const __bf16* qrow = q + ((size_t)bh * T + min(t, T - 1)) * HD + 8 * h2;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) qreg[qi][kc] = t < T ? ld8(qrow + 16 * kc) : zero8();
   }
 
-  f32x16 acc[4];
+  AttnState st;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = zero16();
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qi = 0; qi < 2; ++qi) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.acc[qi][db] = zero16();
+    st.m_ref[qi] = -INFINITY;
+    st.l[qi] = 0.f;
+  }
 
+  // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s
   const int n_tiles = (n_kv + AKT - 1) / AKT;
-  KVRegs regs;
-  attn_load_tile(regs, kh, vh, 0, n_kv, tid);
-  attn_store_tile(regs, lds, tid);
-  __syncthreads();
+  const int iters = (n_tiles + 1) / 2;
+  const int my_cnt = (n_tiles - stream + 1) / 2;
+  // this wave loads region (wave & 1 ? V : K) of stream (wave >> 1)
+  const int ld_stream = wave >> 1;
+  const bool ld_v = wave & 1;
+  const int ld_cnt = (n_tiles - ld_stream + 1) / 2;
+  const __bf16* ld_src = ld_v ? vh : kh;
+  char* ld_base = lds + ld_stream * 4 * TILE_B + (ld_v ? 2 * TILE_B : 0);
+  char* Kbase = lds + stream * 4 * TILE_B;
+  char* Vbase = Kbase + 2 * TILE_B;
 
-  const int krow = perm32(n);
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int k0 = kt * AKT;
-    if (kt + 1 < n_tiles) attn_load_tile(regs, kh, vh, k0 + AKT, n_kv, tid);
-    const __bf16* Ks = lds + (kt & 1) * ASTAGE;
-    const __bf16* Vt = Ks + AKBUF;
-
-    // S^T tile: keys x queries, two 32-key halves.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-      const __bf16* kp = Ks + (kb * 32 + krow) * AKS + 8 * h2;
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) s[kb] = mfma32(ld8(kp + 16 * kc), qreg[kc], s[kb]);
+  auto issue = [&](int j) {   // local tile j of the wave's load region into buffer j & 1
+    if (j < ld_cnt) {
+      if (ld_v) tile_load<true>(ld_base + (j & 1) * TILE_B, ld_src, 2 * j + ld_stream, n_kv, lane);
+      else tile_load<false>(ld_base + (j & 1) * TILE_B, ld_src, 2 * j + ld_stream, n_kv, lane);
     }
-    if (k0 + AKT > n_kv) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (k0 + kb * 32 + 16 * h2 + r >= n_kv) s[kb][r] = -INFINITY;
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, swap_halves(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float corr = exp2f((m_run - m_new) * sl2);
-    const float mc = m_new * sl2;
-    m_run = m_new;
+  };
 
-    bf16x8 pb[2][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[kb][r], sl2, -mc));
-        lsum += p;
-        pb[kb][r >> 3][r & 7] = (__bf16)p;
-      }
-    l_run = fmaf(l_run, corr, lsum);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= corr;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const __bf16* vp = Vt + (32 * db + n) * AVS + 16 * h2;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          acc[db] = mfma32(ld8(vp + kb * 32 + 8 * cc), pb[kb][cc], acc[db]);
-    }
-
-    if (kt + 1 < n_tiles) attn_store_tile(regs, lds + ((kt + 1) & 1) * ASTAGE, tid);
+  // prologue: K(0), V(0)
+  issue(0);
+  for (int it = 0; it < iters; ++it) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    issue(it + 1);
+    if (it < my_cnt) {
+      f32x16 s[2][2];
+      attn_scores(s, Kbase + (it & 1) * TILE_B, lane, qreg, n_kv - (2 * it + stream) * AKT);
+      attn_softmax_pv(st, s, Vbase + (it & 1) * TILE_B, lane, sl2);
+    }
   }
 
-  const float l_tot = l_run + swap_halves(l_run);
-  const float inv = 1.f / l_tot;
-  if (t < T) {
-    __bf16* orow = o + ((size_t)bh * T + t) * HD + 4 * h2;
+  // merge stream B into stream A through LDS
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* ex = reinterpret_cast<float*>(lds) + (wave & 1) * (132 * 64);
+  if (stream == 1) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int qi = 0; qi < 2; ++qi) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 w;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(acc[db][4 * jj + i] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * jj) = w;
-      }
+        for (int r = 0; r < 16; ++r) ex[(qi * 64 + db * 16 + r) * 64 + lane] = st.acc[qi][db][r];
+      ex[(128 + qi) * 64 + lane] = st.m_ref[qi];
+      ex[(130 + qi) * 64 + lane] = st.l[qi];
+    }
+  }
+  __syncthreads();
+  if (stream == 1) return;
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const float mb = ex[(128 + qi) * 64 + lane];
+    const float lb = ex[(130 + qi) * 64 + lane];
+    const float m = fmaxf(st.m_ref[qi], mb);
+    const float fa = __builtin_amdgcn_exp2f((st.m_ref[qi] - m) * sl2);
+    const float fb = __builtin_amdgcn_exp2f((mb - m) * sl2);
+    const float inv = 1.f / halves_sum(st.l[qi] * fa + lb * fb);
+    const int t = tq0 + 32 * qi + n;
+    if (t < T) {
+      __bf16* orow = o + ((size_t)bh * T + t) * HD + 4 * h2;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          bf16x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * jj + i;
+            const float vb = ex[(qi * 64 + db * 16 + r) * 64 + lane];
+            w[i] = (__bf16)((st.acc[qi][db][r] * fa + vb * fb) * inv);
+          }
+          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * jj) = w;
+        }
+    }
   }
 }
 
