@@ -83,32 +83,32 @@ __device__ __forceinline__ uint32_t elem(const uint4& x, int e) {
 // ===========================================================================
 // Intra-frame softmax attention (and the full-KV comparator).
 //
-// One workgroup = 4 waves = 128 query rows of one (b, h). The keys are dealt
-// to two streams (even and odd tiles of 64 keys); waves 0-1 run stream A and
-// waves 2-3 stream B, each wave owning 64 queries (two 32-query MFMA blocks
-// that share every K and V operand read). The two streams' partial results
-// are merged through LDS at the end.
+// One workgroup = 8 waves = 128 query rows of one (b, h). The keys are dealt
+// to two streams (even and odd tiles of 64 keys); waves 0-3 run stream A and
+// waves 4-7 stream B, each wave owning 32 queries, so every SIMD holds one
+// wave of each stream and interleaves the softmax of one with the matrix
+// products of the other. The two streams' partial results are merged through
+// LDS at the end.
 //
 // Tiles reach LDS by direct global->LDS loads (no staging registers), stored
 // unpadded with an XOR swizzle of their 16-byte chunks so that the operand
 // reads are free of bank conflicts: K is read as the A operand of
-// S^T = K Q^T with plain 16-byte reads, V is kept row-major and read as the
+// S^T = K Q^T with plain 16-byte reads, V stays row-major and is read as the
 // A operand of O^T = V^T P^T with transposing reads (ds_read_b64_tr_b16). Each
 // lane therefore holds one query's scores, the row max and sum need a single
 // cross-half exchange, and P^T feeds the second product straight from
 // registers.
 //
-// Pipeline per iteration j: loads of K(j+2), V(j+1) are in flight while the
-// matrix cores compute the scores of tile j+1 and the vector ALUs run the
-// softmax of tile j, then O^T += V(j)^T P(j)^T. The running maximum moves
-// lazily: exponents use a reference maximum that is raised only when a score
-// exceeds it by more than 2^8 in the exponent, so the accumulator rescale is
-// rare.
+// Exponents are taken against a reference maximum fixed for the pass (the
+// first tile's row maximum), so the accumulators are never rescaled inside the
+// loop. If a later tile exceeds it by more than 2^kLazyLimit (never for
+// bounded inputs), the workgroup redoes the pass with the exact row maximum
+// seen in the first pass.
 // ===========================================================================
 constexpr int AQ = 128;                     // queries per workgroup
 constexpr int AKT = 64;                     // keys per tile
 constexpr int TILE_B = AKT * HD * 2;        // one 64 x 128 bf16 tile (16 KB)
-constexpr float kLazyLimit = 8.0f;          // log2 of the largest unscaled p
+constexpr float kLazyLimit = 64.0f;         // log2 of the largest unscaled p
 // LDS: [stream][K buf 0, K buf 1, V buf 0, V buf 1] = 2 x 4 x 16 KB
 constexpr int ALDS = 2 * 4 * TILE_B;
 
@@ -119,44 +119,40 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 
-// Wave-wide load of one 64 x 128 bf16 tile (rows clamped to the last key:
-// their scores are masked and their values meet p = 0) into `dst`, 16-byte
-// chunk p of row r holding global chunk p ^ swz(r).
+// Half-tile load by one wave: rows [32*half, 32*half + 32) of a 64 x 128 bf16
+// tile into `dst` (16-byte chunk p of row r holding global chunk p ^ swz(r)).
+// `off[v]` are the lane's byte offsets within 4 consecutive rows for the
+// swizzle variant v of the instruction; a tail tile clamps rows past the last
+// key to the last key (their scores are masked and their values meet p = 0).
 template <bool IS_V>
-__device__ __forceinline__ void tile_load(char* dst, const __bf16* src, int tile, int n_kv,
-                                          int lane) {
-  const int p = lane & 15;
+__device__ __forceinline__ void tile_load(char* dst, const char* tile_src, const int (&off)[4],
+                                          int half, int rows_valid, int lane) {
+  if (rows_valid >= AKT) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 4 * i + (lane >> 4);
-    const int key = min(tile * AKT + r, n_kv - 1);
-    const int c16 = p ^ (IS_V ? swz_v(r) : swz_k(r));
-    const __bf16* g = src + (size_t)key * HD + c16 * 8;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+    for (int ii = 0; ii < 8; ++ii) {
+      const int i = 8 * half + ii;
+      const int var = IS_V ? 0 : ((i & 1) | ((i >> 1) & 2));
+      const char* g = tile_src + i * 1024 + off[var];
+      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+    }
+  } else {
+    const int p = lane & 15;
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const int i = 8 * half + ii;
+      const int r = 4 * i + (lane >> 4);
+      const int rc = min(r, rows_valid - 1);
+      const int c16 = p ^ (IS_V ? swz_v(r) : swz_k(r));
+      const char* g = tile_src + rc * 256 + c16 * 16;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+    }
   }
 }
 
-__device__ __forceinline__ bf16x8 k_operand(const char* Kb, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(Kb + row * 256 + ((chunk ^ swz_k(row)) << 4));
-}
-
-// A operand of O^T = V^T P^T for d-block db and keys kb*32 + 16*h2 + 8*cc + u
-// (u = 0..7) at column d = 32*db + (lane % 32), by two transposing reads.
-__device__ __forceinline__ bf16x8 v_operand(const char* Vb, int db, int kb, int cc, int lane) {
-  const int G = lane >> 4;
-  const int s = lane & 15, c = s >> 2, j = s & 3;
-  const int d = 32 * db + 16 * (G & 1) + 4 * j;
-  const int c16 = d >> 3, sub = (d & 7) * 2;
-  v4i16 r[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int row = kb * 32 + 16 * (G >> 1) + 8 * cc + 4 * half + c;
-    const char* a = Vb + row * 256 + ((c16 ^ swz_v(row)) << 4) + sub;
-    r[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
-  }
-  const bf16x4 lo = __builtin_bit_cast(bf16x4, r[0]);
-  const bf16x4 hi = __builtin_bit_cast(bf16x4, r[1]);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+// Transposing read of 4 bf16 at a byte address in LDS.
+__device__ __forceinline__ bf16x4 tr_read(const char* a) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
+  return __builtin_bit_cast(bf16x4, r);
 }
 
 // max / sum of x over lanes l and l ^ 32.
@@ -171,196 +167,228 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-struct AttnState {
-  f32x16 acc[2][4];     // [query block][d block] of O^T
-  float m_ref[2];
-  float l[2];
+// Per-lane LDS byte offsets of the operand reads within a tile.
+//   K (A of S^T = K Q^T): lane row kb*32 + perm32(n), 16-byte chunk 2*kc + h2;
+//     kb adds 32 rows (8192 bytes), the swizzle does not depend on kb.
+//   V (A of O^T = V^T P^T, transposing read): source row
+//     kb*32 + 16*(G>>1) + 8*cc + 4*half + c and column 32*db + 16*(G&1) + 4*j,
+//     G = lane/16, c = (lane%16)/4, j = lane%4; kb, cc, half add 8192, 2048,
+//     1024 bytes, the swizzle depends only on c.
+struct AttnOffsets {
+  int k[8];
+  int v[4];
 };
 
-// S^T for both query blocks: s[qi][kb][r] = q_qi . k[kb*32 + 16*h2 + r], masked
-// past `valid` keys.
-__device__ __forceinline__ void attn_scores(f32x16 s[2][2], const char* Kb, int lane,
-                                            const bf16x8 (&qreg)[2][8], int valid) {
+__device__ __forceinline__ AttnOffsets attn_offsets(int lane) {
+  AttnOffsets o;
   const int n = lane & 31, h2 = lane >> 5;
   const int krow = perm32(n);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[0][kb] = zero16();
-    s[1][kb] = zero16();
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const bf16x8 a = k_operand(Kb, kb * 32 + krow, 2 * kc + h2);
-      s[0][kb] = mfma32(a, qreg[0][kc], s[0][kb]);
-      s[1][kb] = mfma32(a, qreg[1][kc], s[1][kb]);
-    }
-  }
-  if (valid < AKT) {
-#pragma unroll
-    for (int qi = 0; qi < 2; ++qi)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 16 * h2 + r >= valid) s[qi][kb][r] = -INFINITY;
-  }
-}
-
-// Softmax of one tile against the lazily moved reference maximum, then
-// O^T += V^T P^T.
-__device__ __forceinline__ void attn_softmax_pv(AttnState& st, const f32x16 (&s)[2][2],
-                                                const char* Vb, int lane, float sl2) {
-  bf16x8 pb[2][2][2];
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qi][kb][r]);
-    mt = halves_max(mt);
-    if (__any((mt - st.m_ref[qi]) * sl2 > kLazyLimit)) {
-      const float m_new = fmaxf(st.m_ref[qi], mt);
-      const float corr = __builtin_amdgcn_exp2f((st.m_ref[qi] - m_new) * sl2);
-      st.m_ref[qi] = m_new;
-      st.l[qi] *= corr;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.acc[qi][db][r] *= corr;
-    }
-    const float mc = st.m_ref[qi] * sl2;
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[qi][kb][r], sl2, -mc));
-        if (r & 1) ls1 += p; else ls0 += p;
-        pb[qi][kb][r >> 3][r & 7] = (__bf16)p;
-      }
-    st.l[qi] += ls0 + ls1;
-  }
+  for (int kc = 0; kc < 8; ++kc) o.k[kc] = krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4);
+  const int G = lane >> 4, s = lane & 15, c = s >> 2, j = s & 3;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
+    o.v[db] = (16 * (G >> 1) + c) * 256 + ((4 * (db ^ c) + 2 * (G & 1) + (j >> 1)) << 4) +
+              (j & 1) * 8;
+  return o;
+}
+
+// S^T: s[kb][r] = q . k[kb*32 + 16*h2 + r]
+__device__ __forceinline__ void attn_qk(f32x16 (&s)[2], const char* Kb, const AttnOffsets& off,
+                                        const bf16x8 (&qreg)[8]) {
+  s[0] = zero16();
+  s[1] = zero16();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kc = 0; kc < 8; ++kc)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const bf16x8 a = v_operand(Vb, db, kb, cc, lane);
-        st.acc[0][db] = mfma32(a, pb[0][kb][cc], st.acc[0][db]);
-        st.acc[1][db] = mfma32(a, pb[1][kb][cc], st.acc[1][db]);
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 8192 + off.k[kc]);
+      s[kb] = mfma32(a, qreg[kc], s[kb]);
+    }
+}
+
+__device__ __forceinline__ void attn_mask(f32x16 (&s)[2], int valid, int lane) {
+  const int h2 = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kb * 32 + 16 * h2 + r >= valid) s[kb][r] = -INFINITY;
+}
+
+__device__ __forceinline__ float attn_tile_max(const f32x16 (&s)[2]) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, s[kb][r]);
+  return halves_max(m);
+}
+
+// p = 2^((s - m_ref) * sl2), row sums in fp32, then O^T += V^T P^T.
+__device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, float m_ref,
+                                                const f32x16 (&s)[2], const char* Vb,
+                                                const AttnOffsets& off, float sl2) {
+  const float mc = m_ref * sl2;
+  bf16x8 pb[2][2];
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -mc));
+      if (r & 1) ls1 += p; else ls0 += p;
+      pb[kb][r >> 3][r & 7] = (__bf16)p;
+    }
+  l += ls0 + ls1;
+  // four independent accumulation chains advance together
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const char* a = Vb + kb * 8192 + cc * 2048 + off.v[db];
+        const bf16x8 va = __builtin_shufflevector(tr_read(a), tr_read(a + 1024), 0, 1, 2, 3, 4,
+                                                  5, 6, 7);
+        acc[db] = mfma32(va, pb[kb][cc], acc[db]);
       }
 }
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(512, 1)
 attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
             long kv_cap, float sl2, int n_qblk) {
   __shared__ __attribute__((aligned(1024))) char lds[ALDS];
+  __shared__ int redo_flag;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h2 = lane >> 5;
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const long bh = blk / n_qblk;
   const int qblk = blk % n_qblk;
-  const int stream = wave >> 1;
-  const int tq0 = qblk * AQ + (wave & 1) * 64;
-  const __bf16* kh = k + (size_t)bh * kv_cap * HD;
-  const __bf16* vh = v + (size_t)bh * kv_cap * HD;
+  const int stream = wave >> 2;
+  const int t = qblk * AQ + (wave & 3) * 32 + n;
 
-  bf16x8 qreg[2][8];
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    const int t = tq0 + 32 * qi + n;
+  bf16x8 qreg[8];
+  {
     const __bf16* qrow = q + ((size_t)bh * T + min(t, T - 1)) * HD + 8 * h2;
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) qreg[qi][kc] = t < T ? ld8(qrow + 16 * kc) : zero8();
+    for (int kc = 0; kc < 8; ++kc) qreg[kc] = t < T ? ld8(qrow + 16 * kc) : zero8();
   }
-
-  AttnState st;
-#pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db) st.acc[qi][db] = zero16();
-    st.m_ref[qi] = -INFINITY;
-    st.l[qi] = 0.f;
-  }
+  const AttnOffsets off = attn_offsets(lane);
 
   // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s
   const int n_tiles = (n_kv + AKT - 1) / AKT;
   const int iters = (n_tiles + 1) / 2;
   const int my_cnt = (n_tiles - stream + 1) / 2;
-  // this wave loads region (wave & 1 ? V : K) of stream (wave >> 1)
-  const int ld_stream = wave >> 1;
-  const bool ld_v = wave & 1;
+  // waves 2r and 2r+1 load the two halves of region r = (stream, K or V)
+  const int region = wave >> 1, ld_half = wave & 1;
+  const int ld_stream = region >> 1;
+  const bool ld_v = region & 1;
   const int ld_cnt = (n_tiles - ld_stream + 1) / 2;
-  const __bf16* ld_src = ld_v ? vh : kh;
+  const char* ld_src = reinterpret_cast<const char*>((ld_v ? v : k) + (size_t)bh * kv_cap * HD);
   char* ld_base = lds + ld_stream * 4 * TILE_B + (ld_v ? 2 * TILE_B : 0);
-  char* Kbase = lds + stream * 4 * TILE_B;
-  char* Vbase = Kbase + 2 * TILE_B;
+  int ld_off[4];
+  {
+    const int p = lane & 15, L4 = lane >> 4;
+#pragma unroll
+    for (int var = 0; var < 4; ++var) {
+      // instruction i with (i & 1, (i >> 2) & 1) = (var & 1, var >> 1) covers rows 4i + L4
+      const int r = 4 * ((var & 1) | ((var >> 1) << 2)) + L4;
+      ld_off[var] = L4 * 256 + ((p ^ (ld_v ? swz_v(r) : swz_k(r))) << 4);
+    }
+  }
+  const char* Kbase = lds + stream * 4 * TILE_B;
+  const char* Vbase = Kbase + 2 * TILE_B;
 
   auto issue = [&](int j) {   // local tile j of the wave's load region into buffer j & 1
     if (j < ld_cnt) {
-      if (ld_v) tile_load<true>(ld_base + (j & 1) * TILE_B, ld_src, 2 * j + ld_stream, n_kv, lane);
-      else tile_load<false>(ld_base + (j & 1) * TILE_B, ld_src, 2 * j + ld_stream, n_kv, lane);
+      const int g = 2 * j + ld_stream;
+      const char* src = ld_src + (size_t)g * TILE_B;
+      char* dst = ld_base + (j & 1) * TILE_B;
+      const int rows = n_kv - g * AKT;
+      if (ld_v) tile_load<true>(dst, src, ld_off, ld_half, rows, lane);
+      else tile_load<false>(dst, src, ld_off, ld_half, rows, lane);
     }
   };
+  // Every wave's loads of the current tile have landed once its own have
+  // (vmcnt) and all waves have reached the barrier.
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
 
-  // prologue: K(0), V(0)
-  issue(0);
-  for (int it = 0; it < iters; ++it) {
+  f32x16 acc[4];
+  float l = 0.f, m_ref = -INFINITY, m_seen = -INFINITY;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = zero16();
+    l = 0.f;
+    m_ref = m_seen;
+    bool over = false;
+    if (tid == 0) redo_flag = 0;
+    issue(0);
+    for (int it = 0; it < iters; ++it) {
+      sync();
+      issue(it + 1);
+      if (it < my_cnt) {
+        const int buf = (it & 1) * TILE_B;
+        f32x16 s[2];
+        attn_qk(s, Kbase + buf, off, qreg);
+        const int valid = n_kv - (2 * it + stream) * AKT;
+        if (valid < AKT) attn_mask(s, valid, lane);
+        const float mt = attn_tile_max(s);
+        if (pass == 0) {
+          if (it == 0) m_ref = mt;
+          m_seen = fmaxf(m_seen, mt);
+          over |= (mt - m_ref) * sl2 > kLazyLimit;
+        }
+        attn_softmax_pv(acc, l, m_ref, s, Vbase + buf, off, sl2);
+      }
+    }
+    if (__any(over)) redo_flag = 1;     // every writer stores 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    issue(it + 1);
-    if (it < my_cnt) {
-      f32x16 s[2][2];
-      attn_scores(s, Kbase + (it & 1) * TILE_B, lane, qreg, n_kv - (2 * it + stream) * AKT);
-      attn_softmax_pv(st, s, Vbase + (it & 1) * TILE_B, lane, sl2);
-    }
+    const int redo = redo_flag;
+    if (!redo) break;
+    __syncthreads();                     // everyone has read the flag
   }
 
   // merge stream B into stream A through LDS
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  float* ex = reinterpret_cast<float*>(lds) + (wave & 1) * (132 * 64);
+  float* ex = reinterpret_cast<float*>(lds) + (wave & 3) * (66 * 64);
   if (stream == 1) {
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ex[(qi * 64 + db * 16 + r) * 64 + lane] = st.acc[qi][db][r];
-      ex[(128 + qi) * 64 + lane] = st.m_ref[qi];
-      ex[(130 + qi) * 64 + lane] = st.l[qi];
-    }
+      for (int r = 0; r < 16; ++r) ex[(db * 16 + r) * 64 + lane] = acc[db][r];
+    ex[64 * 64 + lane] = m_ref;
+    ex[65 * 64 + lane] = l;
   }
   __syncthreads();
   if (stream == 1) return;
+  const float mb = ex[64 * 64 + lane];
+  const float lb = ex[65 * 64 + lane];
+  const float m = fmaxf(m_ref, mb);
+  const float fa = __builtin_amdgcn_exp2f((m_ref - m) * sl2);
+  const float fb = __builtin_amdgcn_exp2f((mb - m) * sl2);
+  const float inv = 1.f / halves_sum(l * fa + lb * fb);
+  if (t < T) {
+    __bf16* orow = o + ((size_t)bh * T + t) * HD + 4 * h2;
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    const float mb = ex[(128 + qi) * 64 + lane];
-    const float lb = ex[(130 + qi) * 64 + lane];
-    const float m = fmaxf(st.m_ref[qi], mb);
-    const float fa = __builtin_amdgcn_exp2f((st.m_ref[qi] - m) * sl2);
-    const float fb = __builtin_amdgcn_exp2f((mb - m) * sl2);
-    const float inv = 1.f / halves_sum(st.l[qi] * fa + lb * fb);
-    const int t = tq0 + 32 * qi + n;
-    if (t < T) {
-      __bf16* orow = o + ((size_t)bh * T + t) * HD + 4 * h2;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 w;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          bf16x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * jj + i;
-            const float vb = ex[(qi * 64 + db * 16 + r) * 64 + lane];
-            w[i] = (__bf16)((st.acc[qi][db][r] * fa + vb * fb) * inv);
-          }
-          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * jj) = w;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * jj + i;
+          const float vb = ex[(db * 16 + r) * 64 + lane];
+          w[i] = (__bf16)((acc[db][r] * fa + vb * fb) * inv);
         }
-    }
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * jj) = w;
+      }
   }
 }
 
@@ -666,7 +694,7 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const voi
                           int64_t n_kv, int64_t kv_cap, hipStream_t s) {
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
-  attn_mfma_k<<<(unsigned)nblk, 256, 0, s>>>(
+  attn_mfma_k<<<(unsigned)nblk, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, (int)n_kv, (long)kv_cap, d.scale * kLog2e, n_qblk);
   return hipGetLastError();
