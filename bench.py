@@ -182,12 +182,16 @@ class Bench:
         ws = arl2.alloc_workspace(sh, arl2.OP_STATE_COMMIT)
         arl2.feature_map(sh, k, L.phi[1], tmp[1], True)
         arl2.feature_map(sh, v, L.phi[2], tmp[2], False)
+        rws = arl2.alloc_workspace(sh, arl2.OP_READ)
+        cws = arl2.alloc_workspace(sh, arl2.OP_COMMIT)
         cases = {
             "intra_attn": lambda: arl2.intra_attn(sh, q, k, v, tmp[0]),
+            "read": lambda: arl2.read(sh, q, k, v, L.phi[0], L.S, tmp[0], ws=rws),
             "feature_map": lambda: arl2.feature_map(sh, q, L.phi[0], tmp[0], False),
-            "inter_read": lambda: arl2.inter_read(sh, tmp[1], L.S, tmp[2], tmp[0]),
             "state_commit": lambda: arl2.state_commit(sh, tmp[1], tmp[2], beta, alpha, L.S,
                                                       S_next, ws),
+            "commit": lambda: arl2.commit(sh, k, v, L.phi[1], L.phi[2], beta, alpha, L.S,
+                                          S_next, cws),
         }
         res = {}
         for name, fn in cases.items():
@@ -361,9 +365,10 @@ def main():
     commit_bytes = w.B * w.H * (2 * w.T * w.D * 2 + 4 * w.T + 2 * w.D * w.D * 4)
     kernels = {
         "intra_attn_us": kt["intra_attn"],
+        "read_us": kt["read"],
         "feature_map_us": kt["feature_map"],
-        "inter_read_us": kt["inter_read"],
         "state_commit_us": kt["state_commit"],
+        "commit_us": kt["commit"],
         "state_commit_hbm_frac": commit_bytes / (kt["state_commit"] * 1e-6) / PEAK_HBM,
         "state_commit_algorithmic_bytes": commit_bytes,
         "copy_calibration": calib,

@@ -96,7 +96,10 @@ size_t commit_ws(const arl2::Dims& d) {
                            : arl2::generic_state_commit_ws_bytes(d);
 }
 
-size_t ws_read(const arl2::Dims& d) { return 2 * arl2::round_up(arl2::act_bytes(d), 256); }
+size_t ws_read(const arl2::Dims& d) {
+  return arl2::use_mfma(d) ? arl2::round_up(arl2::mfma_read_ws_bytes(d), 256)
+                           : 2 * arl2::round_up(arl2::act_bytes(d), 256);
+}
 size_t ws_commit(const arl2::Dims& d) {
   return 2 * arl2::round_up(arl2::act_bytes(d), 256) + arl2::round_up(commit_ws(d), 256);
 }
@@ -133,10 +136,15 @@ hipError_t run_state_commit(const arl2::Dims& d, const void* kp, const void* vp,
                            : arl2::generic_state_commit(d, kp, vp, beta, alpha, Sp, Sn, ws, s);
 }
 
-// Read = feature map of Q, intra attention, inter read + combine.
+// Read = feature map of Q, intra attention, inter read + combine. The bf16
+// D = 128 path fuses them: M = Phi_q S per head, then attention with the
+// epilogue O = O_intra + Q M.
 arl2_status do_read(const arl2::Dims& d, const void* q, const void* k, const void* v,
                     const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
                     void* ws, hipStream_t s) {
+  if (arl2::use_mfma(d))
+    return hip_status(arl2::mfma_read(d, q, k, v, phi_q, S, o, o_intra, o_inter, ws, s),
+                      "fused read");
   const size_t ab = arl2::round_up(arl2::act_bytes(d), 256);
   char* w = static_cast<char*>(ws);
   void* q_prime = w;

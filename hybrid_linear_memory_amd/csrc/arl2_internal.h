@@ -67,6 +67,12 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k,
 hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
                            const void* o_intra, void* o, void* o_inter,
                            hipStream_t s);
+// Fused read (bf16, D = 128): M = Phi_q S per head into `ws`, then the
+// attention kernel with the epilogue O = O_intra + Q M.
+size_t mfma_read_ws_bytes(const Dims& d);
+hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
+                     const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
+                     void* ws, hipStream_t s);
 size_t mfma_state_commit_ws_bytes(const Dims& d);
 hipError_t mfma_state_commit(const Dims& d, const void* k_prime,
                              const void* v_prime, const float* beta,

@@ -255,10 +255,14 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
       }
 }
 
+// With `mt` set (the fused read), the epilogue adds the inter-frame branch
+// O_inter = Q M, M = Phi_q S (given transposed, bf16 [B, H, D_v, D_in]); the
+// two branches can also be written separately to o_intra / o_inter.
 __global__ void __launch_bounds__(512, 1)
 attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
-            long kv_cap, float sl2, int n_qblk) {
+            long kv_cap, float sl2, int n_qblk, const __bf16* __restrict__ mt,
+            __bf16* __restrict__ o_intra, __bf16* __restrict__ o_inter) {
   __shared__ __attribute__((aligned(1024))) char lds[ALDS];
   __shared__ int redo_flag;
   const int tid = threadIdx.x;
@@ -356,8 +360,25 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __syncthreads();                     // everyone has read the flag
   }
 
+  // Inter-frame branch for this wave's queries: O_inter^T = M^T Q^T, each wave
+  // of a stream pair taking two of the four 32-column blocks (stream A blocks
+  // 0-1, stream B blocks 2-3; B hands its blocks over with its partials).
+  f32x16 oi[2];
+  if (mt) {
+    const __bf16* mrow = mt + (size_t)bh * HD * HD + 8 * h2;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const int db = 2 * stream + b2;
+      oi[b2] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        oi[b2] = mfma32(ld8(mrow + (size_t)(32 * db + n) * HD + 16 * kc), qreg[kc], oi[b2]);
+    }
+  }
+
   // merge stream B into stream A through LDS
-  float* ex = reinterpret_cast<float*>(lds) + (wave & 3) * (66 * 64);
+  constexpr int EXW = 98;                 // floats per lane: 64 acc + m + l + 32 inter
+  float* ex = reinterpret_cast<float*>(lds) + (wave & 3) * (EXW * 64);
   if (stream == 1) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -365,6 +386,12 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       for (int r = 0; r < 16; ++r) ex[(db * 16 + r) * 64 + lane] = acc[db][r];
     ex[64 * 64 + lane] = m_ref;
     ex[65 * 64 + lane] = l;
+    if (mt) {
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ex[(66 + b2 * 16 + r) * 64 + lane] = oi[b2][r];
+    }
   }
   __syncthreads();
   if (stream == 1) return;
@@ -375,20 +402,65 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const float fb = __builtin_amdgcn_exp2f((mb - m) * sl2);
   const float inv = 1.f / halves_sum(l * fa + lb * fb);
   if (t < T) {
-    __bf16* orow = o + ((size_t)bh * T + t) * HD + 4 * h2;
+    const size_t row = ((size_t)bh * T + t) * HD + 4 * h2;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 w;
+        bf16x4 w, wi, we;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * jj + i;
           const float vb = ex[(db * 16 + r) * 64 + lane];
-          w[i] = (__bf16)((acc[db][r] * fa + vb * fb) * inv);
+          const float intra = (acc[db][r] * fa + vb * fb) * inv;
+          float inter = 0.f;
+          if (mt) inter = db < 2 ? oi[db][r] : ex[(66 + (db - 2) * 16 + r) * 64 + lane];
+          w[i] = (__bf16)(intra + inter);
+          wi[i] = (__bf16)intra;
+          we[i] = (__bf16)inter;
         }
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * jj) = w;
+        const size_t off_o = row + 32 * db + 8 * jj;
+        *reinterpret_cast<bf16x4*>(o + off_o) = w;
+        if (o_intra) *reinterpret_cast<bf16x4*>(o_intra + off_o) = wi;
+        if (o_inter) *reinterpret_cast<bf16x4*>(o_inter + off_o) = we;
       }
+  }
+}
+
+// ===========================================================================
+// Read preparation for the fused read: M = Phi_q[h] S[b,h] (the inter-frame
+// read Q' S = Q (Phi_q S) folded into one D x D map per head), stored
+// transposed in bf16 so that the attention epilogue reads it as an MFMA A
+// operand. One workgroup per (b, h, 32-column block of M); wave w computes
+// rows [32w, 32w + 32).
+// ===========================================================================
+__global__ void __launch_bounds__(256)
+read_prep_k(const __bf16* __restrict__ phi, const float* __restrict__ S,
+            __bf16* __restrict__ mt, int H) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long bh = blockIdx.x >> 2;
+  const int jb = blockIdx.x & 3;
+  const int j = 32 * jb + n;
+  const float* Sh = S + (size_t)bh * HD * HD;
+  const __bf16* P = phi + (size_t)(bh % H) * HD * HD + (size_t)(32 * wave + n) * HD + 8 * h2;
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    bf16x8 b;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = (__bf16)Sh[(size_t)(16 * kc + 8 * h2 + u) * HD + j];
+    acc = mfma32(ld8(P + 16 * kc), b, acc);
+  }
+  // acc[r] = M[i = 32w + 8(r/4) + 4h2 + r%4][j]  ->  MT[j][i]
+  __bf16* out = mt + (size_t)bh * HD * HD + (size_t)j * HD + 32 * wave + 4 * h2;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    bf16x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (__bf16)acc[4 * jj + i];
+    *reinterpret_cast<bf16x4*>(out + 8 * jj) = w;
   }
 }
 
@@ -696,7 +768,25 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const voi
   const long nblk = (long)d.B * d.H * n_qblk;
   attn_mfma_k<<<(unsigned)nblk, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-      static_cast<__bf16*>(o), d.T, (int)n_kv, (long)kv_cap, d.scale * kLog2e, n_qblk);
+      static_cast<__bf16*>(o), d.T, (int)n_kv, (long)kv_cap, d.scale * kLog2e, n_qblk, nullptr,
+      nullptr, nullptr);
+  return hipGetLastError();
+}
+
+size_t mfma_read_ws_bytes(const Dims& d) { return (size_t)d.B * d.H * HD * HD * 2; }
+
+hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
+                     const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
+                     void* ws, hipStream_t s) {
+  __bf16* mt = static_cast<__bf16*>(ws);
+  read_prep_k<<<(unsigned)(d.B * d.H * 4), 256, 0, s>>>(static_cast<const __bf16*>(phi_q), S, mt,
+                                                       d.H);
+  const int n_qblk = (d.T + AQ - 1) / AQ;
+  const long nblk = (long)d.B * d.H * n_qblk;
+  attn_mfma_k<<<(unsigned)nblk, 512, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk, mt,
+      static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter));
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ def test_version_and_status_strings(arl2):
 def test_workspace_sizes(arl2):
     s = arl2.Shape(1, 12, 1560, 128, arl2.BF16)
     act = 1 * 12 * 1560 * 128 * 2
-    assert arl2.workspace_bytes(s, arl2.OP_READ) >= 2 * act
+    assert arl2.workspace_bytes(s, arl2.OP_READ) >= 12 * 128 * 128 * 2
     assert arl2.workspace_bytes(s, arl2.OP_COMMIT) >= 2 * act
     assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS) == max(
         arl2.workspace_bytes(s, arl2.OP_READ), arl2.workspace_bytes(s, arl2.OP_COMMIT))
