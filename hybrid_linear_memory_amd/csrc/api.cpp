@@ -101,6 +101,7 @@ size_t ws_read(const arl2::Dims& d) {
                            : 2 * arl2::round_up(arl2::act_bytes(d), 256);
 }
 size_t ws_commit(const arl2::Dims& d) {
+  if (arl2::use_mfma(d)) return arl2::round_up(arl2::mfma_commit_ws_bytes(d), 256);
   return 2 * arl2::round_up(arl2::act_bytes(d), 256) + arl2::round_up(commit_ws(d), 256);
 }
 
@@ -161,6 +162,9 @@ arl2_status do_read(const arl2::Dims& d, const void* q, const void* k, const voi
 arl2_status do_commit(const arl2::Dims& d, const void* k, const void* v, const void* phi_k,
                       const void* phi_v, const float* beta, const float* alpha,
                       const float* S_prev, float* S_next, void* ws, hipStream_t s) {
+  if (arl2::use_mfma(d))
+    return hip_status(arl2::mfma_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, s),
+                      "fused commit");
   const size_t ab = arl2::round_up(arl2::act_bytes(d), 256);
   char* w = static_cast<char*>(ws);
   void* kp = w;

@@ -73,6 +73,12 @@ size_t mfma_read_ws_bytes(const Dims& d);
 hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
                      const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
                      void* ws, hipStream_t s);
+// Fused commit (bf16, D = 128) from the raw K, V: feature maps, row norm and
+// the gated delta update in one kernel (+ a fixed-order chunk reduction).
+size_t mfma_commit_ws_bytes(const Dims& d);
+hipError_t mfma_commit(const Dims& d, const void* k, const void* v, const void* phi_k,
+                       const void* phi_v, const float* beta, const float* alpha,
+                       const float* S_prev, float* S_next, void* ws, hipStream_t s);
 size_t mfma_state_commit_ws_bytes(const Dims& d);
 hipError_t mfma_state_commit(const Dims& d, const void* k_prime,
                              const void* v_prime, const float* beta,

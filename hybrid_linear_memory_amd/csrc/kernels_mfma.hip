@@ -155,6 +155,21 @@ __device__ __forceinline__ bf16x4 tr_read(const char* a) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// MFMA operand by two transposing reads from a row-major bf16 matrix in LDS
+// with 256-byte rows stored under the swz_v chunk swizzle: lane (n = lane % 32,
+// h2 = lane / 32) receives M[r0 + hoff*h2 + u][c0 + n] for u = 0..7.
+// r0 and hoff must be multiples of 4.
+__device__ __forceinline__ bf16x8 tr_op(const char* base, int r0, int hoff, int c0, int lane) {
+  const int G = lane >> 4;
+  const int s = lane & 15, c = s >> 2, j = s & 3;
+  const int col = c0 + 16 * (G & 1) + 4 * j;
+  const int c16 = col >> 3, sub = (col & 7) * 2;
+  const int rb = r0 + hoff * (G >> 1) + c;
+  const char* a0 = base + rb * 256 + ((c16 ^ swz_v(rb)) << 4) + sub;
+  const char* a1 = base + (rb + 4) * 256 + ((c16 ^ swz_v(rb + 4)) << 4) + sub;
+  return __builtin_shufflevector(tr_read(a0), tr_read(a1), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // max / sum of x over lanes l and l ^ 32.
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -723,6 +738,190 @@ commit_mfma_k(const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
   }
 }
 
+// ===========================================================================
+// Fused commit from the clean pass's raw K and V: the feature maps
+// K' = rownorm(K Phi_k), V' = V Phi_v and the gated delta update in one pass
+// over the frame's tokens, so K' and V' never leave the chip.
+//
+// One workgroup = 4 waves per (b, h, token chunk); wave w owns output columns
+// [32w, 32w + 32). Phi_k and Phi_v are staged once (row-major, read as MFMA
+// operands with transposing reads). Per 32-token slice:
+//   K~^T = Phi_k^T K^T   (column block w; lane = token, registers = columns,
+//                          so the row norm is an in-lane sum, one half
+//                          exchange and a 4-wave exchange through LDS)
+//   V'   = V Phi_v       (column block w, laid out like P^ below)
+//   K'   = K~ / max(|K~|, 1e-12) -> LDS (two swizzles)
+//   P^   = K' S_prev[:, w]; W = beta (V' - P^); U[:, w] += K'^T W
+// With one chunk the workgroup writes S_next = alpha S_prev + U; otherwise a
+// partial, summed in chunk order by commit_reduce_k.
+// ===========================================================================
+constexpr int FT = 32;                          // tokens per slice
+constexpr int F_PHI_B = HD * HD * 2;            // 32 KB per map
+constexpr int F_SLICE_B = FT * HD * 2;          // 8 KB per 32-token slice
+constexpr int F_PHIK = 0;
+constexpr int F_PHIV = F_PHIK + F_PHI_B;
+constexpr int F_RAW = F_PHIV + F_PHI_B;         // [buf][K, V] raw slices
+constexpr int F_KPA = F_RAW + 4 * F_SLICE_B;    // K' rows, row-read swizzle (swz_k)
+constexpr int F_KPB = F_KPA + F_SLICE_B;        // K' rows, transposing-read swizzle (swz_v)
+constexpr int F_SS = F_KPB + F_SLICE_B;         // [4 waves][32 tokens] partial sums of squares
+constexpr int F_BETA = F_SS + 4 * FT * 4;       // [buf][32] beta
+constexpr int F_LDS = F_BETA + 2 * FT * 4;
+
+__device__ __forceinline__ int swz_r(int r) { return r & 15; }
+
+// Wave-wide DMA of `n_inst` x 4 rows (256-byte rows) starting at row r_begin of
+// a row-major bf16 matrix into LDS under chunk swizzle `swz` (rows past
+// `rows_valid` are clamped to the last valid row).
+template <int SWZ>
+__device__ __forceinline__ void rows_load(char* dst, const char* src, int r_begin, int n_inst,
+                                          int rows_valid, int lane) {
+  const int p = lane & 15;
+  for (int i = 0; i < n_inst; ++i) {
+    const int r = r_begin + 4 * i + (lane >> 4);
+    const int sw = SWZ == 0 ? swz_k(r) : SWZ == 1 ? swz_v(r) : swz_r(r);
+    const int rc = min(r, rows_valid - 1);
+    const char* g = src + (size_t)rc * 256 + ((p ^ sw) << 4);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + (r_begin + 4 * i) * 256),
+                                     16, 0, 0);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+               const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
+               const float* __restrict__ beta, const float* __restrict__ alpha,
+               const float* __restrict__ S_prev, float* __restrict__ S_next,
+               float* __restrict__ partial, int H, int T, int chunk_tokens, int n_chunks,
+               long n_bh) {
+  __shared__ __attribute__((aligned(1024))) char lds[F_LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h2 = lane >> 5;
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const long bh = blk / n_chunks;
+  const int chunk = blk % n_chunks;
+  const int h = (int)(bh % H);
+  const int t_begin = chunk * chunk_tokens;
+  const int t_end = min(T, t_begin + chunk_tokens);
+  const int n_slices = (t_end - t_begin + FT - 1) / FT;
+  const int cb = wave;
+  const int col = 32 * cb + n;
+  const char* kh = reinterpret_cast<const char*>(k + (size_t)bh * T * HD);
+  const char* vh = reinterpret_cast<const char*>(v + (size_t)bh * T * HD);
+  const float* bt = beta + (size_t)bh * T;
+  float* fbeta = reinterpret_cast<float*>(lds + F_BETA);
+  float* fss = reinterpret_cast<float*>(lds + F_SS);
+
+  // maps: waves 0-1 stage Phi_k, waves 2-3 Phi_v (64 rows each)
+  {
+    const char* src = reinterpret_cast<const char*>((wave < 2 ? phi_k : phi_v) + (size_t)h * HD * HD);
+    rows_load<1>(lds + (wave < 2 ? F_PHIK : F_PHIV), src, 64 * (wave & 1), 16, HD, lane);
+  }
+  // raw slice s: waves 0-1 load K rows [16w, 16w + 16), waves 2-3 V rows
+  auto issue = [&](int sl) {
+    const int t0 = t_begin + sl * FT;
+    char* dst = lds + F_RAW + (sl & 1) * 2 * F_SLICE_B + (wave < 2 ? 0 : F_SLICE_B);
+    const char* src = (wave < 2 ? kh : vh) + (size_t)t0 * 256;
+    if (wave < 2) rows_load<2>(dst, src, 16 * (wave & 1), 4, t_end - t0, lane);
+    else rows_load<0>(dst, src, 16 * (wave & 1), 4, t_end - t0, lane);
+    if (tid < FT) fbeta[(sl & 1) * FT + tid] = t0 + tid < t_end ? bt[t0 + tid] : 0.f;
+  };
+  issue(0);
+
+  // S_prev[:, col] as the B operand of P^ = K' S (k = state row)
+  const float* Sp = S_prev + (size_t)bh * HD * HD;
+  bf16x8 sreg[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sreg[kc][u] = (__bf16)Sp[(size_t)(16 * kc + 8 * h2 + u) * HD + col];
+
+  f32x16 uacc[4];
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) uacc[ib] = zero16();
+  const int krow = perm32(n);
+
+  for (int sl = 0; sl < n_slices; ++sl) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();                                    // slice sl and beta visible
+    if (sl + 1 < n_slices) issue(sl + 1);
+    const char* Kr = lds + F_RAW + (sl & 1) * 2 * F_SLICE_B;
+    const char* Vr = Kr + F_SLICE_B;
+
+    // K~^T column block: kt[r] = K~[token n][32cb + 8(r/4) + 4h2 + r%4]
+    f32x16 kt = zero16();
+    // V' block in the P^ layout: vp[r] = V'[token 16h2 + r][col]
+    f32x16 vp = zero16();
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kr + n * 256 + (((2 * kc + h2) ^ swz_r(n)) << 4));
+      kt = mfma32(tr_op(lds + F_PHIK, 16 * kc, 8, 32 * cb, lane), kb, kt);
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vr + krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4));
+      vp = mfma32(va, tr_op(lds + F_PHIV, 16 * kc, 8, 32 * cb, lane), vp);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss = fmaf(kt[r], kt[r], ss);
+    ss = halves_sum(ss);
+    if (h2 == 0) fss[cb * FT + n] = ss;
+    __syncthreads();                                    // partial norms visible
+    const float inv = 1.f / fmaxf(sqrtf(fss[n] + fss[FT + n] + fss[2 * FT + n] + fss[3 * FT + n]),
+                                  1e-12f);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      bf16x4 w4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w4[i] = (__bf16)(kt[4 * jj + i] * inv);
+      const int d = 32 * cb + 8 * jj + 4 * h2;         // 4 consecutive columns of row n
+      const int c16 = d >> 3, sub = (d & 7) * 2;
+      *reinterpret_cast<bf16x4*>(lds + F_KPA + n * 256 + ((c16 ^ swz_k(n)) << 4) + sub) = w4;
+      *reinterpret_cast<bf16x4*>(lds + F_KPB + n * 256 + ((c16 ^ swz_v(n)) << 4) + sub) = w4;
+    }
+    __syncthreads();                                    // K' of the slice visible
+
+    // P^ = K' S[:, col]; register r <-> token 16*h2 + r
+    f32x16 p = zero16();
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + F_KPA + krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4));
+      p = mfma32(a, sreg[kc], p);
+    }
+    bf16x8 wb[2];
+    const float* bsl = fbeta + (sl & 1) * FT + 16 * h2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wb[r >> 3][r & 7] = (__bf16)(bsl[r] * (vp[r] - p[r]));
+    // U[:, col] += K'^T W  (A = K'^T rows d, k = tokens 16*h2 + 8*cc + u)
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        uacc[ib] = mfma32(tr_op(lds + F_KPB, 8 * cc, 16, 32 * ib, lane), wb[cc], uacc[ib]);
+  }
+
+  // uacc[ib][r] = U[row 32*ib + 8*(r/4) + 4*h2 + (r%4)][col]
+  if (n_chunks == 1) {
+    const float a = alpha[bh];
+    float* Sn = S_next + (size_t)bh * HD * HD;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const size_t e = (size_t)(32 * ib + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + col;
+        Sn[e] = fmaf(a, Sp[e], uacc[ib][r]);
+      }
+  } else {
+    float* P = partial + ((size_t)chunk * n_bh + bh) * HD * HD;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const size_t e = (size_t)(32 * ib + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + col;
+        P[e] = uacc[ib][r];
+      }
+  }
+}
+
 // S_next = alpha S_prev + sum over chunks (in chunk order) of the partials.
 __global__ void __launch_bounds__(256)
 commit_reduce_k(const float* __restrict__ partial, const float* __restrict__ alpha,
@@ -807,6 +1006,27 @@ hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
   rowmap_mfma_k<MAP_STATE><<<(unsigned)nblk, 256, 0, s>>>(
       static_cast<const __bf16*>(q_prime), S, static_cast<const __bf16*>(o_intra),
       static_cast<__bf16*>(o), static_cast<__bf16*>(o_inter), d.H, d.T, n_rblk, 0);
+  return hipGetLastError();
+}
+
+size_t mfma_commit_ws_bytes(const Dims& d) { return mfma_state_commit_ws_bytes(d); }
+
+hipError_t mfma_commit(const Dims& d, const void* k, const void* v, const void* phi_k,
+                       const void* phi_v, const float* beta, const float* alpha,
+                       const float* S_prev, float* S_next, void* ws, hipStream_t s) {
+  int ct, nc;
+  commit_split(d, &ct, &nc);
+  const long n_bh = (long)d.B * d.H;
+  float* partial = static_cast<float*>(ws);
+  commit_fused_k<<<(unsigned)(n_bh * nc), 256, 0, s>>>(
+      static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), beta, alpha, S_prev,
+      S_next, partial, d.H, d.T, ct, nc, n_bh);
+  if (nc > 1) {
+    const long total4 = n_bh * HD * HD / 4;
+    commit_reduce_k<<<(unsigned)((total4 + 255) / 256), 256, 0, s>>>(partial, alpha, S_prev,
+                                                                     S_next, nc, n_bh);
+  }
   return hipGetLastError();
 }
 
