@@ -83,8 +83,11 @@ def test_null_shape_dtype_layout_errors(arl2):
 
 
 def test_alias_and_workspace_errors(arl2):
-    s = arl2.Shape(1, 2, 64, 128, arl2.BF16)
+    # T long enough that the commit splits its tokens and needs a workspace, so
+    # every call below fails validation before anything could be launched
+    s = arl2.Shape(1, 2, 1560, 128, arl2.BF16)
     cs = arl2.c_shape
+    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) > 0
     S1, S2, WS = 8 << 20, 16 << 20, 32 << 20
     need = arl2.workspace_bytes(s, arl2.OP_COMMIT)
     # S_prev == S_next
