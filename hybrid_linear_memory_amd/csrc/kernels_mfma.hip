@@ -220,6 +220,14 @@ __device__ __forceinline__ void attn_qk(f32x16 (&s)[2], const char* Kb, const At
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 8192 + off.k[kc]);
       s[kb] = mfma32(a, qreg[kc], s[kb]);
     }
+  // keep only a few operand reads in flight ahead of their products
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+  for (int i = 0; i < 13; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
 }
 
 __device__ __forceinline__ void attn_mask(f32x16 (&s)[2], int valid, int lane) {
@@ -268,6 +276,13 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
                                                   5, 6, 7);
         acc[db] = mfma32(va, pb[kb][cc], acc[db]);
       }
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+  for (int i = 0; i < 13; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
 }
 
 // With `mt` set (the fused read), the epilogue adds the inter-frame branch
@@ -300,7 +315,6 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s
   const int n_tiles = (n_kv + AKT - 1) / AKT;
-  const int iters = (n_tiles + 1) / 2;
   const int my_cnt = (n_tiles - stream + 1) / 2;
   // waves 2r and 2r+1 load the two halves of region r = (stream, K or V)
   const int region = wave >> 1, ld_half = wave & 1;
@@ -339,41 +353,66 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __builtin_amdgcn_s_barrier();
   };
 
+  // The two streams run half an iteration apart so that the two waves sharing
+  // a SIMD alternate between matrix products and the softmax: after barrier
+  // it, stream A computes the scores of its tile it, their softmax and P V,
+  // while stream B first finishes its tile it-1 (softmax, P V, started from
+  // scores kept in registers) and then computes the scores of its tile it.
+  // Stream B's V tiles are therefore loaded one iteration later than its K
+  // tiles.
+  const bool v_late = ld_stream == 1 && ld_v;
+  const int n_iter = max((n_tiles + 1) / 2, n_tiles / 2 + 1);   // same for every wave
   f32x16 acc[4];
   float l = 0.f, m_ref = -INFINITY, m_seen = -INFINITY;
-  for (int pass = 0; pass < 2; ++pass) {
+  // One pass over the keys; returns whether a redo with the exact maximum is
+  // needed. Written as a lambda called twice (rather than a loop) so that the
+  // rarely taken second pass does not extend live ranges in the first.
+  auto run_pass = [&](const int pass) -> bool {
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = zero16();
     l = 0.f;
     m_ref = m_seen;
     bool over = false;
     if (tid == 0) redo_flag = 0;
-    issue(0);
-    for (int it = 0; it < iters; ++it) {
-      sync();
-      issue(it + 1);
-      if (it < my_cnt) {
-        const int buf = (it & 1) * TILE_B;
-        f32x16 s[2];
-        attn_qk(s, Kbase + buf, off, qreg);
-        const int valid = n_kv - (2 * it + stream) * AKT;
-        if (valid < AKT) attn_mask(s, valid, lane);
-        const float mt = attn_tile_max(s);
-        if (pass == 0) {
-          if (it == 0) m_ref = mt;
-          m_seen = fmaxf(m_seen, mt);
-          over |= (mt - m_ref) * sl2 > kLazyLimit;
+    if (!v_late) issue(0);
+    f32x16 s[2];
+    auto scores = [&](int j) {
+      attn_qk(s, Kbase + (j & 1) * TILE_B, off, qreg);
+      const int valid = n_kv - (2 * j + stream) * AKT;
+      if (valid < AKT) attn_mask(s, valid, lane);
+      const float mt = attn_tile_max(s);
+      if (pass == 0) {
+        if (j == 0) m_ref = mt;
+        m_seen = fmaxf(m_seen, mt);
+        over |= (mt - m_ref) * sl2 > kLazyLimit;
+      }
+    };
+    if (stream == 0) {
+      for (int it = 0; it < n_iter; ++it) {
+        sync();
+        issue(it + 1);
+        if (it < my_cnt) {
+          scores(it);
+          attn_softmax_pv(acc, l, m_ref, s, Vbase + (it & 1) * TILE_B, off, sl2);
         }
-        attn_softmax_pv(acc, l, m_ref, s, Vbase + buf, off, sl2);
+      }
+    } else {
+      for (int it = 0; it < n_iter; ++it) {
+        sync();
+        if (it >= 1 && it <= my_cnt)
+          attn_softmax_pv(acc, l, m_ref, s, Vbase + ((it - 1) & 1) * TILE_B, off, sl2);
+        issue(v_late ? it : it + 1);
+        if (it < my_cnt) scores(it);
       }
     }
     if (__any(over)) redo_flag = 1;     // every writer stores 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int redo = redo_flag;
-    if (!redo) break;
     __syncthreads();                     // everyone has read the flag
-  }
+    return redo != 0;
+  };
+  if (run_pass(0)) run_pass(1);
 
   // Inter-frame branch for this wave's queries: O_inter^T = M^T Q^T, each wave
   // of a stream pair taking two of the four 32-column blocks (stream A blocks
