@@ -184,9 +184,13 @@ class Bench:
         arl2.feature_map(sh, v, L.phi[2], tmp[2], False)
         rws = arl2.alloc_workspace(sh, arl2.OP_READ)
         cws = arl2.alloc_workspace(sh, arl2.OP_COMMIT)
+        M = arl2.alloc_prepared(sh)
+        arl2.read_prepare(sh, L.phi[0], L.S, M)
         cases = {
             "intra_attn": lambda: arl2.intra_attn(sh, q, k, v, tmp[0]),
             "read": lambda: arl2.read(sh, q, k, v, L.phi[0], L.S, tmp[0], ws=rws),
+            "read_prepare": lambda: arl2.read_prepare(sh, L.phi[0], L.S, M),
+            "read_prepared": lambda: arl2.read_prepared(sh, q, k, v, M, tmp[0], ws=rws),
             "feature_map": lambda: arl2.feature_map(sh, q, L.phi[0], tmp[0], False),
             "state_commit": lambda: arl2.state_commit(sh, tmp[1], tmp[2], beta, alpha, L.S,
                                                       S_next, ws),
@@ -366,6 +370,8 @@ def main():
     kernels = {
         "intra_attn_us": kt["intra_attn"],
         "read_us": kt["read"],
+        "read_prepare_us": kt["read_prepare"],
+        "read_prepared_us": kt["read_prepared"],
         "feature_map_us": kt["feature_map"],
         "state_commit_us": kt["state_commit"],
         "commit_us": kt["commit"],

@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so
 
 F32 = 0
 BF16 = 1
-OP_READ, OP_CLEAN_PASS, OP_COMMIT, OP_STATE_COMMIT = 0, 1, 2, 3
+OP_READ, OP_CLEAN_PASS, OP_COMMIT, OP_STATE_COMMIT, OP_READ_PREPARED = 0, 1, 2, 3, 4
 
 STATUS_NAMES = {
     0: "ARL2_OK", 1: "ARL2_E_NULL", 2: "ARL2_E_SHAPE", 3: "ARL2_E_DTYPE",
@@ -50,6 +50,9 @@ SIGNATURES = {
     "arl2_clean_pass": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _sz, _vp]),
     "arl2_fullkv_attn": (_i32, [_SP, _vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "arl2_prepared_bytes": (_sz, [_SP]),
+    "arl2_read_prepare": (_i32, [_SP, _vp, _vp, _vp, _vp]),
+    "arl2_read_prepared": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_workspace_bytes": (_sz, [_SP, _i32]),
     "arl2_status_string": (ctypes.c_char_p, [_i32]),
     "arl2_last_error": (ctypes.c_char_p, []),
@@ -182,6 +185,30 @@ def read(shape: Shape, q, k, v, phi_q, S, o, o_intra=None, o_inter=None, ws=None
         _ptr(o_intra, "o_intra", a, optional=True), _ptr(o_inter, "o_inter", a, optional=True),
         _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
         _stream(stream)))
+
+
+def prepared_bytes(shape: Shape) -> int:
+    return _lib.arl2_prepared_bytes(ctypes.byref(shape.c()))
+
+
+def alloc_prepared(shape: Shape, device=None) -> torch.Tensor:
+    return torch.empty(max(prepared_bytes(shape), 16), dtype=torch.uint8, device=device or "cuda")
+
+
+def read_prepare(shape: Shape, phi_q, S, prepared, stream=None):
+    _check(_lib.arl2_read_prepare(ctypes.byref(shape.c()), _ptr(phi_q, "phi_q", shape.torch_dtype),
+                                  _ptr(S, "S", torch.float32), _ptr(prepared, "prepared"),
+                                  _stream(stream)))
+
+
+def read_prepared(shape: Shape, q, k, v, prepared, o, o_intra=None, o_inter=None, ws=None,
+                  stream=None):
+    a = shape.torch_dtype
+    _check(_lib.arl2_read_prepared(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(prepared, "prepared"), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
+        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
 def commit(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, stream=None):

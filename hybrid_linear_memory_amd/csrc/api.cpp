@@ -100,6 +100,12 @@ size_t ws_read(const arl2::Dims& d) {
   return arl2::use_mfma(d) ? arl2::round_up(arl2::mfma_read_ws_bytes(d), 256)
                            : 2 * arl2::round_up(arl2::act_bytes(d), 256);
 }
+size_t prepared_bytes(const arl2::Dims& d) {
+  return (size_t)d.B * d.H * d.D * d.D * (arl2::use_mfma(d) ? 2 : 4);
+}
+size_t ws_read_prepared(const arl2::Dims& d) {
+  return arl2::use_mfma(d) ? 0 : arl2::round_up(arl2::act_bytes(d), 256);
+}
 size_t ws_commit(const arl2::Dims& d) {
   if (arl2::use_mfma(d)) return arl2::round_up(arl2::mfma_commit_ws_bytes(d), 256);
   return 2 * arl2::round_up(arl2::act_bytes(d), 256) + arl2::round_up(commit_ws(d), 256);
@@ -215,6 +221,7 @@ size_t arl2_workspace_bytes(const arl2_shape* shape, int32_t op) {
     case ARL2_OP_COMMIT: return ws_commit(d);
     case ARL2_OP_CLEAN_PASS: return std::max(ws_read(d), ws_commit(d));
     case ARL2_OP_STATE_COMMIT: return commit_ws(d);
+    case ARL2_OP_READ_PREPARED: return ws_read_prepared(d);
     default: return 0;
   }
 }
@@ -314,6 +321,65 @@ arl2_status arl2_read(const arl2_shape* shape, const void* q, const void* k, con
   if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
     return fail(ARL2_E_ALIAS, "outputs o, o_intra, o_inter overlap");
   return do_read(d, q, k, v, phi_q, S, o, o_intra, o_inter, ws, (hipStream_t)stream);
+}
+
+size_t arl2_prepared_bytes(const arl2_shape* shape) {
+  arl2::Dims d;
+  if (check_shape(shape, &d) != ARL2_OK) return 0;
+  return prepared_bytes(d);
+}
+
+arl2_status arl2_read_prepare(const arl2_shape* shape, const void* phi_q, const float* S,
+                              void* prepared, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(phi_q);
+  REQUIRE_PTR(S);
+  REQUIRE_PTR(prepared);
+  const size_t pb = prepared_bytes(d);
+  if (overlap({prepared, pb}, {S, state_bytes(d)}) || overlap({prepared, pb}, {phi_q, phi_bytes(d)}))
+    return fail(ARL2_E_ALIAS, "prepared overlaps phi_q or S");
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(arl2::use_mfma(d)
+                        ? arl2::mfma_read_prepare(d, phi_q, S, prepared, s)
+                        : arl2::generic_read_prepare(d, phi_q, S, static_cast<float*>(prepared), s),
+                    "read preparation");
+}
+
+arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q, const void* k,
+                               const void* v, const void* prepared, void* o, void* o_intra,
+                               void* o_inter, void* ws, size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(prepared);
+  REQUIRE_PTR(o);
+  OPTIONAL_PTR(o_intra);
+  OPTIONAL_PTR(o_inter);
+  const size_t need = ws_read_prepared(d);
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d);
+  const Range outs[3] = {{o, ab}, {o_intra, ab}, {o_inter, ab}};
+  const Range ins[5] = {{q, ab}, {k, ab}, {v, ab}, {prepared, prepared_bytes(d)}, {ws, need}};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return fail(ARL2_E_ALIAS, "outputs o, o_intra, o_inter overlap");
+  hipStream_t s = (hipStream_t)stream;
+  if (arl2::use_mfma(d))
+    return hip_status(arl2::mfma_read_prepared(d, q, k, v, prepared, o, o_intra, o_inter, s),
+                      "prepared read");
+  void* oi = o_intra ? o_intra : ws;
+  hipError_t e = run_attention(d, q, k, v, oi, d.T, d.T, s);
+  if (e != hipSuccess) return hip_status(e, "intra-frame attention");
+  // the inter read with the prepared map: o = o_intra + Q M
+  e = arl2::generic_inter_read(d, q, static_cast<const float*>(prepared), oi, o, o_inter, s);
+  return hip_status(e, "inter-frame read");
 }
 
 arl2_status arl2_commit(const arl2_shape* shape, const void* k, const void* v, const void* phi_k,

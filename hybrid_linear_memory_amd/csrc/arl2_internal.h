@@ -70,6 +70,15 @@ hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
 // Fused read (bf16, D = 128): M = Phi_q S per head into `ws`, then the
 // attention kernel with the epilogue O = O_intra + Q M.
 size_t mfma_read_ws_bytes(const Dims& d);
+// Prepared reads: M^T = (Phi_q S)^T once per frame, then attention + Q M.
+hipError_t mfma_read_prepare(const Dims& d, const void* phi_q, const float* S, void* mt,
+                             hipStream_t s);
+hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const void* v,
+                              const void* mt, void* o, void* o_intra, void* o_inter,
+                              hipStream_t s);
+// float32 / generic: M = Phi_q S (fp32, row-major per head).
+hipError_t generic_read_prepare(const Dims& d, const void* phi_q, const float* S, float* m,
+                                hipStream_t s);
 hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
                      const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
                      void* ws, hipStream_t s);

@@ -185,6 +185,23 @@ commit_update_k(const TI* __restrict__ kp, const float* __restrict__ W,
   S_next[e] = fmaf(alpha[bh], S_prev[e], acc);
 }
 
+// M[bh, i, j] = sum_k phi[h, i, k] S[bh, k, j]  (k summed in order)
+template <typename TI>
+__global__ void __launch_bounds__(256)
+read_prepare_k(const TI* __restrict__ phi, const float* __restrict__ S, float* __restrict__ M,
+               int H, int D, long n) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const long bh = e / ((long)D * D);
+  const int i = (int)((e / D) % D);
+  const int j = (int)(e % D);
+  const TI* ph = phi + ((size_t)(bh % H) * D + i) * D;
+  const float* Sh = S + (size_t)bh * D * D + j;
+  float acc = 0.f;
+  for (int k = 0; k < D; ++k) acc = fmaf(ld(ph, k), Sh[(size_t)k * D], acc);
+  M[e] = acc;
+}
+
 template <typename TI>
 hipError_t feature_map_d(const Dims& d, const void* x, const void* phi, void* out,
                          bool norm, hipStream_t s) {
@@ -292,6 +309,17 @@ hipError_t generic_inter_read(const Dims& d, const void* q_prime, const float* S
                               const void* o_intra, void* o, void* o_inter, hipStream_t s) {
   return d.bf16 ? inter_read_d<__bf16>(d, q_prime, S, o_intra, o, o_inter, s)
                 : inter_read_d<float>(d, q_prime, S, o_intra, o, o_inter, s);
+}
+
+hipError_t generic_read_prepare(const Dims& d, const void* phi_q, const float* S, float* m,
+                                hipStream_t s) {
+  const long n = (long)d.B * d.H * d.D * d.D;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (d.bf16)
+    read_prepare_k<__bf16><<<grid, 256, 0, s>>>(static_cast<const __bf16*>(phi_q), S, m, d.H, d.D, n);
+  else
+    read_prepare_k<float><<<grid, 256, 0, s>>>(static_cast<const float*>(phi_q), S, m, d.H, d.D, n);
+  return hipGetLastError();
 }
 
 size_t generic_state_commit_ws_bytes(const Dims& d) {

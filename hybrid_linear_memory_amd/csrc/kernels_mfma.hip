@@ -1013,19 +1013,32 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const voi
 
 size_t mfma_read_ws_bytes(const Dims& d) { return (size_t)d.B * d.H * HD * HD * 2; }
 
-hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
-                     const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
-                     void* ws, hipStream_t s) {
-  __bf16* mt = static_cast<__bf16*>(ws);
-  read_prep_k<<<(unsigned)(d.B * d.H * 4), 256, 0, s>>>(static_cast<const __bf16*>(phi_q), S, mt,
-                                                       d.H);
+hipError_t mfma_read_prepare(const Dims& d, const void* phi_q, const float* S, void* mt,
+                             hipStream_t s) {
+  read_prep_k<<<(unsigned)(d.B * d.H * 4), 256, 0, s>>>(static_cast<const __bf16*>(phi_q), S,
+                                                       static_cast<__bf16*>(mt), d.H);
+  return hipGetLastError();
+}
+
+hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const void* v,
+                              const void* mt, void* o, void* o_intra, void* o_inter,
+                              hipStream_t s) {
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
   attn_mfma_k<<<(unsigned)nblk, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-      static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk, mt,
-      static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter));
+      static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk,
+      static_cast<const __bf16*>(mt), static_cast<__bf16*>(o_intra),
+      static_cast<__bf16*>(o_inter));
   return hipGetLastError();
+}
+
+hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
+                     const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
+                     void* ws, hipStream_t s) {
+  hipError_t e = mfma_read_prepare(d, phi_q, S, ws, s);
+  if (e != hipSuccess) return e;
+  return mfma_read_prepared(d, q, k, v, ws, o, o_intra, o_inter, s);
 }
 
 hipError_t mfma_feature_map(const Dims& d, const void* x, const void* phi, void* out,

@@ -65,7 +65,7 @@ class Arl2Layer:
     """
 
     def __init__(self, shape: arl2.Shape, phi_q, phi_k, phi_v, n_denoise: int | None = None,
-                 device=None):
+                 device=None, prepared: bool = True):
         self.shape = shape
         self.device = torch.device(device or "cuda")
         dt = shape.torch_dtype
@@ -76,6 +76,16 @@ class Arl2Layer:
         self._cur = 0
         self.ws = arl2.alloc_workspace(shape, arl2.OP_CLEAN_PASS, self.device)
         self.seq = PassSequencer(n_denoise)
+        # Reads of a frame all see the same S_{N-1}, so Phi_q S is formed once
+        # per frame (after each commit) and every read uses it.
+        self.prepared = prepared
+        if prepared:
+            self.M = arl2.alloc_prepared(shape, self.device)
+            self._prepare()
+
+    def _prepare(self):
+        if self.prepared:
+            arl2.read_prepare(self.shape, self.phi[0], self.S, self.M)
 
     @property
     def S(self) -> torch.Tensor:
@@ -91,6 +101,7 @@ class Arl2Layer:
             s.zero_()
         self._cur = 0
         self.seq.restore(0)
+        self._prepare()
 
     def new_output(self):
         s = self.shape
@@ -100,7 +111,11 @@ class Arl2Layer:
         """Denoising read against S_{N-1}; never writes the state."""
         self.seq.before_read()
         o = self.new_output() if o is None else o
-        arl2.read(self.shape, q, k, v, self.phi[0], self.S, o, o_intra, o_inter, self.ws, stream)
+        if self.prepared:
+            arl2.read_prepared(self.shape, q, k, v, self.M, o, o_intra, o_inter, self.ws, stream)
+        else:
+            arl2.read(self.shape, q, k, v, self.phi[0], self.S, o, o_intra, o_inter, self.ws,
+                      stream)
         self.seq.after_read()
         return o
 
@@ -109,10 +124,17 @@ class Arl2Layer:
         self.seq.before_clean_pass()
         o = self.new_output() if o is None else o
         nxt = 1 - self._cur
-        arl2.clean_pass(self.shape, q, k, v, self.phi[0], self.phi[1], self.phi[2], beta, alpha,
-                        self._S[self._cur], self._S[nxt], o, o_intra, o_inter, self.ws, stream)
+        if self.prepared:
+            arl2.read_prepared(self.shape, q, k, v, self.M, o, o_intra, o_inter, self.ws, stream)
+            arl2.commit(self.shape, k, v, self.phi[1], self.phi[2], beta, alpha,
+                        self._S[self._cur], self._S[nxt], self.ws, stream)
+        else:
+            arl2.clean_pass(self.shape, q, k, v, self.phi[0], self.phi[1], self.phi[2], beta,
+                            alpha, self._S[self._cur], self._S[nxt], o, o_intra, o_inter, self.ws,
+                            stream)
         self._cur = nxt
         self.seq.after_clean_pass()
+        self._prepare()
         return o
 
     def commit(self, k, v, beta, alpha, stream=None):
@@ -123,6 +145,7 @@ class Arl2Layer:
                     self._S[nxt], self.ws, stream)
         self._cur = nxt
         self.seq.after_clean_pass()
+        self._prepare()
 
     # checkpoint / resume: the whole cross-frame memory is S plus the frame index
     def state_dict(self) -> dict:
@@ -135,3 +158,4 @@ class Arl2Layer:
         self._S[0].copy_(S)
         self._cur = 0
         self.seq.restore(int(sd["frame"]))
+        self._prepare()

@@ -86,7 +86,8 @@ typedef enum arl2_op {
   ARL2_OP_READ = 0,
   ARL2_OP_CLEAN_PASS = 1,
   ARL2_OP_COMMIT = 2,
-  ARL2_OP_STATE_COMMIT = 3
+  ARL2_OP_STATE_COMMIT = 3,
+  ARL2_OP_READ_PREPARED = 4
 } arl2_op;
 
 /* ------------------------------------------------------------------------
@@ -146,6 +147,28 @@ arl2_status arl2_read(const arl2_shape* shape, const void* q, const void* k,
                       const void* v, const void* phi_q, const float* S,
                       void* o, void* o_intra, void* o_inter, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* Read preparation. Every token and every pass of a frame reads the same
+ * S_{N-1} (frame-level access, §2.2), and Q' S = Q (Phi_q S), so the map
+ * M = Phi_q[h] S[b,h] (D x D per head) can be formed once per frame, after the
+ * commit that produced S, and reused by all of the frame's reads.
+ * arl2_read_prepare writes M into `prepared` (caller-owned device memory of
+ * arl2_prepared_bytes(shape) bytes; its layout is private to the library:
+ * bf16 M^T for bf16 shapes, fp32 M for float32 shapes). S is only read. */
+size_t arl2_prepared_bytes(const arl2_shape* shape);
+arl2_status arl2_read_prepare(const arl2_shape* shape, const void* phi_q,
+                              const float* S, void* prepared, void* stream);
+
+/* Denoising-step read from a prepared map: o = softmax(Q K^T * scale) V + Q M,
+ * identical in meaning to arl2_read with the (Phi_q, S) the map was prepared
+ * from. o_intra / o_inter are optional extra outputs. Needs
+ * arl2_workspace_bytes(shape, ARL2_OP_READ_PREPARED) bytes of workspace (0 for
+ * bf16 shapes). */
+arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q,
+                               const void* k, const void* v,
+                               const void* prepared, void* o, void* o_intra,
+                               void* o_inter, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Commit only (the clean pass's state write without its read):
  * K' = rownorm(K Phi_k[h]), V' = V Phi_v[h], then arl2_state_commit.

@@ -177,3 +177,37 @@ def test_fullkv_comparator(dtype, D):
     K = np.concatenate([f[1] for f in frames], 2)
     V = np.concatenate([f[2] for f in frames], 2)
     assert_close(host(o), oracle.fullkv_attention(q, K, V), TOL[dtype], "fullkv")
+
+
+@pytest.mark.parametrize("case", [("bf16", 1, 3, 300, 128), ("f32", 2, 2, 70, 32)], ids=_ids)
+def test_read_paths_agree(case):
+    """The one-call read (Phi_q and S given) and the prepared read (M = Phi_q S
+    formed once) both match the oracle; on the bf16 path the one-call read is
+    the prepared read, so their bytes agree exactly. (The float32 one-call read
+    forms Q' = Q Phi_q first, so its rounding order differs.)"""
+    import torch
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"read paths {_ids(case)}")
+    sh = shape_of(w)
+    q, k, v = synth.qkv(w, 2, 0)
+    phi = synth.phi_maps(w)[0]
+    g = np.random.default_rng(7)
+    S = (g.standard_normal((w.B, w.H, w.D, w.D)) * 0.05).astype(np.float32)
+    dq, dk, dv, dphi, dS = dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), dev(phi, w.dtype), dev32(S)
+    o1, o2 = dev(np.zeros_like(q), w.dtype), dev(np.zeros_like(q), w.dtype)
+    ws = arl2.alloc_workspace(sh, arl2.OP_READ)
+    arl2.read(sh, dq, dk, dv, dphi, dS, o1, ws=ws)
+    M = arl2.alloc_prepared(sh)
+    arl2.read_prepare(sh, dphi, dS, M)
+    wsp = arl2.alloc_workspace(sh, arl2.OP_READ_PREPARED)
+    oi, oe = dev(np.zeros_like(q), w.dtype), dev(np.zeros_like(q), w.dtype)
+    arl2.read_prepared(sh, dq, dk, dv, M, o2, oi, oe, ws=wsp)
+    torch.cuda.synchronize()
+    if w.dtype == "bf16":
+        assert torch.equal(o1, o2)
+    ref = oracle.read(q, k, v, phi, S)
+    assert_close(host(o1), ref["o"], TOL[w.dtype], "o (one-call read)")
+    assert_close(host(o2), ref["o"], TOL[w.dtype], "o")
+    assert_close(host(oi), ref["o_intra"], TOL[w.dtype], "o_intra")
+    assert_close(host(oe), ref["o_inter"], TOL[w.dtype], "o_inter")
