@@ -109,8 +109,14 @@ constexpr int AQ = 128;                     // queries per workgroup
 constexpr int AKT = 64;                     // keys per tile
 constexpr int TILE_B = AKT * HD * 2;        // one 64 x 128 bf16 tile (16 KB)
 constexpr float kLazyLimit = 64.0f;         // log2 of the largest unscaled p
-// LDS: [stream][K buf 0, K buf 1, V buf 0, V buf 1] = 2 x 4 x 16 KB
-constexpr int ALDS = 2 * 4 * TILE_B;
+// LDS: the tiles of parity p (local tile index & 1) sit in arrays of their
+// own: lk[p] = [stream A K, stream B K] of parity p and lv[p] = [stream A V of
+// parity p, stream B V of parity 1-p] (stream B's V tiles are loaded one
+// iteration after its K tiles). At an iteration of parity p every read is from
+// lk[p] / lv[p] and every load in flight targets lk[1-p] / lv[1-p]: distinct
+// objects, which lets the compiler see that the reads need not wait for the
+// prefetch.
+constexpr int AKV = 2 * TILE_B;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -119,21 +125,27 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 
-// Half-tile load by one wave: rows [32*half, 32*half + 32) of a 64 x 128 bf16
-// tile into `dst` (16-byte chunk p of row r holding global chunk p ^ swz(r)).
-// `off[v]` are the lane's byte offsets within 4 consecutive rows for the
-// swizzle variant v of the instruction; a tail tile clamps rows past the last
-// key to the last key (their scores are masked and their values meet p = 0).
+// Half-tile load by one wave: rows [32*half, 32*half + 32) of the 64 x 128
+// bf16 tile at byte offset `tile_off` of the buffer `src` into `dst` (16-byte
+// chunk p of row r holding global chunk p ^ swz(r)). `off[v]` are the lane's
+// byte offsets within 4 consecutive rows for the swizzle variant v of the
+// instruction; a tail tile clamps rows past the last key to the last key (their
+// scores are masked and their values meet p = 0).
 template <bool IS_V>
-__device__ __forceinline__ void tile_load(char* dst, const char* tile_src, const int (&off)[4],
-                                          int half, int rows_valid, int lane) {
+__device__ __forceinline__ void tile_load(char* dst, __amdgpu_buffer_rsrc_t src, int tile_off,
+                                          const int (&off)[4], int half, int rows_valid,
+                                          int lane) {
+  // Byte offset of the wave's half in the tile, opaque so that the compiler
+  // forms the 8 destination and source offsets in place rather than keeping
+  // them all in scalar registers across the loop.
+  int hoff = half * 8192;
+  asm volatile("" : "+s"(hoff));
   if (rows_valid >= AKT) {
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) {
-      const int i = 8 * half + ii;
-      const int var = IS_V ? 0 : ((i & 1) | ((i >> 1) & 2));
-      const char* g = tile_src + i * 1024 + off[var];
-      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+      const int var = IS_V ? 0 : ((ii & 1) | ((ii >> 1) & 2));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + hoff + ii * 1024), 16,
+                                               off[var], tile_off + hoff + ii * 1024, 0, 0);
     }
   } else {
     const int p = lane & 15;
@@ -143,10 +155,16 @@ __device__ __forceinline__ void tile_load(char* dst, const char* tile_src, const
       const int r = 4 * i + (lane >> 4);
       const int rc = min(r, rows_valid - 1);
       const int c16 = p ^ (IS_V ? swz_v(r) : swz_k(r));
-      const char* g = tile_src + rc * 256 + c16 * 16;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + i * 1024), 16,
+                                               rc * 256 + c16 * 16, tile_off, 0, 0);
     }
   }
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled dwords).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
 // Transposing read of 4 bf16 at a byte address in LDS.
@@ -194,6 +212,13 @@ struct AttnOffsets {
   int v[4];
 };
 
+// The V tiles sit above the first 64 KB of LDS, beyond the reach of a read's
+// 16-bit immediate offset, so the V offsets carry a 64 KB bias (kVBias) that
+// the reads subtract again: the compiler then folds the rest of each address
+// into the immediate instead of forming one register per read. The offsets are
+// made opaque so that they stay one register each.
+constexpr int kVBias = 65536;
+
 __device__ __forceinline__ AttnOffsets attn_offsets(int lane) {
   AttnOffsets o;
   const int n = lane & 31, h2 = lane >> 5;
@@ -202,9 +227,11 @@ __device__ __forceinline__ AttnOffsets attn_offsets(int lane) {
   for (int kc = 0; kc < 8; ++kc) o.k[kc] = krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4);
   const int G = lane >> 4, s = lane & 15, c = s >> 2, j = s & 3;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db) {
     o.v[db] = (16 * (G >> 1) + c) * 256 + ((4 * (db ^ c) + 2 * (G & 1) + (j >> 1)) << 4) +
-              (j & 1) * 8;
+              (j & 1) * 8 + kVBias;
+    asm volatile("" : "+v"(o.v[db]));
+  }
   return o;
 }
 
@@ -271,7 +298,7 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const char* a = Vb + kb * 8192 + cc * 2048 + off.v[db];
+        const char* a = Vb + (off.v[db] - kVBias) + kb * 8192 + cc * 2048;
         const bf16x8 va = __builtin_shufflevector(tr_read(a), tr_read(a + 1024), 0, 1, 2, 3, 4,
                                                   5, 6, 7);
         acc[db] = mfma32(va, pb[kb][cc], acc[db]);
@@ -293,7 +320,11 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
             long kv_cap, float sl2, int n_qblk, const __bf16* __restrict__ mt,
             __bf16* __restrict__ o_intra, __bf16* __restrict__ o_inter) {
-  __shared__ __attribute__((aligned(1024))) char lds[ALDS];
+  __shared__ __attribute__((aligned(1024))) char lk0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lk1[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv1[AKV];
+  __shared__ float mlx[8][2][64];
   __shared__ int redo_flag;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -313,16 +344,14 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
   const AttnOffsets off = attn_offsets(lane);
 
-  // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s
+  // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s.
+  // Waves 4s + 2u + c load half c of the stream's K (u = 0) or V (u = 1) tiles.
   const int n_tiles = (n_kv + AKT - 1) / AKT;
   const int my_cnt = (n_tiles - stream + 1) / 2;
-  // waves 2r and 2r+1 load the two halves of region r = (stream, K or V)
-  const int region = wave >> 1, ld_half = wave & 1;
-  const int ld_stream = region >> 1;
-  const bool ld_v = region & 1;
-  const int ld_cnt = (n_tiles - ld_stream + 1) / 2;
-  const char* ld_src = reinterpret_cast<const char*>((ld_v ? v : k) + (size_t)bh * kv_cap * HD);
-  char* ld_base = lds + ld_stream * 4 * TILE_B + (ld_v ? 2 * TILE_B : 0);
+  const int ld_half = wave & 1;
+  const bool ld_v = (wave >> 1) & 1;
+  const __amdgpu_buffer_rsrc_t ld_src =
+      buffer_rsrc((ld_v ? v : k) + (size_t)bh * kv_cap * HD, (uint32_t)n_kv * (HD * 2));
   int ld_off[4];
   {
     const int p = lane & 15, L4 = lane >> 4;
@@ -333,22 +362,17 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       ld_off[var] = L4 * 256 + ((p ^ (ld_v ? swz_v(r) : swz_k(r))) << 4);
     }
   }
-  const char* Kbase = lds + stream * 4 * TILE_B;
-  const char* Vbase = Kbase + 2 * TILE_B;
-
-  auto issue = [&](int j) {   // local tile j of the wave's load region into buffer j & 1
-    if (j < ld_cnt) {
-      const int g = 2 * j + ld_stream;
-      const char* src = ld_src + (size_t)g * TILE_B;
-      char* dst = ld_base + (j & 1) * TILE_B;
-      const int rows = n_kv - g * AKT;
-      if (ld_v) tile_load<true>(dst, src, ld_off, ld_half, rows, lane);
-      else tile_load<false>(dst, src, ld_off, ld_half, rows, lane);
-    }
+  auto load_k = [&](char* dst, int j) __attribute__((always_inline)) {
+    const int g = 2 * j + stream;
+    tile_load<false>(dst, ld_src, g * TILE_B, ld_off, ld_half, n_kv - g * AKT, lane);
+  };
+  auto load_v = [&](char* dst, int j) __attribute__((always_inline)) {
+    const int g = 2 * j + stream;
+    tile_load<true>(dst, ld_src, g * TILE_B, ld_off, ld_half, n_kv - g * AKT, lane);
   };
   // Every wave's loads of the current tile have landed once its own have
   // (vmcnt) and all waves have reached the barrier.
-  auto sync = [&]() {
+  auto sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0070);     // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
   };
@@ -358,9 +382,6 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // it, stream A computes the scores of its tile it, their softmax and P V,
   // while stream B first finishes its tile it-1 (softmax, P V, started from
   // scores kept in registers) and then computes the scores of its tile it.
-  // Stream B's V tiles are therefore loaded one iteration later than its K
-  // tiles.
-  const bool v_late = ld_stream == 1 && ld_v;
   const int n_iter = max((n_tiles + 1) / 2, n_tiles / 2 + 1);   // same for every wave
   f32x16 acc[4];
   float l = 0.f, m_ref = -INFINITY, m_seen = -INFINITY;
@@ -374,10 +395,9 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     m_ref = m_seen;
     bool over = false;
     if (tid == 0) redo_flag = 0;
-    if (!v_late) issue(0);
     f32x16 s[2];
-    auto scores = [&](int j) {
-      attn_qk(s, Kbase + (j & 1) * TILE_B, off, qreg);
+    auto scores = [&](int j, const char* Kb) __attribute__((always_inline)) {
+      attn_qk(s, Kb, off, qreg);
       const int valid = n_kv - (2 * j + stream) * AKT;
       if (valid < AKT) attn_mask(s, valid, lane);
       const float mt = attn_tile_max(s);
@@ -387,22 +407,43 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         over |= (mt - m_ref) * sl2 > kLazyLimit;
       }
     };
+    // Iteration it of parity p: kc / vc = lk[p] / lv[p] (read), kn / vn =
+    // lk[1-p] / lv[1-p] (loaded).
+    auto step_a = [&](int it, char* kc, char* vc, char* kn, char* vn)
+        __attribute__((always_inline)) {
+      sync();
+      if (it + 1 < my_cnt) {
+        if (ld_v) load_v(vn, it + 1);
+        else load_k(kn, it + 1);
+      }
+      if (it < my_cnt) {
+        scores(it, kc);
+        attn_softmax_pv(acc, l, m_ref, s, vc, off, sl2);
+      }
+    };
+    auto step_b = [&](int it, char* kc, char* vc, char* kn, char* vn)
+        __attribute__((always_inline)) {
+      sync();
+      if (it >= 1 && it <= my_cnt) attn_softmax_pv(acc, l, m_ref, s, vc + TILE_B, off, sl2);
+      if (ld_v) {
+        if (it < my_cnt) load_v(vn + TILE_B, it);
+      } else {
+        if (it + 1 < my_cnt) load_k(kn + TILE_B, it + 1);
+      }
+      if (it < my_cnt) scores(it, kc + TILE_B);
+    };
     if (stream == 0) {
-      for (int it = 0; it < n_iter; ++it) {
-        sync();
-        issue(it + 1);
-        if (it < my_cnt) {
-          scores(it);
-          attn_softmax_pv(acc, l, m_ref, s, Vbase + (it & 1) * TILE_B, off, sl2);
-        }
+      if (ld_v) load_v(lv0, 0);
+      else load_k(lk0, 0);
+      for (int it = 0; it < n_iter; it += 2) {
+        step_a(it, lk0, lv0, lk1, lv1);
+        if (it + 1 < n_iter) step_a(it + 1, lk1, lv1, lk0, lv0);
       }
     } else {
-      for (int it = 0; it < n_iter; ++it) {
-        sync();
-        if (it >= 1 && it <= my_cnt)
-          attn_softmax_pv(acc, l, m_ref, s, Vbase + ((it - 1) & 1) * TILE_B, off, sl2);
-        issue(v_late ? it : it + 1);
-        if (it < my_cnt) scores(it);
+      if (!ld_v && my_cnt > 0) load_k(lk0 + TILE_B, 0);
+      for (int it = 0; it < n_iter; it += 2) {
+        step_b(it, lk0, lv0, lk1, lv1);
+        if (it + 1 < n_iter) step_b(it + 1, lk1, lv1, lk0, lv0);
       }
     }
     if (__any(over)) redo_flag = 1;     // every writer stores 1
@@ -414,9 +455,10 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   };
   if (run_pass(0)) run_pass(1);
 
-  // Inter-frame branch for this wave's queries: O_inter^T = M^T Q^T, each wave
-  // of a stream pair taking two of the four 32-column blocks (stream A blocks
-  // 0-1, stream B blocks 2-3; B hands its blocks over with its partials).
+  // Stream A finalises output columns 0-63 (blocks 0-1) and stream B columns
+  // 64-127 (blocks 2-3); the two waves of a pair swap the other half of their
+  // accumulators through LDS. The inter-frame branch of a wave's columns,
+  // O_inter^T = M^T Q^T, is computed by the wave that writes them.
   f32x16 oi[2];
   if (mt) {
     const __bf16* mrow = mt + (size_t)bh * HD * HD + 8 * h2;
@@ -429,28 +471,21 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         oi[b2] = mfma32(ld8(mrow + (size_t)(32 * db + n) * HD + 16 * kc), qreg[kc], oi[b2]);
     }
   }
-
-  // merge stream B into stream A through LDS
-  constexpr int EXW = 98;                 // floats per lane: 64 acc + m + l + 32 inter
-  float* ex = reinterpret_cast<float*>(lds) + (wave & 3) * (EXW * 64);
-  if (stream == 1) {
+  float* ex_w = reinterpret_cast<float*>(stream == 0 ? lk0 : lk1) + (wave & 3) * (32 * 64);
+  const float* ex_r =
+      reinterpret_cast<const float*>(stream == 0 ? lk1 : lk0) + (wave & 3) * (32 * 64);
+  // (selected whole, so that the accumulators are never indexed at run time)
+  const f32x16 give[2] = {stream == 0 ? acc[2] : acc[0], stream == 0 ? acc[3] : acc[1]};
+  const f32x16 keep[2] = {stream == 0 ? acc[0] : acc[2], stream == 0 ? acc[1] : acc[3]};
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ex[(db * 16 + r) * 64 + lane] = acc[db][r];
-    ex[64 * 64 + lane] = m_ref;
-    ex[65 * 64 + lane] = l;
-    if (mt) {
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ex[(66 + b2 * 16 + r) * 64 + lane] = oi[b2][r];
-    }
-  }
+    for (int r = 0; r < 16; ++r) ex_w[(b2 * 16 + r) * 64 + lane] = give[b2][r];
+  mlx[wave][0][lane] = m_ref;
+  mlx[wave][1][lane] = l;
   __syncthreads();
-  if (stream == 1) return;
-  const float mb = ex[64 * 64 + lane];
-  const float lb = ex[65 * 64 + lane];
+  const float mb = mlx[wave ^ 4][0][lane];
+  const float lb = mlx[wave ^ 4][1][lane];
   const float m = fmaxf(m_ref, mb);
   const float fa = __builtin_amdgcn_exp2f((m_ref - m) * sl2);
   const float fb = __builtin_amdgcn_exp2f((mb - m) * sl2);
@@ -458,17 +493,17 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (t < T) {
     const size_t row = ((size_t)bh * T + t) * HD + 4 * h2;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const int db = 2 * stream + b2;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         bf16x4 w, wi, we;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * jj + i;
-          const float vb = ex[(db * 16 + r) * 64 + lane];
-          const float intra = (acc[db][r] * fa + vb * fb) * inv;
-          float inter = 0.f;
-          if (mt) inter = db < 2 ? oi[db][r] : ex[(66 + (db - 2) * 16 + r) * 64 + lane];
+          const float vb = ex_r[(b2 * 16 + r) * 64 + lane];
+          const float intra = (keep[b2][r] * fa + vb * fb) * inv;
+          const float inter = mt ? oi[b2][r] : 0.f;
           w[i] = (__bf16)(intra + inter);
           wi[i] = (__bf16)intra;
           we[i] = (__bf16)inter;
@@ -478,6 +513,7 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         if (o_intra) *reinterpret_cast<bf16x4*>(o_intra + off_o) = wi;
         if (o_inter) *reinterpret_cast<bf16x4*>(o_inter + off_o) = we;
       }
+    }
   }
 }
 
