@@ -124,6 +124,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
+__device__ __forceinline__ int swz_r(int r) { return r & 15; }
 
 // Half-tile load by one wave: rows [32*half, 32*half + 32) of the 64 x 128
 // bf16 tile at byte offset `tile_off` of the buffer `src` into `dst` (16-byte
@@ -151,11 +152,10 @@ __device__ __forceinline__ void tile_load(char* dst, __amdgpu_buffer_rsrc_t src,
     const int p = lane & 15;
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) {
-      const int i = 8 * half + ii;
-      const int r = 4 * i + (lane >> 4);
+      const int r = 32 * half + 4 * ii + (lane >> 4);
       const int rc = min(r, rows_valid - 1);
       const int c16 = p ^ (IS_V ? swz_v(r) : swz_k(r));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + i * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + hoff + ii * 1024), 16,
                                                rc * 256 + c16 * 16, tile_off, 0, 0);
     }
   }
@@ -370,6 +370,24 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int g = 2 * j + stream;
     tile_load<true>(dst, ld_src, g * TILE_B, ld_off, ld_half, n_kv - g * AKT, lane);
   };
+  // M^T (the inter-frame map, 32 KB) is loaded during the last iteration into
+  // the K buffers that iteration leaves idle (rows under the swz_r swizzle),
+  // wave w taking rows [16w, 16w + 16).
+  const char* m_src = mt ? reinterpret_cast<const char*>(mt + (size_t)bh * HD * HD) : nullptr;
+  auto load_m = [&](char* dst) __attribute__((always_inline)) {
+    if (!m_src) return;
+    // (offsets formed here, not hoisted out of the loop into live registers)
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    const __amdgpu_buffer_rsrc_t mr = buffer_rsrc(m_src, HD * HD * 2);
+#pragma unroll
+    for (int qi = 0; qi < 4; ++qi) {
+      const int r = 16 * wave + 4 * qi + (lo >> 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_void_t*)(dst + (16 * wave + 4 * qi) * 256),
+                                               16, r * 256 + (((lo & 15) ^ swz_r(r)) << 4), 0, 0,
+                                               0);
+    }
+  };
   // Every wave's loads of the current tile have landed once its own have
   // (vmcnt) and all waves have reached the barrier.
   auto sync = [&]() __attribute__((always_inline)) {
@@ -412,6 +430,7 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     auto step_a = [&](int it, char* kc, char* vc, char* kn, char* vn)
         __attribute__((always_inline)) {
       sync();
+      if (it == n_iter - 1) load_m(kn);
       if (it + 1 < my_cnt) {
         if (ld_v) load_v(vn, it + 1);
         else load_k(kn, it + 1);
@@ -424,6 +443,7 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     auto step_b = [&](int it, char* kc, char* vc, char* kn, char* vn)
         __attribute__((always_inline)) {
       sync();
+      if (it == n_iter - 1) load_m(kn);
       if (it >= 1 && it <= my_cnt) attn_softmax_pv(acc, l, m_ref, s, vc + TILE_B, off, sl2);
       if (ld_v) {
         if (it < my_cnt) load_v(vn + TILE_B, it);
@@ -458,22 +478,26 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // Stream A finalises output columns 0-63 (blocks 0-1) and stream B columns
   // 64-127 (blocks 2-3); the two waves of a pair swap the other half of their
   // accumulators through LDS. The inter-frame branch of a wave's columns,
-  // O_inter^T = M^T Q^T, is computed by the wave that writes them.
+  // O_inter^T = M^T Q^T, is computed by the wave that writes them, from M^T in
+  // the K buffers of parity n_iter & 1.
   f32x16 oi[2];
   if (mt) {
-    const __bf16* mrow = mt + (size_t)bh * HD * HD + 8 * h2;
+    const char* mb = (n_iter & 1) ? lk1 : lk0;
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
-      const int db = 2 * stream + b2;
+      const int row = 32 * (2 * stream + b2) + n;
       oi[b2] = zero16();
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        oi[b2] = mfma32(ld8(mrow + (size_t)(32 * db + n) * HD + 16 * kc), qreg[kc], oi[b2]);
+      for (int kc = 0; kc < 8; ++kc) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(mb + row * 256 + (((2 * kc + h2) ^ swz_r(row)) << 4));
+        oi[b2] = mfma32(a, qreg[kc], oi[b2]);
+      }
     }
   }
-  float* ex_w = reinterpret_cast<float*>(stream == 0 ? lk0 : lk1) + (wave & 3) * (32 * 64);
+  float* ex_w = reinterpret_cast<float*>(stream == 0 ? lv0 : lv1) + (wave & 3) * (32 * 64);
   const float* ex_r =
-      reinterpret_cast<const float*>(stream == 0 ? lk1 : lk0) + (wave & 3) * (32 * 64);
+      reinterpret_cast<const float*>(stream == 0 ? lv1 : lv0) + (wave & 3) * (32 * 64);
   // (selected whole, so that the accumulators are never indexed at run time)
   const f32x16 give[2] = {stream == 0 ? acc[2] : acc[0], stream == 0 ? acc[3] : acc[1]};
   const f32x16 keep[2] = {stream == 0 ? acc[0] : acc[2], stream == 0 ? acc[1] : acc[3]};
@@ -842,7 +866,6 @@ constexpr int F_SS = F_KPB + F_SLICE_B;         // [4 waves][32 tokens] partial 
 constexpr int F_BETA = F_SS + 4 * FT * 4;       // [buf][32] beta
 constexpr int F_LDS = F_BETA + 2 * FT * 4;
 
-__device__ __forceinline__ int swz_r(int r) { return r & 15; }
 
 // Wave-wide DMA of `n_inst` x 4 rows (256-byte rows) starting at row r_begin of
 // a row-major bf16 matrix into LDS under chunk swizzle `swz` (rows past
