@@ -101,14 +101,17 @@ __device__ __forceinline__ uint32_t elem(const uint4& x, int e) {
 //
 // Exponents are taken against a reference maximum fixed for the pass (the
 // first tile's row maximum), so the accumulators are never rescaled inside the
-// loop. If a later tile exceeds it by more than 2^kLazyLimit (never for
-// bounded inputs), the workgroup redoes the pass with the exact row maximum
-// seen in the first pass.
+// loop and later tiles need no row maximum at all. Each p is at most the
+// lane's running sum l; if some l ends above 2^64 (a later tile exceeding the
+// reference by more than 64 in log2 units, never for bounded inputs), the
+// workgroup finds the exact row maxima in a scores-only pass and redoes the
+// pass against them. Row sums add the bf16-rounded p that enter P V, so the
+// normalised weights sum to one.
 // ===========================================================================
 constexpr int AQ = 128;                     // queries per workgroup
 constexpr int AKT = 64;                     // keys per tile
 constexpr int TILE_B = AKT * HD * 2;        // one 64 x 128 bf16 tile (16 KB)
-constexpr float kLazyLimit = 64.0f;         // log2 of the largest unscaled p
+constexpr float kRedoSum = 18446744073709551616.0f;   // 2^64: largest accepted l
 // LDS: the tiles of parity p (local tile index & 1) sit in arrays of their
 // own: lk[p] = [stream A K, stream B K] of parity p and lv[p] = [stream A V of
 // parity p, stream B V of parity 1-p] (stream B's V tiles are loaded one
@@ -281,14 +284,24 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
                                                 const AttnOffsets& off, float sl2) {
   const float mc = m_ref * sl2;
   bf16x8 pb[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      pb[kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -mc));
+  // row sums of the rounded p, two at a time (dot with (1, 1))
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -mc));
-      if (r & 1) ls1 += p; else ls0 += p;
-      pb[kb][r >> 3][r & 7] = (__bf16)p;
+    for (int cc = 0; cc < 2; ++cc) {
+      const bf16x8 x = pb[kb][cc];
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, ls1, false);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, ls1, false);
     }
   l += ls0 + ls1;
   // four independent accumulation chains advance together
@@ -312,9 +325,11 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
   __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
 }
 
-// With `mt` set (the fused read), the epilogue adds the inter-frame branch
-// O_inter = Q M, M = Phi_q S (given transposed, bf16 [B, H, D_v, D_in]); the
-// two branches can also be written separately to o_intra / o_inter.
+// With INTER (the fused read), the epilogue adds the inter-frame branch
+// O_inter = Q M, M = Phi_q S (given transposed in `mt`, bf16 [B, H, D_v,
+// D_in]); the two branches can also be written separately to o_intra /
+// o_inter.
+template <bool INTER>
 __global__ void __launch_bounds__(512, 1)
 attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
@@ -373,9 +388,9 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // M^T (the inter-frame map, 32 KB) is loaded during the last iteration into
   // the K buffers that iteration leaves idle (rows under the swz_r swizzle),
   // wave w taking rows [16w, 16w + 16).
-  const char* m_src = mt ? reinterpret_cast<const char*>(mt + (size_t)bh * HD * HD) : nullptr;
+  const char* m_src = INTER ? reinterpret_cast<const char*>(mt + (size_t)bh * HD * HD) : nullptr;
   auto load_m = [&](char* dst) __attribute__((always_inline)) {
-    if (!m_src) return;
+    if (!INTER) return;
     // (offsets formed here, not hoisted out of the loop into live registers)
     int lo = lane;
     asm volatile("" : "+v"(lo));
@@ -402,28 +417,25 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // scores kept in registers) and then computes the scores of its tile it.
   const int n_iter = max((n_tiles + 1) / 2, n_tiles / 2 + 1);   // same for every wave
   f32x16 acc[4];
-  float l = 0.f, m_ref = -INFINITY, m_seen = -INFINITY;
-  // One pass over the keys; returns whether a redo with the exact maximum is
-  // needed. Written as a lambda called twice (rather than a loop) so that the
-  // rarely taken second pass does not extend live ranges in the first.
-  auto run_pass = [&](const int pass) -> bool {
+  float l = 0.f, m_ref = -INFINITY;
+  // One pass over the keys. Mode 0: reference maximum from the stream's first
+  // tile; returns whether the sums call for a redo. Mode 1: scores only, exact
+  // row maxima into m_ref. Mode 2: the pass against the exact maxima. Written
+  // as a lambda called per mode (rather than a loop) so that the rarely taken
+  // later modes do not extend live ranges in the first.
+  auto run_pass = [&](const int mode) -> bool {
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = zero16();
     l = 0.f;
-    m_ref = m_seen;
-    bool over = false;
+    if (mode == 1) m_ref = -INFINITY;
     if (tid == 0) redo_flag = 0;
     f32x16 s[2];
     auto scores = [&](int j, const char* Kb) __attribute__((always_inline)) {
       attn_qk(s, Kb, off, qreg);
       const int valid = n_kv - (2 * j + stream) * AKT;
       if (valid < AKT) attn_mask(s, valid, lane);
-      const float mt = attn_tile_max(s);
-      if (pass == 0) {
-        if (j == 0) m_ref = mt;
-        m_seen = fmaxf(m_seen, mt);
-        over |= (mt - m_ref) * sl2 > kLazyLimit;
-      }
+      if (mode == 1) m_ref = fmaxf(m_ref, attn_tile_max(s));
+      if (mode == 0 && j == 0) m_ref = attn_tile_max(s);
     };
     // Iteration it of parity p: kc / vc = lk[p] / lv[p] (read), kn / vn =
     // lk[1-p] / lv[1-p] (loaded).
@@ -437,14 +449,15 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
       if (it < my_cnt) {
         scores(it, kc);
-        attn_softmax_pv(acc, l, m_ref, s, vc, off, sl2);
+        if (mode != 1) attn_softmax_pv(acc, l, m_ref, s, vc, off, sl2);
       }
     };
     auto step_b = [&](int it, char* kc, char* vc, char* kn, char* vn)
         __attribute__((always_inline)) {
       sync();
       if (it == n_iter - 1) load_m(kn);
-      if (it >= 1 && it <= my_cnt) attn_softmax_pv(acc, l, m_ref, s, vc + TILE_B, off, sl2);
+      if (mode != 1 && it >= 1 && it <= my_cnt)
+        attn_softmax_pv(acc, l, m_ref, s, vc + TILE_B, off, sl2);
       if (ld_v) {
         if (it < my_cnt) load_v(vn + TILE_B, it);
       } else {
@@ -466,14 +479,17 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         if (it + 1 < n_iter) step_b(it + 1, lk1, lv1, lk0, lv0);
       }
     }
-    if (__any(over)) redo_flag = 1;     // every writer stores 1
+    if (mode == 0 && __any(l > kRedoSum)) redo_flag = 1;     // every writer stores 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int redo = redo_flag;
     __syncthreads();                     // everyone has read the flag
-    return redo != 0;
+    return mode == 0 && redo != 0;
   };
-  if (run_pass(0)) run_pass(1);
+  if (run_pass(0)) {
+    run_pass(1);
+    run_pass(2);
+  }
 
   // Stream A finalises output columns 0-63 (blocks 0-1) and stream B columns
   // 64-127 (blocks 2-3); the two waves of a pair swap the other half of their
@@ -481,7 +497,7 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // O_inter^T = M^T Q^T, is computed by the wave that writes them, from M^T in
   // the K buffers of parity n_iter & 1.
   f32x16 oi[2];
-  if (mt) {
+  if (INTER) {
     const char* mb = (n_iter & 1) ? lk1 : lk0;
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
@@ -527,7 +543,7 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           const int r = 4 * jj + i;
           const float vb = ex_r[(b2 * 16 + r) * 64 + lane];
           const float intra = (keep[b2][r] * fa + vb * fb) * inv;
-          const float inter = mt ? oi[b2][r] : 0.f;
+          const float inter = INTER ? oi[b2][r] : 0.f;
           w[i] = (__bf16)(intra + inter);
           wi[i] = (__bf16)intra;
           we[i] = (__bf16)inter;
@@ -1063,7 +1079,7 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const voi
                           int64_t n_kv, int64_t kv_cap, hipStream_t s) {
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
-  attn_mfma_k<<<(unsigned)nblk, 512, 0, s>>>(
+  attn_mfma_k<false><<<(unsigned)nblk, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, (int)n_kv, (long)kv_cap, d.scale * kLog2e, n_qblk, nullptr,
       nullptr, nullptr);
@@ -1084,7 +1100,7 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
                               hipStream_t s) {
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
-  attn_mfma_k<<<(unsigned)nblk, 512, 0, s>>>(
+  attn_mfma_k<true><<<(unsigned)nblk, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk,
       static_cast<const __bf16*>(mt), static_cast<__bf16*>(o_intra),

@@ -70,6 +70,25 @@ def test_intra_attn(case, stress):
     assert_close(host(o)[:, :, rows], ref, TOL[w.dtype], "o_intra")
 
 
+def test_intra_attn_far_maximum():
+    """Keys whose scores exceed every score of their stream's first tile by
+    far more than 64 in log2 units (beyond the fixed-reference exponent range):
+    the kernel must take its exact-maximum redo and still match the oracle."""
+    from hybrid_linear_memory_amd import arl2
+    w = _w("bf16", 1, 2, 300, 128)
+    log("intra_attn far maximum")
+    q, k, v = synth.qkv(w, 0, 1)
+    q = synth.bf16_round(q + np.where(np.arange(128) == 0, 4.0, 0.0).astype(np.float32))
+    k = k.copy()
+    for t in (250, 290):             # second tiles of streams B (keys 192-255) and A (256-299)
+        k[:, :, t, :] = 0.0
+        k[:, :, t, 0] = 250.0
+    o = dev(np.zeros_like(q), w.dtype)
+    arl2.intra_attn(shape_of(w), dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), o)
+    ref = oracle.intra_attention(q, k, v)
+    assert_close(host(o), ref, TOL[w.dtype], "o_intra")
+
+
 @pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
 def test_inter_read(case):
     from hybrid_linear_memory_amd import arl2
