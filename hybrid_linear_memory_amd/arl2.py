@@ -21,6 +21,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so
 F32 = 0
 BF16 = 1
 OP_READ, OP_CLEAN_PASS, OP_COMMIT, OP_STATE_COMMIT, OP_READ_PREPARED = 0, 1, 2, 3, 4
+OP_CLEAN_PASS_PREPARED = 5
 
 STATUS_NAMES = {
     0: "ARL2_OK", 1: "ARL2_E_NULL", 2: "ARL2_E_SHAPE", 3: "ARL2_E_DTYPE",
@@ -53,6 +54,8 @@ SIGNATURES = {
     "arl2_prepared_bytes": (_sz, [_SP]),
     "arl2_read_prepare": (_i32, [_SP, _vp, _vp, _vp, _vp]),
     "arl2_read_prepared": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "arl2_clean_pass_prepared": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_workspace_bytes": (_sz, [_SP, _i32]),
     "arl2_status_string": (ctypes.c_char_p, [_i32]),
     "arl2_last_error": (ctypes.c_char_p, []),
@@ -207,6 +210,18 @@ def read_prepared(shape: Shape, q, k, v, prepared, o, o_intra=None, o_inter=None
     _check(_lib.arl2_read_prepared(
         ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
         _ptr(prepared, "prepared"), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
+        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def clean_pass_prepared(shape: Shape, q, k, v, prepared, phi_k, phi_v, beta, alpha, S_prev,
+                        S_next, o, o_intra=None, o_inter=None, ws=None, stream=None):
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_clean_pass_prepared(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(prepared, "prepared"), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
+        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
+        _ptr(S_next, "S_next", f), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
         _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 

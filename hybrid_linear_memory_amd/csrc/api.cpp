@@ -110,6 +110,11 @@ size_t ws_commit(const arl2::Dims& d) {
   if (arl2::use_mfma(d)) return arl2::round_up(arl2::mfma_commit_ws_bytes(d), 256);
   return 2 * arl2::round_up(arl2::act_bytes(d), 256) + arl2::round_up(commit_ws(d), 256);
 }
+// bf16: the commit partials of the one-launch clean pass; otherwise the read
+// and the commit run one after the other in the same workspace.
+size_t ws_clean_pass_prepared(const arl2::Dims& d) {
+  return arl2::use_mfma(d) ? ws_commit(d) : std::max(ws_read_prepared(d), ws_commit(d));
+}
 
 arl2_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return ARL2_OK;
@@ -222,6 +227,7 @@ size_t arl2_workspace_bytes(const arl2_shape* shape, int32_t op) {
     case ARL2_OP_CLEAN_PASS: return std::max(ws_read(d), ws_commit(d));
     case ARL2_OP_STATE_COMMIT: return commit_ws(d);
     case ARL2_OP_READ_PREPARED: return ws_read_prepared(d);
+    case ARL2_OP_CLEAN_PASS_PREPARED: return ws_clean_pass_prepared(d);
     default: return 0;
   }
 }
@@ -441,6 +447,59 @@ arl2_status arl2_clean_pass(const arl2_shape* shape, const void* q, const void* 
   st = do_read(d, q, k, v, phi_q, S_prev, o, o_intra, o_inter, ws, (hipStream_t)stream);
   if (st != ARL2_OK) return st;
   return do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, (hipStream_t)stream);
+}
+
+arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q, const void* k,
+                                     const void* v, const void* prepared, const void* phi_k,
+                                     const void* phi_v, const float* beta, const float* alpha,
+                                     const float* S_prev, float* S_next, void* o, void* o_intra,
+                                     void* o_inter, void* ws, size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(prepared);
+  REQUIRE_PTR(phi_k);
+  REQUIRE_PTR(phi_v);
+  REQUIRE_PTR(beta);
+  REQUIRE_PTR(alpha);
+  REQUIRE_PTR(S_prev);
+  REQUIRE_PTR(S_next);
+  REQUIRE_PTR(o);
+  OPTIONAL_PTR(o_intra);
+  OPTIONAL_PTR(o_inter);
+  if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
+  const size_t need = ws_clean_pass_prepared(d);
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d);
+  const Range outs[4] = {{o, ab}, {o_intra, ab}, {o_inter, ab}, {S_next, state_bytes(d)}};
+  const Range ins[10] = {{q, ab},
+                         {k, ab},
+                         {v, ab},
+                         {prepared, prepared_bytes(d)},
+                         {phi_k, phi_bytes(d)},
+                         {phi_v, phi_bytes(d)},
+                         {S_prev, state_bytes(d)},
+                         {ws, need},
+                         {beta, (size_t)d.B * d.H * d.T * 4},
+                         {alpha, (size_t)d.B * d.H * 4}};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ARL2_E_ALIAS, "two outputs overlap");
+  hipStream_t s = (hipStream_t)stream;
+  if (arl2::use_mfma(d))
+    return hip_status(arl2::mfma_clean_pass_prepared(d, q, k, v, prepared, phi_k, phi_v, beta,
+                                                     alpha, S_prev, S_next, o, o_intra, o_inter,
+                                                     ws, s),
+                      "clean pass");
+  st = arl2_read_prepared(shape, q, k, v, prepared, o, o_intra, o_inter, ws, ws_bytes, stream);
+  if (st != ARL2_OK) return st;
+  return do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, s);
 }
 
 arl2_status arl2_fullkv_attn(const arl2_shape* shape, const void* q, const void* k_cache,

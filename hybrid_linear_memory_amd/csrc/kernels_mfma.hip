@@ -329,23 +329,20 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
 // O_inter = Q M, M = Phi_q S (given transposed in `mt`, bf16 [B, H, D_v,
 // D_in]); the two branches can also be written separately to o_intra /
 // o_inter.
+// One workgroup (logical block `blk`) of the attention; the LDS arrays are the
+// kernel's (see AKV) and reach here as parameters so that, once inlined, every
+// access still names its own array.
 template <bool INTER>
-__global__ void __launch_bounds__(512, 1)
-attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-            const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
-            long kv_cap, float sl2, int n_qblk, const __bf16* __restrict__ mt,
-            __bf16* __restrict__ o_intra, __bf16* __restrict__ o_inter) {
-  __shared__ __attribute__((aligned(1024))) char lk0[AKV];
-  __shared__ __attribute__((aligned(1024))) char lk1[AKV];
-  __shared__ __attribute__((aligned(1024))) char lv0[AKV];
-  __shared__ __attribute__((aligned(1024))) char lv1[AKV];
-  __shared__ float mlx[8][2][64];
-  __shared__ int redo_flag;
+__device__ __forceinline__ void attn_block(
+    int blk, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv, long kv_cap,
+    float sl2, int n_qblk, const __bf16* __restrict__ mt, __bf16* __restrict__ o_intra,
+    __bf16* __restrict__ o_inter, char* lk0, char* lk1, char* lv0, char* lv1,
+    float (*mlx)[2][64], int& redo_flag) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const long bh = blk / n_qblk;
   const int qblk = blk % n_qblk;
   const int stream = wave >> 2;
@@ -555,6 +552,22 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
     }
   }
+}
+
+template <bool INTER>
+__global__ void __launch_bounds__(512, 1)
+attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+            const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
+            long kv_cap, float sl2, int n_qblk, const __bf16* __restrict__ mt,
+            __bf16* __restrict__ o_intra, __bf16* __restrict__ o_inter) {
+  __shared__ __attribute__((aligned(1024))) char lk0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lk1[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv1[AKV];
+  __shared__ float mlx[8][2][64];
+  __shared__ int redo_flag;
+  attn_block<INTER>(xcd_remap(blockIdx.x, gridDim.x), q, k, v, o, T, n_kv, kv_cap, sl2, n_qblk,
+                    mt, o_intra, o_inter, lk0, lk1, lv0, lv1, mlx, redo_flag);
 }
 
 // ===========================================================================
@@ -873,14 +886,15 @@ commit_mfma_k(const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
 constexpr int FT = 32;                          // tokens per slice
 constexpr int F_PHI_B = HD * HD * 2;            // 32 KB per map
 constexpr int F_SLICE_B = FT * HD * 2;          // 8 KB per 32-token slice
-constexpr int F_PHIK = 0;
-constexpr int F_PHIV = F_PHIK + F_PHI_B;
-constexpr int F_RAW = F_PHIV + F_PHI_B;         // [buf][K, V] raw slices
-constexpr int F_KPA = F_RAW + 4 * F_SLICE_B;    // K' rows, row-read swizzle (swz_k)
+// LDS: four regions, each within one 32 KB array: Phi_k, Phi_v, the raw
+// slices ([buf][K, V]) and the K' region below.
+constexpr int F_RAW_B = 4 * F_SLICE_B;          // 32 KB
+constexpr int F_KPA = 0;                        // K' rows, row-read swizzle (swz_k)
 constexpr int F_KPB = F_KPA + F_SLICE_B;        // K' rows, transposing-read swizzle (swz_v)
 constexpr int F_SS = F_KPB + F_SLICE_B;         // [4 waves][32 tokens] partial sums of squares
 constexpr int F_BETA = F_SS + 4 * FT * 4;       // [buf][32] beta
-constexpr int F_LDS = F_BETA + 2 * FT * 4;
+constexpr int F_KP_B = F_BETA + 2 * FT * 4;
+static_assert(F_KP_B <= AKV && F_RAW_B <= AKV && F_PHI_B <= AKV, "commit regions fit the arrays");
 
 
 // Wave-wide DMA of `n_inst` x 4 rows (256-byte rows) starting at row r_begin of
@@ -900,19 +914,20 @@ __device__ __forceinline__ void rows_load(char* dst, const char* src, int r_begi
   }
 }
 
-__global__ void __launch_bounds__(256)
-commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-               const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
-               const float* __restrict__ beta, const float* __restrict__ alpha,
-               const float* __restrict__ S_prev, float* __restrict__ S_next,
-               float* __restrict__ partial, int H, int T, int chunk_tokens, int n_chunks,
-               long n_bh) {
-  __shared__ __attribute__((aligned(1024))) char lds[F_LDS];
+// One workgroup (logical block `blk`, threads 0-255) of the fused commit, on
+// the LDS regions l_phik, l_phiv (32 KB each), l_raw (F_RAW_B) and l_kp
+// (F_KP_B).
+__device__ __forceinline__ void commit_block(
+    int blk, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
+    const float* __restrict__ beta, const float* __restrict__ alpha,
+    const float* __restrict__ S_prev, float* __restrict__ S_next, float* __restrict__ partial,
+    int H, int T, int chunk_tokens, int n_chunks, long n_bh, char* l_phik, char* l_phiv,
+    char* l_raw, char* l_kp) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const long bh = blk / n_chunks;
   const int chunk = blk % n_chunks;
   const int h = (int)(bh % H);
@@ -924,18 +939,18 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
   const char* kh = reinterpret_cast<const char*>(k + (size_t)bh * T * HD);
   const char* vh = reinterpret_cast<const char*>(v + (size_t)bh * T * HD);
   const float* bt = beta + (size_t)bh * T;
-  float* fbeta = reinterpret_cast<float*>(lds + F_BETA);
-  float* fss = reinterpret_cast<float*>(lds + F_SS);
+  float* fbeta = reinterpret_cast<float*>(l_kp + F_BETA);
+  float* fss = reinterpret_cast<float*>(l_kp + F_SS);
 
   // maps: waves 0-1 stage Phi_k, waves 2-3 Phi_v (64 rows each)
   {
     const char* src = reinterpret_cast<const char*>((wave < 2 ? phi_k : phi_v) + (size_t)h * HD * HD);
-    rows_load<1>(lds + (wave < 2 ? F_PHIK : F_PHIV), src, 64 * (wave & 1), 16, HD, lane);
+    rows_load<1>(wave < 2 ? l_phik : l_phiv, src, 64 * (wave & 1), 16, HD, lane);
   }
   // raw slice s: waves 0-1 load K rows [16w, 16w + 16), waves 2-3 V rows
   auto issue = [&](int sl) {
     const int t0 = t_begin + sl * FT;
-    char* dst = lds + F_RAW + (sl & 1) * 2 * F_SLICE_B + (wave < 2 ? 0 : F_SLICE_B);
+    char* dst = l_raw + (sl & 1) * 2 * F_SLICE_B + (wave < 2 ? 0 : F_SLICE_B);
     const char* src = (wave < 2 ? kh : vh) + (size_t)t0 * 256;
     if (wave < 2) rows_load<2>(dst, src, 16 * (wave & 1), 4, t_end - t0, lane);
     else rows_load<0>(dst, src, 16 * (wave & 1), 4, t_end - t0, lane);
@@ -960,7 +975,7 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();                                    // slice sl and beta visible
     if (sl + 1 < n_slices) issue(sl + 1);
-    const char* Kr = lds + F_RAW + (sl & 1) * 2 * F_SLICE_B;
+    const char* Kr = l_raw + (sl & 1) * 2 * F_SLICE_B;
     const char* Vr = Kr + F_SLICE_B;
 
     // K~^T column block: kt[r] = K~[token n][32cb + 8(r/4) + 4h2 + r%4]
@@ -970,9 +985,9 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kr + n * 256 + (((2 * kc + h2) ^ swz_r(n)) << 4));
-      kt = mfma32(tr_op(lds + F_PHIK, 16 * kc, 8, 32 * cb, lane), kb, kt);
+      kt = mfma32(tr_op(l_phik, 16 * kc, 8, 32 * cb, lane), kb, kt);
       const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vr + krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4));
-      vp = mfma32(va, tr_op(lds + F_PHIV, 16 * kc, 8, 32 * cb, lane), vp);
+      vp = mfma32(va, tr_op(l_phiv, 16 * kc, 8, 32 * cb, lane), vp);
     }
     float ss = 0.f;
 #pragma unroll
@@ -989,8 +1004,8 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
       for (int i = 0; i < 4; ++i) w4[i] = (__bf16)(kt[4 * jj + i] * inv);
       const int d = 32 * cb + 8 * jj + 4 * h2;         // 4 consecutive columns of row n
       const int c16 = d >> 3, sub = (d & 7) * 2;
-      *reinterpret_cast<bf16x4*>(lds + F_KPA + n * 256 + ((c16 ^ swz_k(n)) << 4) + sub) = w4;
-      *reinterpret_cast<bf16x4*>(lds + F_KPB + n * 256 + ((c16 ^ swz_v(n)) << 4) + sub) = w4;
+      *reinterpret_cast<bf16x4*>(l_kp + F_KPA + n * 256 + ((c16 ^ swz_k(n)) << 4) + sub) = w4;
+      *reinterpret_cast<bf16x4*>(l_kp + F_KPB + n * 256 + ((c16 ^ swz_v(n)) << 4) + sub) = w4;
     }
     __syncthreads();                                    // K' of the slice visible
 
@@ -998,7 +1013,7 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     f32x16 p = zero16();
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + F_KPA + krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(l_kp + F_KPA + krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4));
       p = mfma32(a, sreg[kc], p);
     }
     bf16x8 wb[2];
@@ -1010,7 +1025,7 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
-        uacc[ib] = mfma32(tr_op(lds + F_KPB, 8 * cc, 16, 32 * ib, lane), wb[cc], uacc[ib]);
+        uacc[ib] = mfma32(tr_op(l_kp + F_KPB, 8 * cc, 16, 32 * ib, lane), wb[cc], uacc[ib]);
   }
 
   // uacc[ib][r] = U[row 32*ib + 8*(r/4) + 4*h2 + (r%4)][col]
@@ -1033,6 +1048,54 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
         const size_t e = (size_t)(32 * ib + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + col;
         P[e] = uacc[ib][r];
       }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+               const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
+               const float* __restrict__ beta, const float* __restrict__ alpha,
+               const float* __restrict__ S_prev, float* __restrict__ S_next,
+               float* __restrict__ partial, int H, int T, int chunk_tokens, int n_chunks,
+               long n_bh) {
+  __shared__ __attribute__((aligned(1024))) char l_phik[F_PHI_B];
+  __shared__ __attribute__((aligned(1024))) char l_phiv[F_PHI_B];
+  __shared__ __attribute__((aligned(1024))) char l_raw[F_RAW_B];
+  __shared__ __attribute__((aligned(1024))) char l_kp[F_KP_B];
+  commit_block(xcd_remap(blockIdx.x, gridDim.x), k, v, phi_k, phi_v, beta, alpha, S_prev, S_next,
+               partial, H, T, chunk_tokens, n_chunks, n_bh, l_phik, l_phiv, l_raw, l_kp);
+}
+
+// The clean pass of the prepared read in one launch: blocks [0, n_attn) are
+// the fused read's workgroups (taking the compute units first, being dispatched
+// first), blocks [n_attn_pad, ...) the commit's (threads 0-255; the other four
+// waves leave), which run on the compute units the read leaves idle. The
+// commit reuses the read's LDS arrays; the padding keeps each role's blocks
+// dealt round-robin over the XCDs from XCD 0.
+__global__ void __launch_bounds__(512, 1)
+clean_fused_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+              const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, float sl2,
+              int n_qblk, const __bf16* __restrict__ mt, __bf16* __restrict__ o_intra,
+              __bf16* __restrict__ o_inter, int n_attn, int n_attn_pad,
+              const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
+              const float* __restrict__ beta, const float* __restrict__ alpha,
+              const float* __restrict__ S_prev, float* __restrict__ S_next,
+              float* __restrict__ partial, int H, int chunk_tokens, int n_chunks, long n_bh) {
+  __shared__ __attribute__((aligned(1024))) char lk0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lk1[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv1[AKV];
+  __shared__ float mlx[8][2][64];
+  __shared__ int redo_flag;
+  const int b = blockIdx.x;
+  if (b < n_attn_pad) {
+    if (b < n_attn)
+      attn_block<true>(xcd_remap(b, n_attn), q, k, v, o, T, T, T, sl2, n_qblk, mt, o_intra,
+                       o_inter, lk0, lk1, lv0, lv1, mlx, redo_flag);
+  } else if (threadIdx.x < 256) {
+    const int c = b - n_attn_pad;
+    commit_block(xcd_remap(c, (int)gridDim.x - n_attn_pad), k, v, phi_k, phi_v, beta, alpha,
+                 S_prev, S_next, partial, H, T, chunk_tokens, n_chunks, n_bh, lk0, lk1, lv0, lv1);
   }
 }
 
@@ -1105,6 +1168,32 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
       static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk,
       static_cast<const __bf16*>(mt), static_cast<__bf16*>(o_intra),
       static_cast<__bf16*>(o_inter));
+  return hipGetLastError();
+}
+
+hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k, const void* v,
+                                    const void* mt, const void* phi_k, const void* phi_v,
+                                    const float* beta, const float* alpha, const float* S_prev,
+                                    float* S_next, void* o, void* o_intra, void* o_inter,
+                                    void* ws, hipStream_t s) {
+  int ct, nc;
+  commit_split(d, &ct, &nc);
+  const long n_bh = (long)d.B * d.H;
+  const int n_qblk = (d.T + AQ - 1) / AQ;
+  const long n_attn = n_bh * n_qblk;
+  const long n_pad = (n_attn + 7) / 8 * 8;
+  float* partial = static_cast<float*>(ws);
+  clean_fused_k<<<(unsigned)(n_pad + n_bh * nc), 512, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<__bf16*>(o), d.T, d.scale * kLog2e, n_qblk, static_cast<const __bf16*>(mt),
+      static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter), (int)n_attn, (int)n_pad,
+      static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), beta, alpha, S_prev,
+      S_next, partial, d.H, ct, nc, n_bh);
+  if (nc > 1) {
+    const long total4 = n_bh * HD * HD / 4;
+    commit_reduce_k<<<(unsigned)((total4 + 255) / 256), 256, 0, s>>>(partial, alpha, S_prev,
+                                                                     S_next, nc, n_bh);
+  }
   return hipGetLastError();
 }
 

@@ -62,10 +62,14 @@ class Arl2Layer:
     """One hybrid attention layer over B streams on the current device.
 
     phi_q, phi_k, phi_v: [H, D, D] tensors of the activation dtype.
+
+    With prepared reads (the default) the clean pass is one library call
+    (arl2_clean_pass_prepared: read and commit in one launch on bf16 shapes);
+    ``fused_clean=False`` issues the read and the commit as two calls instead.
     """
 
     def __init__(self, shape: arl2.Shape, phi_q, phi_k, phi_v, n_denoise: int | None = None,
-                 device=None, prepared: bool = True):
+                 device=None, prepared: bool = True, fused_clean: bool = True):
         self.shape = shape
         self.device = torch.device(device or "cuda")
         dt = shape.torch_dtype
@@ -74,7 +78,10 @@ class Arl2Layer:
         self._S = [torch.zeros(st, dtype=torch.float32, device=self.device),
                    torch.zeros(st, dtype=torch.float32, device=self.device)]
         self._cur = 0
-        self.ws = arl2.alloc_workspace(shape, arl2.OP_CLEAN_PASS, self.device)
+        ws_bytes = max(arl2.workspace_bytes(shape, op) for op in
+                       (arl2.OP_CLEAN_PASS, arl2.OP_CLEAN_PASS_PREPARED, arl2.OP_COMMIT))
+        self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        self.fused_clean = fused_clean
         self.seq = PassSequencer(n_denoise)
         # Reads of a frame all see the same S_{N-1}, so Phi_q S is formed once
         # per frame (after each commit) and every read uses it.
@@ -83,9 +90,9 @@ class Arl2Layer:
             self.M = arl2.alloc_prepared(shape, self.device)
             self._prepare()
 
-    def _prepare(self):
+    def _prepare(self, stream=None):
         if self.prepared:
-            arl2.read_prepare(self.shape, self.phi[0], self.S, self.M)
+            arl2.read_prepare(self.shape, self.phi[0], self.S, self.M, stream)
 
     @property
     def S(self) -> torch.Tensor:
@@ -124,7 +131,11 @@ class Arl2Layer:
         self.seq.before_clean_pass()
         o = self.new_output() if o is None else o
         nxt = 1 - self._cur
-        if self.prepared:
+        if self.prepared and self.fused_clean:
+            arl2.clean_pass_prepared(self.shape, q, k, v, self.M, self.phi[1], self.phi[2], beta,
+                                     alpha, self._S[self._cur], self._S[nxt], o, o_intra,
+                                     o_inter, self.ws, stream)
+        elif self.prepared:
             arl2.read_prepared(self.shape, q, k, v, self.M, o, o_intra, o_inter, self.ws, stream)
             arl2.commit(self.shape, k, v, self.phi[1], self.phi[2], beta, alpha,
                         self._S[self._cur], self._S[nxt], self.ws, stream)
@@ -134,7 +145,7 @@ class Arl2Layer:
                             stream)
         self._cur = nxt
         self.seq.after_clean_pass()
-        self._prepare()
+        self._prepare(stream)
         return o
 
     def commit(self, k, v, beta, alpha, stream=None):
@@ -145,7 +156,7 @@ class Arl2Layer:
                     self._S[nxt], self.ws, stream)
         self._cur = nxt
         self.seq.after_clean_pass()
-        self._prepare()
+        self._prepare(stream)
 
     # checkpoint / resume: the whole cross-frame memory is S plus the frame index
     def state_dict(self) -> dict:

@@ -53,7 +53,7 @@ def shape_of(w: synth.Workload):
 
 
 def lockstep_rollout(w: synth.Workload, read_frames, row_sample=None, check_state=True,
-                     frames=None):
+                     frames=None, **layer_kwargs):
     """Drive Arl2Layer and the oracle frame by frame.
 
     Frames in ``read_frames`` run every denoising read and the clean pass, and
@@ -66,7 +66,7 @@ def lockstep_rollout(w: synth.Workload, read_frames, row_sample=None, check_stat
 
     tol = TOL[w.dtype]
     phis = synth.phi_maps(w)
-    layer = Arl2Layer(shape_of(w), *[dev(p, w.dtype) for p in phis])
+    layer = Arl2Layer(shape_of(w), *[dev(p, w.dtype) for p in phis], **layer_kwargs)
     S_ref = np.zeros((w.B, w.H, w.D, w.D))
     worst = {"S": 0.0, "o": 0.0, "o_intra": 0.0, "o_inter": 0.0}
     n_frames = w.frames if frames is None else frames

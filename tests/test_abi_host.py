@@ -47,6 +47,10 @@ def test_workspace_sizes(arl2):
     assert arl2.workspace_bytes(s, arl2.OP_COMMIT) >= arl2.workspace_bytes(s, arl2.OP_STATE_COMMIT)
     assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS) == max(
         arl2.workspace_bytes(s, arl2.OP_READ), arl2.workspace_bytes(s, arl2.OP_COMMIT))
+    # one-launch clean pass (bf16): the commit partials only
+    assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED) == arl2.workspace_bytes(
+        s, arl2.OP_COMMIT)
+    assert arl2.workspace_bytes(s, arl2.OP_READ_PREPARED) == 0
     assert arl2.workspace_bytes(s, 17) == 0
     assert arl2.workspace_bytes(arl2.Shape(0, 1, 1, 128), arl2.OP_READ) == 0
     f = arl2.Shape(1, 1, 64, 16, arl2.F32)
@@ -101,6 +105,13 @@ def test_alias_and_workspace_errors(arl2):
     # read outputs overlapping inputs
     rneed = arl2.workspace_bytes(s, arl2.OP_READ)
     assert _st(arl2, "arl2_read", cs(s), A, B, B, B, S1, A, None, None, WS, rneed, None) == 5
+    # one-launch clean pass: S_next aliasing S_prev, missing workspace
+    cneed = arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED)
+    assert cneed > 0
+    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, A, A, A, A, S1, S1, B, None,
+               None, WS, cneed, None) == 5
+    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, A, A, A, A, S1, S2, B, None,
+               None, None, 0, None) == 6
     # fullkv: n_kv beyond capacity
     assert _st(arl2, "arl2_fullkv_attn", cs(s), A, B, S1, 200, 100, WS, None) == 2
 

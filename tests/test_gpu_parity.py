@@ -128,11 +128,51 @@ def test_state_commit(case):
     assert_close(host(Sn), ref, TOL[w.dtype], "S_next")
 
 
+@pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
+def test_clean_pass_prepared(case):
+    """The one-call clean pass from a prepared map: every output and S_next
+    against the oracle's read and commit."""
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"clean_pass_prepared {_ids(case)}")
+    sh = shape_of(w)
+    q, k, v = synth.qkv(w, 1, w.passes - 1)
+    beta, alpha = synth.gates(w, 1)
+    phis = synth.phi_maps(w)
+    g = np.random.default_rng(8)
+    S = (g.standard_normal((w.B, w.H, w.D, w.D)) * 0.05).astype(np.float32)
+    dS, Sn = dev32(S), dev32(np.zeros_like(S))
+    M = arl2.alloc_prepared(sh)
+    arl2.read_prepare(sh, dev(phis[0], w.dtype), dS, M)
+    o, oi, oe = (dev(np.zeros_like(q), w.dtype) for _ in range(3))
+    ws = arl2.alloc_workspace(sh, arl2.OP_CLEAN_PASS_PREPARED)
+    arl2.clean_pass_prepared(sh, dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), M,
+                             dev(phis[1], w.dtype), dev(phis[2], w.dtype), dev32(beta),
+                             dev32(alpha), dS, Sn, o, oi, oe, ws)
+    rows = slice(None) if w.T <= 600 else np.r_[0:40, 700:740, w.T - 40:w.T]
+    ref = oracle.read(q[:, :, rows], k, v, phis[0], S)
+    for name, got in (("o", o), ("o_intra", oi), ("o_inter", oe)):
+        assert_close(host(got)[:, :, rows], ref[name], TOL[w.dtype], name)
+    assert_close(host(Sn), oracle.commit(k, v, phis[1], phis[2], beta, alpha, S), TOL[w.dtype],
+                 "S_next")
+
+
 def test_rollout_tiny_fp32_all_passes():
     """Workload 0: every pass of every frame, every row, and the state."""
     w = synth.WORKLOADS[0]
     log("rollout tiny fp32")
     worst = lockstep_rollout(w, read_frames=set(range(w.frames)))
+    log(f"worst relative errors {worst}")
+
+
+@pytest.mark.parametrize("prepared", [True, False])
+def test_rollout_clean_pass_as_two_calls(prepared):
+    """The layer with its clean pass issued as a read and a commit (not the
+    one-launch clean pass), with and without prepared reads."""
+    w = synth.WORKLOADS[1]
+    log(f"rollout, clean pass as two calls, prepared={prepared}")
+    worst = lockstep_rollout(w, read_frames={0, 2}, row_sample=np.r_[0:16, w.T - 16:w.T],
+                             frames=3, prepared=prepared, fused_clean=False)
     log(f"worst relative errors {worst}")
 
 
