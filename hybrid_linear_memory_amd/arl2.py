@@ -55,7 +55,7 @@ SIGNATURES = {
     "arl2_read_prepare": (_i32, [_SP, _vp, _vp, _vp, _vp]),
     "arl2_read_prepared": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_clean_pass_prepared": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                        _vp, _vp, _vp, _vp, _sz, _vp]),
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_workspace_bytes": (_sz, [_SP, _i32]),
     "arl2_status_string": (ctypes.c_char_p, [_i32]),
     "arl2_last_error": (ctypes.c_char_p, []),
@@ -215,15 +215,18 @@ def read_prepared(shape: Shape, q, k, v, prepared, o, o_intra=None, o_inter=None
 
 
 def clean_pass_prepared(shape: Shape, q, k, v, prepared, phi_k, phi_v, beta, alpha, S_prev,
-                        S_next, o, o_intra=None, o_inter=None, ws=None, stream=None):
+                        S_next, o, o_intra=None, o_inter=None, ws=None, stream=None, phi_q=None,
+                        prepared_next=None):
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_clean_pass_prepared(
         ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(prepared, "prepared"), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
-        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
-        _ptr(S_next, "S_next", f), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
-        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
-        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+        _ptr(prepared, "prepared"), _ptr(phi_q, "phi_q", a, optional=True),
+        _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f),
+        _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f), _ptr(S_next, "S_next", f),
+        _ptr(prepared_next, "prepared_next", optional=True), _ptr(o, "o", a),
+        _ptr(o_intra, "o_intra", a, optional=True), _ptr(o_inter, "o_inter", a, optional=True),
+        _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(stream)))
 
 
 def commit(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, stream=None):

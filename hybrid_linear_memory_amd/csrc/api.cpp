@@ -450,10 +450,11 @@ arl2_status arl2_clean_pass(const arl2_shape* shape, const void* q, const void* 
 }
 
 arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q, const void* k,
-                                     const void* v, const void* prepared, const void* phi_k,
-                                     const void* phi_v, const float* beta, const float* alpha,
-                                     const float* S_prev, float* S_next, void* o, void* o_intra,
-                                     void* o_inter, void* ws, size_t ws_bytes, void* stream) {
+                                     const void* v, const void* prepared, const void* phi_q,
+                                     const void* phi_k, const void* phi_v, const float* beta,
+                                     const float* alpha, const float* S_prev, float* S_next,
+                                     void* prepared_next, void* o, void* o_intra, void* o_inter,
+                                     void* ws, size_t ws_bytes, void* stream) {
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
@@ -470,15 +471,20 @@ arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q, con
   REQUIRE_PTR(o);
   OPTIONAL_PTR(o_intra);
   OPTIONAL_PTR(o_inter);
+  OPTIONAL_PTR(prepared_next);
+  if (prepared_next) REQUIRE_PTR(phi_q);
   if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
   const size_t need = ws_clean_pass_prepared(d);
   if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
   const size_t ab = arl2::act_bytes(d);
-  const Range outs[4] = {{o, ab}, {o_intra, ab}, {o_inter, ab}, {S_next, state_bytes(d)}};
-  const Range ins[10] = {{q, ab},
+  const size_t pb = prepared_bytes(d);
+  const Range outs[5] = {{o, ab}, {o_intra, ab}, {o_inter, ab}, {S_next, state_bytes(d)},
+                         {prepared_next, pb}};
+  const Range ins[11] = {{q, ab},
                          {k, ab},
                          {v, ab},
-                         {prepared, prepared_bytes(d)},
+                         {prepared, pb},
+                         {phi_q, prepared_next ? phi_bytes(d) : 0},
                          {phi_k, phi_bytes(d)},
                          {phi_v, phi_bytes(d)},
                          {S_prev, state_bytes(d)},
@@ -488,18 +494,22 @@ arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q, con
   for (const Range& a : outs)
     for (const Range& b : ins)
       if (overlap(a, b)) return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
       if (overlap(outs[i], outs[j])) return fail(ARL2_E_ALIAS, "two outputs overlap");
   hipStream_t s = (hipStream_t)stream;
   if (arl2::use_mfma(d))
-    return hip_status(arl2::mfma_clean_pass_prepared(d, q, k, v, prepared, phi_k, phi_v, beta,
-                                                     alpha, S_prev, S_next, o, o_intra, o_inter,
-                                                     ws, s),
+    return hip_status(arl2::mfma_clean_pass_prepared(d, q, k, v, prepared, phi_q, phi_k, phi_v,
+                                                     beta, alpha, S_prev, S_next, prepared_next,
+                                                     o, o_intra, o_inter, ws, s),
                       "clean pass");
   st = arl2_read_prepared(shape, q, k, v, prepared, o, o_intra, o_inter, ws, ws_bytes, stream);
   if (st != ARL2_OK) return st;
-  return do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, s);
+  st = do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, s);
+  if (st != ARL2_OK || !prepared_next) return st;
+  return hip_status(
+      arl2::generic_read_prepare(d, phi_q, S_next, static_cast<float*>(prepared_next), s),
+      "read preparation");
 }
 
 arl2_status arl2_fullkv_attn(const arl2_shape* shape, const void* q, const void* k_cache,

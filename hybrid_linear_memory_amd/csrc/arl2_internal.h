@@ -77,13 +77,14 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
                               const void* mt, void* o, void* o_intra, void* o_inter,
                               hipStream_t s);
 // Clean pass from a prepared map in one launch (fused read workgroups plus the
-// fused commit's workgroups), then the chunk reduction; ws holds the commit
-// partials (mfma_commit_ws_bytes).
+// fused commit's workgroups), then the chunk reduction, which also forms the
+// map of S_next into mt_next when mt_next is given (phi_q then required); ws
+// holds the commit partials (mfma_commit_ws_bytes).
 hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k, const void* v,
-                                    const void* mt, const void* phi_k, const void* phi_v,
-                                    const float* beta, const float* alpha, const float* S_prev,
-                                    float* S_next, void* o, void* o_intra, void* o_inter,
-                                    void* ws, hipStream_t s);
+                                    const void* mt, const void* phi_q, const void* phi_k,
+                                    const void* phi_v, const float* beta, const float* alpha,
+                                    const float* S_prev, float* S_next, void* mt_next, void* o,
+                                    void* o_intra, void* o_inter, void* ws, hipStream_t s);
 // float32 / generic: M = Phi_q S (fp32, row-major per head).
 hipError_t generic_read_prepare(const Dims& d, const void* phi_q, const float* S, float* m,
                                 hipStream_t s);

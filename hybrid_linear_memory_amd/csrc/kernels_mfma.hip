@@ -1125,6 +1125,76 @@ commit_reduce_k(const float* __restrict__ partial, const float* __restrict__ alp
   reinterpret_cast<float4*>(S_next)[q4] = r;
 }
 
+// End of the clean pass when the next frame's map is wanted: S_next = alpha
+// S_prev + the chunk partials summed in chunk order (as commit_reduce_k; with a
+// single chunk the commit has written S_next already), then the prepared map of
+// S_next, M^T[j][i] = sum_k Phi_q[i][k] S_next[k][j] in bf16 (as read_prep_k).
+// One workgroup of 512 threads per (b, h, 32-column block jb): thread t sums
+// row t / 4, columns 32 jb + 8 (t % 4) + 0..7; the block goes through LDS
+// transposed (column-major, bf16) as the B operand of M = Phi_q S.
+constexpr int FIN_LD = HD + 8;                  // padded row of the transposed block
+__global__ void __launch_bounds__(512)
+commit_finish_k(const float* __restrict__ partial, const float* __restrict__ alpha,
+                const float* __restrict__ S_prev, float* __restrict__ S_next, int n_chunks,
+                long n_bh, const __bf16* __restrict__ phi_q, __bf16* __restrict__ mt, int H) {
+  __shared__ __attribute__((aligned(16))) __bf16 st[32 * FIN_LD];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long bh = blockIdx.x >> 2;
+  const int jb = blockIdx.x & 3;
+  const int kr = tid >> 2, cq = 8 * (tid & 3);
+  const size_t e = ((size_t)bh * HD + kr) * HD + 32 * jb + cq;
+  float r[8];
+  if (n_chunks > 1) {
+    const size_t stride = (size_t)n_bh * HD * HD;
+    float4 a0 = *reinterpret_cast<const float4*>(partial + e);
+    float4 a1 = *reinterpret_cast<const float4*>(partial + e + 4);
+    for (int c = 1; c < n_chunks; ++c) {
+      const float4 x0 = *reinterpret_cast<const float4*>(partial + c * stride + e);
+      const float4 x1 = *reinterpret_cast<const float4*>(partial + c * stride + e + 4);
+      a0.x += x0.x; a0.y += x0.y; a0.z += x0.z; a0.w += x0.w;
+      a1.x += x1.x; a1.y += x1.y; a1.z += x1.z; a1.w += x1.w;
+    }
+    const float al = alpha[bh];
+    const float4 s0 = *reinterpret_cast<const float4*>(S_prev + e);
+    const float4 s1 = *reinterpret_cast<const float4*>(S_prev + e + 4);
+    const float4 r0 = {fmaf(al, s0.x, a0.x), fmaf(al, s0.y, a0.y), fmaf(al, s0.z, a0.z),
+                       fmaf(al, s0.w, a0.w)};
+    const float4 r1 = {fmaf(al, s1.x, a1.x), fmaf(al, s1.y, a1.y), fmaf(al, s1.z, a1.z),
+                       fmaf(al, s1.w, a1.w)};
+    *reinterpret_cast<float4*>(S_next + e) = r0;
+    *reinterpret_cast<float4*>(S_next + e + 4) = r1;
+    r[0] = r0.x; r[1] = r0.y; r[2] = r0.z; r[3] = r0.w;
+    r[4] = r1.x; r[5] = r1.y; r[6] = r1.z; r[7] = r1.w;
+  } else {
+    const float4 r0 = *reinterpret_cast<const float4*>(S_next + e);
+    const float4 r1 = *reinterpret_cast<const float4*>(S_next + e + 4);
+    r[0] = r0.x; r[1] = r0.y; r[2] = r0.z; r[3] = r0.w;
+    r[4] = r1.x; r[5] = r1.y; r[6] = r1.z; r[7] = r1.w;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) st[(cq + u) * FIN_LD + kr] = (__bf16)r[u];
+  __syncthreads();
+  if (wave >= 4) return;
+  // wave w: rows i in [32w, 32w + 32) of M, columns j = 32 jb + n
+  const __bf16* P = phi_q + (size_t)(bh % H) * HD * HD + (size_t)(32 * wave + n) * HD + 8 * h2;
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+    acc = mfma32(ld8(P + 16 * kc),
+                 *reinterpret_cast<const bf16x8*>(st + n * FIN_LD + 16 * kc + 8 * h2), acc);
+  // acc[r] = M[i = 32w + 8(r/4) + 4h2 + r%4][j]  ->  MT[j][i]
+  __bf16* out = mt + (size_t)bh * HD * HD + (size_t)(32 * jb + n) * HD + 32 * wave + 4 * h2;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    bf16x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (__bf16)acc[4 * jj + i];
+    *reinterpret_cast<bf16x4*>(out + 8 * jj) = w;
+  }
+}
+
 void commit_split(const Dims& d, int* chunk_tokens, int* n_chunks) {
   const long bh = (long)d.B * d.H;
   const int max_chunks = (d.T + 127) / 128;
@@ -1172,10 +1242,10 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
 }
 
 hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k, const void* v,
-                                    const void* mt, const void* phi_k, const void* phi_v,
-                                    const float* beta, const float* alpha, const float* S_prev,
-                                    float* S_next, void* o, void* o_intra, void* o_inter,
-                                    void* ws, hipStream_t s) {
+                                    const void* mt, const void* phi_q, const void* phi_k,
+                                    const void* phi_v, const float* beta, const float* alpha,
+                                    const float* S_prev, float* S_next, void* mt_next, void* o,
+                                    void* o_intra, void* o_inter, void* ws, hipStream_t s) {
   int ct, nc;
   commit_split(d, &ct, &nc);
   const long n_bh = (long)d.B * d.H;
@@ -1189,7 +1259,11 @@ hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k,
       static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter), (int)n_attn, (int)n_pad,
       static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), beta, alpha, S_prev,
       S_next, partial, d.H, ct, nc, n_bh);
-  if (nc > 1) {
+  if (mt_next) {
+    commit_finish_k<<<(unsigned)(n_bh * 4), 512, 0, s>>>(partial, alpha, S_prev, S_next, nc, n_bh,
+                                                        static_cast<const __bf16*>(phi_q),
+                                                        static_cast<__bf16*>(mt_next), d.H);
+  } else if (nc > 1) {
     const long total4 = n_bh * HD * HD / 4;
     commit_reduce_k<<<(unsigned)((total4 + 255) / 256), 256, 0, s>>>(partial, alpha, S_prev,
                                                                      S_next, nc, n_bh);

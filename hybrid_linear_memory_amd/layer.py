@@ -87,8 +87,17 @@ class Arl2Layer:
         # per frame (after each commit) and every read uses it.
         self.prepared = prepared
         if prepared:
-            self.M = arl2.alloc_prepared(shape, self.device)
+            # double-buffered like the state: the clean pass reads one map and
+            # writes the next frame's into the other
+            self._M = [arl2.alloc_prepared(shape, self.device),
+                       arl2.alloc_prepared(shape, self.device)]
+            self._mcur = 0
             self._prepare()
+
+    @property
+    def M(self) -> torch.Tensor:
+        """The prepared map of S_{N-1} that the current frame's reads use."""
+        return self._M[self._mcur]
 
     def _prepare(self, stream=None):
         if self.prepared:
@@ -132,9 +141,15 @@ class Arl2Layer:
         o = self.new_output() if o is None else o
         nxt = 1 - self._cur
         if self.prepared and self.fused_clean:
+            # also forms the next frame's map, into the other map buffer
             arl2.clean_pass_prepared(self.shape, q, k, v, self.M, self.phi[1], self.phi[2], beta,
                                      alpha, self._S[self._cur], self._S[nxt], o, o_intra,
-                                     o_inter, self.ws, stream)
+                                     o_inter, self.ws, stream, phi_q=self.phi[0],
+                                     prepared_next=self._M[1 - self._mcur])
+            self._mcur = 1 - self._mcur
+            self._cur = nxt
+            self.seq.after_clean_pass()
+            return o
         elif self.prepared:
             arl2.read_prepared(self.shape, q, k, v, self.M, o, o_intra, o_inter, self.ws, stream)
             arl2.commit(self.shape, k, v, self.phi[1], self.phi[2], beta, alpha,

@@ -193,20 +193,23 @@ arl2_status arl2_clean_pass(const arl2_shape* shape, const void* q,
 
 /* Clean pass from a prepared map (§2.2: the frame's last pass reads S_{N-1}
  * like every other pass, then writes S_N once): o = softmax(Q K^T * scale) V +
- * Q M with the map M of S_prev (arl2_read_prepare), and S_next from K, V, beta,
- * alpha and S_prev as in arl2_commit. On bf16 shapes the read and the commit
- * run in one launch, the commit on the compute units the read leaves idle, then
- * a reduction over token chunks. The prepared map is not updated: call
- * arl2_read_prepare with S_next before the next frame's reads. Needs
- * arl2_workspace_bytes(shape, ARL2_OP_CLEAN_PASS_PREPARED) bytes of
- * workspace. Outputs must not overlap each other, the inputs or the
- * workspace. */
+ * Q M with the map M of S_prev in `prepared` (arl2_read_prepare), and S_next
+ * from K, V, beta, alpha and S_prev as in arl2_commit. When prepared_next is
+ * not NULL it also receives the map of S_next (what arl2_read_prepare(phi_q,
+ * S_next) would write; phi_q is then required), ready for the next frame's
+ * reads; it must be a different buffer from `prepared`. On bf16 shapes the
+ * read and the commit run in one launch, the commit on the compute units the
+ * read leaves idle, followed by one launch that sums the commit's token chunks
+ * and forms the next map. Needs arl2_workspace_bytes(shape,
+ * ARL2_OP_CLEAN_PASS_PREPARED) bytes of workspace. Outputs must not overlap
+ * each other, the inputs or the workspace. */
 arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q,
                                      const void* k, const void* v,
-                                     const void* prepared, const void* phi_k,
-                                     const void* phi_v, const float* beta,
-                                     const float* alpha, const float* S_prev,
-                                     float* S_next, void* o, void* o_intra,
+                                     const void* prepared, const void* phi_q,
+                                     const void* phi_k, const void* phi_v,
+                                     const float* beta, const float* alpha,
+                                     const float* S_prev, float* S_next,
+                                     void* prepared_next, void* o, void* o_intra,
                                      void* o_inter, void* ws, size_t ws_bytes,
                                      void* stream);
 

@@ -108,10 +108,13 @@ def test_alias_and_workspace_errors(arl2):
     # one-launch clean pass: S_next aliasing S_prev, missing workspace
     cneed = arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED)
     assert cneed > 0
-    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, A, A, A, A, S1, S1, B, None,
-               None, WS, cneed, None) == 5
-    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, A, A, A, A, S1, S2, B, None,
-               None, None, 0, None) == 6
+    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, None, A, A, A, A, S1, S1,
+               None, B, None, None, WS, cneed, None) == 5
+    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, None, A, A, A, A, S1, S2,
+               None, B, None, None, None, 0, None) == 6
+    # the next map wanted without phi_q
+    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, None, A, A, A, A, S1, S2,
+               B + 4096, B, None, None, WS, cneed, None) == 1
     # fullkv: n_kv beyond capacity
     assert _st(arl2, "arl2_fullkv_attn", cs(s), A, B, S1, 200, 100, WS, None) == 2
 

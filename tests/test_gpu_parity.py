@@ -131,7 +131,8 @@ def test_state_commit(case):
 @pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
 def test_clean_pass_prepared(case):
     """The one-call clean pass from a prepared map: every output and S_next
-    against the oracle's read and commit."""
+    against the oracle's read and commit, and the next frame's map."""
+    import torch
     from hybrid_linear_memory_amd import arl2
     w = _w(*case)
     log(f"clean_pass_prepared {_ids(case)}")
@@ -146,15 +147,23 @@ def test_clean_pass_prepared(case):
     arl2.read_prepare(sh, dev(phis[0], w.dtype), dS, M)
     o, oi, oe = (dev(np.zeros_like(q), w.dtype) for _ in range(3))
     ws = arl2.alloc_workspace(sh, arl2.OP_CLEAN_PASS_PREPARED)
+    M_next = arl2.alloc_prepared(sh)
+    dphi_q = dev(phis[0], w.dtype)
     arl2.clean_pass_prepared(sh, dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), M,
                              dev(phis[1], w.dtype), dev(phis[2], w.dtype), dev32(beta),
-                             dev32(alpha), dS, Sn, o, oi, oe, ws)
+                             dev32(alpha), dS, Sn, o, oi, oe, ws, phi_q=dphi_q,
+                             prepared_next=M_next)
     rows = slice(None) if w.T <= 600 else np.r_[0:40, 700:740, w.T - 40:w.T]
     ref = oracle.read(q[:, :, rows], k, v, phis[0], S)
     for name, got in (("o", o), ("o_intra", oi), ("o_inter", oe)):
         assert_close(host(got)[:, :, rows], ref[name], TOL[w.dtype], name)
     assert_close(host(Sn), oracle.commit(k, v, phis[1], phis[2], beta, alpha, S), TOL[w.dtype],
                  "S_next")
+    # the next map is exactly what a separate preparation from S_next forms
+    M_sep = arl2.alloc_prepared(sh)
+    arl2.read_prepare(sh, dphi_q, Sn, M_sep)
+    torch.cuda.synchronize()
+    assert torch.equal(M_next, M_sep)
 
 
 def test_rollout_tiny_fp32_all_passes():
