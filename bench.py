@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="timed frames")
     ap.add_argument("--warmup", type=int, default=20, help="untimed frames")
-    ap.add_argument("--pool", type=int, default=4, help="distinct resident input frames")
+    ap.add_argument("--pool", type=int, default=8,
+                    help="distinct resident input frames (even; one graph covers them all)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly, no HIP graph")
     ap.add_argument("--kernel-iters", type=int, default=50)
     ap.add_argument("--rollout-frames", type=int, default=240)
@@ -118,44 +119,43 @@ class Bench:
         for i in range(n_frames):
             self.frame(start + i)
 
-    def make_graphs(self):
-        """One graph per pair of pool frames: the state ping-pongs between
-        the layer's two buffers, so a pair returns it to the same buffer."""
+    def make_graph(self):
+        """One graph over all pool frames (an even number: the state and the
+        prepared map ping-pong between two buffers each, so the graph returns
+        them to the buffers it started from)."""
         torch = self.torch
         assert len(self.pool) % 2 == 0
-        graphs = []
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for i in range(0, len(self.pool), 2):
-                self.layer.seq.restore(self.layer.frame)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=s):
+            self.layer.seq.restore(self.layer.frame)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(len(self.pool)):
                     self.frame(i)
-                    self.frame(i + 1)
-                graphs.append(g)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        return graphs
+        return g
 
     def timed(self, steps, warmup, use_graph):
         torch = self.torch
         if use_graph:
-            graphs = self.make_graphs()
-            n_pairs = (steps + 1) // 2
-            for i in range(max(1, warmup // 2)):
-                graphs[i % len(graphs)].replay()
+            g = self.make_graph()
+            per = len(self.pool)
+            n_rep = (steps + per - 1) // per
+            for i in range(max(1, (warmup + per - 1) // per)):
+                g.replay()
             torch.cuda.synchronize()
             t0 = torch.cuda.Event(enable_timing=True)
             t1 = torch.cuda.Event(enable_timing=True)
             t0.record()
             w0 = time.perf_counter()
-            for i in range(n_pairs):
-                graphs[i % len(graphs)].replay()
+            for i in range(n_rep):
+                g.replay()
             t1.record()
             torch.cuda.synchronize()
             wall = time.perf_counter() - w0
-            frames = 2 * n_pairs
+            frames = per * n_rep
         else:
             self.run_frames(warmup)
             torch.cuda.synchronize()

@@ -1145,6 +1145,13 @@ commit_finish_k(const float* __restrict__ partial, const float* __restrict__ alp
   const int jb = blockIdx.x & 3;
   const int kr = tid >> 2, cq = 8 * (tid & 3);
   const size_t e = ((size_t)bh * HD + kr) * HD + 32 * jb + cq;
+  // waves 0-3 fetch their Phi_q rows first, so that the fetch overlaps the sum
+  bf16x8 pq[8];
+  if (wave < 4) {
+    const __bf16* P = phi_q + (size_t)(bh % H) * HD * HD + (size_t)(32 * wave + n) * HD + 8 * h2;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) pq[kc] = ld8(P + 16 * kc);
+  }
   float r[8];
   if (n_chunks > 1) {
     const size_t stride = (size_t)n_bh * HD * HD;
@@ -1178,12 +1185,11 @@ commit_finish_k(const float* __restrict__ partial, const float* __restrict__ alp
   __syncthreads();
   if (wave >= 4) return;
   // wave w: rows i in [32w, 32w + 32) of M, columns j = 32 jb + n
-  const __bf16* P = phi_q + (size_t)(bh % H) * HD * HD + (size_t)(32 * wave + n) * HD + 8 * h2;
   f32x16 acc = zero16();
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc)
-    acc = mfma32(ld8(P + 16 * kc),
-                 *reinterpret_cast<const bf16x8*>(st + n * FIN_LD + 16 * kc + 8 * h2), acc);
+    acc = mfma32(pq[kc], *reinterpret_cast<const bf16x8*>(st + n * FIN_LD + 16 * kc + 8 * h2),
+                 acc);
   // acc[r] = M[i = 32w + 8(r/4) + 4h2 + r%4][j]  ->  MT[j][i]
   __bf16* out = mt + (size_t)bh * HD * HD + (size_t)(32 * jb + n) * HD + 32 * wave + 4 * h2;
 #pragma unroll
@@ -1200,6 +1206,29 @@ void commit_split(const Dims& d, int* chunk_tokens, int* n_chunks) {
   const int max_chunks = (d.T + 127) / 128;
   long want = (512 + bh - 1) / bh;
   int c = (int)std::min<long>(std::max<long>(want, 1), max_chunks);
+  int ct = (d.T + c - 1) / c;
+  ct = (ct + CT - 1) / CT * CT;
+  *chunk_tokens = ct;
+  *n_chunks = (d.T + ct - 1) / ct;
+}
+
+// Token chunks of the commit inside the one-launch clean pass: as many as the
+// compute units the read leaves idle hold at once (fewer partials to sum than
+// the standalone split), else the standalone split.
+void clean_commit_split(const Dims& d, long n_attn, int* chunk_tokens, int* n_chunks) {
+  const long bh = (long)d.B * d.H;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 0;
+  const long idle = (long)n_cu - n_attn;
+  if (idle < bh) {
+    commit_split(d, chunk_tokens, n_chunks);
+    return;
+  }
+  int ct0, nc0;
+  commit_split(d, &ct0, &nc0);              // never more chunks than its workspace holds
+  const int c = (int)std::min<long>(idle / bh, nc0);
   int ct = (d.T + c - 1) / c;
   ct = (ct + CT - 1) / CT * CT;
   *chunk_tokens = ct;
@@ -1246,11 +1275,11 @@ hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k,
                                     const void* phi_v, const float* beta, const float* alpha,
                                     const float* S_prev, float* S_next, void* mt_next, void* o,
                                     void* o_intra, void* o_inter, void* ws, hipStream_t s) {
-  int ct, nc;
-  commit_split(d, &ct, &nc);
   const long n_bh = (long)d.B * d.H;
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long n_attn = n_bh * n_qblk;
+  int ct, nc;
+  clean_commit_split(d, n_attn, &ct, &nc);
   const long n_pad = (n_attn + 7) / 8 * 8;
   float* partial = static_cast<float*>(ws);
   clean_fused_k<<<(unsigned)(n_pad + n_bh * nc), 512, 0, s>>>(
