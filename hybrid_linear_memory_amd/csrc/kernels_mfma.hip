@@ -129,39 +129,21 @@ __device__ __forceinline__ int swz_k(int r) { return (r & 7) | (((r >> 4) & 1) <
 __device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 __device__ __forceinline__ int swz_r(int r) { return r & 15; }
 
-// Half-tile load by one wave: rows [32*half, 32*half + 32) of the 64 x 128
-// bf16 tile at byte offset `tile_off` of the buffer `src` into `dst` (16-byte
-// chunk p of row r holding global chunk p ^ swz(r)). `off[v]` are the lane's
-// byte offsets within 4 consecutive rows for the swizzle variant v of the
-// instruction; a tail tile clamps rows past the last key to the last key (their
-// scores are masked and their values meet p = 0).
+// Quarter-tile load by one wave of a stream: rows [16 q, 16 q + 16) (four
+// 4-row instructions; qoff = 4096 q) of the 64 x 128 bf16 tile at byte offset
+// `tile_off` of the buffer `src` into `dst`, 16-byte chunk p of row r holding
+// global chunk p ^ swz(r). `off` holds the lane's byte offsets within 4 rows
+// (K: by instruction parity; V: one). Rows past the end of the buffer (a tail
+// tile past the last key) arrive as zeros: their scores are masked and their
+// values meet p = 0.
 template <bool IS_V>
-__device__ __forceinline__ void tile_load(char* dst, __amdgpu_buffer_rsrc_t src, int tile_off,
-                                          const int (&off)[4], int half, int rows_valid,
-                                          int lane) {
-  // Byte offset of the wave's half in the tile, opaque so that the compiler
-  // forms the 8 destination and source offsets in place rather than keeping
-  // them all in scalar registers across the loop.
-  int hoff = half * 8192;
-  asm volatile("" : "+s"(hoff));
-  if (rows_valid >= AKT) {
+__device__ __forceinline__ void tile_quarter(char* dst, __amdgpu_buffer_rsrc_t src, int tile_off,
+                                             int qoff, const int (&off)[2]) {
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const int var = IS_V ? 0 : ((ii & 1) | ((ii >> 1) & 2));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + hoff + ii * 1024), 16,
-                                               off[var], tile_off + hoff + ii * 1024, 0, 0);
-    }
-  } else {
-    const int p = lane & 15;
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const int r = 32 * half + 4 * ii + (lane >> 4);
-      const int rc = min(r, rows_valid - 1);
-      const int c16 = p ^ (IS_V ? swz_v(r) : swz_k(r));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + hoff + ii * 1024), 16,
-                                               rc * 256 + c16 * 16, tile_off, 0, 0);
-    }
-  }
+  for (int ii = 0; ii < 4; ++ii)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + qoff + ii * 1024), 16,
+                                             IS_V ? off[0] : off[ii & 1],
+                                             tile_off + qoff + ii * 1024, 0, 0);
 }
 
 // Buffer resource over `bytes` bytes at `base` (raw, unswizzled dwords).
@@ -357,30 +339,30 @@ __device__ __forceinline__ void attn_block(
   const AttnOffsets off = attn_offsets(lane);
 
   // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s.
-  // Waves 4s + 2u + c load half c of the stream's K (u = 0) or V (u = 1) tiles.
+  // Wave 4s + w loads rows [16w, 16w + 16) of the stream's K and V tiles.
   const int n_tiles = (n_kv + AKT - 1) / AKT;
   const int my_cnt = (n_tiles - stream + 1) / 2;
-  const int ld_half = wave & 1;
-  const bool ld_v = (wave >> 1) & 1;
-  const __amdgpu_buffer_rsrc_t ld_src =
-      buffer_rsrc((ld_v ? v : k) + (size_t)bh * kv_cap * HD, (uint32_t)n_kv * (HD * 2));
-  int ld_off[4];
+  const uint32_t kv_bytes = (uint32_t)n_kv * (HD * 2);
+  const __amdgpu_buffer_rsrc_t k_src = buffer_rsrc(k + (size_t)bh * kv_cap * HD, kv_bytes);
+  const __amdgpu_buffer_rsrc_t v_src = buffer_rsrc(v + (size_t)bh * kv_cap * HD, kv_bytes);
+  int k_off[2], v_off[2];
   {
     const int p = lane & 15, L4 = lane >> 4;
+    // rows 16 (wave & 1) + 4 e + L4 carry the K swizzle of instruction parity e
 #pragma unroll
-    for (int var = 0; var < 4; ++var) {
-      // instruction i with (i & 1, (i >> 2) & 1) = (var & 1, var >> 1) covers rows 4i + L4
-      const int r = 4 * ((var & 1) | ((var >> 1) << 2)) + L4;
-      ld_off[var] = L4 * 256 + ((p ^ (ld_v ? swz_v(r) : swz_k(r))) << 4);
-    }
+    for (int e = 0; e < 2; ++e)
+      k_off[e] = L4 * 256 + ((p ^ swz_k(16 * (wave & 1) + 4 * e + L4)) << 4);
+    v_off[0] = v_off[1] = L4 * 256 + ((p ^ swz_v(L4)) << 4);
   }
   auto load_k = [&](char* dst, int j) __attribute__((always_inline)) {
-    const int g = 2 * j + stream;
-    tile_load<false>(dst, ld_src, g * TILE_B, ld_off, ld_half, n_kv - g * AKT, lane);
+    int qoff = (wave & 3) * 4096;       // opaque: offsets formed in place
+    asm volatile("" : "+s"(qoff));
+    tile_quarter<false>(dst, k_src, (2 * j + stream) * TILE_B, qoff, k_off);
   };
   auto load_v = [&](char* dst, int j) __attribute__((always_inline)) {
-    const int g = 2 * j + stream;
-    tile_load<true>(dst, ld_src, g * TILE_B, ld_off, ld_half, n_kv - g * AKT, lane);
+    int qoff = (wave & 3) * 4096;
+    asm volatile("" : "+s"(qoff));
+    tile_quarter<true>(dst, v_src, (2 * j + stream) * TILE_B, qoff, v_off);
   };
   // M^T (the inter-frame map, 32 KB) is loaded during the last iteration into
   // the K buffers that iteration leaves idle (rows under the swz_r swizzle),
@@ -441,8 +423,8 @@ __device__ __forceinline__ void attn_block(
       sync();
       if (it == n_iter - 1) load_m(kn);
       if (it + 1 < my_cnt) {
-        if (ld_v) load_v(vn, it + 1);
-        else load_k(kn, it + 1);
+        load_k(kn, it + 1);
+        load_v(vn, it + 1);
       }
       if (it < my_cnt) {
         scores(it, kc);
@@ -455,22 +437,19 @@ __device__ __forceinline__ void attn_block(
       if (it == n_iter - 1) load_m(kn);
       if (mode != 1 && it >= 1 && it <= my_cnt)
         attn_softmax_pv(acc, l, m_ref, s, vc + TILE_B, off, sl2);
-      if (ld_v) {
-        if (it < my_cnt) load_v(vn + TILE_B, it);
-      } else {
-        if (it + 1 < my_cnt) load_k(kn + TILE_B, it + 1);
-      }
+      if (it < my_cnt) load_v(vn + TILE_B, it);
+      if (it + 1 < my_cnt) load_k(kn + TILE_B, it + 1);
       if (it < my_cnt) scores(it, kc + TILE_B);
     };
     if (stream == 0) {
-      if (ld_v) load_v(lv0, 0);
-      else load_k(lk0, 0);
+      load_k(lk0, 0);
+      load_v(lv0, 0);
       for (int it = 0; it < n_iter; it += 2) {
         step_a(it, lk0, lv0, lk1, lv1);
         if (it + 1 < n_iter) step_a(it + 1, lk1, lv1, lk0, lv0);
       }
     } else {
-      if (!ld_v && my_cnt > 0) load_k(lk0 + TILE_B, 0);
+      if (my_cnt > 0) load_k(lk0 + TILE_B, 0);
       for (int it = 0; it < n_iter; it += 2) {
         step_b(it, lk0, lv0, lk1, lv1);
         if (it + 1 < n_iter) step_b(it + 1, lk1, lv1, lk0, lv0);
