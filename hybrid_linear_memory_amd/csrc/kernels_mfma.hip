@@ -533,20 +533,65 @@ __device__ __forceinline__ void attn_block(
   }
 }
 
+// L2 warm-up by a workgroup on an otherwise idle compute unit: block i of the
+// role (i = 0, 1, ...; blocks are dealt to the XCDs round-robin, so it runs on
+// XCD i % 8) reads, tile by tile in the order the attention consumes them, the
+// K and V of the heads whose attention workgroups the XCD holds (the logical
+// blocks xcd_remap gives it), so that their tile loads find L2 warm. The data
+// lands in this workgroup's own LDS and is discarded.
+__device__ __forceinline__ void attn_l2_warm(int i, int per_xcd, int n_attn, int n_qblk,
+                                             const __bf16* k, const __bf16* v, int n_kv,
+                                             long kv_cap, char* scratch) {
+  constexpr int X = 8;
+  const int x = i % X, part = i / X;
+  const int per = n_attn / X, rem = n_attn % X;
+  const int first = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  const int cnt = per + (x < rem ? 1 : 0);
+  if (cnt == 0) return;
+  const int h0 = first / n_qblk, nh = (first + cnt - 1) / n_qblk - h0 + 1;
+  const int n_tiles = (n_kv + AKT - 1) / AKT;
+  const long units = (long)n_tiles * nh * 2;          // (tile, head, K or V), tile-major
+  const long u0 = units * part / per_xcd, u1 = units * (part + 1) / per_xcd;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t kv_bytes = (uint32_t)n_kv * (HD * 2);
+  for (long u = u0; u < u1; ++u) {
+    const int g = (int)(u / (2 * nh));
+    const int hh = (int)(u % (2 * nh)) >> 1;
+    const __bf16* base = ((u & 1) ? v : k) + (size_t)(h0 + hh) * kv_cap * HD;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base, kv_bytes);
+    // 16 KB tile: two 1 KB pieces per wave
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(scratch + wave * 1024), 16,
+                                               lane * 16, g * TILE_B + (2 * wave + c) * 1024, 0,
+                                               0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Blocks [0, n_attn): attention workgroups; blocks from n_attn_pad (n_attn
+// rounded up to the XCD count): the L2 warm-up role (when the grid leaves
+// compute units idle).
 template <bool INTER>
 __global__ void __launch_bounds__(512, 1)
 attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
             long kv_cap, float sl2, int n_qblk, const __bf16* __restrict__ mt,
-            __bf16* __restrict__ o_intra, __bf16* __restrict__ o_inter) {
+            __bf16* __restrict__ o_intra, __bf16* __restrict__ o_inter, int n_attn,
+            int n_attn_pad) {
   __shared__ __attribute__((aligned(1024))) char lk0[AKV];
   __shared__ __attribute__((aligned(1024))) char lk1[AKV];
   __shared__ __attribute__((aligned(1024))) char lv0[AKV];
   __shared__ __attribute__((aligned(1024))) char lv1[AKV];
   __shared__ float mlx[8][2][64];
   __shared__ int redo_flag;
-  attn_block<INTER>(xcd_remap(blockIdx.x, gridDim.x), q, k, v, o, T, n_kv, kv_cap, sl2, n_qblk,
-                    mt, o_intra, o_inter, lk0, lk1, lv0, lv1, mlx, redo_flag);
+  const int b = blockIdx.x;
+  if (b < n_attn)
+    attn_block<INTER>(xcd_remap(b, n_attn), q, k, v, o, T, n_kv, kv_cap, sl2, n_qblk, mt,
+                      o_intra, o_inter, lk0, lk1, lv0, lv1, mlx, redo_flag);
+  else if (b >= n_attn_pad)
+    attn_l2_warm(b - n_attn_pad, ((int)gridDim.x - n_attn_pad) / 8, n_attn, n_qblk, k, v, n_kv,
+                 kv_cap, lk0);
 }
 
 // ===========================================================================
@@ -1216,14 +1261,28 @@ void clean_commit_split(const Dims& d, long n_attn, int* chunk_tokens, int* n_ch
 
 }  // namespace
 
+// Grid of the attention: its workgroups, then (when they leave compute units
+// idle) up to 8 L2 warm-up workgroups per XCD.
+void attn_grid(long n_attn, long* n_pad, long* total) {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 0;
+  *n_pad = (n_attn + 7) / 8 * 8;
+  const long per_xcd = std::min<long>(8, std::max<long>(0, n_cu - *n_pad) / 8);
+  *total = per_xcd > 0 ? *n_pad + 8 * per_xcd : n_attn;
+}
+
 hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const void* v, void* o,
                           int64_t n_kv, int64_t kv_cap, hipStream_t s) {
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
-  attn_mfma_k<false><<<(unsigned)nblk, 512, 0, s>>>(
+  long n_pad, total;
+  attn_grid(nblk, &n_pad, &total);
+  attn_mfma_k<false><<<(unsigned)total, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, (int)n_kv, (long)kv_cap, d.scale * kLog2e, n_qblk, nullptr,
-      nullptr, nullptr);
+      nullptr, nullptr, (int)nblk, (int)n_pad);
   return hipGetLastError();
 }
 
@@ -1241,11 +1300,13 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
                               hipStream_t s) {
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
-  attn_mfma_k<true><<<(unsigned)nblk, 512, 0, s>>>(
+  long n_pad, total;
+  attn_grid(nblk, &n_pad, &total);
+  attn_mfma_k<true><<<(unsigned)total, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk,
       static_cast<const __bf16*>(mt), static_cast<__bf16*>(o_intra),
-      static_cast<__bf16*>(o_inter));
+      static_cast<__bf16*>(o_inter), (int)nblk, (int)n_pad);
   return hipGetLastError();
 }
 
