@@ -7,8 +7,9 @@ state): 4 denoising reads and the clean pass (its read plus the state commit),
 i.e. every step of the hot path: feature maps, intra-frame softmax, inter-frame
 read, combine, state commit. Inputs are seeded synthetic tensors resident in
 HBM before timing starts (a pool of frames is cycled); the state carries over
-from frame to frame. By default each frame's launches are replayed from a HIP
-graph.
+from frame to frame. Each frame's calls are launched on the stream as the layer
+driver issues them (replays of a HIP graph of the same launches are timed
+beside, or instead with --graph; on this stack the graph replays run slower).
 
 Printed (one JSON line): frames/s (value) and tokens/s, the roofline of the
 dominant kernel (the fused read: intra-frame attention plus the inter-frame
@@ -44,7 +45,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20, help="untimed frames")
     ap.add_argument("--pool", type=int, default=8,
                     help="distinct resident input frames (even; one graph covers them all)")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly, no HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph of the pool's frames instead of launching "
+                         "each frame's calls on the stream")
+    ap.add_argument("--no-graph-compare", action="store_true",
+                    help="skip the extra graph-replay timing reported beside the value")
     ap.add_argument("--kernel-iters", type=int, default=50)
     ap.add_argument("--rollout-frames", type=int, default=240)
     ap.add_argument("--skip-rollout", action="store_true")
@@ -363,12 +368,12 @@ def main():
     w = b.w
     calib = b.copy_calibration()
     print("[bench] timing frames", file=sys.stderr, flush=True)
-    frames, secs, gpu_secs = b.timed(args.steps, args.warmup, use_graph=not args.no_graph)
+    frames, secs, gpu_secs = b.timed(args.steps, args.warmup, use_graph=args.graph)
     fps = w.B * frames / secs
-    eager = None
-    if not args.no_graph:
-        ef, es, _ = b.timed(max(20, args.steps // 4), 5, use_graph=False)
-        eager = w.B * ef / es
+    other = None
+    if not args.no_graph_compare:
+        of, os_, _ = b.timed(max(40, args.steps // 2), 8, use_graph=not args.graph)
+        other = w.B * of / os_
     print("[bench] timing kernels", file=sys.stderr, flush=True)
     kt = b.kernel_times(args.kernel_iters)
     # The dominant kernel: the fused read (attn_mfma_k<true>), five launches per
@@ -419,9 +424,9 @@ def main():
                                "4 denoising reads + clean pass (read + state commit) per frame, "
                                "bf16 activations, fp32 state",
                    "B": w.B, "H": w.H, "D": w.D, "T": w.T, "passes_per_frame": w.passes,
-                   "hip_graph": not args.no_graph},
+                   "hip_graph": args.graph},
         "tokens_per_s": fps * w.T,
-        "frames_per_s_eager": eager,
+        ("frames_per_s_stream" if args.graph else "frames_per_s_graph"): other,
         "roofline": {"bound": "mfma",
                      "kernel": "attn_mfma_k<true> (fused read: intra-frame softmax + Q M)",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
