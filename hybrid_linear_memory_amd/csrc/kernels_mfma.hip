@@ -1135,9 +1135,17 @@ commit_reduce_k(const float* __restrict__ partial, const float* __restrict__ alp
   const size_t stride4 = (size_t)n_bh * HD * HD / 4;
   const float4* P = reinterpret_cast<const float4*>(partial) + q4;
   float4 acc = P[0];
-  for (int c = 1; c < n_chunks; ++c) {
-    const float4 x = P[(size_t)c * stride4];
-    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  // chunks in order; the loads of 8 chunks are issued before their sums
+  for (int c0 = 1; c0 < n_chunks; c0 += 8) {
+    float4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < n_chunks) x[u] = P[(size_t)(c0 + u) * stride4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < n_chunks) {
+        acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w;
+      }
   }
   const float a = alpha[bh];
   const float4 s = reinterpret_cast<const float4*>(S_prev)[q4];
@@ -1181,11 +1189,21 @@ commit_finish_k(const float* __restrict__ partial, const float* __restrict__ alp
     const size_t stride = (size_t)n_bh * HD * HD;
     float4 a0 = *reinterpret_cast<const float4*>(partial + e);
     float4 a1 = *reinterpret_cast<const float4*>(partial + e + 4);
-    for (int c = 1; c < n_chunks; ++c) {
-      const float4 x0 = *reinterpret_cast<const float4*>(partial + c * stride + e);
-      const float4 x1 = *reinterpret_cast<const float4*>(partial + c * stride + e + 4);
-      a0.x += x0.x; a0.y += x0.y; a0.z += x0.z; a0.w += x0.w;
-      a1.x += x1.x; a1.y += x1.y; a1.z += x1.z; a1.w += x1.w;
+    // chunks in order; the loads of 8 chunks are issued before their sums
+    for (int c0 = 1; c0 < n_chunks; c0 += 8) {
+      float4 x0[8], x1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < n_chunks) {
+          x0[u] = *reinterpret_cast<const float4*>(partial + (c0 + u) * stride + e);
+          x1[u] = *reinterpret_cast<const float4*>(partial + (c0 + u) * stride + e + 4);
+        }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < n_chunks) {
+          a0.x += x0[u].x; a0.y += x0[u].y; a0.z += x0[u].z; a0.w += x0[u].w;
+          a1.x += x1[u].x; a1.y += x1[u].y; a1.z += x1[u].z; a1.w += x1[u].w;
+        }
     }
     const float al = alpha[bh];
     const float4 s0 = *reinterpret_cast<const float4*>(S_prev + e);
