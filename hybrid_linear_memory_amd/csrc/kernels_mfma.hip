@@ -1091,16 +1091,17 @@ commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
 }
 
 // The clean pass of the prepared read in one launch: blocks [0, n_attn) are
-// the fused read's workgroups (taking the compute units first, being dispatched
-// first), blocks [n_attn_pad, ...) the commit's (threads 0-255; the other four
+// the fused read's workgroups (dispatched first, they take their compute units
+// first), the next n_warm blocks (from n_attn_pad) the attention's L2 warm-up
+// role (short-lived), then the commit's blocks (threads 0-255; the other four
 // waves leave), which run on the compute units the read leaves idle. The
-// commit reuses the read's LDS arrays; the padding keeps each role's blocks
-// dealt round-robin over the XCDs from XCD 0.
+// commit reuses the read's LDS arrays; n_attn_pad and n_warm are multiples of
+// 8, so each role's blocks are dealt round-robin over the XCDs from XCD 0.
 __global__ void __launch_bounds__(512, 1)
 clean_fused_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, float sl2,
               int n_qblk, const __bf16* __restrict__ mt, __bf16* __restrict__ o_intra,
-              __bf16* __restrict__ o_inter, int n_attn, int n_attn_pad,
+              __bf16* __restrict__ o_inter, int n_attn, int n_attn_pad, int n_warm,
               const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
               const float* __restrict__ beta, const float* __restrict__ alpha,
               const float* __restrict__ S_prev, float* __restrict__ S_next,
@@ -1116,10 +1117,13 @@ clean_fused_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (b < n_attn)
       attn_block<true>(xcd_remap(b, n_attn), q, k, v, o, T, T, T, sl2, n_qblk, mt, o_intra,
                        o_inter, lk0, lk1, lv0, lv1, mlx, redo_flag);
+  } else if (b < n_attn_pad + n_warm) {
+    attn_l2_warm(b - n_attn_pad, n_warm / 8, n_attn, n_qblk, k, v, T, T, lk0);
   } else if (threadIdx.x < 256) {
-    const int c = b - n_attn_pad;
-    commit_block(xcd_remap(c, (int)gridDim.x - n_attn_pad), k, v, phi_k, phi_v, beta, alpha,
-                 S_prev, S_next, partial, H, T, chunk_tokens, n_chunks, n_bh, lk0, lk1, lv0, lv1);
+    const int c = b - n_attn_pad - n_warm;
+    commit_block(xcd_remap(c, (int)gridDim.x - n_attn_pad - n_warm), k, v, phi_k, phi_v, beta,
+                 alpha, S_prev, S_next, partial, H, T, chunk_tokens, n_chunks, n_bh, lk0, lk1,
+                 lv0, lv1);
   }
 }
 
@@ -1280,14 +1284,17 @@ void clean_commit_split(const Dims& d, long n_attn, int* chunk_tokens, int* n_ch
 }  // namespace
 
 // Grid of the attention: its workgroups, then (when they leave compute units
-// idle) up to 8 L2 warm-up workgroups per XCD.
-void attn_grid(long n_attn, long* n_pad, long* total) {
+// idle, and the heads' K and V are short enough to stay in L2 until used: up to
+// kWarmMaxKeys keys) up to 8 L2 warm-up workgroups per XCD.
+constexpr long kWarmMaxKeys = 4096;
+static void attn_grid(long n_attn, long n_kv, long* n_pad, long* total) {
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     n_cu = 0;
   *n_pad = (n_attn + 7) / 8 * 8;
-  const long per_xcd = std::min<long>(8, std::max<long>(0, n_cu - *n_pad) / 8);
+  const long per_xcd =
+      n_kv <= kWarmMaxKeys ? std::min<long>(8, std::max<long>(0, n_cu - *n_pad) / 8) : 0;
   *total = per_xcd > 0 ? *n_pad + 8 * per_xcd : n_attn;
 }
 
@@ -1296,7 +1303,7 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const voi
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
   long n_pad, total;
-  attn_grid(nblk, &n_pad, &total);
+  attn_grid(nblk, n_kv, &n_pad, &total);
   attn_mfma_k<false><<<(unsigned)total, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, (int)n_kv, (long)kv_cap, d.scale * kLog2e, n_qblk, nullptr,
@@ -1319,7 +1326,7 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
   long n_pad, total;
-  attn_grid(nblk, &n_pad, &total);
+  attn_grid(nblk, d.T, &n_pad, &total);
   attn_mfma_k<true><<<(unsigned)total, 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk,
@@ -1338,13 +1345,15 @@ hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k,
   const long n_attn = n_bh * n_qblk;
   int ct, nc;
   clean_commit_split(d, n_attn, &ct, &nc);
-  const long n_pad = (n_attn + 7) / 8 * 8;
+  long n_pad, total;
+  attn_grid(n_attn, d.T, &n_pad, &total);
+  const long n_warm = total > n_attn ? total - n_pad : 0;
   float* partial = static_cast<float*>(ws);
-  clean_fused_k<<<(unsigned)(n_pad + n_bh * nc), 512, 0, s>>>(
+  clean_fused_k<<<(unsigned)(n_pad + n_warm + n_bh * nc), 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, d.scale * kLog2e, n_qblk, static_cast<const __bf16*>(mt),
       static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter), (int)n_attn, (int)n_pad,
-      static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), beta, alpha, S_prev,
+      (int)n_warm, static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), beta, alpha, S_prev,
       S_next, partial, d.H, ct, nc, n_bh);
   if (mt_next) {
     commit_finish_k<<<(unsigned)(n_bh * 4), 512, 0, s>>>(partial, alpha, S_prev, S_next, nc, n_bh,

@@ -12,10 +12,12 @@ from .arl2_oracle import (  # noqa: F401
     default_scale,
     feature_map,
     fullkv_attention,
+    hybrid_stack_rollout,
     inter_read,
     intra_attention,
     l2_normalize_rows,
     read,
     rollout,
+    softmax_layer_rollout,
     state_commit,
 )

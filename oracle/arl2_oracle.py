@@ -208,3 +208,48 @@ def rollout(frames, phi_q, phi_k, phi_v, S0=None, scale=None,
         S = commit(kc, vc, phi_k, phi_v, fr["beta"], fr["alpha"], S)
         states.append(S)
     return outputs, states
+
+
+def softmax_layer_rollout(frames, scale=None, eval_pass=None):
+    """A softmax attention layer of the autoregressive video model, the kind
+    the hybrid replaces (ARL2 summary §1: every generated block's keys and
+    values join a KV cache that later blocks attend to; §3: the layers not
+    replaced keep softmax attention). Every pass of frame f attends, with no
+    mask, over the clean-pass keys and values of frames 0..f-1 (the cache) plus
+    the pass's own; after the frame its clean-pass K and V join the cache.
+
+    frames: as for ``rollout`` ("beta"/"alpha" unused). Returns outputs[(f, p)]
+    = O [B, H, T, d] for the evaluated passes."""
+    cache_k, cache_v = [], []
+    outputs = {}
+    for f, fr in enumerate(frames):
+        n_pass = len(fr["passes"])
+        for p, (q, k, v) in enumerate(fr["passes"]):
+            if eval_pass is None or eval_pass(f, p):
+                k_all = np.concatenate([_f64(c) for c in cache_k] + [_f64(k)], axis=2)
+                v_all = np.concatenate([_f64(c) for c in cache_v] + [_f64(v)], axis=2)
+                outputs[(f, p)] = fullkv_attention(q, k_all, v_all, scale)
+        _, kc, vc = fr["passes"][n_pass - 1]
+        cache_k.append(kc)
+        cache_v.append(vc)
+    return outputs
+
+
+def hybrid_stack_rollout(layers, mask, scale=None, eval_pass=None):
+    """A stack of attention layers in which the layers marked in ``mask`` are
+    hybrid ARL2 layers (state S, ``rollout``) and the others softmax layers
+    with a KV cache (``softmax_layer_rollout``); the summary's hybrid model
+    replaces a fraction of a 30-layer model's attention layers (§3: 50% or 75%).
+    Each layer takes its own inputs: layers[l] = {"frames": ..., "phis":
+    (phi_q, phi_k, phi_v)} ("phis" unused for softmax layers).
+
+    Returns per layer: {"o": outputs[(f, p)] -> O} and, for ARL2 layers,
+    "states" (S_0..S_F)."""
+    res = []
+    for lay, is_arl2 in zip(layers, mask):
+        if is_arl2:
+            outs, states = rollout(lay["frames"], *lay["phis"], scale=scale, eval_pass=eval_pass)
+            res.append({"o": {key: r["o"] for key, r in outs.items()}, "states": states})
+        else:
+            res.append({"o": softmax_layer_rollout(lay["frames"], scale, eval_pass)})
+    return res

@@ -109,3 +109,34 @@ def rollout(frames, phi_q, phi_k, phi_v, scale):
         S = commit_tokens(kp, vp, fr["beta"], fr["alpha"], S)
         states.append(S)
     return outputs, states
+
+
+def softmax_layer_rollout(frames, scale):
+    """One head of a KV-cache softmax layer: each pass of frame f attends over
+    the clean-pass keys/values of frames 0..f-1 followed by its own, written as
+    explicit loops over the cached tokens. frames[f] = {"passes": [(q, k, v)]}.
+    Returns outputs[(f, p)] = O."""
+    cache_k, cache_v = [], []
+    outputs = {}
+    for f, fr in enumerate(frames):
+        for p, (q, k, v) in enumerate(fr["passes"]):
+            keys = [row for row in cache_k] + [row for row in k]
+            vals = [row for row in cache_v] + [row for row in v]
+            out = []
+            for t in range(len(q)):
+                logits = []
+                for s in range(len(keys)):
+                    dot = 0.0
+                    for i in range(len(q[t])):
+                        dot += float(q[t][i]) * float(keys[s][i])
+                    logits.append(dot * scale)
+                m = max(logits)
+                w = [math.exp(a - m) for a in logits]
+                z = sum(w)
+                out.append([sum(w[s] / z * float(vals[s][j]) for s in range(len(keys)))
+                            for j in range(len(vals[0]))])
+            outputs[(f, p)] = out
+        _, kc, vc = fr["passes"][-1]
+        cache_k.extend(kc)
+        cache_v.extend(vc)
+    return outputs

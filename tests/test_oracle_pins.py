@@ -395,3 +395,74 @@ def test_planted_mistakes_are_caught():
     beta = _as_array(gd["beta"])[0]; alpha = float(_as_array(gd["alpha"])[0, 0])
     decay_first = alpha * S + K.T @ np.diag(beta) @ (V - K @ (alpha * S))
     assert np.abs(decay_first - _as_array(gd["S_next"])).max() > 0.1
+
+
+# ------------------------------------------------- KV-cache softmax layer, stack
+def _frames(g, B, H, T, d, F, P):
+    frames = []
+    for _ in range(F):
+        passes = [tuple(g.standard_normal((B, H, T, d)) for _ in range(3)) for _ in range(P)]
+        frames.append({"passes": passes, "beta": g.uniform(0, 0.3, (B, H, T)),
+                       "alpha": g.uniform(0.5, 1, (B, H))})
+    return frames
+
+
+def test_softmax_layer_bruteforce():
+    """The KV-cache layer equals scalar loops over cached tokens: only clean
+    passes enter the cache, in frame order, and each pass sees its own keys
+    (caching a noisy pass, skipping the current pass or reversing the cache
+    order fail)."""
+    g = _rs(21)
+    B, H, T, d, F, P = 1, 2, 3, 4, 3, 3
+    frames = _frames(g, B, H, T, d, F, P)
+    outs = oracle.softmax_layer_rollout(frames)
+    for h in range(H):
+        bframes = [{"passes": [tuple(x[0, h].tolist() for x in p) for p in fr["passes"]]}
+                   for fr in frames]
+        bouts = bf.softmax_layer_rollout(bframes, 1 / math.sqrt(d))
+        for key, val in bouts.items():
+            np.testing.assert_allclose(outs[key][0, h], np.array(val), rtol=0, atol=1e-12)
+
+
+def test_softmax_layer_first_frame_and_uniform_cache():
+    """Frame 0 has an empty cache, so it is the intra-frame softmax; with all
+    keys zero every weight is equal and O is the mean of the cached clean V
+    rows and the pass's own V rows."""
+    g = _rs(22)
+    B, H, T, d, F, P = 1, 1, 4, 3, 3, 2
+    frames = _frames(g, B, H, T, d, F, P)
+    outs = oracle.softmax_layer_rollout(frames)
+    for p, (q, k, v) in enumerate(frames[0]["passes"]):
+        np.testing.assert_allclose(outs[(0, p)], oracle.intra_attention(q, k, v), rtol=0, atol=0)
+    for fr in frames:
+        fr["passes"] = [(q, np.zeros_like(k), v) for (q, k, v) in fr["passes"]]
+    outs = oracle.softmax_layer_rollout(frames)
+    clean_v = [fr["passes"][-1][2] for fr in frames]
+    for f in range(F):
+        for p, (_, _, v) in enumerate(frames[f]["passes"]):
+            rows = np.concatenate(clean_v[:f] + [v], axis=2)
+            mean = np.broadcast_to(rows.mean(axis=2, keepdims=True), outs[(f, p)].shape)
+            np.testing.assert_allclose(outs[(f, p)], mean, rtol=0, atol=1e-14)
+
+
+def test_hybrid_stack_composes_its_layers():
+    """A stack with a mixed mask gives each layer exactly what that layer's
+    own rollout gives, in layer order (swapping two layers' kinds or inputs
+    fails)."""
+    g = _rs(23)
+    B, H, T, d, F, P = 1, 1, 3, 4, 3, 2
+    layers = [{"frames": _frames(g, B, H, T, d, F, P),
+               "phis": tuple(g.standard_normal((H, d, d)) for _ in range(3))} for _ in range(4)]
+    mask = [True, False, False, True]
+    res = oracle.hybrid_stack_rollout(layers, mask)
+    for lay, is_arl2, r in zip(layers, mask, res):
+        if is_arl2:
+            outs, states = oracle.rollout(lay["frames"], *lay["phis"])
+            for key in outs:
+                np.testing.assert_array_equal(r["o"][key], outs[key]["o"])
+            assert len(r["states"]) == F + 1
+        else:
+            ref = oracle.softmax_layer_rollout(lay["frames"])
+            for key in ref:
+                np.testing.assert_array_equal(r["o"][key], ref[key])
+            assert "states" not in r
