@@ -20,4 +20,6 @@ from .arl2_oracle import (  # noqa: F401
     rollout,
     softmax_layer_rollout,
     state_commit,
+    token_level_read,
+    token_level_rollout,
 )

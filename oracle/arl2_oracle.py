@@ -48,6 +48,13 @@ applied by exactly one function below):
       reads S_{N-1} and produces O, then commits.
   A12 Frames are indexed 0..F-1 here: frame f reads S_f and commits S_{f+1}.
   A13 The commit uses the clean pass's K and V.
+  A15 Token-level access (the ablated alternative, §4), not defined further by
+      the pages: within a pass, token t reads the state left by the tokens
+      before it in the frame, S_t = S_{t-1} + beta_t k'_t^T (v'_t - k'_t
+      S_{t-1}) starting from S_{N-1}, o_inter_t = q'_t S_{t-1}; denoising
+      passes discard these updates, the clean pass commits
+      S_N = alpha_N S_{N-1} + (S_T - S_{N-1}) (the frame's gate applied once,
+      as in the frame-level update). With T = 1 it equals frame-level access.
 
 Every function in this module is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, exact rational worked examples and scalar
@@ -253,3 +260,49 @@ def hybrid_stack_rollout(layers, mask, scale=None, eval_pass=None):
         else:
             res.append({"o": softmax_layer_rollout(lay["frames"], scale, eval_pass)})
     return res
+
+
+def token_level_read(q, k, v, phi_q, phi_k, phi_v, beta, S, scale=None) -> dict:
+    """One pass under token-level access (reading A15; ARL2 summary §4 ablation):
+    the intra-frame softmax as in ``read``, and an inter-frame branch in which
+    token t reads the state updated by the frame's earlier tokens, in token
+    order, starting from S = S_{N-1}:
+        o_inter_t = q'_t S_{t-1};  S_t = S_{t-1} + beta_t k'_t^T (v'_t - k'_t S_{t-1}).
+    Returns o, o_intra, o_inter and S_T (the state after the last token)."""
+    q_prime = feature_map(q, phi_q)
+    k_prime, v_prime = commit_inputs(k, v, phi_k, phi_v)
+    beta = _f64(beta)
+    St = _f64(S).copy()                               # [B, H, d, d]
+    o_inter = np.zeros(q_prime.shape[:3] + (St.shape[-1],))
+    for t in range(q_prime.shape[2]):
+        o_inter[:, :, t] = np.einsum("bhi,bhij->bhj", q_prime[:, :, t], St)
+        kt, vt = k_prime[:, :, t], v_prime[:, :, t]
+        resid = vt - np.einsum("bhi,bhij->bhj", kt, St)
+        St = St + beta[:, :, t, None, None] * kt[..., :, None] * resid[..., None, :]
+    o_intra = intra_attention(q, k, v, scale)
+    return {"o": o_intra + o_inter, "o_intra": o_intra, "o_inter": o_inter, "S_T": St}
+
+
+def token_level_rollout(frames, phi_q, phi_k, phi_v, S0=None, scale=None, eval_pass=None):
+    """The streaming loop under token-level access (reading A15): every pass
+    runs ``token_level_read`` from S_{N-1}; the clean pass's end state commits
+    S_N = alpha S_{N-1} + (S_T - S_{N-1}). Same arguments and returns as
+    ``rollout``."""
+    first_q = frames[0]["passes"][0][0]
+    B, H, _, d = np.shape(first_q)
+    S = np.zeros((B, H, d, d)) if S0 is None else _f64(S0).copy()
+    states = [S]
+    outputs = {}
+    for f, fr in enumerate(frames):
+        n_pass = len(fr["passes"])
+        clean = None
+        for p, (q, k, v) in enumerate(fr["passes"]):
+            if p == n_pass - 1 or eval_pass is None or eval_pass(f, p):
+                r = token_level_read(q, k, v, phi_q, phi_k, phi_v, fr["beta"], S, scale)
+                outputs[(f, p)] = r
+                if p == n_pass - 1:
+                    clean = r
+        alpha = _f64(fr["alpha"])[:, :, None, None]
+        S = alpha * S + (clean["S_T"] - S)
+        states.append(S)
+    return outputs, states

@@ -140,3 +140,22 @@ def softmax_layer_rollout(frames, scale):
         cache_k.extend(kc)
         cache_v.extend(vc)
     return outputs
+
+
+def token_level_read(q, k, v, phi_q, phi_k, phi_v, beta, S, scale):
+    """One head under token-level access: token t reads the state left by the
+    earlier tokens of the frame, then updates it with its own delta-rule term.
+    Returns (o_inter, S_T)."""
+    qp = feature_map(q, phi_q)
+    kp = unit_rows(feature_map(k, phi_k))
+    vp = feature_map(v, phi_v)
+    dk, dv = len(S), len(S[0])
+    St = [[float(S[i][j]) for j in range(dv)] for i in range(dk)]
+    o = []
+    for t in range(len(qp)):
+        o.append([sum(qp[t][i] * St[i][j] for i in range(dk)) for j in range(dv)])
+        pred = [sum(kp[t][i] * St[i][j] for i in range(dk)) for j in range(dv)]
+        for i in range(dk):
+            for j in range(dv):
+                St[i][j] += float(beta[t]) * kp[t][i] * (vp[t][j] - pred[j])
+    return o, St

@@ -466,3 +466,80 @@ def test_hybrid_stack_composes_its_layers():
             for key in ref:
                 np.testing.assert_array_equal(r["o"][key], ref[key])
             assert "states" not in r
+
+
+# ------------------------------------------------------ token-level access (A15)
+def _tl_inputs(g, B, H, T, d, beta_hi=0.3):
+    q, k, v = (g.standard_normal((B, H, T, d)) for _ in range(3))
+    phis = [g.standard_normal((H, d, d)) / math.sqrt(d) for _ in range(3)]
+    beta = g.uniform(0, beta_hi, (B, H, T))
+    S = g.standard_normal((B, H, d, d)) * 0.3
+    return q, k, v, phis, beta, S
+
+
+def test_token_level_bruteforce():
+    """Token-level read and end state equal scalar loops (reading a token's own
+    update, or the pre-frame state for every token, fail)."""
+    g = _rs(31)
+    B, H, T, d = 1, 2, 5, 4
+    q, k, v, phis, beta, S = _tl_inputs(g, B, H, T, d)
+    r = oracle.token_level_read(q, k, v, *phis, beta, S)
+    for h in range(H):
+        o, St = bf.token_level_read(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(),
+                                    phis[0][h].tolist(), phis[1][h].tolist(),
+                                    phis[2][h].tolist(), beta[0, h].tolist(), S[0, h].tolist(),
+                                    1 / math.sqrt(d))
+        np.testing.assert_allclose(r["o_inter"][0, h], np.array(o), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["S_T"][0, h], np.array(St), rtol=0, atol=1e-12)
+
+
+def test_token_level_chunk_closed_form():
+    """The token recurrence in closed form over a chunk (the triangular-solve
+    form a chunked kernel uses): U = (I + tril(diag(beta) K'K'^T, -1))^-1
+    diag(beta) (V' - K' S0), O_inter = Q' S0 + tril(Q' K'^T, -1) U,
+    S_T = S0 + K'^T U."""
+    g = _rs(32)
+    B, H, T, d = 1, 1, 7, 5
+    q, k, v, phis, beta, S = _tl_inputs(g, B, H, T, d, beta_hi=0.9)
+    r = oracle.token_level_read(q, k, v, *phis, beta, S)
+    Qp = q[0, 0] @ phis[0][0]
+    Kt = k[0, 0] @ phis[1][0]
+    Kp = Kt / np.linalg.norm(Kt, axis=1, keepdims=True)
+    Vp = v[0, 0] @ phis[2][0]
+    b = beta[0, 0]
+    A = np.eye(T) + np.tril(b[:, None] * (Kp @ Kp.T), -1)
+    U = np.linalg.solve(A, b[:, None] * (Vp - Kp @ S[0, 0]))
+    np.testing.assert_allclose(r["o_inter"][0, 0], Qp @ S[0, 0] + np.tril(Qp @ Kp.T, -1) @ U,
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["S_T"][0, 0], S[0, 0] + Kp.T @ U, rtol=0, atol=1e-12)
+
+
+def test_token_level_reduces_to_frame_level():
+    """T = 1: token-level and frame-level access coincide (read and commit).
+    beta = 0: the reads coincide and the commit is pure decay. Orthonormal
+    keys (phi_k = phi_v = I): the commits coincide, since no key sees another's
+    update."""
+    g = _rs(33)
+    B, H, d = 1, 2, 4
+    q, k, v, phis, beta, S = _tl_inputs(g, B, H, 1, d)
+    alpha = g.uniform(0.5, 1, (B, H))
+    frames = [{"passes": [(q, k, v)], "beta": beta, "alpha": alpha}]
+    outs_t, st_t = oracle.token_level_rollout(frames, *phis, S0=S)
+    outs_f, st_f = oracle.rollout(frames, *phis, S0=S)
+    np.testing.assert_allclose(outs_t[(0, 0)]["o"], outs_f[(0, 0)]["o"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st_t[1], st_f[1], rtol=0, atol=1e-13)
+    T = 6
+    q, k, v, phis, beta, S = _tl_inputs(g, B, H, T, d)
+    r = oracle.token_level_read(q, k, v, *phis, np.zeros_like(beta), S)
+    np.testing.assert_allclose(r["o"], oracle.read(q, k, v, phis[0], S)["o"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["S_T"], S, rtol=0, atol=0)
+    eye = np.broadcast_to(np.eye(d), (H, d, d))
+    korth = np.zeros((B, H, d, d))
+    for h in range(H):
+        korth[0, h] = np.linalg.qr(g.standard_normal((d, d)))[0].T     # orthonormal rows
+    beta = g.uniform(0, 1, (B, H, d))
+    alpha = g.uniform(0.5, 1, (B, H))
+    frames = [{"passes": [(q[:, :, :d], korth, v[:, :, :d])], "beta": beta, "alpha": alpha}]
+    _, st_t = oracle.token_level_rollout(frames, eye, eye, eye, S0=S)
+    _, st_f = oracle.rollout(frames, eye, eye, eye, S0=S)
+    np.testing.assert_allclose(st_t[1], st_f[1], rtol=0, atol=1e-12)
