@@ -20,29 +20,6 @@ inline size_t act_bytes(const Dims& d) {
   return (size_t)d.B * d.H * d.T * d.D * (d.bf16 ? 2 : 4);
 }
 
-// ---- a1: X' = X Phi[h] (optionally row-normalised) ------------------------
-hipError_t launch_feature_map(const Dims& d, const void* x, const void* phi,
-                              void* out, bool normalize, hipStream_t s);
-
-// ---- a2 (and the full-KV comparator): softmax(Q K^T * scale) V ------------
-// K and V hold n_kv valid tokens per head at a per-head stride of kv_cap
-// tokens; Q and O are [B,H,T,D].
-hipError_t launch_attention(const Dims& d, const void* q, const void* k,
-                            const void* v, void* o, int64_t n_kv,
-                            int64_t kv_cap, hipStream_t s);
-
-// ---- a3 + a4: o = o_intra + Q' S  (o_intra may be NULL; o_inter optional) -
-hipError_t launch_inter_read(const Dims& d, const void* q_prime,
-                             const float* S, const void* o_intra, void* o,
-                             void* o_inter, hipStream_t s);
-
-// ---- a5: S_next = alpha S_prev + K'^T diag(beta) (V' - K' S_prev) ---------
-size_t state_commit_ws_bytes(const Dims& d);
-hipError_t launch_state_commit(const Dims& d, const void* k_prime,
-                               const void* v_prime, const float* beta,
-                               const float* alpha, const float* S_prev,
-                               float* S_next, void* ws, hipStream_t s);
-
 // Generic (scalar-FMA) implementations, any supported D, either dtype. The
 // MFMA implementations take over for bf16 at D = 128.
 hipError_t generic_feature_map(const Dims& d, const void* x, const void* phi,
