@@ -22,6 +22,7 @@ F32 = 0
 BF16 = 1
 OP_READ, OP_CLEAN_PASS, OP_COMMIT, OP_STATE_COMMIT, OP_READ_PREPARED = 0, 1, 2, 3, 4
 OP_CLEAN_PASS_PREPARED = 5
+OP_TOKEN_LEVEL = 6
 
 STATUS_NAMES = {
     0: "ARL2_OK", 1: "ARL2_E_NULL", 2: "ARL2_E_SHAPE", 3: "ARL2_E_DTYPE",
@@ -56,6 +57,10 @@ SIGNATURES = {
     "arl2_read_prepared": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_clean_pass_prepared": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "arl2_token_read": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _sz, _vp]),
+    "arl2_token_clean_pass": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _vp, _vp, _sz, _vp]),
     "arl2_workspace_bytes": (_sz, [_SP, _i32]),
     "arl2_status_string": (ctypes.c_char_p, [_i32]),
     "arl2_last_error": (ctypes.c_char_p, []),
@@ -242,6 +247,32 @@ def clean_pass(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, 
                o_intra=None, o_inter=None, ws=None, stream=None):
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_clean_pass(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(phi_q, "phi_q", a), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
+        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
+        _ptr(S_next, "S_next", f), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
+        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def token_read(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, S, o, o_intra=None,
+               o_inter=None, ws=None, stream=None):
+    """Read under token-level access (token t sees the frame's earlier tokens)."""
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_token_read(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(phi_q, "phi_q", a), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
+        _ptr(beta, "beta", f), _ptr(S, "S", f), _ptr(o, "o", a),
+        _ptr(o_intra, "o_intra", a, optional=True), _ptr(o_inter, "o_inter", a, optional=True),
+        _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(stream)))
+
+
+def token_clean_pass(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, S_next, o,
+                     o_intra=None, o_inter=None, ws=None, stream=None):
+    """Clean pass under token-level access: the read, then S_next from its end state."""
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_token_clean_pass(
         ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
         _ptr(phi_q, "phi_q", a), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
         _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),

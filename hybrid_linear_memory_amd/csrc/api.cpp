@@ -116,6 +116,12 @@ size_t ws_clean_pass_prepared(const arl2::Dims& d) {
   return arl2::use_mfma(d) ? ws_commit(d) : std::max(ws_read_prepared(d), ws_commit(d));
 }
 
+// Token-level access: Q', K', V', an o_intra buffer, then the scan's own.
+size_t ws_token(const arl2::Dims& d) {
+  return 4 * arl2::round_up(arl2::act_bytes(d), 256) +
+         arl2::round_up(arl2::token_level_scan_ws_bytes(d), 256);
+}
+
 arl2_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return ARL2_OK;
   if (!ws) return fail(ARL2_E_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -190,6 +196,71 @@ arl2_status do_commit(const arl2::Dims& d, const void* k, const void* v, const v
   return ok();
 }
 
+// One pass under token-level access; alpha and S_next null for a read.
+arl2_status do_token(const arl2::Dims& d, const void* q, const void* k, const void* v,
+                     const void* phi_q, const void* phi_k, const void* phi_v, const float* beta,
+                     const float* alpha, const float* S_prev, float* S_next, void* o,
+                     void* o_intra, void* o_inter, void* ws, hipStream_t s) {
+  const size_t ab = arl2::round_up(arl2::act_bytes(d), 256);
+  char* w = static_cast<char*>(ws);
+  void* qp = w;
+  void* kp = w + ab;
+  void* vp = w + 2 * ab;
+  void* oi = o_intra ? o_intra : (void*)(w + 3 * ab);
+  hipError_t e = run_feature_map(d, q, phi_q, qp, false, s);
+  if (e != hipSuccess) return hip_status(e, "feature map (phi_q)");
+  e = run_feature_map(d, k, phi_k, kp, true, s);
+  if (e != hipSuccess) return hip_status(e, "feature map (phi_k)");
+  e = run_feature_map(d, v, phi_v, vp, false, s);
+  if (e != hipSuccess) return hip_status(e, "feature map (phi_v)");
+  e = run_attention(d, q, k, v, oi, d.T, d.T, s);
+  if (e != hipSuccess) return hip_status(e, "intra-frame attention");
+  e = arl2::token_level_scan(d, qp, kp, vp, beta, S_prev, alpha, S_next, oi, o, o_inter,
+                             w + 4 * ab, s);
+  return hip_status(e, "token-level scan");
+}
+
+// Validation shared by the two token-level entry points.
+arl2_status check_token(const arl2::Dims& d, const void* q, const void* k, const void* v,
+                        const void* phi_q, const void* phi_k, const void* phi_v,
+                        const float* beta, const float* alpha, const float* S_prev,
+                        float* S_next, void* o, void* o_intra, void* o_inter, void* ws,
+                        size_t ws_bytes) {
+  arl2_status st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_q);
+  REQUIRE_PTR(phi_k);
+  REQUIRE_PTR(phi_v);
+  REQUIRE_PTR(beta);
+  REQUIRE_PTR(S_prev);
+  REQUIRE_PTR(o);
+  OPTIONAL_PTR(o_intra);
+  OPTIONAL_PTR(o_inter);
+  const size_t need = ws_token(d);
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d), sb = (size_t)d.B * d.H * d.D * d.D * sizeof(float);
+  const Range outs[4] = {{o, ab}, {o_intra, ab}, {o_inter, ab}, {S_next, S_next ? sb : 0}};
+  const Range ins[10] = {{q, ab},
+                         {k, ab},
+                         {v, ab},
+                         {phi_q, phi_bytes(d)},
+                         {phi_k, phi_bytes(d)},
+                         {phi_v, phi_bytes(d)},
+                         {S_prev, sb},
+                         {ws, need},
+                         {beta, (size_t)d.B * d.H * d.T * 4},
+                         {alpha, alpha ? (size_t)d.B * d.H * 4 : 0}};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ARL2_E_ALIAS, "two outputs overlap");
+  return ARL2_OK;
+}
+
 arl2_status check_state_pair(const arl2::Dims& d, const float* S_prev, const float* S_next) {
   if (overlap({S_prev, state_bytes(d)}, {S_next, state_bytes(d)}))
     return fail(ARL2_E_ALIAS, "S_prev and S_next overlap; the state must be double-buffered");
@@ -228,6 +299,7 @@ size_t arl2_workspace_bytes(const arl2_shape* shape, int32_t op) {
     case ARL2_OP_STATE_COMMIT: return commit_ws(d);
     case ARL2_OP_READ_PREPARED: return ws_read_prepared(d);
     case ARL2_OP_CLEAN_PASS_PREPARED: return ws_clean_pass_prepared(d);
+    case ARL2_OP_TOKEN_LEVEL: return ws_token(d);
     default: return 0;
   }
 }
@@ -510,6 +582,38 @@ arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q, con
   return hip_status(
       arl2::generic_read_prepare(d, phi_q, S_next, static_cast<float*>(prepared_next), s),
       "read preparation");
+}
+
+arl2_status arl2_token_read(const arl2_shape* shape, const void* q, const void* k, const void* v,
+                            const void* phi_q, const void* phi_k, const void* phi_v,
+                            const float* beta, const float* S, void* o, void* o_intra,
+                            void* o_inter, void* ws, size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  st = check_token(d, q, k, v, phi_q, phi_k, phi_v, beta, nullptr, S, nullptr, o, o_intra,
+                   o_inter, ws, ws_bytes);
+  if (st != ARL2_OK) return st;
+  return do_token(d, q, k, v, phi_q, phi_k, phi_v, beta, nullptr, S, nullptr, o, o_intra,
+                  o_inter, ws, (hipStream_t)stream);
+}
+
+arl2_status arl2_token_clean_pass(const arl2_shape* shape, const void* q, const void* k,
+                                  const void* v, const void* phi_q, const void* phi_k,
+                                  const void* phi_v, const float* beta, const float* alpha,
+                                  const float* S_prev, float* S_next, void* o, void* o_intra,
+                                  void* o_inter, void* ws, size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(alpha);
+  REQUIRE_PTR(S_next);
+  if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
+  st = check_token(d, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, S_next, o, o_intra,
+                   o_inter, ws, ws_bytes);
+  if (st != ARL2_OK) return st;
+  return do_token(d, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, S_next, o, o_intra,
+                  o_inter, ws, (hipStream_t)stream);
 }
 
 arl2_status arl2_fullkv_attn(const arl2_shape* shape, const void* q, const void* k_cache,

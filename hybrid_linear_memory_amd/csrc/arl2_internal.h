@@ -80,6 +80,16 @@ hipError_t mfma_state_commit(const Dims& d, const void* k_prime,
                              const float* alpha, const float* S_prev,
                              float* S_next, void* ws, hipStream_t s);
 
+// Token-level access (the ablated alternative to frame-level access): from
+// mapped Q', K', V' and o_intra, o = o_intra + o_inter with token t reading the
+// state updated by the frame's earlier tokens from S_prev; with S_next given,
+// the end state S_T commits S_next = alpha S_prev + (S_T - S_prev).
+size_t token_level_scan_ws_bytes(const Dims& d);
+hipError_t token_level_scan(const Dims& d, const void* q_prime, const void* k_prime,
+                            const void* v_prime, const float* beta, const float* S_prev,
+                            const float* alpha, float* S_next, const void* o_intra, void* o,
+                            void* o_inter, void* ws, hipStream_t s);
+
 inline bool use_mfma(const Dims& d) { return d.bf16 && d.D == 128; }
 
 }  // namespace arl2

@@ -66,10 +66,21 @@ class Arl2Layer:
     With prepared reads (the default) the clean pass is one library call
     (arl2_clean_pass_prepared: read and commit in one launch on bf16 shapes);
     ``fused_clean=False`` issues the read and the commit as two calls instead.
+
+    ``access="token"`` runs the ablated alternative to frame-level access
+    (the summary's §4): within each pass token t reads the state updated by
+    the frame's earlier tokens (arl2_token_read / arl2_token_clean_pass); the
+    state is still written once per frame, by the clean pass.
     """
 
     def __init__(self, shape: arl2.Shape, phi_q, phi_k, phi_v, n_denoise: int | None = None,
-                 device=None, prepared: bool = True, fused_clean: bool = True):
+                 device=None, prepared: bool = True, fused_clean: bool = True,
+                 access: str = "frame"):
+        if access not in ("frame", "token"):
+            raise ValueError(f"access must be 'frame' or 'token' (got {access!r})")
+        self.access = access
+        if access == "token":
+            prepared = False
         self.shape = shape
         self.device = torch.device(device or "cuda")
         dt = shape.torch_dtype
@@ -78,8 +89,9 @@ class Arl2Layer:
         self._S = [torch.zeros(st, dtype=torch.float32, device=self.device),
                    torch.zeros(st, dtype=torch.float32, device=self.device)]
         self._cur = 0
-        ws_bytes = max(arl2.workspace_bytes(shape, op) for op in
-                       (arl2.OP_CLEAN_PASS, arl2.OP_CLEAN_PASS_PREPARED, arl2.OP_COMMIT))
+        ops = ((arl2.OP_TOKEN_LEVEL,) if access == "token" else
+               (arl2.OP_CLEAN_PASS, arl2.OP_CLEAN_PASS_PREPARED, arl2.OP_COMMIT))
+        ws_bytes = max(arl2.workspace_bytes(shape, op) for op in ops)
         self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
         self.fused_clean = fused_clean
         self.seq = PassSequencer(n_denoise)
@@ -123,11 +135,17 @@ class Arl2Layer:
         s = self.shape
         return torch.empty((s.B, s.H, s.T, s.D), dtype=s.torch_dtype, device=self.device)
 
-    def read(self, q, k, v, o=None, o_intra=None, o_inter=None, stream=None):
-        """Denoising read against S_{N-1}; never writes the state."""
+    def read(self, q, k, v, o=None, o_intra=None, o_inter=None, stream=None, beta=None):
+        """Denoising read against S_{N-1}; never writes the state. Under
+        token-level access the in-frame updates need the frame's beta."""
+        if self.access == "token" and beta is None:
+            raise ValueError("token-level reads need the frame's beta")
         self.seq.before_read()
         o = self.new_output() if o is None else o
-        if self.prepared:
+        if self.access == "token":
+            arl2.token_read(self.shape, q, k, v, *self.phi, beta, self.S, o, o_intra, o_inter,
+                            self.ws, stream)
+        elif self.prepared:
             arl2.read_prepared(self.shape, q, k, v, self.M, o, o_intra, o_inter, self.ws, stream)
         else:
             arl2.read(self.shape, q, k, v, self.phi[0], self.S, o, o_intra, o_inter, self.ws,
@@ -140,7 +158,10 @@ class Arl2Layer:
         self.seq.before_clean_pass()
         o = self.new_output() if o is None else o
         nxt = 1 - self._cur
-        if self.prepared and self.fused_clean:
+        if self.access == "token":
+            arl2.token_clean_pass(self.shape, q, k, v, *self.phi, beta, alpha, self._S[self._cur],
+                                  self._S[nxt], o, o_intra, o_inter, self.ws, stream)
+        elif self.prepared and self.fused_clean:
             # also forms the next frame's map, into the other map buffer
             arl2.clean_pass_prepared(self.shape, q, k, v, self.M, self.phi[1], self.phi[2], beta,
                                      alpha, self._S[self._cur], self._S[nxt], o, o_intra,
@@ -167,8 +188,14 @@ class Arl2Layer:
         """State write of the clean pass without its read."""
         self.seq.before_clean_pass()
         nxt = 1 - self._cur
-        arl2.commit(self.shape, k, v, self.phi[1], self.phi[2], beta, alpha, self._S[self._cur],
-                    self._S[nxt], self.ws, stream)
+        if self.access == "token":
+            # the end state depends on K, V and beta only: any query will do,
+            # and the read's outputs are discarded
+            arl2.token_clean_pass(self.shape, k, k, v, *self.phi, beta, alpha, self._S[self._cur],
+                                  self._S[nxt], self.new_output(), None, None, self.ws, stream)
+        else:
+            arl2.commit(self.shape, k, v, self.phi[1], self.phi[2], beta, alpha,
+                        self._S[self._cur], self._S[nxt], self.ws, stream)
         self._cur = nxt
         self.seq.after_clean_pass()
         self._prepare(stream)

@@ -88,7 +88,8 @@ typedef enum arl2_op {
   ARL2_OP_COMMIT = 2,
   ARL2_OP_STATE_COMMIT = 3,
   ARL2_OP_READ_PREPARED = 4,
-  ARL2_OP_CLEAN_PASS_PREPARED = 5
+  ARL2_OP_CLEAN_PASS_PREPARED = 5,
+  ARL2_OP_TOKEN_LEVEL = 6
 } arl2_op;
 
 /* ------------------------------------------------------------------------
@@ -212,6 +213,46 @@ arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q,
                                      void* prepared_next, void* o, void* o_intra,
                                      void* o_inter, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Token-level access: the alternative to frame-level access that the
+ * summary's ablation (§4) compares against and finds worse. The pages do not
+ * define it further; these calls take the plainest reading: within a pass,
+ * token t reads the state left by the frame's earlier tokens, starting from
+ * S_{N-1},
+ *   o_inter_t = q'_t S_{t-1},
+ *   S_t = S_{t-1} + beta_t k'_t^T (v'_t - k'_t S_{t-1})   (S_0 = S_{N-1}),
+ * and o = o_intra + o_inter with o_intra the intra-frame softmax as in
+ * arl2_read. A read discards S_T; the clean pass commits
+ *   S_next = alpha * S_prev + (S_T - S_prev)
+ * (the frame's gate applied once, as in the frame-level update). With T = 1
+ * both calls equal their frame-level counterparts. On bf16 shapes the scan runs
+ * in chunks of 64 tokens (the closed form of the recurrence over a chunk,
+ * formed by a triangular solve); the state is carried in float32 and enters
+ * the chunk products as bfloat16. Both calls need arl2_workspace_bytes(shape,
+ * ARL2_OP_TOKEN_LEVEL) bytes of workspace; outputs must not overlap each
+ * other, the inputs or the workspace.
+ * ------------------------------------------------------------------------ */
+
+/* Denoising-step read under token-level access. S (float32 [B,H,D,D]) is
+ * only read. o_intra / o_inter are optional extra outputs. */
+arl2_status arl2_token_read(const arl2_shape* shape, const void* q,
+                            const void* k, const void* v, const void* phi_q,
+                            const void* phi_k, const void* phi_v,
+                            const float* beta, const float* S, void* o,
+                            void* o_intra, void* o_inter, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Clean pass under token-level access: the read above against S_prev, and
+ * the commit of its end state into S_next (which must not overlap S_prev). */
+arl2_status arl2_token_clean_pass(const arl2_shape* shape, const void* q,
+                                  const void* k, const void* v,
+                                  const void* phi_q, const void* phi_k,
+                                  const void* phi_v, const float* beta,
+                                  const float* alpha, const float* S_prev,
+                                  float* S_next, void* o, void* o_intra,
+                                  void* o_inter, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------
  * Comparator: the cross-frame softmax over a growing KV cache that the

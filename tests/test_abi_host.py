@@ -55,6 +55,11 @@ def test_workspace_sizes(arl2):
     assert arl2.workspace_bytes(arl2.Shape(0, 1, 1, 128), arl2.OP_READ) == 0
     f = arl2.Shape(1, 1, 64, 16, arl2.F32)
     assert arl2.workspace_bytes(f, arl2.OP_STATE_COMMIT) == 64 * 16 * 4
+    # token-level access: Q', K', V', o_intra, then (bf16) W and U [T, D] and
+    # Pq [64, 64] fp32 per 64-token chunk of each head
+    chunks = 12 * ((1560 + 63) // 64)
+    assert arl2.workspace_bytes(s, arl2.OP_TOKEN_LEVEL) == 4 * act + chunks * 64 * (256 + 64) * 4
+    assert arl2.workspace_bytes(f, arl2.OP_TOKEN_LEVEL) == 4 * 64 * 16 * 4
 
 
 A = 1 << 20     # fake, 16-byte aligned "device" addresses: validation fails before any use
@@ -115,6 +120,17 @@ def test_alias_and_workspace_errors(arl2):
     # the next map wanted without phi_q
     assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, None, A, A, A, A, S1, S2,
                B + 4096, B, None, None, WS, cneed, None) == 1
+    # token-level access: S_next aliasing S_prev, missing alpha, workspace short,
+    # an output over an input
+    tneed = arl2.workspace_bytes(s, arl2.OP_TOKEN_LEVEL)
+    assert _st(arl2, "arl2_token_clean_pass", cs(s), A, A, A, A, A, A, A, A, S1, S1, B, None,
+               None, WS, tneed, None) == 5
+    assert _st(arl2, "arl2_token_clean_pass", cs(s), A, A, A, A, A, A, A, None, S1, S2, B, None,
+               None, WS, tneed, None) == 1
+    assert _st(arl2, "arl2_token_read", cs(s), A, A, A, A, A, A, A, S1, B, None, None, WS,
+               tneed - 1, None) == 6
+    assert _st(arl2, "arl2_token_read", cs(s), A, A, A, A, A, A, A, S1, A, None, None, WS, tneed,
+               None) == 5
     # fullkv: n_kv beyond capacity
     assert _st(arl2, "arl2_fullkv_attn", cs(s), A, B, S1, 200, 100, WS, None) == 2
 
