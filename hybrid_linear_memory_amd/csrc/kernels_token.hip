@@ -6,10 +6,11 @@
 // and the clean pass commits S_N = alpha S_{N-1} + (S_T - S_{N-1}).
 //
 // bf16, d = 128: the recurrence runs in chunks of TC tokens in closed form.
-// With A = I + tril(diag(beta) K' K'^T, -1) over a chunk, W = A^-1 diag(beta) K'
-// and U = A^-1 diag(beta) V' do not depend on the state, so every chunk forms
-// them at once (tl_chunk_k, by forward substitution); a sequential pass over
-// the chunks (tl_scan_k) then carries the state:
+// Over a chunk, A X = diag(beta) (V' - K' S) with A = I + tril(diag(beta) K'K'^T, -1)
+// gives every token's update x_t at once; with T = A^-1 (unit lower triangular),
+// W = T diag(beta) K' and U = T diag(beta) V' do not depend on the state, so
+// every chunk forms them in parallel (tl_chunk_k); a sequential pass over the
+// chunks (tl_scan_k) then carries the state:
 //   X = U - W S,  O_inter = Q' S + tril(Q' K'^T, -1) X,  S <- S + K'^T X.
 // float32 (any supported d): one workgroup per (b, h) walks the tokens
 // (tl_seq_k).
@@ -22,52 +23,60 @@ namespace arl2 {
 namespace {
 
 constexpr int TC = 64;                      // tokens per chunk
-constexpr int AP = TC + 4;                  // padded row of A in LDS (fp32, 16-byte rows)
-constexpr int XP = TC + 8;                  // padded row of X^T in LDS (bf16)
-constexpr int SP = HD + 8;                  // padded row of S^T in LDS (bf16)
+constexpr int AP = TC + 4;                  // fp32 row of A / T in LDS (16-byte rows)
+constexpr int LP = TC + 8;                  // bf16 row of T diag(beta) in LDS (144 bytes)
+constexpr int XP = TC + 8;                  // bf16 row of X^T in LDS
+constexpr int SP = HD + 8;                  // bf16 row of S^T in LDS
 
-// Row-read swizzled bf16 chunk of `rows` x 128 (256-byte rows) into LDS: chunk
-// p of row r at (p ^ swz) where swz is swz_r (row reads) or swz_v (transposing
-// reads); rows past `valid` are zero.
-template <bool TR>
+// bf16 chunk of `rows` x 128 (256-byte rows) into LDS under the swz_v chunk
+// swizzle (chunk p of row r at p ^ swz_v(r)); rows past `valid` are zero.
 __device__ __forceinline__ void stage_rows(char* dst, const __bf16* src, int rows, int valid) {
   for (int idx = threadIdx.x; idx < rows * 16; idx += blockDim.x) {
     const int r = idx >> 4, p = idx & 15;
     uint4 val = {0u, 0u, 0u, 0u};
     if (r < valid) val = *reinterpret_cast<const uint4*>(src + (size_t)r * HD + 8 * p);
-    *reinterpret_cast<uint4*>(dst + r * 256 + ((p ^ (TR ? swz_v(r) : swz_r(r))) << 4)) = val;
+    *reinterpret_cast<uint4*>(dst + r * 256 + ((p ^ swz_v(r)) << 4)) = val;
   }
 }
 
+// Row operand (8 consecutive columns 16 kc + 8 h2 ..) from a swz_v-staged chunk.
 __device__ __forceinline__ bf16x8 row_op(const char* base, int row, int kc, int h2) {
-  return *reinterpret_cast<const bf16x8*>(base + row * 256 + (((2 * kc + h2) ^ swz_r(row)) << 4));
+  return *reinterpret_cast<const bf16x8*>(base + row * 256 + (((2 * kc + h2) ^ swz_v(row)) << 4));
 }
 
-__device__ __forceinline__ bf16x8 f32_to_bf16x8(const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  bf16x8 r;
-  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
-  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
-  return r;
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ float4 fma4(float a, float4 b, float4 c) {
+  return make_float4(fmaf(a, b.x, c.x), fmaf(a, b.y, c.y), fmaf(a, b.z, c.z), fmaf(a, b.w, c.w));
 }
 
 // ---------------------------------------------------------------------------
 // Chunk preparation. One workgroup (4 waves) per (b, h, chunk):
-//   A = I + tril(diag(beta) K'K'^T, -1) into LDS, Pq = tril(Q'K'^T, -1) out,
-//   W = A^-1 diag(beta) K' and U = A^-1 diag(beta) V' out (fp32), solved by
-//   forward substitution: thread c < 128 owns column c of W, thread 128 + c
-//   column c of U, with the column in registers.
-// Workspace layout per (bh, chunk): W [TC][128], U [TC][128], Pq [TC][TC].
+//   Pq = tril(Q'K'^T, -1) (bf16, out) and A = tril(diag(beta) K'K'^T, -1) (fp32,
+//   LDS) on MFMA; T = (I + A)^-1 in fp32 by blocks: the four 16 x 16 diagonal
+//   blocks by forward substitution, then two doublings, each forming the
+//   off-diagonal block of a 2 x 2 blocking as  T_10 = -T_11 A_10 T_00;
+//   W = T diag(beta) K' (bf16, out) and U = T diag(beta) V' (fp32, out) on MFMA
+//   with T diag(beta) split into a bf16 high and low part, so that both
+//   products carry fp32-level accuracy.
+// Workspace per (bh, chunk): W bf16 [TC][128] row-major; U fp32 as eight 32 x 32
+// tiles (token tile ti, feature tile tf) each in MFMA accumulator order (lane
+// l's 16 values, rows 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32,
+// contiguous), the order in which the scan consumes them; Pq bf16 [TC][TC].
+// Tokens past the frame's end have beta = 0 and zero K', so their rows of W and
+// U are zero and they leave the state alone.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 tl_chunk_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
            const __bf16* __restrict__ vp, const float* __restrict__ beta,
-           float* __restrict__ w_out, float* __restrict__ u_out, float* __restrict__ pq_out,
+           __bf16* __restrict__ w_out, float* __restrict__ u_out, __bf16* __restrict__ pq_out,
            int T, int n_ch) {
   __shared__ __attribute__((aligned(16))) char lk[TC * 256];
-  __shared__ __attribute__((aligned(16))) char lq[TC * 256];
-  __shared__ float la[TC * AP];
+  __shared__ __attribute__((aligned(16))) char lv[TC * 256];
+  __shared__ __attribute__((aligned(16))) float la[TC * AP];
+  __shared__ __attribute__((aligned(16))) float ly[32 * 32];
+  __shared__ __attribute__((aligned(16))) __bf16 lth[TC * LP];
+  __shared__ __attribute__((aligned(16))) __bf16 ltl[TC * LP];
   __shared__ float lb[TC];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -77,87 +86,179 @@ tl_chunk_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
   const int t0 = ch * TC;
   const int valid = min(TC, T - t0);
   const size_t row0 = (size_t)bh * T + t0;
-  stage_rows<false>(lk, kp + row0 * HD, TC, valid);
-  stage_rows<false>(lq, qp + row0 * HD, TC, valid);
+  const size_t cbase = (size_t)bh * n_ch + ch;
+  stage_rows(lk, kp + row0 * HD, TC, valid);
+  stage_rows(lv, vp + row0 * HD, TC, valid);
   if (tid < TC) lb[tid] = tid < valid ? beta[row0 + tid] : 0.f;
   __syncthreads();
 
-  // wave w: 32 x 32 tile (ti, tj) of K'K'^T and of Q'K'^T
-  const int ti = wave >> 1, tj = wave & 1;
-  f32x16 g = zero16(), pq = zero16();
+  // G = K'K'^T and Q'K'^T on the lower 32 x 32 tiles (0,0), (1,0), (1,1);
+  // the upper tile of Pq is zero
+  __bf16* pq_c = pq_out + cbase * TC * TC;
+  if (wave < 3) {
+    const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
+    const __bf16* qr = qp + (row0 + min(32 * ti + n, valid - 1)) * HD + 8 * h2;
+    f32x16 g = zero16(), pq = zero16();
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    const bf16x8 b = row_op(lk, 32 * tj + n, kc, h2);
-    g = mfma32(row_op(lk, 32 * ti + n, kc, h2), b, g);
-    pq = mfma32(row_op(lq, 32 * ti + n, kc, h2), b, pq);
-  }
-  const size_t cbase = (size_t)bh * n_ch + ch;
-  float* pq_c = pq_out + cbase * TC * TC;
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8 b = row_op(lk, 32 * tj + n, kc, h2);
+      g = mfma32(row_op(lk, 32 * ti + n, kc, h2), b, g);
+      pq = mfma32(ld8(qr + 16 * kc), b, pq);
+    }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 32 * ti + 8 * (r >> 2) + 4 * h2 + (r & 3), j = 32 * tj + n;
-    la[i * AP + j] = i > j ? lb[i] * g[r] : 0.f;
-    pq_c[i * TC + j] = i > j ? pq[r] : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * ti + 8 * (r >> 2) + 4 * h2 + (r & 3), j = 32 * tj + n;
+      la[i * AP + j] = i > j ? lb[i] * g[r] : 0.f;
+      pq_c[i * TC + j] = (__bf16)(i > j ? pq[r] : 0.f);
+    }
+  } else {
+    for (int e = lane; e < 32 * 32; e += 64) pq_c[(e >> 5) * TC + 32 + (e & 31)] = (__bf16)0.f;
   }
   __syncthreads();
 
-  // forward substitution, one column per thread: x = diag(beta) rhs first
-  // (all loads in flight at once), then x_i -= sum_{j<i} A_ij x_j in order
-  const int c = tid & 127;
-  const bool is_u = tid >= 128;
-  float x[TC];
+  // T on the 16 x 16 diagonal blocks: lane (b, c) solves column c of block b
+  if (wave == 0) {
+    const int b = lane >> 4, c = lane & 15;
+    float* ab = la + 16 * b * AP + 16 * b;
+    float t[16];
 #pragma unroll
-  for (int i = 0; i < TC; ++i) {
-    float rhs;
-    if (is_u) {
-      rhs = i < valid ? (float)vp[(row0 + i) * HD + c] : 0.f;
-    } else {
-      const __bf16* kr = reinterpret_cast<const __bf16*>(
-          lk + i * 256 + (((c >> 3) ^ swz_r(i)) << 4));
-      rhs = (float)kr[c & 7];
+    for (int r = 0; r < 16; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < r; ++j) acc = fmaf(ab[r * AP + j], t[j], acc);
+      t[r] = r == c ? 1.f : -acc;
     }
-    x[i] = lb[i] * rhs;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ab[r * AP + c] = t[r];
   }
+  __syncthreads();
+
+  // 32 x 32 diagonal blocks: T_10 = -T_11 (A_10 T_00) with 16 x 16 blocks, for
+  // the block pairs at rows / columns 0 and 32
+  const int p2 = tid >> 6, r2 = (tid >> 2) & 15, c2 = 4 * (tid & 3);
+  if (tid < 128) {
+    const int o0 = 32 * p2;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int i = 1; i < TC; ++i) {
-    float acc = x[i];
-#pragma unroll
-    for (int j = 0; j < i; ++j) acc = fmaf(-la[i * AP + j], x[j], acc);
-    x[i] = acc;
-    // keep each row's LDS reads next to their use (bounds register pressure)
-    __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < 16; ++k)
+      y = fma4(la[(o0 + 16 + r2) * AP + o0 + k], ld4(la + (o0 + k) * AP + o0 + c2), y);
+    st4(ly + p2 * 256 + r2 * 16 + c2, y);
   }
-  float* out = (is_u ? u_out : w_out) + cbase * TC * HD + c;
+  __syncthreads();
+  if (tid < 128) {
+    const int o0 = 32 * p2;
+    float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int i = 0; i < TC; ++i) out[(size_t)i * HD] = x[i];
+    for (int k = 0; k < 16; ++k)
+      z = fma4(la[(o0 + 16 + r2) * AP + o0 + 16 + k], ld4(ly + p2 * 256 + k * 16 + c2), z);
+    st4(la + (o0 + 16 + r2) * AP + o0 + c2, make_float4(-z.x, -z.y, -z.z, -z.w));
+  }
+  __syncthreads();
+
+  // the whole 64 x 64: T_10 = -T_11 (A_10 T_00) with 32 x 32 blocks
+  const int r3 = tid >> 3, c3 = 4 * (tid & 7);
+  {
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) y = fma4(la[(32 + r3) * AP + k], ld4(la + k * AP + c3), y);
+    st4(ly + r3 * 32 + c3, y);
+  }
+  __syncthreads();
+  {
+    float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) z = fma4(la[(32 + r3) * AP + 32 + k], ld4(ly + k * 32 + c3), z);
+    st4(la + (32 + r3) * AP + c3, make_float4(-z.x, -z.y, -z.z, -z.w));
+  }
+  __syncthreads();
+
+  // T diag(beta) as bf16 high + low parts (zero above the diagonal)
+  {
+    const int t = tid >> 2, j0 = 16 * (tid & 3);
+    bf16x8 hi[2], lo[2];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + u;
+      const float val = j <= t ? la[t * AP + j] * lb[j] : 0.f;
+      const __bf16 h = (__bf16)val;
+      hi[u >> 3][u & 7] = h;
+      lo[u >> 3][u & 7] = (__bf16)(val - (float)h);
+    }
+    *reinterpret_cast<bf16x8*>(lth + t * LP + j0) = hi[0];
+    *reinterpret_cast<bf16x8*>(lth + t * LP + j0 + 8) = hi[1];
+    *reinterpret_cast<bf16x8*>(ltl + t * LP + j0) = lo[0];
+    *reinterpret_cast<bf16x8*>(ltl + t * LP + j0 + 8) = lo[1];
+  }
+  __syncthreads();
+
+  // W (waves 0-1) and U (waves 2-3): wave covers feature tiles 2 (wave & 1) + {0, 1}
+  const bool is_u = wave >= 2;
+  const char* src = is_u ? lv : lk;
+  __bf16* w_c = w_out + cbase * TC * HD;
+  float* u_c = u_out + cbase * TC * HD;
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti) {
+#pragma unroll
+    for (int tfi = 0; tfi < 2; ++tfi) {
+      const int tf = 2 * (wave & 1) + tfi;
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int kc = 0; kc < 2 + 2 * ti; ++kc) {
+        const bf16x8 b = tr_op(src, 16 * kc, 8, 32 * tf, lane);
+        const int off = (32 * ti + n) * LP + 16 * kc + 8 * h2;
+        acc = mfma32(ld8(lth + off), b, acc);
+        acc = mfma32(ld8(ltl + off), b, acc);
+      }
+      if (is_u) {
+        // U tile (ti, tf) in accumulator order: lane-contiguous 16 floats
+        float* ut = u_c + ((ti * 4 + tf) * 64 + lane) * 16;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          st4(ut + 4 * q4, make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          w_c[(32 * ti + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + 32 * tf + n] = (__bf16)acc[r];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Sequential pass over the chunks. One workgroup (4 waves) per (b, h, 32-column
-// block cb of the state). Wave w holds state rows [32w, 32w + 32) of the block
-// as an MFMA accumulator; per chunk:
-//   X = U - W S (waves 0-1: tokens [32w, 32w + 32)),
-//   O_inter = Q' S + Pq X (waves 0-1), o = o_intra + O_inter,
-//   S += K'^T X (all waves; K' staged for transposing reads).
-// The state reaches the B operands as S^T in bf16 through LDS, X as X^T.
-// With S_next given, the end state commits S_next = alpha S_prev + (S_T - S_prev).
+// block cb of the state); the four blocks of a head share an XCD (and its L2).
+// Wave w holds state rows [32w, 32w + 32) of the block as an MFMA accumulator.
+// Per chunk, after the state S^T (bf16) is in LDS:
+//   A: waves 0-1 form X = U - W S for tokens [32w, 32w + 32) (X^T to LDS),
+//      waves 2-3 form Q' S for tokens [32(w-2), ..);
+//   B: waves 2-3 add tril(Q'K'^T, -1) X and write o = o_intra + O_inter,
+//      all waves add K'^T X to their state rows (K' staged for transposing
+//      reads).
+// The next chunk's operands (K' staging, W and U, or Q', Pq and o_intra) are
+// loaded into registers while the current chunk computes, each as soon as its
+// register is free. With S_next given,
+// the end state commits S_next = alpha S_prev + (S_T - S_prev).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 tl_scan_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
-          const float* __restrict__ w_in, const float* __restrict__ u_in,
-          const float* __restrict__ pq_in, const float* __restrict__ S_prev,
+          const __bf16* __restrict__ w_in, const float* __restrict__ u_in,
+          const __bf16* __restrict__ pq_in, const float* __restrict__ S_prev,
           const float* __restrict__ alpha, float* __restrict__ S_next,
           const __bf16* __restrict__ o_intra, __bf16* __restrict__ o,
           __bf16* __restrict__ o_inter, int T, int n_ch) {
-  __shared__ __attribute__((aligned(16))) char lk[TC * 256];
+  __shared__ __attribute__((aligned(16))) char lk0[TC * 256];
+  __shared__ __attribute__((aligned(16))) char lk1[TC * 256];
   __shared__ __attribute__((aligned(16))) __bf16 st[32 * SP];
   __shared__ __attribute__((aligned(16))) __bf16 xt[32 * XP];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
-  const long bh = blockIdx.x >> 2;
-  const int cb = blockIdx.x & 3;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const long bh = logical >> 2;
+  const int cb = logical & 3;
   const int col = 32 * cb + n;                       // this lane's state column
+  const bool xw = wave < 2;                          // X waves (else O waves)
+  const int rw = 32 * (wave & 1);                    // the wave's token rows in a chunk
   const float* Sp = S_prev + (size_t)bh * HD * HD;
   // state rows 32 w + 8 (r / 4) + 4 h2 + r % 4 of column `col`
   f32x16 sacc;
@@ -165,66 +266,129 @@ tl_scan_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
   for (int r = 0; r < 16; ++r)
     sacc[r] = Sp[(size_t)(32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + col];
 
-  for (int ch = 0; ch < n_ch; ++ch) {
-    const int t0 = ch * TC;
-    const int valid = min(TC, T - t0);
-    const size_t row0 = (size_t)bh * T + t0;
-    const size_t cbase = (size_t)bh * n_ch + ch;
+  // one chunk's operands: am = W rows (X waves) or Q' rows (O waves); pm = Pq
+  // rows (O waves); um = U (X waves) or o_intra (O waves) at the accumulator's
+  // positions; kn = this thread's share of the next K' chunk. Each is reloaded
+  // for the next chunk as soon as its last use in the current one has passed.
+  bf16x8 am[8], pm[4];
+  float um[16];
+  uint4 kn[4];
+  // this head's o_intra, o, o_inter as buffers: accumulator register r sits
+  // row_off(r) bytes past the lane's base offset
+  const uint32_t head_bytes = (uint32_t)T * HD * 2;
+  const size_t head_off = (size_t)bh * T * HD;
+  const __amdgpu_buffer_rsrc_t r_oi = buffer_rsrc(o_intra + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t r_o = buffer_rsrc(o + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t r_oe = buffer_rsrc(o_inter ? o_inter + head_off : o, head_bytes);
+  auto row_off = [](int r) { return (8 * (r >> 2) + (r & 3)) * HD * 2; };
+  auto load_k = [&](int c) {
+    const int valid = min(TC, T - c * TC);
+    const size_t row0 = (size_t)bh * T + c * TC;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e, r = idx >> 4, p = idx & 15;
+      kn[e] = r < valid ? *reinterpret_cast<const uint4*>(kp + (row0 + r) * HD + 8 * p)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_k = [&](char* dst) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e, r = idx >> 4, p = idx & 15;
+      *reinterpret_cast<uint4*>(dst + r * 256 + ((p ^ swz_v(r)) << 4)) = kn[e];
+    }
+  };
+  // phase A operands: W and U (X waves) or Q' (O waves)
+  auto load_a = [&](int c) {
+    const int valid = min(TC, T - c * TC);
+    const size_t row0 = (size_t)bh * T + c * TC;
+    const size_t cbase = (size_t)bh * n_ch + c;
+    if (xw) {
+      const __bf16* wr = w_in + (cbase * TC + rw + n) * HD + 8 * h2;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) am[kc] = ld8(wr + 16 * kc);
+      const float* ut = u_in + cbase * TC * HD + (((wave & 1) * 4 + cb) * 64 + lane) * 16;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = ld4(ut + 4 * q4);
+        um[4 * q4] = x.x;
+        um[4 * q4 + 1] = x.y;
+        um[4 * q4 + 2] = x.z;
+        um[4 * q4 + 3] = x.w;
+      }
+    } else {
+      const __bf16* qr = qp + (row0 + min(rw + n, valid - 1)) * HD + 8 * h2;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) am[kc] = ld8(qr + 16 * kc);
+    }
+  };
+  // phase B operands of the O waves: Pq rows and o_intra
+  auto load_b = [&](int c) {
+    const size_t cbase = (size_t)bh * n_ch + c;
+    const __bf16* pr = pq_in + (cbase * TC + rw + n) * TC + 8 * h2;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) pm[kc] = ld8(pr + 16 * kc);
+    // rows past the frame's end lie past the buffer's range and read as zero
+    const int vo = ((c * TC + rw + 4 * h2) * HD + col) * 2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r_oi, vo, row_off(r), 0);
+      um[r] = __builtin_bit_cast(float, h << 16);
+    }
+  };
+
+  load_k(0);
+  store_k(lk0);
+  load_a(0);
+  if (!xw) load_b(0);
+  for (int c = 0; c < n_ch; ++c) {
+    const char* lkc = (c & 1) ? lk1 : lk0;
+    char* lkn = (c & 1) ? lk0 : lk1;
+    const bool more = c + 1 < n_ch;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       st[n * SP + 32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3)] = (__bf16)sacc[r];
-    stage_rows<true>(lk, kp + row0 * HD, TC, valid);
+    if (more) load_k(c + 1);
     __syncthreads();
 
-    f32x16 xacc;
-    if (wave < 2) {
-      // X = U - W S for tokens [32 wave, 32 wave + 32) of the chunk
-      const float* wr = w_in + (cbase * TC + 32 * wave + n) * HD + 8 * h2;
-      f32x16 ws = zero16();
+    // A: W S (X waves) or Q' S (O waves)
+    f32x16 acc = zero16();
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        ws = mfma32(f32_to_bf16x8(wr + 16 * kc),
-                    *reinterpret_cast<const bf16x8*>(st + n * SP + 16 * kc + 8 * h2), ws);
-      const float* ur = u_in + cbase * TC * HD + col;
+    for (int kc = 0; kc < 8; ++kc)
+      acc = mfma32(am[kc], *reinterpret_cast<const bf16x8*>(st + n * SP + 16 * kc + 8 * h2), acc);
+    if (xw) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tk = 32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        xacc[r] = ur[(size_t)tk * HD] - ws[r];
-        xt[n * XP + tk] = (__bf16)xacc[r];
-      }
+      for (int r = 0; r < 16; ++r)
+        xt[n * XP + rw + 8 * (r >> 2) + 4 * h2 + (r & 3)] = (__bf16)(um[r] - acc[r]);
     }
+    if (more) load_a(c + 1);
     __syncthreads();
 
-    if (wave < 2) {
-      // O_inter = Q' S + Pq X for tokens [32 wave, 32 wave + 32)
-      const __bf16* qr = qp + (row0 + min(32 * wave + n, valid - 1)) * HD + 8 * h2;
-      f32x16 oi = zero16();
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        oi = mfma32(ld8(qr + 16 * kc),
-                    *reinterpret_cast<const bf16x8*>(st + n * SP + 16 * kc + 8 * h2), oi);
-      const float* pr = pq_in + (cbase * TC + 32 * wave + n) * TC + 8 * h2;
+    // B: O_inter += Pq X and the output (O waves); S += K'^T X (all waves)
+    if (!xw) {
 #pragma unroll
       for (int kc = 0; kc < TC / 16; ++kc)
-        oi = mfma32(f32_to_bf16x8(pr + 16 * kc),
-                    *reinterpret_cast<const bf16x8*>(xt + n * XP + 16 * kc + 8 * h2), oi);
+        acc = mfma32(pm[kc], *reinterpret_cast<const bf16x8*>(xt + n * XP + 16 * kc + 8 * h2),
+                     acc);
+      // rows past the frame's end fall outside the buffers' range: not written
+      const int vo = ((c * TC + rw + 4 * h2) * HD + col) * 2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tk = 32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (tk < valid) {
-          const size_t e = (row0 + tk) * HD + col;
-          const float inter = oi[r];
-          o[e] = (__bf16)((float)o_intra[e] + inter);
-          if (o_inter) o_inter[e] = (__bf16)inter;
-        }
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b16(
+            __builtin_bit_cast(unsigned short, (__bf16)(um[r] + acc[r])), r_o, vo, row_off(r), 0);
+      if (o_inter) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)acc[r]),
+                                                r_oe, vo, row_off(r), 0);
       }
+      if (more) load_b(c + 1);
     }
-    // S += K'^T X: A = K'^T rows (state rows 32 wave + n) by transposing reads
 #pragma unroll
     for (int kc = 0; kc < TC / 16; ++kc)
-      sacc = mfma32(tr_op(lk, 16 * kc, 8, 32 * wave, lane),
+      sacc = mfma32(tr_op(lkc, 16 * kc, 8, 32 * wave, lane),
                     *reinterpret_cast<const bf16x8*>(xt + n * XP + 16 * kc + 8 * h2), sacc);
-    __syncthreads();
+    if (more) store_k(lkn);
   }
   if (S_next) {
     const float a = alpha[bh];
@@ -285,7 +449,7 @@ int n_chunks(const Dims& d) { return (d.T + TC - 1) / TC; }
 size_t token_level_scan_ws_bytes(const Dims& d) {
   if (!(d.bf16 && d.D == HD)) return 0;
   const size_t nc = (size_t)d.B * d.H * n_chunks(d);
-  return nc * TC * (2 * HD + TC) * sizeof(float);
+  return nc * TC * (HD * (sizeof(__bf16) + sizeof(float)) + TC * sizeof(__bf16));
 }
 
 hipError_t token_level_scan(const Dims& d, const void* q_prime, const void* k_prime,
@@ -295,9 +459,9 @@ hipError_t token_level_scan(const Dims& d, const void* q_prime, const void* k_pr
   const long n_bh = (long)d.B * d.H;
   if (d.bf16 && d.D == HD) {
     const int nc = n_chunks(d);
-    float* w = static_cast<float*>(ws);
-    float* u = w + (size_t)n_bh * nc * TC * HD;
-    float* pq = u + (size_t)n_bh * nc * TC * HD;
+    __bf16* w = static_cast<__bf16*>(ws);
+    float* u = reinterpret_cast<float*>(w + (size_t)n_bh * nc * TC * HD);
+    __bf16* pq = reinterpret_cast<__bf16*>(u + (size_t)n_bh * nc * TC * HD);
     tl_chunk_k<<<(unsigned)(n_bh * nc), 256, 0, s>>>(
         static_cast<const __bf16*>(q_prime), static_cast<const __bf16*>(k_prime),
         static_cast<const __bf16*>(v_prime), beta, w, u, pq, d.T, nc);

@@ -55,10 +55,11 @@ def test_workspace_sizes(arl2):
     assert arl2.workspace_bytes(arl2.Shape(0, 1, 1, 128), arl2.OP_READ) == 0
     f = arl2.Shape(1, 1, 64, 16, arl2.F32)
     assert arl2.workspace_bytes(f, arl2.OP_STATE_COMMIT) == 64 * 16 * 4
-    # token-level access: Q', K', V', o_intra, then (bf16) W and U [T, D] and
-    # Pq [64, 64] fp32 per 64-token chunk of each head
+    # token-level access: Q', K', V', o_intra, then (bf16) per 64-token chunk of
+    # each head W [64, D] bf16, U [64, D] fp32 and Pq [64, 64] bf16
     chunks = 12 * ((1560 + 63) // 64)
-    assert arl2.workspace_bytes(s, arl2.OP_TOKEN_LEVEL) == 4 * act + chunks * 64 * (256 + 64) * 4
+    assert arl2.workspace_bytes(s, arl2.OP_TOKEN_LEVEL) == 4 * act + chunks * 64 * (
+        128 * 2 + 128 * 4 + 64 * 2)
     assert arl2.workspace_bytes(f, arl2.OP_TOKEN_LEVEL) == 4 * 64 * 16 * 4
 
 
