@@ -56,9 +56,11 @@ __device__ __forceinline__ float4 fma4(float a, float4 b, float4 c) {
 //   LDS) on MFMA; T = (I + A)^-1 in fp32 by blocks: the four 16 x 16 diagonal
 //   blocks by forward substitution, then two doublings, each forming the
 //   off-diagonal block of a 2 x 2 blocking as  T_10 = -T_11 A_10 T_00;
-//   W = T diag(beta) K' (bf16, out) and U = T diag(beta) V' (fp32, out) on MFMA
-//   with T diag(beta) split into a bf16 high and low part, so that both
-//   products carry fp32-level accuracy.
+//   W = T diag(beta) K' (bf16, out) and U = T diag(beta) V' (fp32, out) on MFMA,
+//   the A operand T diag(beta) formed from T in registers and split into a
+//   bf16 high and low part, so that both products carry fp32-level accuracy.
+// Q' rows and the V' chunk are loaded into registers at the start; V' goes to
+// LDS (over the doubling scratch) once T is done. About 50 KB of LDS.
 // Workspace per (bh, chunk): W bf16 [TC][128] row-major; U fp32 as eight 32 x 32
 // tiles (token tile ti, feature tile tf) each in MFMA accumulator order (lane
 // l's 16 values, rows 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32,
@@ -72,12 +74,10 @@ tl_chunk_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
            __bf16* __restrict__ w_out, float* __restrict__ u_out, __bf16* __restrict__ pq_out,
            int T, int n_ch) {
   __shared__ __attribute__((aligned(16))) char lk[TC * 256];
-  __shared__ __attribute__((aligned(16))) char lv[TC * 256];
+  __shared__ __attribute__((aligned(16))) char lv[TC * 256];   // doubling scratch, then V'
   __shared__ __attribute__((aligned(16))) float la[TC * AP];
-  __shared__ __attribute__((aligned(16))) float ly[32 * 32];
-  __shared__ __attribute__((aligned(16))) __bf16 lth[TC * LP];
-  __shared__ __attribute__((aligned(16))) __bf16 ltl[TC * LP];
   __shared__ float lb[TC];
+  float* ly = reinterpret_cast<float*>(lv);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
@@ -87,8 +87,21 @@ tl_chunk_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
   const int valid = min(TC, T - t0);
   const size_t row0 = (size_t)bh * T + t0;
   const size_t cbase = (size_t)bh * n_ch + ch;
+  const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;   // G / Pq tile of waves 0-2
+  bf16x8 qa[8];
+  if (wave < 3) {
+    const __bf16* qr = qp + (row0 + min(32 * ti + n, valid - 1)) * HD + 8 * h2;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) qa[kc] = ld8(qr + 16 * kc);
+  }
+  uint4 vr[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 256 * e, r = idx >> 4, p = idx & 15;
+    vr[e] = r < valid ? *reinterpret_cast<const uint4*>(vp + (row0 + r) * HD + 8 * p)
+                      : make_uint4(0u, 0u, 0u, 0u);
+  }
   stage_rows(lk, kp + row0 * HD, TC, valid);
-  stage_rows(lv, vp + row0 * HD, TC, valid);
   if (tid < TC) lb[tid] = tid < valid ? beta[row0 + tid] : 0.f;
   __syncthreads();
 
@@ -96,14 +109,12 @@ tl_chunk_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
   // the upper tile of Pq is zero
   __bf16* pq_c = pq_out + cbase * TC * TC;
   if (wave < 3) {
-    const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
-    const __bf16* qr = qp + (row0 + min(32 * ti + n, valid - 1)) * HD + 8 * h2;
     f32x16 g = zero16(), pq = zero16();
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const bf16x8 b = row_op(lk, 32 * tj + n, kc, h2);
       g = mfma32(row_op(lk, 32 * ti + n, kc, h2), b, g);
-      pq = mfma32(ld8(qr + 16 * kc), b, pq);
+      pq = mfma32(qa[kc], b, pq);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -171,23 +182,11 @@ tl_chunk_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
     st4(la + (32 + r3) * AP + c3, make_float4(-z.x, -z.y, -z.z, -z.w));
   }
   __syncthreads();
-
-  // T diag(beta) as bf16 high + low parts (zero above the diagonal)
-  {
-    const int t = tid >> 2, j0 = 16 * (tid & 3);
-    bf16x8 hi[2], lo[2];
+  // V' over the scratch (its last reads were before the barrier above)
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int j = j0 + u;
-      const float val = j <= t ? la[t * AP + j] * lb[j] : 0.f;
-      const __bf16 h = (__bf16)val;
-      hi[u >> 3][u & 7] = h;
-      lo[u >> 3][u & 7] = (__bf16)(val - (float)h);
-    }
-    *reinterpret_cast<bf16x8*>(lth + t * LP + j0) = hi[0];
-    *reinterpret_cast<bf16x8*>(lth + t * LP + j0 + 8) = hi[1];
-    *reinterpret_cast<bf16x8*>(ltl + t * LP + j0) = lo[0];
-    *reinterpret_cast<bf16x8*>(ltl + t * LP + j0 + 8) = lo[1];
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 256 * e, r = idx >> 4, p = idx & 15;
+    *reinterpret_cast<uint4*>(lv + r * 256 + ((p ^ swz_v(r)) << 4)) = vr[e];
   }
   __syncthreads();
 
@@ -197,28 +196,44 @@ tl_chunk_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
   __bf16* w_c = w_out + cbase * TC * HD;
   float* u_c = u_out + cbase * TC * HD;
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti) {
+  for (int tr = 0; tr < 2; ++tr) {
+    f32x16 acc[2] = {zero16(), zero16()};
+    const int t = 32 * tr + n;                    // this lane's row of T diag(beta)
+#pragma unroll
+    for (int kc = 0; kc < 2 + 2 * tr; ++kc) {
+      // A operand: (T diag(beta))[t][16 kc + 8 h2 + u], zero above the diagonal
+      const int j0 = 16 * kc + 8 * h2;
+      const float4 x0 = ld4(la + t * AP + j0), x1 = ld4(la + t * AP + j0 + 4);
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float val = j0 + u <= t ? xv[u] * lb[j0 + u] : 0.f;
+        hi[u] = (__bf16)val;
+        lo[u] = (__bf16)(val - (float)hi[u]);
+      }
+#pragma unroll
+      for (int tfi = 0; tfi < 2; ++tfi) {
+        const bf16x8 b = tr_op(src, 16 * kc, 8, 32 * (2 * (wave & 1) + tfi), lane);
+        acc[tfi] = mfma32(hi, b, acc[tfi]);
+        acc[tfi] = mfma32(lo, b, acc[tfi]);
+      }
+    }
 #pragma unroll
     for (int tfi = 0; tfi < 2; ++tfi) {
       const int tf = 2 * (wave & 1) + tfi;
-      f32x16 acc = zero16();
-#pragma unroll
-      for (int kc = 0; kc < 2 + 2 * ti; ++kc) {
-        const bf16x8 b = tr_op(src, 16 * kc, 8, 32 * tf, lane);
-        const int off = (32 * ti + n) * LP + 16 * kc + 8 * h2;
-        acc = mfma32(ld8(lth + off), b, acc);
-        acc = mfma32(ld8(ltl + off), b, acc);
-      }
       if (is_u) {
-        // U tile (ti, tf) in accumulator order: lane-contiguous 16 floats
-        float* ut = u_c + ((ti * 4 + tf) * 64 + lane) * 16;
+        // U tile (tr, tf) in accumulator order: lane-contiguous 16 floats
+        float* ut = u_c + ((tr * 4 + tf) * 64 + lane) * 16;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          st4(ut + 4 * q4, make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]));
+          st4(ut + 4 * q4, make_float4(acc[tfi][4 * q4], acc[tfi][4 * q4 + 1],
+                                       acc[tfi][4 * q4 + 2], acc[tfi][4 * q4 + 3]));
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          w_c[(32 * ti + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + 32 * tf + n] = (__bf16)acc[r];
+          w_c[(32 * tr + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + 32 * tf + n] =
+              (__bf16)acc[tfi][r];
       }
     }
   }
@@ -266,29 +281,25 @@ tl_scan_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
   for (int r = 0; r < 16; ++r)
     sacc[r] = Sp[(size_t)(32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + col];
 
-  // one chunk's operands: am = W rows (X waves) or Q' rows (O waves); pm = Pq
-  // rows (O waves); um = U (X waves) or o_intra (O waves) at the accumulator's
-  // positions; kn = this thread's share of the next K' chunk. Each is reloaded
-  // for the next chunk as soon as its last use in the current one has passed.
-  bf16x8 am[8], pm[4];
-  float um[16];
-  uint4 kn[4];
-  // this head's o_intra, o, o_inter as buffers: accumulator register r sits
-  // row_off(r) bytes past the lane's base offset
+  // Each role runs its own straight-line loop (two barriers per chunk in both),
+  // so that every wait for a prefetched operand counts exactly the loads
+  // issued after it. Operands: am = W rows (X waves) or Q' rows (O waves);
+  // um = U (X waves) or o_intra (O waves) at the accumulator's positions;
+  // pm = Pq rows (O waves); kn = this thread's share of the next K' chunk (the
+  // last chunk reloads itself). Global rows past the frame's end lie outside
+  // the buffers' ranges: they read as zero and are not written.
   const uint32_t head_bytes = (uint32_t)T * HD * 2;
   const size_t head_off = (size_t)bh * T * HD;
-  const __amdgpu_buffer_rsrc_t r_oi = buffer_rsrc(o_intra + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t r_o = buffer_rsrc(o + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t r_oe = buffer_rsrc(o_inter ? o_inter + head_off : o, head_bytes);
-  auto row_off = [](int r) { return (8 * (r >> 2) + (r & 3)) * HD * 2; };
+  const __amdgpu_buffer_rsrc_t r_k = buffer_rsrc(kp + head_off, head_bytes);
+  bf16x8 am[8];
+  float um[16];
+  uint4 kn[4];
   auto load_k = [&](int c) {
-    const int valid = min(TC, T - c * TC);
-    const size_t row0 = (size_t)bh * T + c * TC;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + 256 * e, r = idx >> 4, p = idx & 15;
-      kn[e] = r < valid ? *reinterpret_cast<const uint4*>(kp + (row0 + r) * HD + 8 * p)
-                        : make_uint4(0u, 0u, 0u, 0u);
+      kn[e] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(r_k, ((c * TC + r) * HD + 8 * p) * 2, 0, 0));
     }
   };
   auto store_k = [&](char* dst) {
@@ -298,97 +309,126 @@ tl_scan_k(const __bf16* __restrict__ qp, const __bf16* __restrict__ kp,
       *reinterpret_cast<uint4*>(dst + r * 256 + ((p ^ swz_v(r)) << 4)) = kn[e];
     }
   };
-  // phase A operands: W and U (X waves) or Q' (O waves)
-  auto load_a = [&](int c) {
-    const int valid = min(TC, T - c * TC);
-    const size_t row0 = (size_t)bh * T + c * TC;
-    const size_t cbase = (size_t)bh * n_ch + c;
-    if (xw) {
-      const __bf16* wr = w_in + (cbase * TC + rw + n) * HD + 8 * h2;
+  auto state_to_lds = [&]() {
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) am[kc] = ld8(wr + 16 * kc);
-      const float* ut = u_in + cbase * TC * HD + (((wave & 1) * 4 + cb) * 64 + lane) * 16;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 x = ld4(ut + 4 * q4);
-        um[4 * q4] = x.x;
-        um[4 * q4 + 1] = x.y;
-        um[4 * q4 + 2] = x.z;
-        um[4 * q4 + 3] = x.w;
-      }
-    } else {
-      const __bf16* qr = qp + (row0 + min(rw + n, valid - 1)) * HD + 8 * h2;
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) am[kc] = ld8(qr + 16 * kc);
-    }
+    for (int r = 0; r < 16; ++r)
+      st[n * SP + 32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3)] = (__bf16)sacc[r];
   };
-  // phase B operands of the O waves: Pq rows and o_intra
-  auto load_b = [&](int c) {
-    const size_t cbase = (size_t)bh * n_ch + c;
-    const __bf16* pr = pq_in + (cbase * TC + rw + n) * TC + 8 * h2;
+  auto x_op = [&](int kc) {
+    return *reinterpret_cast<const bf16x8*>(xt + n * XP + 16 * kc + 8 * h2);
+  };
+  auto update_state = [&](const char* lkc) {   // S += K'^T X
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) pm[kc] = ld8(pr + 16 * kc);
-    // rows past the frame's end lie past the buffer's range and read as zero
-    const int vo = ((c * TC + rw + 4 * h2) * HD + col) * 2;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r_oi, vo, row_off(r), 0);
-      um[r] = __builtin_bit_cast(float, h << 16);
-    }
+    for (int kc = 0; kc < TC / 16; ++kc)
+      sacc = mfma32(tr_op(lkc, 16 * kc, 8, 32 * wave, lane), x_op(kc), sacc);
   };
 
   load_k(0);
   store_k(lk0);
-  load_a(0);
-  if (!xw) load_b(0);
-  for (int c = 0; c < n_ch; ++c) {
-    const char* lkc = (c & 1) ? lk1 : lk0;
-    char* lkn = (c & 1) ? lk0 : lk1;
-    const bool more = c + 1 < n_ch;
+  // Two sets of the operands that phase A needs, alternating between chunks
+  // (the loop body covers a pair of chunks): each step first issues the next
+  // chunk's loads into the other set, so they have a whole chunk of work to
+  // arrive; phase B operands (Pq, o_intra) come at the start of their own step.
+  if (xw) {
+    bf16x8 am2[8];
+    float um2[16];
+    auto load_wu = [&](int c, bf16x8 (&a)[8], float (&u)[16]) {
+      const size_t cbase = (size_t)bh * n_ch + c;
+      const __bf16* wr = w_in + (cbase * TC + rw + n) * HD + 8 * h2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      st[n * SP + 32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3)] = (__bf16)sacc[r];
-    if (more) load_k(c + 1);
-    __syncthreads();
-
-    // A: W S (X waves) or Q' S (O waves)
-    f32x16 acc = zero16();
+      for (int kc = 0; kc < 8; ++kc) a[kc] = ld8(wr + 16 * kc);
+      const float* ut = u_in + cbase * TC * HD + (((wave & 1) * 4 + cb) * 64 + lane) * 16;
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc)
-      acc = mfma32(am[kc], *reinterpret_cast<const bf16x8*>(st + n * SP + 16 * kc + 8 * h2), acc);
-    if (xw) {
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = ld4(ut + 4 * q4);
+        u[4 * q4] = x.x;
+        u[4 * q4 + 1] = x.y;
+        u[4 * q4 + 2] = x.z;
+        u[4 * q4 + 3] = x.w;
+      }
+    };
+    auto step = [&](int c, bf16x8 (&a)[8], float (&u)[16], bf16x8 (&a_nx)[8],
+                    float (&u_nx)[16]) {
+      const int cn = min(c + 1, n_ch - 1);
+      state_to_lds();
+      load_k(cn);
+      load_wu(cn, a_nx, u_nx);
+      __syncthreads();
+      f32x16 acc = zero16();                       // W S
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        acc = mfma32(a[kc], *reinterpret_cast<const bf16x8*>(st + n * SP + 16 * kc + 8 * h2), acc);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        xt[n * XP + rw + 8 * (r >> 2) + 4 * h2 + (r & 3)] = (__bf16)(um[r] - acc[r]);
+        xt[n * XP + rw + 8 * (r >> 2) + 4 * h2 + (r & 3)] = (__bf16)(u[r] - acc[r]);
+      __syncthreads();
+      update_state((c & 1) ? lk1 : lk0);
+      store_k((c & 1) ? lk0 : lk1);
+    };
+    load_wu(0, am, um);
+    int c = 0;
+    for (; c + 1 < n_ch; c += 2) {
+      step(c, am, um, am2, um2);
+      step(c + 1, am2, um2, am, um);
     }
-    if (more) load_a(c + 1);
-    __syncthreads();
-
-    // B: O_inter += Pq X and the output (O waves); S += K'^T X (all waves)
-    if (!xw) {
+    if (c < n_ch) step(c, am, um, am2, um2);
+  } else {
+    const __amdgpu_buffer_rsrc_t r_oi = buffer_rsrc(o_intra + head_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t r_o = buffer_rsrc(o + head_off, head_bytes);
+    // without o_inter, a buffer of no bytes: its stores are dropped
+    const __amdgpu_buffer_rsrc_t r_oe =
+        o_inter ? buffer_rsrc(o_inter + head_off, head_bytes) : buffer_rsrc(o, 0);
+    auto row_off = [](int r) { return (8 * (r >> 2) + (r & 3)) * HD * 2; };
+    bf16x8 am2[8], pm[4];
+    uint32_t oi[16];                               // o_intra, raw bf16 bits
+    auto load_q = [&](int c, bf16x8 (&a)[8]) {
+      const int valid = min(TC, T - c * TC);
+      const __bf16* qr = qp + ((size_t)bh * T + c * TC + min(rw + n, valid - 1)) * HD + 8 * h2;
 #pragma unroll
-      for (int kc = 0; kc < TC / 16; ++kc)
-        acc = mfma32(pm[kc], *reinterpret_cast<const bf16x8*>(xt + n * XP + 16 * kc + 8 * h2),
-                     acc);
-      // rows past the frame's end fall outside the buffers' range: not written
+      for (int kc = 0; kc < 8; ++kc) a[kc] = ld8(qr + 16 * kc);
+    };
+    // phase B operands of chunk c, loaded at the start of its own step
+    auto load_pb = [&](int c) {
+      const __bf16* pr = pq_in + (((size_t)bh * n_ch + c) * TC + rw + n) * TC + 8 * h2;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) pm[kc] = ld8(pr + 16 * kc);
       const int vo = ((c * TC + rw + 4 * h2) * HD + col) * 2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) oi[r] = __builtin_amdgcn_raw_buffer_load_b16(r_oi, vo, row_off(r), 0);
+    };
+    auto step = [&](int c, bf16x8 (&a)[8], bf16x8 (&a_nx)[8]) {
+      const int cn = min(c + 1, n_ch - 1);
+      state_to_lds();
+      load_k(cn);
+      load_q(cn, a_nx);
+      load_pb(c);
+      __syncthreads();
+      f32x16 acc = zero16();                       // Q' S
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        acc = mfma32(a[kc], *reinterpret_cast<const bf16x8*>(st + n * SP + 16 * kc + 8 * h2), acc);
+      __syncthreads();
+#pragma unroll
+      for (int kc = 0; kc < TC / 16; ++kc) acc = mfma32(pm[kc], x_op(kc), acc);   // + Pq X
+      const int vo = ((c * TC + rw + 4 * h2) * HD + col) * 2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float o_in = __builtin_bit_cast(float, oi[r] << 16);
         __builtin_amdgcn_raw_buffer_store_b16(
-            __builtin_bit_cast(unsigned short, (__bf16)(um[r] + acc[r])), r_o, vo, row_off(r), 0);
-      if (o_inter) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)acc[r]),
-                                                r_oe, vo, row_off(r), 0);
+            __builtin_bit_cast(unsigned short, (__bf16)(o_in + acc[r])), r_o, vo, row_off(r), 0);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)acc[r]),
+                                              r_oe, vo, row_off(r), 0);
       }
-      if (more) load_b(c + 1);
+      update_state((c & 1) ? lk1 : lk0);
+      store_k((c & 1) ? lk0 : lk1);
+    };
+    load_q(0, am);
+    int c = 0;
+    for (; c + 1 < n_ch; c += 2) {
+      step(c, am, am2);
+      step(c + 1, am2, am);
     }
-#pragma unroll
-    for (int kc = 0; kc < TC / 16; ++kc)
-      sacc = mfma32(tr_op(lkc, 16 * kc, 8, 32 * wave, lane),
-                    *reinterpret_cast<const bf16x8*>(xt + n * XP + 16 * kc + 8 * h2), sacc);
-    if (more) store_k(lkn);
+    if (c < n_ch) step(c, am, am2);
   }
   if (S_next) {
     const float a = alpha[bh];
