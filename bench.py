@@ -58,10 +58,14 @@ def parse():
     return ap.parse_args()
 
 
+# the sources the frame-level kernels are compiled from
+FRAME_KERNEL_SOURCES = ("kernels_mfma.hip", "mfma_common.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "hybrid_linear_memory_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in FRAME_KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())

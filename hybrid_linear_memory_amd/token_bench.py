@@ -31,6 +31,9 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=3, help="timed rollouts (best is reported)")
     ap.add_argument("--n-denoise", type=int, default=4)
     ap.add_argument("--pool", type=int, default=6)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one 1 GiB device-to-device copy (a known-size reference "
+                         "for rocprofv3 FETCH_SIZE / WRITE_SIZE runs)")
     args = ap.parse_args(argv)
 
     import torch
@@ -39,6 +42,12 @@ def main(argv=None):
     from .layer import Arl2Layer
 
     assert torch.cuda.is_available(), "token_bench needs a GPU"
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     shape = arl2.Shape(args.B, args.H, args.T, 128, arl2.BF16)
     dims = (shape.B, shape.H, shape.T, shape.D)
     g = torch.Generator(device="cuda").manual_seed(0)
