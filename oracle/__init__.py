@@ -8,6 +8,7 @@ from .arl2_oracle import (  # noqa: F401
     L2_EPS,
     attention_weights,
     commit,
+    commit_backward,
     commit_inputs,
     default_scale,
     feature_map,
@@ -15,11 +16,15 @@ from .arl2_oracle import (  # noqa: F401
     hybrid_stack_rollout,
     inter_read,
     intra_attention,
+    intra_attention_backward,
     l2_normalize_rows,
     read,
+    read_backward,
     rollout,
+    rollout_backward,
     softmax_layer_rollout,
     state_commit,
+    state_scan,
     token_level_read,
     token_level_rollout,
 )

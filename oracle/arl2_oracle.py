@@ -55,6 +55,17 @@ applied by exactly one function below):
       passes discard these updates, the clean pass commits
       S_N = alpha_N S_{N-1} + (S_T - S_{N-1}) (the frame's gate applied once,
       as in the frame-level update). With T = 1 it equals frame-level access.
+  A16 Training (the summary's §2.3 two-stage distillation fine-tunes the
+      hybrid model end to end; the pages give no backward pass): the
+      gradients are the exact derivatives of the forward step as read above,
+      with respect to every input of a pass (q, k, v, phi_q, phi_k, phi_v,
+      beta, alpha and the state). phi maps are shared by the B videos, so
+      their gradients sum over videos and tokens. Below the 1e-12 floor of
+      reading A6 the row map is x / 1e-12, differentiated as such.
+  A17 The clean-state precompute for training (a scan over frames: the states
+      S_0..S_F that the clean passes commit, computed ahead of the reads, as in
+      the prefetch of clean hidden states) is ``rollout``'s commit sequence
+      without its reads.
 
 Every function in this module is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, exact rational worked examples and scalar
@@ -260,6 +271,135 @@ def hybrid_stack_rollout(layers, mask, scale=None, eval_pass=None):
         else:
             res.append({"o": softmax_layer_rollout(lay["frames"], scale, eval_pass)})
     return res
+
+
+def intra_attention_backward(q, k, v, d_o, scale: float | None = None) -> dict:
+    """Gradients of O_intra = softmax(Q K^T * scale) V (ARL2 summary §2.1
+    intra-frame branch; reading A16) given dL/dO_intra = d_o:
+        P = softmax(Q K^T * scale),  dV = P^T dO,  dP = dO V^T,
+        dZ = P * (dP - rowsum(P * dP)),  dQ = scale dZ K,  dK = scale dZ^T Q."""
+    q, k, v, d_o = _f64(q), _f64(k), _f64(v), _f64(d_o)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    P = attention_weights(q, k, scale)
+    dP = np.matmul(d_o, _t(v))
+    dZ = P * (dP - np.sum(P * dP, axis=-1, keepdims=True))
+    return {"dq": scale * np.matmul(dZ, k), "dk": scale * np.matmul(_t(dZ), q),
+            "dv": np.matmul(_t(P), d_o)}
+
+
+def read_backward(q, k, v, phi_q, S, d_o, scale: float | None = None) -> dict:
+    """Gradients of one read, O = softmax(Q K^T * scale) V + (Q Phi_q) S
+    (ARL2 summary §2.1; readings A9, A16), given dL/dO = d_o. Returns dq, dk,
+    dv, dphi_q (summed over videos and tokens) and dS:
+        dQ' = dO S^T,  dS = Q'^T dO,  dQ += dQ' Phi_q^T,  dPhi_q = sum_b Q^T dQ'."""
+    q, S, d_o = _f64(q), _f64(S), _f64(d_o)
+    g = intra_attention_backward(q, k, v, d_o, scale)
+    q_prime = feature_map(q, phi_q)
+    dq_prime = np.matmul(d_o, _t(S))
+    g["dq"] = g["dq"] + np.matmul(dq_prime, _t(_f64(phi_q))[None])
+    g["dphi_q"] = np.sum(np.matmul(_t(q), dq_prime), axis=0)
+    g["dS"] = np.matmul(_t(q_prime), d_o)
+    return g
+
+
+def commit_backward(k, v, phi_k, phi_v, beta, alpha, S_prev, dS_next) -> dict:
+    """Gradients of the clean-pass commit S_next = alpha S_prev +
+    K'^T diag(beta) (V' - K' S_prev), K' = rownorm(K Phi_k), V' = V Phi_v
+    (ARL2 summary §2.1 update equation; readings A1-A7, A16), given
+    G = dL/dS_next:
+        R = V' - K' S_prev
+        dalpha = <S_prev, G>,   dS_prev = alpha G - K'^T diag(beta) K' G
+        dV' = diag(beta) K' G,  dbeta = rowsum((K' G) * R)
+        dK' = diag(beta) (R G^T - K' G S_prev^T)
+    then through the row normalisation and the maps: dK~ = (dK' - K' rowsum(K'
+    * dK')) / ||K~|| (dK' / 1e-12 below the floor), dK = dK~ Phi_k^T,
+    dPhi_k = sum_b K^T dK~, dV = dV' Phi_v^T, dPhi_v = sum_b V^T dV'."""
+    k, v, beta, alpha = _f64(k), _f64(v), _f64(beta), _f64(alpha)
+    S_prev, G = _f64(S_prev), _f64(dS_next)
+    k_raw = feature_map(k, phi_k)
+    norm = np.sqrt(np.sum(k_raw * k_raw, axis=-1, keepdims=True))
+    k_prime = k_raw / np.maximum(norm, L2_EPS)
+    v_prime = feature_map(v, phi_v)
+    R = v_prime - np.matmul(k_prime, S_prev)
+    KG = np.matmul(k_prime, G)
+    b = beta[..., :, None]
+    d_v_prime = b * KG
+    d_k_prime = b * (np.matmul(R, _t(G)) - np.matmul(KG, _t(S_prev)))
+    above = norm > L2_EPS
+    d_k_raw = np.where(above,
+                       (d_k_prime - k_prime * np.sum(k_prime * d_k_prime, axis=-1, keepdims=True))
+                       / np.maximum(norm, L2_EPS),
+                       d_k_prime / L2_EPS)
+    return {
+        "dk": np.matmul(d_k_raw, _t(_f64(phi_k))[None]),
+        "dv": np.matmul(d_v_prime, _t(_f64(phi_v))[None]),
+        "dphi_k": np.sum(np.matmul(_t(k), d_k_raw), axis=0),
+        "dphi_v": np.sum(np.matmul(_t(v), d_v_prime), axis=0),
+        "dbeta": np.sum(KG * R, axis=-1),
+        "dalpha": np.sum(S_prev * G, axis=(-2, -1)),
+        "dS_prev": alpha[..., None, None] * G - np.matmul(_t(k_prime), b * KG),
+    }
+
+
+def state_scan(frames, phi_k, phi_v, S0=None) -> list:
+    """The clean-state precompute (reading A17): the states S_0..S_F that the
+    frames' clean passes commit, without any read. frames as for ``rollout``
+    (only the clean pass's k, v and the gates are used)."""
+    _, k0, _ = frames[0]["passes"][-1]
+    B, H, _, d = np.shape(k0)
+    S = np.zeros((B, H, d, d)) if S0 is None else _f64(S0).copy()
+    states = [S]
+    for fr in frames:
+        _, kc, vc = fr["passes"][-1]
+        S = commit(kc, vc, phi_k, phi_v, fr["beta"], fr["alpha"], S)
+        states.append(S)
+    return states
+
+
+def rollout_backward(frames, phi_q, phi_k, phi_v, d_outputs, S0=None, scale=None,
+                     dS_final=None) -> dict:
+    """Gradients of a loss on the outputs of a rollout (ARL2 summary §2.2
+    streaming loop; reading A16), backpropagated through the frame recurrence.
+
+    d_outputs[(f, p)] = dL/dO of pass p of frame f (passes without an entry
+    take no gradient); dS_final = dL/dS_F (default 0). Frame f's reads use S_f
+    and its commit maps S_f to S_{f+1}, so with G = dL/dS_{f+1} the frames are
+    visited backwards: the commit's backward turns G into its share of
+    dL/dS_f, the reads add dS = Q'^T dO. Returns "d_passes"[(f, p)] = (dq, dk,
+    dv), "dbeta"[f], "dalpha"[f], dphi_q, dphi_k, dphi_v and dS0."""
+    states = state_scan(frames, phi_k, phi_v, S0)
+    _, k0, _ = frames[0]["passes"][-1]
+    H, d = np.shape(k0)[1], np.shape(k0)[3]
+    out = {"d_passes": {}, "dbeta": {}, "dalpha": {},
+           "dphi_q": np.zeros((H, d, d)), "dphi_k": np.zeros((H, d, d)),
+           "dphi_v": np.zeros((H, d, d))}
+    G = np.zeros_like(states[-1]) if dS_final is None else _f64(dS_final).copy()
+    for f in range(len(frames) - 1, -1, -1):
+        fr = frames[f]
+        n_pass = len(fr["passes"])
+        _, kc, vc = fr["passes"][n_pass - 1]
+        cb = commit_backward(kc, vc, phi_k, phi_v, fr["beta"], fr["alpha"], states[f], G)
+        out["dbeta"][f] = cb["dbeta"]
+        out["dalpha"][f] = cb["dalpha"]
+        out["dphi_k"] += cb["dphi_k"]
+        out["dphi_v"] += cb["dphi_v"]
+        G = cb["dS_prev"]
+        for p, (q, k, v) in enumerate(fr["passes"]):
+            dq = np.zeros(np.shape(q))
+            dk = np.zeros(np.shape(k))
+            dv = np.zeros(np.shape(v))
+            if (f, p) in d_outputs:
+                rb = read_backward(q, k, v, phi_q, states[f], d_outputs[(f, p)], scale)
+                dq, dk, dv = rb["dq"], dk + rb["dk"], dv + rb["dv"]
+                out["dphi_q"] += rb["dphi_q"]
+                G = G + rb["dS"]
+            if p == n_pass - 1:
+                dk = dk + cb["dk"]
+                dv = dv + cb["dv"]
+            out["d_passes"][(f, p)] = (dq, dk, dv)
+    out["dS0"] = G
+    return out
 
 
 def token_level_read(q, k, v, phi_q, phi_k, phi_v, beta, S, scale=None) -> dict:

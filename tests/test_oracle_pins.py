@@ -543,3 +543,149 @@ def test_token_level_reduces_to_frame_level():
     _, st_t = oracle.token_level_rollout(frames, eye, eye, eye, S0=S)
     _, st_f = oracle.rollout(frames, eye, eye, eye, S0=S)
     np.testing.assert_allclose(st_t[1], st_f[1], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------ training-side gradients
+# Every gradient of the oracle is pinned by central finite differences of the
+# (already pinned) forward functions, in float64: for L = <W, f(x)> with a
+# random W, dL/dx_i ~ (L(x + h e_i) - L(x - h e_i)) / 2h, h = 1e-6 (truncation
+# O(h^2), rounding O(1e-16 / h)), checked to 1e-6 relative on every
+# coordinate of tiny inputs.
+
+def _fd_check(loss, x, grad, name, h=1e-6, rel=1e-6, coords=None):
+    x = np.asarray(x, dtype=np.float64)
+    grad = np.asarray(grad, dtype=np.float64)
+    assert grad.shape == x.shape, name
+    flat = x.reshape(-1)
+    idx = range(flat.size) if coords is None else coords
+    fd = []
+    an = []
+    for i in idx:
+        old = flat[i]
+        flat[i] = old + h
+        lp = loss()
+        flat[i] = old - h
+        lm = loss()
+        flat[i] = old
+        fd.append((lp - lm) / (2 * h))
+        an.append(grad.reshape(-1)[i])
+    fd, an = np.array(fd), np.array(an)
+    scale = max(np.abs(fd).max(), 1e-30)
+    assert np.abs(fd - an).max() <= rel * scale, f"{name}: {np.abs(fd - an).max():.3e} vs {scale:.3e}"
+
+
+def test_intra_attention_backward_finite_differences():
+    g = _rs(40)
+    q, k, v = (g.standard_normal((2, 2, 5, 4)) for _ in range(3))
+    W = g.standard_normal((2, 2, 5, 4))
+    gr = oracle.intra_attention_backward(q, k, v, W, 0.7)
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        _fd_check(lambda: np.sum(W * oracle.intra_attention(q, k, v, 0.7)), x, gr[name], name)
+
+
+def test_intra_attention_backward_closed_forms():
+    """One key: the weights are the constant 1, so dQ = dK = 0 and dV = sum of
+    dO over queries; identical value rows make O independent of the scores,
+    so dQ = dK = 0 again."""
+    g = _rs(41)
+    q, k, v = (g.standard_normal((1, 2, 1, 4)) for _ in range(3))
+    d_o = g.standard_normal((1, 2, 1, 4))
+    gr = oracle.intra_attention_backward(q, k, v, d_o)
+    assert np.abs(gr["dq"]).max() == 0 and np.abs(gr["dk"]).max() == 0
+    assert np.allclose(gr["dv"], d_o)
+    q, k = (g.standard_normal((1, 1, 6, 4)) for _ in range(2))
+    v = np.repeat(g.standard_normal((1, 1, 1, 4)), 6, axis=2)
+    gr = oracle.intra_attention_backward(q, k, v, g.standard_normal((1, 1, 6, 4)))
+    assert np.abs(gr["dq"]).max() < 1e-12 and np.abs(gr["dk"]).max() < 1e-12
+
+
+def test_read_backward_finite_differences():
+    g = _rs(42)
+    q, k, v = (g.standard_normal((2, 2, 5, 4)) for _ in range(3))
+    phi_q = g.standard_normal((2, 4, 4)) * 0.5
+    S = g.standard_normal((2, 2, 4, 4))
+    W = g.standard_normal((2, 2, 5, 4))
+    gr = oracle.read_backward(q, k, v, phi_q, S, W)
+
+    def loss():
+        return np.sum(W * oracle.read(q, k, v, phi_q, S)["o"])
+    for name, x in (("dq", q), ("dk", k), ("dv", v), ("dphi_q", phi_q), ("dS", S)):
+        _fd_check(loss, x, gr[name], name)
+
+
+def test_commit_backward_finite_differences():
+    g = _rs(43)
+    B, H, T, d = 2, 2, 5, 4
+    k, v = (g.standard_normal((B, H, T, d)) for _ in range(2))
+    phi_k, phi_v = (g.standard_normal((H, d, d)) * 0.5 for _ in range(2))
+    beta = g.uniform(0.1, 0.9, (B, H, T))
+    alpha = g.uniform(0.5, 1.0, (B, H))
+    S = g.standard_normal((B, H, d, d))
+    G = g.standard_normal((B, H, d, d))
+    gr = oracle.commit_backward(k, v, phi_k, phi_v, beta, alpha, S, G)
+
+    def loss():
+        return np.sum(G * oracle.commit(k, v, phi_k, phi_v, beta, alpha, S))
+    for name, x in (("dk", k), ("dv", v), ("dphi_k", phi_k), ("dphi_v", phi_v),
+                    ("dbeta", beta), ("dalpha", alpha), ("dS_prev", S)):
+        _fd_check(loss, x, gr[name], name)
+
+
+def test_commit_backward_closed_forms():
+    """beta = 0: the commit is alpha S, so dS_prev = alpha G, dalpha = <S, G>
+    and no gradient reaches K, V or the maps; dbeta is then the first-order
+    change of <G, S_next>: rowsum((K'G) * (V' - K'S))."""
+    g = _rs(44)
+    B, H, T, d = 1, 2, 4, 3
+    k, v = (g.standard_normal((B, H, T, d)) for _ in range(2))
+    phi_k, phi_v = (g.standard_normal((H, d, d)) for _ in range(2))
+    alpha = g.uniform(0.5, 1.0, (B, H))
+    S, G = (g.standard_normal((B, H, d, d)) for _ in range(2))
+    gr = oracle.commit_backward(k, v, phi_k, phi_v, np.zeros((B, H, T)), alpha, S, G)
+    assert np.allclose(gr["dS_prev"], alpha[..., None, None] * G)
+    assert np.allclose(gr["dalpha"], np.sum(S * G, axis=(-2, -1)))
+    for name in ("dk", "dv", "dphi_k", "dphi_v"):
+        assert np.abs(gr[name]).max() == 0, name
+    kp = oracle.l2_normalize_rows(oracle.feature_map(k, phi_k))
+    vp = oracle.feature_map(v, phi_v)
+    expect = np.einsum("bhti,bhij,bhtj->bht", kp, G, vp - kp @ S)
+    assert np.allclose(gr["dbeta"], expect)
+
+
+def test_state_scan_is_the_rollout_commit_sequence():
+    g = _rs(45)
+    frames = _frames(g, 1, 2, 5, 3, 3, 2)
+    phis = [g.standard_normal((2, 3, 3)) for _ in range(3)]
+    _, states = oracle.rollout(frames, *phis)
+    scanned = oracle.state_scan(frames, phis[1], phis[2])
+    assert len(scanned) == len(states)
+    for a, b in zip(scanned, states):
+        assert np.array_equal(a, b)
+
+
+def test_rollout_backward_finite_differences():
+    """Gradients through the frame recurrence: every q, k, v of every pass,
+    the gates of every frame, the three maps and S_0, for a loss on every
+    pass's output of a 3-frame, 2-pass rollout."""
+    g = _rs(46)
+    B, H, T, d, F, P = 1, 2, 4, 3, 3, 2
+    frames = _frames(g, B, H, T, d, F, P)
+    phis = [g.standard_normal((H, d, d)) * 0.6 for _ in range(3)]
+    S0 = g.standard_normal((B, H, d, d)) * 0.3
+    W = {(f, p): g.standard_normal((B, H, T, d)) for f in range(F) for p in range(P)}
+    Wfin = g.standard_normal((B, H, d, d))
+    gr = oracle.rollout_backward(frames, *phis, W, S0=S0, dS_final=Wfin)
+
+    def loss():
+        outs, states = oracle.rollout(frames, *phis, S0=S0)
+        return sum(np.sum(W[key] * r["o"]) for key, r in outs.items()) + np.sum(Wfin * states[-1])
+    for f in range(F):
+        for p in range(P):
+            for j, name in enumerate(("dq", "dk", "dv")):
+                _fd_check(loss, frames[f]["passes"][p][j], gr["d_passes"][(f, p)][j],
+                          f"{name} f{f} p{p}")
+        _fd_check(loss, frames[f]["beta"], gr["dbeta"][f], f"dbeta f{f}")
+        _fd_check(loss, frames[f]["alpha"], gr["dalpha"][f], f"dalpha f{f}")
+    for j, name in enumerate(("dphi_q", "dphi_k", "dphi_v")):
+        _fd_check(loss, phis[j], gr[name], name)
+    _fd_check(loss, S0, gr["dS0"], "dS0")
