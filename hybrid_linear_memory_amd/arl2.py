@@ -23,6 +23,7 @@ BF16 = 1
 OP_READ, OP_CLEAN_PASS, OP_COMMIT, OP_STATE_COMMIT, OP_READ_PREPARED = 0, 1, 2, 3, 4
 OP_CLEAN_PASS_PREPARED = 5
 OP_TOKEN_LEVEL = 6
+OP_INTRA_ATTN_BACKWARD, OP_READ_BACKWARD, OP_COMMIT_BACKWARD = 7, 8, 9
 
 STATUS_NAMES = {
     0: "ARL2_OK", 1: "ARL2_E_NULL", 2: "ARL2_E_SHAPE", 3: "ARL2_E_DTYPE",
@@ -61,6 +62,10 @@ SIGNATURES = {
                                _sz, _vp]),
     "arl2_token_clean_pass": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _sz, _vp]),
+    "arl2_intra_attn_backward": (_i32, [_SP] + [_vp] * 8 + [_i32, _vp, _sz, _vp]),
+    "arl2_read_backward": (_i32, [_SP] + [_vp] * 12 + [_i32, _vp, _sz, _vp]),
+    "arl2_commit_backward": (_i32, [_SP] + [_vp] * 15 + [_i32, _vp, _sz, _vp]),
+    "arl2_state_scan": (_i32, [_SP, _i32] + [_vp] * 9 + [_sz, _vp]),
     "arl2_workspace_bytes": (_sz, [_SP, _i32]),
     "arl2_status_string": (ctypes.c_char_p, [_i32]),
     "arl2_last_error": (ctypes.c_char_p, []),
@@ -279,6 +284,59 @@ def token_clean_pass(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_
         _ptr(S_next, "S_next", f), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
         _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def _ws(ws):
+    return _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0
+
+
+def intra_attn_backward(shape: Shape, q, k, v, o_intra, d_o, dq, dk, dv, accumulate=False,
+                        ws=None, stream=None):
+    """dq, dk, dv of the intra-frame softmax from its output o_intra and dL/dO_intra."""
+    a = shape.torch_dtype
+    _check(_lib.arl2_intra_attn_backward(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(o_intra, "o_intra", a), _ptr(d_o, "d_o", a), _ptr(dq, "dq", a), _ptr(dk, "dk", a),
+        _ptr(dv, "dv", a), 1 if accumulate else 0, *_ws(ws), _stream(stream)))
+
+
+def read_backward(shape: Shape, q, k, v, phi_q, S, o_intra, d_o, dq, dk, dv, dphi_q, dS,
+                  accumulate=False, ws=None, stream=None):
+    """Gradients of a read O = O_intra + (Q Phi_q) S given dL/dO."""
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_read_backward(
+        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(phi_q, "phi_q", a), _ptr(S, "S", f), _ptr(o_intra, "o_intra", a),
+        _ptr(d_o, "d_o", a), _ptr(dq, "dq", a), _ptr(dk, "dk", a), _ptr(dv, "dv", a),
+        _ptr(dphi_q, "dphi_q", f), _ptr(dS, "dS", f), 1 if accumulate else 0, *_ws(ws),
+        _stream(stream)))
+
+
+def commit_backward(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S_prev, dS_next, dk, dv,
+                    dphi_k, dphi_v, dbeta, dalpha, dS_prev, accumulate=False, ws=None,
+                    stream=None):
+    """Gradients of the commit given dL/dS_next."""
+    a, f = shape.torch_dtype, torch.float32
+    _check(_lib.arl2_commit_backward(
+        ctypes.byref(shape.c()), _ptr(k, "k", a), _ptr(v, "v", a), _ptr(phi_k, "phi_k", a),
+        _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f), _ptr(alpha, "alpha", f),
+        _ptr(S_prev, "S_prev", f), _ptr(dS_next, "dS_next", f), _ptr(dk, "dk", a),
+        _ptr(dv, "dv", a), _ptr(dphi_k, "dphi_k", f), _ptr(dphi_v, "dphi_v", f),
+        _ptr(dbeta, "dbeta", f), _ptr(dalpha, "dalpha", f), _ptr(dS_prev, "dS_prev", f),
+        1 if accumulate else 0, *_ws(ws), _stream(stream)))
+
+
+def state_scan(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S0, states, ws=None, stream=None):
+    """states[0] = S0 and states[f + 1] = the commit of frame f (k, v: [F, B, H, T, D])."""
+    a, f = shape.torch_dtype, torch.float32
+    n_frames = int(k.shape[0])
+    if tuple(states.shape[:1]) != (n_frames + 1,):
+        raise ValueError("states needs n_frames + 1 entries")
+    _check(_lib.arl2_state_scan(
+        ctypes.byref(shape.c()), n_frames, _ptr(k, "k", a), _ptr(v, "v", a),
+        _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f),
+        _ptr(alpha, "alpha", f), _ptr(S0, "S0", f), _ptr(states, "states", f), *_ws(ws),
+        _stream(stream)))
 
 
 def fullkv_attn(shape: Shape, q, k_cache, v_cache, n_kv: int, o, stream=None):

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libarl2.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_token.hip"]
+SOURCES = ["api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_token.hip",
+           "kernels_train.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

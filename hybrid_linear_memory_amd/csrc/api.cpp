@@ -261,6 +261,17 @@ arl2_status check_token(const arl2::Dims& d, const void* q, const void* k, const
   return ARL2_OK;
 }
 
+arl2_status check_disjoint(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ARL2_E_ALIAS, "two outputs overlap");
+  }
+  return ARL2_OK;
+}
+
 arl2_status check_state_pair(const arl2::Dims& d, const float* S_prev, const float* S_next) {
   if (overlap({S_prev, state_bytes(d)}, {S_next, state_bytes(d)}))
     return fail(ARL2_E_ALIAS, "S_prev and S_next overlap; the state must be double-buffered");
@@ -300,6 +311,9 @@ size_t arl2_workspace_bytes(const arl2_shape* shape, int32_t op) {
     case ARL2_OP_READ_PREPARED: return ws_read_prepared(d);
     case ARL2_OP_CLEAN_PASS_PREPARED: return ws_clean_pass_prepared(d);
     case ARL2_OP_TOKEN_LEVEL: return ws_token(d);
+    case ARL2_OP_INTRA_ATTN_BACKWARD: return arl2::attn_backward_ws_bytes(d);
+    case ARL2_OP_READ_BACKWARD: return arl2::read_backward_ws_bytes(d);
+    case ARL2_OP_COMMIT_BACKWARD: return arl2::commit_backward_ws_bytes(d);
     default: return 0;
   }
 }
@@ -614,6 +628,150 @@ arl2_status arl2_token_clean_pass(const arl2_shape* shape, const void* q, const 
   if (st != ARL2_OK) return st;
   return do_token(d, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, S_next, o, o_intra,
                   o_inter, ws, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------- training side
+
+arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q, const void* k,
+                                     const void* v, const void* o_intra, const void* d_o,
+                                     void* dq, void* dk, void* dv, int32_t accumulate, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o_intra);
+  REQUIRE_PTR(d_o);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dk);
+  REQUIRE_PTR(dv);
+  const size_t need = arl2::attn_backward_ws_bytes(d);
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d);
+  const Range outs[3] = {{dq, ab}, {dk, ab}, {dv, ab}};
+  const Range ins[6] = {{q, ab}, {k, ab}, {v, ab}, {o_intra, ab}, {d_o, ab}, {ws, need}};
+  if ((st = check_disjoint(outs, 3, ins, 6)) != ARL2_OK) return st;
+  return hip_status(arl2::attn_backward(d, q, k, v, o_intra, d_o, dq, dk, dv, accumulate != 0,
+                                        ws, (hipStream_t)stream),
+                    "attention backward");
+}
+
+arl2_status arl2_read_backward(const arl2_shape* shape, const void* q, const void* k,
+                               const void* v, const void* phi_q, const float* S,
+                               const void* o_intra, const void* d_o, void* dq, void* dk,
+                               void* dv, float* dphi_q, float* dS, int32_t accumulate, void* ws,
+                               size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_q);
+  REQUIRE_PTR(S);
+  REQUIRE_PTR(o_intra);
+  REQUIRE_PTR(d_o);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dk);
+  REQUIRE_PTR(dv);
+  REQUIRE_PTR(dphi_q);
+  REQUIRE_PTR(dS);
+  const size_t need = arl2::read_backward_ws_bytes(d);
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d);
+  const size_t pb = (size_t)d.H * d.D * d.D * 4;
+  const Range outs[5] = {{dq, ab}, {dk, ab}, {dv, ab}, {dphi_q, pb}, {dS, state_bytes(d)}};
+  const Range ins[8] = {{q, ab},       {k, ab},   {v, ab},   {phi_q, phi_bytes(d)},
+                        {S, state_bytes(d)}, {o_intra, ab}, {d_o, ab}, {ws, need}};
+  if ((st = check_disjoint(outs, 5, ins, 8)) != ARL2_OK) return st;
+  return hip_status(arl2::read_backward(d, q, k, v, phi_q, S, o_intra, d_o, dq, dk, dv, dphi_q,
+                                        dS, accumulate != 0, ws, (hipStream_t)stream),
+                    "read backward");
+}
+
+arl2_status arl2_commit_backward(const arl2_shape* shape, const void* k, const void* v,
+                                 const void* phi_k, const void* phi_v, const float* beta,
+                                 const float* alpha, const float* S_prev, const float* dS_next,
+                                 void* dk, void* dv, float* dphi_k, float* dphi_v, float* dbeta,
+                                 float* dalpha, float* dS_prev, int32_t accumulate, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_k);
+  REQUIRE_PTR(phi_v);
+  REQUIRE_PTR(beta);
+  REQUIRE_PTR(alpha);
+  REQUIRE_PTR(S_prev);
+  REQUIRE_PTR(dS_next);
+  REQUIRE_PTR(dk);
+  REQUIRE_PTR(dv);
+  REQUIRE_PTR(dphi_k);
+  REQUIRE_PTR(dphi_v);
+  REQUIRE_PTR(dbeta);
+  REQUIRE_PTR(dalpha);
+  REQUIRE_PTR(dS_prev);
+  const size_t need = arl2::commit_backward_ws_bytes(d);
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d), sb = state_bytes(d);
+  const size_t pb = (size_t)d.H * d.D * d.D * 4;
+  const size_t bb = (size_t)d.B * d.H * d.T * 4, gb = (size_t)d.B * d.H * 4;
+  const Range outs[7] = {{dk, ab},     {dv, ab},     {dphi_k, pb}, {dphi_v, pb},
+                         {dbeta, bb},  {dalpha, gb}, {dS_prev, sb}};
+  const Range ins[9] = {{k, ab},          {v, ab},       {phi_k, phi_bytes(d)},
+                        {phi_v, phi_bytes(d)}, {beta, bb}, {alpha, gb},
+                        {S_prev, sb},     {dS_next, sb}, {ws, need}};
+  if ((st = check_disjoint(outs, 7, ins, 9)) != ARL2_OK) return st;
+  return hip_status(arl2::commit_backward(d, k, v, phi_k, phi_v, beta, alpha, S_prev, dS_next, dk,
+                                          dv, dphi_k, dphi_v, dbeta, dalpha, dS_prev,
+                                          accumulate != 0, ws, (hipStream_t)stream),
+                    "commit backward");
+}
+
+arl2_status arl2_state_scan(const arl2_shape* shape, int32_t n_frames, const void* k,
+                            const void* v, const void* phi_k, const void* phi_v,
+                            const float* beta, const float* alpha, const float* S0,
+                            float* states, void* ws, size_t ws_bytes, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  if (n_frames < 1) return fail(ARL2_E_SHAPE, "n_frames must be >= 1 (got %d)", n_frames);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_k);
+  REQUIRE_PTR(phi_v);
+  REQUIRE_PTR(beta);
+  REQUIRE_PTR(alpha);
+  REQUIRE_PTR(S0);
+  REQUIRE_PTR(states);
+  const size_t need = ws_commit(d);
+  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  const size_t ab = arl2::act_bytes(d), sb = state_bytes(d);
+  const size_t F = (size_t)n_frames;
+  const Range outs[1] = {{states, (F + 1) * sb}};
+  const Range ins[8] = {{k, F * ab},
+                        {v, F * ab},
+                        {phi_k, phi_bytes(d)},
+                        {phi_v, phi_bytes(d)},
+                        {beta, F * d.B * d.H * d.T * 4},
+                        {alpha, F * d.B * d.H * 4},
+                        {S0, sb},
+                        {ws, need}};
+  if ((st = check_disjoint(outs, 1, ins, 8)) != ARL2_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t sn = sb / 4;
+  if ((st = hip_status(arl2::copy_state(S0, states, sn, s), "state copy")) != ARL2_OK) return st;
+  for (size_t f = 0; f < F; ++f) {
+    st = do_commit(d, static_cast<const char*>(k) + f * ab, static_cast<const char*>(v) + f * ab,
+                   phi_k, phi_v, beta + f * d.B * d.H * d.T, alpha + f * d.B * d.H,
+                   states + f * sn, states + (f + 1) * sn, ws, s);
+    if (st != ARL2_OK) return st;
+  }
+  return ok();
 }
 
 arl2_status arl2_fullkv_attn(const arl2_shape* shape, const void* q, const void* k_cache,

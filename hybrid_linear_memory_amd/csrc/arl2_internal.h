@@ -90,6 +90,25 @@ hipError_t token_level_scan(const Dims& d, const void* q_prime, const void* k_pr
                             const float* alpha, float* S_next, const void* o_intra, void* o,
                             void* o_inter, void* ws, hipStream_t s);
 
+// Training side: exact derivatives of the read and of the commit (accumulate:
+// add every gradient to its output instead of overwriting it).
+size_t attn_backward_ws_bytes(const Dims& d);
+size_t read_backward_ws_bytes(const Dims& d);
+size_t commit_backward_ws_bytes(const Dims& d);
+hipError_t attn_backward(const Dims& d, const void* q, const void* k, const void* v,
+                         const void* o_intra, const void* d_o, void* dq, void* dk, void* dv,
+                         bool accumulate, void* ws, hipStream_t s);
+hipError_t read_backward(const Dims& d, const void* q, const void* k, const void* v,
+                         const void* phi_q, const float* S, const void* o_intra, const void* d_o,
+                         void* dq, void* dk, void* dv, float* dphi_q, float* dS, bool accumulate,
+                         void* ws, hipStream_t s);
+hipError_t commit_backward(const Dims& d, const void* k, const void* v, const void* phi_k,
+                           const void* phi_v, const float* beta, const float* alpha,
+                           const float* S_prev, const float* dS_next, void* dk, void* dv,
+                           float* dphi_k, float* dphi_v, float* dbeta, float* dalpha,
+                           float* dS_prev, bool accumulate, void* ws, hipStream_t s);
+hipError_t copy_state(const float* src, float* dst, size_t n, hipStream_t s);
+
 inline bool use_mfma(const Dims& d) { return d.bf16 && d.D == 128; }
 
 }  // namespace arl2

@@ -1,0 +1,1005 @@
+// Training-side kernels: the backward of the read and of the commit, and the
+// clean-state scan over frames. The summary's two-stage distillation (§2.3)
+// fine-tunes the hybrid model end to end; these compute the exact derivatives
+// of the forward step:
+//   read    O = softmax(Q K^T * scale) V + (Q Phi_q) S
+//   commit  S_next = alpha S + K'^T diag(beta) (V' - K' S),
+//           K' = rownorm(K Phi_k), V' = V Phi_v.
+//
+// Building blocks (bf16 on MFMA at d = 128; plain float32 loops otherwise):
+//   nt_gemm   Y = X Bt^T per (b, h) with an elementwise epilogue
+//   xty       C = X^T Y summed over tokens (and over videos for the maps'
+//             gradients), in fixed-order chunk partials
+//   row kernels for the row normalisation, beta and the norm's backward
+//   attention backward: per-row log-sum-exp and dO.O, then dK, dV (one
+//             workgroup per key block) and dQ (one per query block), each
+//             recomputing the scores, so no accumulation crosses workgroups.
+#include <math.h>
+
+#include "arl2_internal.h"
+#include "mfma_common.h"
+
+namespace arl2 {
+namespace {
+
+constexpr float kNormFloor = 1e-12f;          // row-norm floor of the key map
+
+template <typename Tx>
+__device__ __forceinline__ float ldf(const Tx* p, size_t i) { return (float)p[i]; }
+template <typename Tx>
+__device__ __forceinline__ void stf(Tx* p, size_t i, float x) { p[i] = (Tx)x; }
+
+// ---------------------------------------------------------------------------
+// Epilogue of the GEMM-shaped steps: y = (z ? z - acc : acc), written to y32
+// (float) and / or yx (activation type), added to what is there when
+// accumulate is set.
+// ---------------------------------------------------------------------------
+struct Epi {
+  const void* z;        // activation type, or float when z_f32
+  int z_f32;
+  float* y32;
+  void* yx;
+  int accumulate;
+};
+
+template <typename Tx>
+__device__ __forceinline__ void epilogue(const Epi& ep, size_t idx, float acc) {
+  float y = acc;
+  if (ep.z) y = (ep.z_f32 ? static_cast<const float*>(ep.z)[idx]
+                          : ldf(static_cast<const Tx*>(ep.z), idx)) - y;
+  if (ep.y32) ep.y32[idx] = ep.accumulate ? ep.y32[idx] + y : y;
+  if (ep.yx) {
+    Tx* yx = static_cast<Tx*>(ep.yx);
+    stf(yx, idx, ep.accumulate ? ldf(yx, idx) + y : y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 building blocks (any D <= 128)
+// ---------------------------------------------------------------------------
+
+// Y[g][t][n] = sum_k X[gx][t][k] * B(n, k), B(n, k) = bt[gb][n][k] (or
+// bt[gb][k][n] when bt_trans); gx = x_per_head ? g % H : g, same for gb.
+__global__ void nt_gemm_f32_k(const float* __restrict__ x, const float* __restrict__ bt,
+                              Epi ep, int rows, int D, int H, int x_per_head,
+                              int bt_per_head, int bt_trans, long n_out) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_out) return;
+  const int n = (int)(idx % D);
+  const long gr = idx / D;
+  const int t = (int)(gr % rows);
+  const long g = gr / rows;
+  const float* xr = x + ((x_per_head ? g % H : g) * rows + t) * (long)D;
+  const float* bm = bt + (bt_per_head ? g % H : g) * (long)D * D;
+  float acc = 0.f;
+  for (int k = 0; k < D; ++k) acc = fmaf(xr[k], bt_trans ? bm[(long)k * D + n] : bm[(long)n * D + k], acc);
+  epilogue<float>(ep, idx, acc);
+}
+
+// C[go][e][v] = base + delta * sum_{b} sum_t X[g][t][e] Y[g][t][v] with
+// g = b * H + h over all b when sum_b (go = h), else g = go alone;
+// base = gamma[go] * base_mat[go][e][v] when base_mat is given; added to C
+// when accumulate.
+__global__ void xty_f32_k(const float* __restrict__ x, const float* __restrict__ y,
+                          float* __restrict__ out, const float* __restrict__ base_mat,
+                          const float* __restrict__ gamma, float delta, int accumulate, int T,
+                          int D, int B, int H, int sum_b, long n_out) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_out) return;
+  const int v = (int)(idx % D);
+  const int e = (int)((idx / D) % D);
+  const long go = idx / ((long)D * D);
+  float acc = 0.f;
+  const int nb = sum_b ? B : 1;
+  for (int b = 0; b < nb; ++b) {
+    const long g = sum_b ? (long)b * H + go : go;
+    const float* xg = x + g * (long)T * D;
+    const float* yg = y + g * (long)T * D;
+    for (int t = 0; t < T; ++t) acc = fmaf(xg[(long)t * D + e], yg[(long)t * D + v], acc);
+  }
+  float r = delta * acc;
+  if (base_mat) r += gamma[go] * base_mat[idx];
+  out[idx] = accumulate ? out[idx] + r : r;
+}
+
+// Per query row: lse = max + log(sum exp(s - max)) of s = scale q.k over the
+// frame's keys, and dsum = dO . O_intra.
+__global__ void attn_pre_f32_k(const float* __restrict__ q, const float* __restrict__ k,
+                               const float* __restrict__ o, const float* __restrict__ d_o,
+                               float* __restrict__ lse, float* __restrict__ dsum, int T, int D,
+                               float scale, long n_rows) {
+  const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  const long g = r / T;
+  const float* qr = q + r * D;
+  const float* kg = k + g * (long)T * D;
+  float m = -INFINITY;
+  for (int j = 0; j < T; ++j) {
+    float s = 0.f;
+    for (int e = 0; e < D; ++e) s = fmaf(qr[e], kg[(long)j * D + e], s);
+    m = fmaxf(m, s * scale);
+  }
+  float l = 0.f;
+  for (int j = 0; j < T; ++j) {
+    float s = 0.f;
+    for (int e = 0; e < D; ++e) s = fmaf(qr[e], kg[(long)j * D + e], s);
+    l += expf(s * scale - m);
+  }
+  lse[r] = m + logf(l);
+  float dd = 0.f;
+  for (int e = 0; e < D; ++e) dd = fmaf(d_o[r * D + e], o[r * D + e], dd);
+  dsum[r] = dd;
+}
+
+// P_ij = exp(scale q_i.k_j - lse_i), dS_ij = P_ij (dO_i.v_j - dsum_i).
+__device__ __forceinline__ void attn_pd_f32(const float* qi, const float* kj, const float* doi,
+                                            const float* vj, int D, float scale, float lse_i,
+                                            float dsum_i, float* p, float* ds) {
+  float s = 0.f, dp = 0.f;
+  for (int e = 0; e < D; ++e) {
+    s = fmaf(qi[e], kj[e], s);
+    dp = fmaf(doi[e], vj[e], dp);
+  }
+  *p = expf(s * scale - lse_i);
+  *ds = *p * (dp - dsum_i);
+}
+
+// dQ[i][e] = scale sum_j dS_ij K[j][e]   (one thread per element)
+__global__ void attn_dq_f32_k(const float* __restrict__ q, const float* __restrict__ k,
+                              const float* __restrict__ v, const float* __restrict__ d_o,
+                              const float* __restrict__ lse, const float* __restrict__ dsum,
+                              float* __restrict__ dq, int T, int D, float scale, int accumulate,
+                              long n_out) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_out) return;
+  const int e = (int)(idx % D);
+  const long r = idx / D;
+  const long g = r / T;
+  const float* kg = k + g * (long)T * D;
+  const float* vg = v + g * (long)T * D;
+  float acc = 0.f;
+  for (int j = 0; j < T; ++j) {
+    float p, ds;
+    attn_pd_f32(q + r * D, kg + (long)j * D, d_o + r * D, vg + (long)j * D, D, scale, lse[r],
+                dsum[r], &p, &ds);
+    acc = fmaf(ds, kg[(long)j * D + e], acc);
+  }
+  acc *= scale;
+  dq[idx] = accumulate ? dq[idx] + acc : acc;
+}
+
+// dK[j][e] = scale sum_i dS_ij Q[i][e], dV[j][e] = sum_i P_ij dO[i][e]
+__global__ void attn_dkdv_f32_k(const float* __restrict__ q, const float* __restrict__ k,
+                                const float* __restrict__ v, const float* __restrict__ d_o,
+                                const float* __restrict__ lse, const float* __restrict__ dsum,
+                                float* __restrict__ dk, float* __restrict__ dv, int T, int D,
+                                float scale, int accumulate, long n_out) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_out) return;
+  const int e = (int)(idx % D);
+  const long rj = idx / D;
+  const long g = rj / T;
+  const long r0 = g * T;
+  float ak = 0.f, av = 0.f;
+  for (int i = 0; i < T; ++i) {
+    float p, ds;
+    attn_pd_f32(q + (r0 + i) * D, k + rj * D, d_o + (r0 + i) * D, v + rj * D, D, scale,
+                lse[r0 + i], dsum[r0 + i], &p, &ds);
+    ak = fmaf(ds, q[(r0 + i) * D + e], ak);
+    av = fmaf(p, d_o[(r0 + i) * D + e], av);
+  }
+  ak *= scale;
+  dk[idx] = accumulate ? dk[idx] + ak : ak;
+  dv[idx] = accumulate ? dv[idx] + av : av;
+}
+
+// ---------------------------------------------------------------------------
+// Row kernels (either activation type; one thread per row)
+// ---------------------------------------------------------------------------
+
+// out = x / max(||x||, floor) and the raw norm
+template <typename Tx>
+__global__ void rownorm_k(const Tx* __restrict__ x, Tx* __restrict__ out, float* __restrict__ nrm,
+                          int D, long n_rows) {
+  const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  float ss = 0.f;
+  for (int e = 0; e < D; ++e) {
+    const float a = ldf(x, r * D + e);
+    ss = fmaf(a, a, ss);
+  }
+  const float n = sqrtf(ss);
+  const float inv = 1.f / fmaxf(n, kNormFloor);
+  for (int e = 0; e < D; ++e) stf(out, r * D + e, ldf(x, r * D + e) * inv);
+  nrm[r] = n;
+}
+
+// dbeta_t (+)= sum_v KG[t][v] R[t][v];  dV'[t][v] = beta_t KG[t][v]
+template <typename Tx>
+__global__ void commit_rows1_k(const float* __restrict__ kg, const float* __restrict__ rr,
+                               const float* __restrict__ beta, float* __restrict__ dbeta,
+                               Tx* __restrict__ dvp, int D, int accumulate, long n_rows) {
+  const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  float acc = 0.f;
+  const float b = beta[r];
+  for (int e = 0; e < D; ++e) {
+    const float x = kg[r * D + e];
+    acc = fmaf(x, rr[r * D + e], acc);
+    stf(dvp, r * D + e, b * x);
+  }
+  dbeta[r] = accumulate ? dbeta[r] + acc : acc;
+}
+
+// dK~ = (dK' - K' (K'.dK')) / n with dK' = beta_t dKraw (dK' / floor below it)
+template <typename Tx>
+__global__ void commit_rows2_k(const float* __restrict__ dkraw, const Tx* __restrict__ kp,
+                               const float* __restrict__ nrm, const float* __restrict__ beta,
+                               Tx* __restrict__ dkt, int D, long n_rows) {
+  const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  const float b = beta[r], n = nrm[r];
+  if (n > kNormFloor) {
+    float dot = 0.f;
+    for (int e = 0; e < D; ++e) dot = fmaf(ldf(kp, r * D + e), dkraw[r * D + e], dot);
+    const float inv = 1.f / n;
+    for (int e = 0; e < D; ++e)
+      stf(dkt, r * D + e, b * (dkraw[r * D + e] - ldf(kp, r * D + e) * dot) * inv);
+  } else {
+    for (int e = 0; e < D; ++e) stf(dkt, r * D + e, b * dkraw[r * D + e] / kNormFloor);
+  }
+}
+
+// dalpha[g] (+)= <S[g], G[g]>  (one workgroup of 256 per (b, h), fixed order)
+__global__ void __launch_bounds__(256)
+dalpha_k(const float* __restrict__ S, const float* __restrict__ G, float* __restrict__ dalpha,
+         int DD, int accumulate) {
+  __shared__ float red[256];
+  const long g = blockIdx.x;
+  float acc = 0.f;
+  for (int i = threadIdx.x; i < DD; i += 256) acc = fmaf(S[g * DD + i], G[g * DD + i], acc);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dalpha[g] = accumulate ? dalpha[g] + red[0] : red[0];
+}
+
+// bf16 copies of a float [n][128][128] matrix set, row-major and transposed
+__global__ void to_bf16_pair_k(const float* __restrict__ m, __bf16* __restrict__ mb,
+                               __bf16* __restrict__ mtb, long n_out) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_out) return;
+  const int c = (int)(idx % HD), r = (int)((idx / HD) % HD);
+  const long g = idx / (HD * HD);
+  const __bf16 x = (__bf16)m[idx];
+  if (mb) mb[idx] = x;
+  if (mtb) mtb[g * HD * HD + (long)c * HD + r] = x;
+}
+
+__global__ void copy_f32_k(const float* __restrict__ a, float* __restrict__ b, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) b[i] = a[i];
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA building blocks (d = 128)
+// ---------------------------------------------------------------------------
+
+// Y = X Bt^T: one workgroup of 4 waves per 128 rows of one g; wave w computes
+// rows 32w.. against all 128 columns (4 tiles), operands straight from memory
+// (Bt, 32 KB, stays in L2).
+__global__ void __launch_bounds__(256)
+nt_gemm_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ bt, Epi ep, int rows,
+               int H, int x_per_head, int bt_per_head, int n_rblk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long g = blockIdx.x / n_rblk;
+  const int row0 = (blockIdx.x % n_rblk) * 128 + 32 * wave;
+  const __bf16* xg = x + (x_per_head ? g % H : g) * (long)rows * HD;
+  const __bf16* bg = bt + (bt_per_head ? g % H : g) * (long)HD * HD;
+  const __bf16* xr = xg + (long)min(row0 + n, rows - 1) * HD + 8 * h2;
+  bf16x8 a[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) a[kc] = ld8(xr + 16 * kc);
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    const __bf16* br = bg + (long)(32 * tn + n) * HD + 8 * h2;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) acc = mfma32(a[kc], ld8(br + 16 * kc), acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+      if (row < rows) epilogue<__bf16>(ep, ((size_t)g * rows + row) * HD + 32 * tn + n, acc[r]);
+    }
+  }
+}
+
+// bf16 chunk of `rows` x 128 into LDS under the swz_v swizzle, zero past `valid`
+__device__ __forceinline__ void stage_tr(char* dst, const __bf16* src, int rows, int valid) {
+  for (int idx = threadIdx.x; idx < rows * 16; idx += blockDim.x) {
+    const int r = idx >> 4, p = idx & 15;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (r < valid) val = *reinterpret_cast<const uint4*>(src + (size_t)r * HD + 8 * p);
+    *reinterpret_cast<uint4*>(dst + r * 256 + ((p ^ swz_v(r)) << 4)) = val;
+  }
+}
+
+constexpr int XTY_CHUNK = 256;                // tokens per partial
+constexpr int XTY_SUB = 64;                   // tokens staged at a time
+
+// Partial X^T Y over one chunk of tokens of one g, as 16 tiles of 32 x 32 in
+// MFMA accumulator order: part[(g * nch + ch) * 16 + tile][lane][16].
+__global__ void __launch_bounds__(256)
+xty_part_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ y,
+                float* __restrict__ part, int T, int nch) {
+  __shared__ __attribute__((aligned(16))) char lx[XTY_SUB * 256];
+  __shared__ __attribute__((aligned(16))) char ly[XTY_SUB * 256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long g = blockIdx.x / nch;
+  const int ch = blockIdx.x % nch;
+  f32x16 acc[4] = {zero16(), zero16(), zero16(), zero16()};
+  for (int s0 = ch * XTY_CHUNK; s0 < min(T, (ch + 1) * XTY_CHUNK); s0 += XTY_SUB) {
+    const int valid = min(XTY_SUB, T - s0);
+    stage_tr(lx, x + ((size_t)g * T + s0) * HD, XTY_SUB, valid);
+    stage_tr(ly, y + ((size_t)g * T + s0) * HD, XTY_SUB, valid);
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < XTY_SUB / 16; ++kc) {
+      const bf16x8 a = tr_op(lx, 16 * kc, 8, 32 * wave, lane);   // X^T rows e
+#pragma unroll
+      for (int tv = 0; tv < 4; ++tv)
+        acc[tv] = mfma32(a, tr_op(ly, 16 * kc, 8, 32 * tv, lane), acc[tv]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int tv = 0; tv < 4; ++tv) {
+    float* p = part + (((size_t)g * nch + ch) * 16 + 4 * wave + tv) * 1024 + lane * 16;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<float4*>(p + 4 * q4) =
+          make_float4(acc[tv][4 * q4], acc[tv][4 * q4 + 1], acc[tv][4 * q4 + 2], acc[tv][4 * q4 + 3]);
+  }
+}
+
+// out[go][e][v] (+)= gamma[go] base[go][e][v] + delta * sum_b sum_ch part:
+// one thread per (go, tile, lane), 16 outputs each, chunks summed in order.
+__global__ void xty_reduce_mfma_k(const float* __restrict__ part, float* __restrict__ out,
+                                  const float* __restrict__ base_mat,
+                                  const float* __restrict__ gamma, float delta, int accumulate,
+                                  int nch, int B, int H, int sum_b, long n_thr) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_thr) return;
+  const int lane = (int)(idx & 63);
+  const int tile = (int)((idx >> 6) & 15);
+  const long go = idx >> 10;
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int nb = sum_b ? B : 1;
+  for (int b = 0; b < nb; ++b) {
+    const long g = sum_b ? (long)b * H + go : go;
+    for (int ch = 0; ch < nch; ++ch) {
+      const float* p = part + (((size_t)g * nch + ch) * 16 + tile) * 1024 + lane * 16;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = *reinterpret_cast<const float4*>(p + 4 * q4);
+        acc[4 * q4] += x.x;
+        acc[4 * q4 + 1] += x.y;
+        acc[4 * q4 + 2] += x.z;
+        acc[4 * q4 + 3] += x.w;
+      }
+    }
+  }
+  const int n = lane & 31, h2 = lane >> 5;
+  const int v = 32 * (tile & 3) + n;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int e = 32 * (tile >> 2) + 8 * (r >> 2) + 4 * h2 + (r & 3);
+    const size_t o = (size_t)go * HD * HD + (size_t)e * HD + v;
+    float val = delta * acc[r];
+    if (base_mat) val += gamma[go] * base_mat[o];
+    out[o] = accumulate ? out[o] + val : val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention backward, bf16 MFMA (d = 128). The exponent base is 2: with
+// c = scale log2(e), P_ij = exp2(c q_i.k_j - lse2_i), lse2 in log2 units.
+// ---------------------------------------------------------------------------
+constexpr int AB_STAGE = 64;                  // keys (or queries) staged per step
+
+// Row operand (8 consecutive columns 16 kc + 8 h2 ..) of a swz_v-staged tile.
+__device__ __forceinline__ bf16x8 row_op_v(const char* base, int row, int kc, int h2) {
+  return *reinterpret_cast<const bf16x8*>(base + row * 256 + (((2 * kc + h2) ^ swz_v(row)) << 4));
+}
+
+// A operand by transposing reads whose contraction slots follow an MFMA
+// accumulator's register order: lane (n, h2) receives M[r0 + 4 h2 + u][c0 + n]
+// for u = 0..3 and M[r0 + 8 + 4 h2 + u - 4][c0 + n] for u = 4..7, i.e. the rows
+// that registers 8 kc .. 8 kc + 7 of a 32 x 32 accumulator hold (r0 = 32 t + 16 kc).
+__device__ __forceinline__ bf16x8 tr_op_acc(const char* base, int r0, int c0, int lane) {
+  const int G = lane >> 4;
+  const int s = lane & 15, c = s >> 2, j = s & 3;
+  const int col = c0 + 16 * (G & 1) + 4 * j;
+  const int c16 = col >> 3, sub = (col & 7) * 2;
+  const int rb = r0 + 4 * (G >> 1) + c;
+  const char* a0 = base + rb * 256 + ((c16 ^ swz_v(rb)) << 4) + sub;
+  const char* a1 = base + (rb + 8) * 256 + ((c16 ^ swz_v(rb + 8)) << 4) + sub;
+  return __builtin_shufflevector(tr_read(a0), tr_read(a1), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// registers 8 kc .. 8 kc + 7 of an accumulator as a bf16 operand
+__device__ __forceinline__ bf16x8 acc_op(const float* a, int kc) {
+  bf16x8 r;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) r[u] = (__bf16)a[8 * kc + u];
+  return r;
+}
+
+// Per query row: lse2 = log2 sum_j exp2(c q.k_j) and dsum = dO . O_intra. One
+// workgroup of 4 waves per 128 queries; wave w holds queries 32 w.. as the
+// columns of S^T = K Q^T (a lane's running max and sum cover half the keys;
+// the halves combine at the end).
+__global__ void __launch_bounds__(256)
+attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
+                float* __restrict__ lse2, float* __restrict__ dsum, int T, float c, int n_qblk) {
+  __shared__ __attribute__((aligned(16))) char lk[AB_STAGE * 256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long g = blockIdx.x / n_qblk;
+  const int i = (blockIdx.x % n_qblk) * 128 + 32 * wave + n;     // this lane's query
+  const size_t gbase = (size_t)g * T;
+  const __bf16* qr = q + (gbase + min(i, T - 1)) * HD + 8 * h2;
+  bf16x8 qb[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) qb[kc] = ld8(qr + 16 * kc);
+  float m = -INFINITY, l = 0.f;
+  for (int j0 = 0; j0 < T; j0 += AB_STAGE) {
+    stage_tr(lk, k + (gbase + j0) * HD, AB_STAGE, min(AB_STAGE, T - j0));
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < AB_STAGE / 32; ++sub) {
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) acc = mfma32(row_op_v(lk, 32 * sub + n, kc, h2), qb[kc], acc);
+      float sv[16], mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        sv[r] = j < T ? acc[r] * c : -INFINITY;
+        mt = fmaxf(mt, sv[r]);
+      }
+      const float mn = fmaxf(m, mt);
+      if (mn > -INFINITY) {
+        float add = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) add += exp2f(sv[r] - mn);
+        l = l * exp2f(m - mn) + add;
+        m = mn;
+      }
+    }
+    __syncthreads();
+  }
+  const float mo = swap_halves(m), lo = swap_halves(l);
+  const float M = fmaxf(m, mo);
+  const float L = (m > -INFINITY ? l * exp2f(m - M) : 0.f) + (mo > -INFINITY ? lo * exp2f(mo - M) : 0.f);
+  // dO . O over this lane's half of the features, then both halves
+  const __bf16* dr = d_o + (gbase + min(i, T - 1)) * HD + 64 * h2;
+  const __bf16* orr = o + (gbase + min(i, T - 1)) * HD + 64 * h2;
+  float dd = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const bf16x8 a = ld8(dr + 8 * u), b = ld8(orr + 8 * u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dd = fmaf((float)a[e], (float)b[e], dd);
+  }
+  dd += swap_halves(dd);
+  if (h2 == 0 && i < T) {
+    lse2[gbase + i] = M + log2f(L);
+    dsum[gbase + i] = dd;
+  }
+}
+
+// dQ = scale sum_j dS_ij K_j (+ dO M^T when mt_rows is given: the inter-frame
+// branch with M = Phi_q S, bf16 row-major [e][v]). One workgroup of 4 waves
+// per 128 queries; wave w accumulates dQ^T for queries 32 w.. (lane = query,
+// registers = features), key and value tiles staged in LDS.
+__global__ void __launch_bounds__(256)
+attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+               const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+               const float* __restrict__ lse2, const float* __restrict__ dsum,
+               const __bf16* __restrict__ m_rows, __bf16* __restrict__ dq, int T, float c,
+               float scale, int n_qblk, int accumulate) {
+  __shared__ __attribute__((aligned(16))) char lk[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lv[AB_STAGE * 256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long g = blockIdx.x / n_qblk;
+  const int i = (blockIdx.x % n_qblk) * 128 + 32 * wave + n;
+  const size_t gbase = (size_t)g * T;
+  const size_t qrow = gbase + min(i, T - 1);
+  bf16x8 qb[8], ob[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    qb[kc] = ld8(q + qrow * HD + 16 * kc + 8 * h2);
+    ob[kc] = ld8(d_o + qrow * HD + 16 * kc + 8 * h2);
+  }
+  const float li = lse2[qrow], di = dsum[qrow];
+  f32x16 dacc[4] = {zero16(), zero16(), zero16(), zero16()};
+  for (int j0 = 0; j0 < T; j0 += AB_STAGE) {
+    const int valid = min(AB_STAGE, T - j0);
+    stage_tr(lk, k + (gbase + j0) * HD, AB_STAGE, valid);
+    stage_tr(lv, v + (gbase + j0) * HD, AB_STAGE, valid);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < AB_STAGE / 32; ++sub) {
+      f32x16 st = zero16(), dp = zero16();
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        st = mfma32(row_op_v(lk, 32 * sub + n, kc, h2), qb[kc], st);
+        dp = mfma32(row_op_v(lv, 32 * sub + n, kc, h2), ob[kc], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const float p = j < T ? exp2f(st[r] * c - li) : 0.f;
+        ds[r] = p * (dp[r] - di);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const bf16x8 b = acc_op(ds, kc);
+#pragma unroll
+        for (int te = 0; te < 4; ++te)
+          dacc[te] = mfma32(tr_op_acc(lk, 32 * sub + 16 * kc, 32 * te, lane), b, dacc[te]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int te = 0; te < 4; ++te) dacc[te] *= scale;
+  if (m_rows) {
+    const __bf16* mg = m_rows + (size_t)g * HD * HD;
+#pragma unroll
+    for (int te = 0; te < 4; ++te) {
+      const __bf16* mr = mg + (size_t)(32 * te + n) * HD + 8 * h2;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) dacc[te] = mfma32(ld8(mr + 16 * kc), ob[kc], dacc[te]);
+    }
+  }
+  if (i < T) {
+    __bf16* out = dq + (gbase + i) * HD;
+#pragma unroll
+    for (int te = 0; te < 4; ++te) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4* p4 = reinterpret_cast<bf16x4*>(out + 32 * te + 8 * rg + 4 * h2);
+        bf16x4 w, old;
+        if (accumulate) old = *p4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          w[u] = (__bf16)(dacc[te][4 * rg + u] + (accumulate ? (float)old[u] : 0.f));
+        *p4 = w;
+      }
+    }
+  }
+}
+
+// dK = scale sum_i dS_ij Q_i and dV = sum_i P_ij dO_i. One workgroup of 4
+// waves per 128 keys; wave w holds keys 32 w.. as the columns of S = Q K^T and
+// accumulates dK^T and dV^T (lane = key, registers = features); query, dO,
+// lse2 and dsum tiles staged in LDS.
+__global__ void __launch_bounds__(256)
+attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                 const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+                 const float* __restrict__ lse2, const float* __restrict__ dsum,
+                 __bf16* __restrict__ dk, __bf16* __restrict__ dv, int T, float c, float scale,
+                 int n_kblk, int accumulate) {
+  __shared__ __attribute__((aligned(16))) char lq[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lo[AB_STAGE * 256];
+  __shared__ float ll[AB_STAGE], ld[AB_STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long g = blockIdx.x / n_kblk;
+  const int j = (blockIdx.x % n_kblk) * 128 + 32 * wave + n;     // this lane's key
+  const size_t gbase = (size_t)g * T;
+  const size_t krow = gbase + min(j, T - 1);
+  bf16x8 kb[8], vb[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    kb[kc] = ld8(k + krow * HD + 16 * kc + 8 * h2);
+    vb[kc] = ld8(v + krow * HD + 16 * kc + 8 * h2);
+  }
+  f32x16 kacc[4] = {zero16(), zero16(), zero16(), zero16()};
+  f32x16 vacc[4] = {zero16(), zero16(), zero16(), zero16()};
+  const bool key_ok = j < T;
+  for (int i0 = 0; i0 < T; i0 += AB_STAGE) {
+    const int valid = min(AB_STAGE, T - i0);
+    stage_tr(lq, q + (gbase + i0) * HD, AB_STAGE, valid);
+    stage_tr(lo, d_o + (gbase + i0) * HD, AB_STAGE, valid);
+    if (threadIdx.x < AB_STAGE) {
+      const int t = threadIdx.x;
+      ll[t] = t < valid ? lse2[gbase + i0 + t] : 0.f;
+      ld[t] = t < valid ? dsum[gbase + i0 + t] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < AB_STAGE / 32; ++sub) {
+      f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        sc = mfma32(row_op_v(lq, 32 * sub + n, kc, h2), kb[kc], sc);
+        dp = mfma32(row_op_v(lo, 32 * sub + n, kc, h2), vb[kc], dp);
+      }
+      float pv[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const float p = (key_ok && i0 + il < T) ? exp2f(sc[r] * c - ll[il]) : 0.f;
+        pv[r] = p;
+        ds[r] = p * (dp[r] - ld[il]);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const bf16x8 pb = acc_op(pv, kc), db = acc_op(ds, kc);
+#pragma unroll
+        for (int te = 0; te < 4; ++te) {
+          vacc[te] = mfma32(tr_op_acc(lo, 32 * sub + 16 * kc, 32 * te, lane), pb, vacc[te]);
+          kacc[te] = mfma32(tr_op_acc(lq, 32 * sub + 16 * kc, 32 * te, lane), db, kacc[te]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (key_ok) {
+    __bf16* ok = dk + (gbase + j) * HD;
+    __bf16* ov = dv + (gbase + j) * HD;
+#pragma unroll
+    for (int te = 0; te < 4; ++te) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4* pk = reinterpret_cast<bf16x4*>(ok + 32 * te + 8 * rg + 4 * h2);
+        bf16x4* pv4 = reinterpret_cast<bf16x4*>(ov + 32 * te + 8 * rg + 4 * h2);
+        bf16x4 wk, wv, okd, ovd;
+        if (accumulate) {
+          okd = *pk;
+          ovd = *pv4;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wk[u] = (__bf16)(scale * kacc[te][4 * rg + u] + (accumulate ? (float)okd[u] : 0.f));
+          wv[u] = (__bf16)(vacc[te][4 * rg + u] + (accumulate ? (float)ovd[u] : 0.f));
+        }
+        *pk = wk;
+        *pv4 = wv;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// ===========================================================================
+// Host side
+// ===========================================================================
+namespace {
+
+inline unsigned blocks(long n, int per) { return (unsigned)((n + per - 1) / per); }
+
+Epi make_epi(const void* z, bool z_f32, float* y32, void* yx, bool accumulate) {
+  Epi e;
+  e.z = z;
+  e.z_f32 = z_f32 ? 1 : 0;
+  e.y32 = y32;
+  e.yx = yx;
+  e.accumulate = accumulate ? 1 : 0;
+  return e;
+}
+
+// Y = X B^T per g over n_g = B*H matrices of `rows` rows; bt_trans (float32
+// only) reads B^T from a row-major B instead.
+hipError_t nt_gemm(const Dims& d, const void* x, int rows, bool x_per_head, const void* bt,
+                   bool bt_per_head, bool bt_trans, const Epi& ep, hipStream_t s) {
+  const long n_g = (long)d.B * d.H;
+  if (use_mfma(d)) {
+    if (bt_trans) return hipErrorInvalidValue;
+    const int n_rblk = (rows + 127) / 128;
+    nt_gemm_mfma_k<<<(unsigned)(n_g * n_rblk), 256, 0, s>>>(
+        static_cast<const __bf16*>(x), static_cast<const __bf16*>(bt), ep, rows, d.H,
+        x_per_head ? 1 : 0, bt_per_head ? 1 : 0, n_rblk);
+  } else {
+    const long n_out = n_g * rows * d.D;
+    nt_gemm_f32_k<<<blocks(n_out, 256), 256, 0, s>>>(
+        static_cast<const float*>(x), static_cast<const float*>(bt), ep, rows, d.D, d.H,
+        x_per_head ? 1 : 0, bt_per_head ? 1 : 0, bt_trans ? 1 : 0, n_out);
+  }
+  return hipGetLastError();
+}
+
+size_t xty_ws_bytes(const Dims& d) {
+  if (!use_mfma(d)) return 0;
+  const long nch = (d.T + XTY_CHUNK - 1) / XTY_CHUNK;
+  return (size_t)d.B * d.H * nch * HD * HD * sizeof(float);
+}
+
+// out (+)= gamma * base + delta * sum_t X^T Y, per (b, h) or summed over b
+// into per-head outputs.
+hipError_t xty(const Dims& d, const void* x, const void* y, float* out, bool sum_b,
+               const float* base_mat, const float* gamma, float delta, bool accumulate, void* ws,
+               hipStream_t s) {
+  const long n_go = sum_b ? d.H : (long)d.B * d.H;
+  if (use_mfma(d)) {
+    const int nch = (d.T + XTY_CHUNK - 1) / XTY_CHUNK;
+    float* part = static_cast<float*>(ws);
+    xty_part_mfma_k<<<(unsigned)((long)d.B * d.H * nch), 256, 0, s>>>(
+        static_cast<const __bf16*>(x), static_cast<const __bf16*>(y), part, d.T, nch);
+    const long n_thr = n_go * 1024;
+    xty_reduce_mfma_k<<<blocks(n_thr, 256), 256, 0, s>>>(part, out, base_mat, gamma, delta,
+                                                         accumulate ? 1 : 0, nch, d.B, d.H,
+                                                         sum_b ? 1 : 0, n_thr);
+  } else {
+    const long n_out = n_go * d.D * d.D;
+    xty_f32_k<<<blocks(n_out, 256), 256, 0, s>>>(
+        static_cast<const float*>(x), static_cast<const float*>(y), out, base_mat, gamma, delta,
+        accumulate ? 1 : 0, d.T, d.D, d.B, d.H, sum_b ? 1 : 0, n_out);
+  }
+  return hipGetLastError();
+}
+
+// Scratch carved from the caller's workspace in a fixed order; with a null
+// base it only measures.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <typename P>
+  P* take(size_t bytes) {
+    off = round_up(off, 256);
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+size_t act_elem(const Dims& d) { return d.bf16 ? 2 : 4; }
+size_t mat_count(const Dims& d) { return (size_t)d.B * d.H * d.D * d.D; }
+size_t row_count(const Dims& d) { return (size_t)d.B * d.H * d.T; }
+
+hipError_t feature_map_any(const Dims& d, const void* x, const void* phi, void* out, bool norm,
+                           hipStream_t s) {
+  return use_mfma(d) ? mfma_feature_map(d, x, phi, out, norm, s)
+                     : generic_feature_map(d, x, phi, out, norm, s);
+}
+
+// lse, dsum, then dQ (with the inter term dO M^T on bf16 shapes when m_rows is
+// given), dK and dV.
+hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, const void* v,
+                               const void* o_intra, const void* d_o, void* dq, void* dk, void* dv,
+                               const void* m_rows, bool accumulate, Carve& c, hipStream_t s) {
+  const long n_rows = (long)row_count(d);
+  float* lse = c.take<float>(n_rows * sizeof(float));
+  float* dsum = c.take<float>(n_rows * sizeof(float));
+  if (!c.base) return hipSuccess;
+  const int acc = accumulate ? 1 : 0;
+  if (use_mfma(d)) {
+    const float cl = d.scale * kLog2e;
+    const int nb = (d.T + 127) / 128;
+    const unsigned grid = (unsigned)((long)d.B * d.H * nb);
+    const __bf16* qb = static_cast<const __bf16*>(q);
+    const __bf16* kb = static_cast<const __bf16*>(k);
+    const __bf16* vb = static_cast<const __bf16*>(v);
+    const __bf16* ob = static_cast<const __bf16*>(d_o);
+    attn_pre_mfma_k<<<grid, 256, 0, s>>>(qb, kb, static_cast<const __bf16*>(o_intra), ob, lse,
+                                         dsum, d.T, cl, nb);
+    attn_dq_mfma_k<<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum,
+                                        static_cast<const __bf16*>(m_rows),
+                                        static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
+    attn_dkdv_mfma_k<<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum, static_cast<__bf16*>(dk),
+                                          static_cast<__bf16*>(dv), d.T, cl, d.scale, nb, acc);
+  } else {
+    const float* qf = static_cast<const float*>(q);
+    const float* kf = static_cast<const float*>(k);
+    const float* vf = static_cast<const float*>(v);
+    const float* of = static_cast<const float*>(d_o);
+    const long n_el = n_rows * d.D;
+    attn_pre_f32_k<<<blocks(n_rows, 128), 128, 0, s>>>(qf, kf, static_cast<const float*>(o_intra),
+                                                       of, lse, dsum, d.T, d.D, d.scale, n_rows);
+    attn_dq_f32_k<<<blocks(n_el, 128), 128, 0, s>>>(qf, kf, vf, of, lse, dsum,
+                                                    static_cast<float*>(dq), d.T, d.D, d.scale,
+                                                    acc, n_el);
+    attn_dkdv_f32_k<<<blocks(n_el, 128), 128, 0, s>>>(qf, kf, vf, of, lse, dsum,
+                                                      static_cast<float*>(dk),
+                                                      static_cast<float*>(dv), d.T, d.D, d.scale,
+                                                      acc, n_el);
+  }
+  return hipGetLastError();
+}
+
+hipError_t read_backward_steps(const Dims& d, const void* q, const void* k, const void* v,
+                               const void* phi_q, const float* S, const void* o_intra,
+                               const void* d_o, void* dq, void* dk, void* dv, float* dphi_q,
+                               float* dS, bool accumulate, Carve& c, hipStream_t s) {
+  const size_t ab = act_bytes(d);
+  const bool mf = use_mfma(d);
+  __bf16* Sb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
+  __bf16* Stb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
+  void* Mm = c.take<char>(mat_count(d) * (mf ? 2 : 4));     // M = Phi_q S per (b, h)
+  void* qp = c.take<char>(ab);
+  void* dqp = c.take<char>(ab);
+  void* part = c.take<char>(xty_ws_bytes(d));
+  hipError_t e;
+  if (c.base) {
+    if (mf) {
+      to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(S, Sb, Stb, (long)mat_count(d));
+      // M[e][v] = sum_d Phi_q[e][d] S[d][v]: rows of Phi_q against S^T
+      e = nt_gemm(d, phi_q, HD, true, Stb, false, false, make_epi(nullptr, false, nullptr, Mm, false), s);
+    } else {
+      e = nt_gemm(d, phi_q, d.D, true, S, false, true,
+                  make_epi(nullptr, false, static_cast<float*>(Mm), nullptr, false), s);
+    }
+    if (e != hipSuccess) return e;
+  }
+  e = attn_backward_steps(d, q, k, v, o_intra, d_o, dq, dk, dv, mf ? Mm : nullptr, accumulate, c, s);
+  if (e != hipSuccess || !c.base) return e;
+  if (!mf) {
+    // dQ += dO M^T
+    e = nt_gemm(d, d_o, d.T, false, Mm, false, false, make_epi(nullptr, false, nullptr, dq, true), s);
+    if (e != hipSuccess) return e;
+  }
+  // dS (+)= Q'^T dO
+  if ((e = feature_map_any(d, q, phi_q, qp, false, s)) != hipSuccess) return e;
+  if ((e = xty(d, qp, d_o, dS, false, nullptr, nullptr, 1.f, accumulate, part, s)) != hipSuccess)
+    return e;
+  // dQ' = dO S^T, dPhi_q (+)= sum_b Q^T dQ'
+  e = nt_gemm(d, d_o, d.T, false, mf ? (const void*)Sb : (const void*)S, false, false,
+              make_epi(nullptr, false, nullptr, dqp, false), s);
+  if (e != hipSuccess) return e;
+  return xty(d, q, dqp, dphi_q, true, nullptr, nullptr, 1.f, accumulate, part, s);
+}
+
+hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, const void* phi_k,
+                                 const void* phi_v, const float* beta, const float* alpha,
+                                 const float* S, const float* G, void* dk, void* dv,
+                                 float* dphi_k, float* dphi_v, float* dbeta, float* dalpha,
+                                 float* dS_prev, bool accumulate, Carve& c, hipStream_t s) {
+  const size_t ab = act_bytes(d);
+  const size_t fb = row_count(d) * d.D * sizeof(float);
+  const bool mf = use_mfma(d);
+  void* kt = c.take<char>(ab);            // K Phi_k
+  void* kp = c.take<char>(ab);            // K'
+  float* nrm = c.take<float>(row_count(d) * sizeof(float));
+  void* vp = c.take<char>(ab);            // V'
+  float* r32 = c.take<float>(fb);         // R = V' - K'S
+  void* rx = c.take<char>(ab);
+  float* kg32 = c.take<float>(fb);        // K'G
+  void* kgx = c.take<char>(ab);
+  void* dvx = c.take<char>(ab);           // dV'
+  float* dkr = c.take<float>(fb);         // R G^T - K'G S^T
+  void* dktx = c.take<char>(ab);          // dK~
+  __bf16* Sb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
+  __bf16* Stb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
+  __bf16* Gb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
+  __bf16* Gtb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
+  void* part = c.take<char>(xty_ws_bytes(d));
+  if (!c.base) return hipSuccess;
+  const long n_rows = (long)row_count(d);
+  const int acc = accumulate ? 1 : 0;
+  hipError_t e;
+  if ((e = feature_map_any(d, k, phi_k, kt, false, s)) != hipSuccess) return e;
+  if ((e = feature_map_any(d, v, phi_v, vp, false, s)) != hipSuccess) return e;
+  if (mf) {
+    rownorm_k<__bf16><<<blocks(n_rows, 128), 128, 0, s>>>(static_cast<const __bf16*>(kt),
+                                                          static_cast<__bf16*>(kp), nrm, d.D, n_rows);
+    to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(S, Sb, Stb, (long)mat_count(d));
+    to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(G, Gb, Gtb, (long)mat_count(d));
+  } else {
+    rownorm_k<float><<<blocks(n_rows, 128), 128, 0, s>>>(static_cast<const float*>(kt),
+                                                         static_cast<float*>(kp), nrm, d.D, n_rows);
+  }
+  // R = V' - K' S ;  K'G
+  const void* bS_t = mf ? (const void*)Stb : (const void*)S;
+  const void* bG_t = mf ? (const void*)Gtb : (const void*)G;
+  e = nt_gemm(d, kp, d.T, false, bS_t, false, !mf, make_epi(vp, false, r32, rx, false), s);
+  if (e != hipSuccess) return e;
+  e = nt_gemm(d, kp, d.T, false, bG_t, false, !mf, make_epi(nullptr, false, kg32, kgx, false), s);
+  if (e != hipSuccess) return e;
+  // dbeta, dV' = beta K'G
+  if (mf)
+    commit_rows1_k<__bf16><<<blocks(n_rows, 128), 128, 0, s>>>(kg32, r32, beta, dbeta,
+                                                               static_cast<__bf16*>(dvx), d.D, acc,
+                                                               n_rows);
+  else
+    commit_rows1_k<float><<<blocks(n_rows, 128), 128, 0, s>>>(kg32, r32, beta, dbeta,
+                                                              static_cast<float*>(dvx), d.D, acc,
+                                                              n_rows);
+  // dKraw = R G^T - K'G S^T
+  const void* bG = mf ? (const void*)Gb : (const void*)G;
+  const void* bS = mf ? (const void*)Sb : (const void*)S;
+  e = nt_gemm(d, rx, d.T, false, bG, false, false, make_epi(nullptr, false, dkr, nullptr, false), s);
+  if (e != hipSuccess) return e;
+  e = nt_gemm(d, kgx, d.T, false, bS, false, false, make_epi(dkr, true, dkr, nullptr, false), s);
+  if (e != hipSuccess) return e;
+  // dK~ through beta and the row normalisation
+  if (mf)
+    commit_rows2_k<__bf16><<<blocks(n_rows, 128), 128, 0, s>>>(
+        dkr, static_cast<const __bf16*>(kp), nrm, beta, static_cast<__bf16*>(dktx), d.D, n_rows);
+  else
+    commit_rows2_k<float><<<blocks(n_rows, 128), 128, 0, s>>>(
+        dkr, static_cast<const float*>(kp), nrm, beta, static_cast<float*>(dktx), d.D, n_rows);
+  // dK = dK~ Phi_k^T, dV = dV' Phi_v^T
+  e = nt_gemm(d, dktx, d.T, false, phi_k, true, false, make_epi(nullptr, false, nullptr, dk, accumulate), s);
+  if (e != hipSuccess) return e;
+  e = nt_gemm(d, dvx, d.T, false, phi_v, true, false, make_epi(nullptr, false, nullptr, dv, accumulate), s);
+  if (e != hipSuccess) return e;
+  // dPhi_k = sum_b K^T dK~, dPhi_v = sum_b V^T dV'
+  if ((e = xty(d, k, dktx, dphi_k, true, nullptr, nullptr, 1.f, accumulate, part, s)) != hipSuccess)
+    return e;
+  if ((e = xty(d, v, dvx, dphi_v, true, nullptr, nullptr, 1.f, accumulate, part, s)) != hipSuccess)
+    return e;
+  // dS_prev = alpha G - K'^T dV'
+  if ((e = xty(d, kp, dvx, dS_prev, false, G, alpha, -1.f, accumulate, part, s)) != hipSuccess)
+    return e;
+  dalpha_k<<<(unsigned)((long)d.B * d.H), 256, 0, s>>>(S, G, dalpha, d.D * d.D, acc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_backward_ws_bytes(const Dims& d) {
+  Carve c(nullptr);
+  (void)attn_backward_steps(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, false, c, nullptr);
+  return c.off;
+}
+size_t read_backward_ws_bytes(const Dims& d) {
+  Carve c(nullptr);
+  (void)read_backward_steps(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, false, c, nullptr);
+  return c.off;
+}
+size_t commit_backward_ws_bytes(const Dims& d) {
+  Carve c(nullptr);
+  (void)commit_backward_steps(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false, c,
+                        nullptr);
+  return c.off;
+}
+
+hipError_t attn_backward(const Dims& d, const void* q, const void* k, const void* v,
+                         const void* o_intra, const void* d_o, void* dq, void* dk, void* dv,
+                         bool accumulate, void* ws, hipStream_t s) {
+  Carve c(ws);
+  return attn_backward_steps(d, q, k, v, o_intra, d_o, dq, dk, dv, nullptr, accumulate, c, s);
+}
+
+hipError_t read_backward(const Dims& d, const void* q, const void* k, const void* v,
+                         const void* phi_q, const float* S, const void* o_intra, const void* d_o,
+                         void* dq, void* dk, void* dv, float* dphi_q, float* dS, bool accumulate,
+                         void* ws, hipStream_t s) {
+  Carve c(ws);
+  return read_backward_steps(d, q, k, v, phi_q, S, o_intra, d_o, dq, dk, dv, dphi_q, dS,
+                             accumulate, c, s);
+}
+
+hipError_t commit_backward(const Dims& d, const void* k, const void* v, const void* phi_k,
+                           const void* phi_v, const float* beta, const float* alpha,
+                           const float* S_prev, const float* dS_next, void* dk, void* dv,
+                           float* dphi_k, float* dphi_v, float* dbeta, float* dalpha,
+                           float* dS_prev, bool accumulate, void* ws, hipStream_t s) {
+  Carve c(ws);
+  return commit_backward_steps(d, k, v, phi_k, phi_v, beta, alpha, S_prev, dS_next, dk, dv,
+                               dphi_k, dphi_v, dbeta, dalpha, dS_prev, accumulate, c, s);
+}
+
+hipError_t copy_state(const float* src, float* dst, size_t n, hipStream_t s) {
+  copy_f32_k<<<blocks((long)n, 256), 256, 0, s>>>(src, dst, (long)n);
+  return hipGetLastError();
+}
+
+}  // namespace arl2

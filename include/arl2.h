@@ -89,7 +89,10 @@ typedef enum arl2_op {
   ARL2_OP_STATE_COMMIT = 3,
   ARL2_OP_READ_PREPARED = 4,
   ARL2_OP_CLEAN_PASS_PREPARED = 5,
-  ARL2_OP_TOKEN_LEVEL = 6
+  ARL2_OP_TOKEN_LEVEL = 6,
+  ARL2_OP_INTRA_ATTN_BACKWARD = 7,
+  ARL2_OP_READ_BACKWARD = 8,
+  ARL2_OP_COMMIT_BACKWARD = 9
 } arl2_op;
 
 /* ------------------------------------------------------------------------
@@ -253,6 +256,71 @@ arl2_status arl2_token_clean_pass(const arl2_shape* shape, const void* q,
                                   float* S_next, void* o, void* o_intra,
                                   void* o_inter, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * Training side. The summary's two-stage distillation (§2.3) fine-tunes the
+ * hybrid model end to end and prints no backward pass; these calls compute
+ * the exact derivatives of the forward step defined above.
+ *   Gradient outputs: activation gradients act_dtype [B,H,T,D]; map gradients
+ *   float32 [H,D,D], summed over the B videos and the tokens; state gradients
+ *   float32 [B,H,D,D]; dbeta float32 [B,H,T]; dalpha float32 [B,H].
+ *   accumulate != 0 adds every gradient to what its output holds (so passes
+ *   and frames sum in place); 0 overwrites. Outputs must not overlap each
+ *   other, the inputs or the workspace. Reductions run in a fixed order:
+ *   identical inputs give bit-identical gradients.
+ * ------------------------------------------------------------------------ */
+
+/* Backward of the intra-frame softmax (arl2_intra_attn): from the forward's
+ * o_intra and d_o = dL/dO_intra,
+ *   P = softmax(Q K^T * scale), dV = P^T dO, dP = dO V^T,
+ *   dZ = P * (dP - rowsum(dO * O_intra)), dQ = scale dZ K, dK = scale dZ^T Q.
+ * Needs arl2_workspace_bytes(shape, ARL2_OP_INTRA_ATTN_BACKWARD). */
+arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q,
+                                     const void* k, const void* v,
+                                     const void* o_intra, const void* d_o,
+                                     void* dq, void* dk, void* dv,
+                                     int32_t accumulate, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* Backward of a read, O = softmax(Q K^T * scale) V + (Q Phi_q) S, from the
+ * read's o_intra and d_o = dL/dO: dq, dk, dv, dphi_q and dS, with
+ *   dQ += dO (Phi_q S)^T, dS = (Q Phi_q)^T dO, dPhi_q = sum_b Q^T dO S^T.
+ * Needs arl2_workspace_bytes(shape, ARL2_OP_READ_BACKWARD). */
+arl2_status arl2_read_backward(const arl2_shape* shape, const void* q,
+                               const void* k, const void* v, const void* phi_q,
+                               const float* S, const void* o_intra,
+                               const void* d_o, void* dq, void* dk, void* dv,
+                               float* dphi_q, float* dS, int32_t accumulate,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the commit (arl2_commit) from dS_next = dL/dS_next = G, with
+ * K' = rownorm(K Phi_k), V' = V Phi_v, R = V' - K' S_prev:
+ *   dalpha = <S_prev, G>, dS_prev = alpha G - K'^T diag(beta) K' G,
+ *   dbeta = rowsum((K' G) * R), dV' = diag(beta) K' G,
+ *   dK' = diag(beta) (R G^T - K' G S_prev^T),
+ * then through the row normalisation and the maps (dK, dV, dPhi_k, dPhi_v).
+ * Needs arl2_workspace_bytes(shape, ARL2_OP_COMMIT_BACKWARD). */
+arl2_status arl2_commit_backward(const arl2_shape* shape, const void* k,
+                                 const void* v, const void* phi_k,
+                                 const void* phi_v, const float* beta,
+                                 const float* alpha, const float* S_prev,
+                                 const float* dS_next, void* dk, void* dv,
+                                 float* dphi_k, float* dphi_v, float* dbeta,
+                                 float* dalpha, float* dS_prev,
+                                 int32_t accumulate, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Clean-state scan (the clean states ahead of the reads, as training with
+ * clean frames needs them): the states S_0..S_F that n_frames frames' clean
+ * passes commit, arl2_commit frame after frame, no reads. k, v:
+ * [n_frames,B,H,T,D] act_dtype; beta [n_frames,B,H,T]; alpha [n_frames,B,H];
+ * S0 [B,H,D,D]; states [n_frames+1,B,H,D,D] float32 receives S0 then every
+ * committed state. Needs arl2_workspace_bytes(shape, ARL2_OP_COMMIT). */
+arl2_status arl2_state_scan(const arl2_shape* shape, int32_t n_frames,
+                            const void* k, const void* v, const void* phi_k,
+                            const void* phi_v, const float* beta,
+                            const float* alpha, const float* S0, float* states,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Comparator: the cross-frame softmax over a growing KV cache that the

@@ -132,6 +132,18 @@ def test_alias_and_workspace_errors(arl2):
                tneed - 1, None) == 6
     assert _st(arl2, "arl2_token_read", cs(s), A, A, A, A, A, A, A, S1, A, None, None, WS, tneed,
                None) == 5
+    # training side: workspace short, dS_prev over dS_next, outputs overlapping
+    cb = arl2.workspace_bytes(s, arl2.OP_COMMIT_BACKWARD)
+    assert _st(arl2, "arl2_commit_backward", cs(s), A, A, A, A, A, A, S1, S2, B, B + (2 << 20),
+               B + (4 << 20), B + (5 << 20), B + (6 << 20), B + (7 << 20), S2, 0, WS, cb - 1,
+               None) == 6
+    assert _st(arl2, "arl2_commit_backward", cs(s), A, A, A, A, A, A, S1, S2, B, B + (2 << 20),
+               B + (4 << 20), B + (5 << 20), B + (6 << 20), B + (7 << 20), S2, 0, WS, cb,
+               None) == 5
+    rb = arl2.workspace_bytes(s, arl2.OP_READ_BACKWARD)
+    assert _st(arl2, "arl2_read_backward", cs(s), A, A, A, A, S1, A, A, B, B, B + (4 << 20),
+               B + (6 << 20), S2, 0, WS, rb, None) == 5
+    assert _st(arl2, "arl2_state_scan", cs(s), 0, A, A, A, A, A, A, S1, S2, WS, need, None) == 2
     # fullkv: n_kv beyond capacity
     assert _st(arl2, "arl2_fullkv_attn", cs(s), A, B, S1, 200, 100, WS, None) == 2
 
