@@ -16,6 +16,8 @@
 //             recomputing the scores, so no accumulation crosses workgroups.
 #include <math.h>
 
+#include <algorithm>
+
 #include "arl2_internal.h"
 #include "mfma_common.h"
 
@@ -194,77 +196,98 @@ __global__ void attn_dkdv_f32_k(const float* __restrict__ q, const float* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Row kernels (either activation type; one thread per row)
+// Row kernels (either activation type): one wave per row, lane l holding
+// elements l and l + 64 (D <= 128), 4 rows per workgroup of 256.
 // ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
 
 // out = x / max(||x||, floor) and the raw norm
 template <typename Tx>
-__global__ void rownorm_k(const Tx* __restrict__ x, Tx* __restrict__ out, float* __restrict__ nrm,
-                          int D, long n_rows) {
-  const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void __launch_bounds__(256)
+rownorm_k(const Tx* __restrict__ x, Tx* __restrict__ out, float* __restrict__ nrm, int D,
+          long n_rows) {
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
   if (r >= n_rows) return;
-  float ss = 0.f;
-  for (int e = 0; e < D; ++e) {
-    const float a = ldf(x, r * D + e);
-    ss = fmaf(a, a, ss);
-  }
-  const float n = sqrtf(ss);
+  const bool h0 = l < D, h1 = l + 64 < D;
+  const float a0 = h0 ? ldf(x, r * D + l) : 0.f, a1 = h1 ? ldf(x, r * D + l + 64) : 0.f;
+  const float n = sqrtf(wave_sum(a0 * a0 + a1 * a1));
   const float inv = 1.f / fmaxf(n, kNormFloor);
-  for (int e = 0; e < D; ++e) stf(out, r * D + e, ldf(x, r * D + e) * inv);
-  nrm[r] = n;
+  if (h0) stf(out, r * D + l, a0 * inv);
+  if (h1) stf(out, r * D + l + 64, a1 * inv);
+  if (l == 0) nrm[r] = n;
 }
 
 // dbeta_t (+)= sum_v KG[t][v] R[t][v];  dV'[t][v] = beta_t KG[t][v]
 template <typename Tx>
-__global__ void commit_rows1_k(const float* __restrict__ kg, const float* __restrict__ rr,
-                               const float* __restrict__ beta, float* __restrict__ dbeta,
-                               Tx* __restrict__ dvp, int D, int accumulate, long n_rows) {
-  const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void __launch_bounds__(256)
+commit_rows1_k(const float* __restrict__ kg, const float* __restrict__ rr,
+               const float* __restrict__ beta, float* __restrict__ dbeta, Tx* __restrict__ dvp,
+               int D, int accumulate, long n_rows) {
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
   if (r >= n_rows) return;
-  float acc = 0.f;
+  const bool h0 = l < D, h1 = l + 64 < D;
   const float b = beta[r];
-  for (int e = 0; e < D; ++e) {
-    const float x = kg[r * D + e];
-    acc = fmaf(x, rr[r * D + e], acc);
-    stf(dvp, r * D + e, b * x);
-  }
-  dbeta[r] = accumulate ? dbeta[r] + acc : acc;
+  const float x0 = h0 ? kg[r * D + l] : 0.f, x1 = h1 ? kg[r * D + l + 64] : 0.f;
+  const float y0 = h0 ? rr[r * D + l] : 0.f, y1 = h1 ? rr[r * D + l + 64] : 0.f;
+  const float acc = wave_sum(x0 * y0 + x1 * y1);
+  if (h0) stf(dvp, r * D + l, b * x0);
+  if (h1) stf(dvp, r * D + l + 64, b * x1);
+  if (l == 0) dbeta[r] = accumulate ? dbeta[r] + acc : acc;
 }
 
 // dK~ = (dK' - K' (K'.dK')) / n with dK' = beta_t dKraw (dK' / floor below it)
 template <typename Tx>
-__global__ void commit_rows2_k(const float* __restrict__ dkraw, const Tx* __restrict__ kp,
-                               const float* __restrict__ nrm, const float* __restrict__ beta,
-                               Tx* __restrict__ dkt, int D, long n_rows) {
-  const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void __launch_bounds__(256)
+commit_rows2_k(const float* __restrict__ dkraw, const Tx* __restrict__ kp,
+               const float* __restrict__ nrm, const float* __restrict__ beta,
+               Tx* __restrict__ dkt, int D, long n_rows) {
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
   if (r >= n_rows) return;
+  const bool h0 = l < D, h1 = l + 64 < D;
   const float b = beta[r], n = nrm[r];
-  if (n > kNormFloor) {
-    float dot = 0.f;
-    for (int e = 0; e < D; ++e) dot = fmaf(ldf(kp, r * D + e), dkraw[r * D + e], dot);
-    const float inv = 1.f / n;
-    for (int e = 0; e < D; ++e)
-      stf(dkt, r * D + e, b * (dkraw[r * D + e] - ldf(kp, r * D + e) * dot) * inv);
-  } else {
-    for (int e = 0; e < D; ++e) stf(dkt, r * D + e, b * dkraw[r * D + e] / kNormFloor);
-  }
+  const float d0 = h0 ? dkraw[r * D + l] : 0.f, d1 = h1 ? dkraw[r * D + l + 64] : 0.f;
+  const float k0 = h0 ? ldf(kp, r * D + l) : 0.f, k1 = h1 ? ldf(kp, r * D + l + 64) : 0.f;
+  const float dot = wave_sum(k0 * d0 + k1 * d1);
+  const bool above = n > kNormFloor;
+  const float inv = above ? 1.f / n : 1.f / kNormFloor;
+  const float pr = above ? dot : 0.f;
+  if (h0) stf(dkt, r * D + l, b * (d0 - k0 * pr) * inv);
+  if (h1) stf(dkt, r * D + l + 64, b * (d1 - k1 * pr) * inv);
 }
 
 // dalpha[g] (+)= <S[g], G[g]>  (one workgroup of 256 per (b, h), fixed order)
 __global__ void __launch_bounds__(256)
 dalpha_k(const float* __restrict__ S, const float* __restrict__ G, float* __restrict__ dalpha,
          int DD, int accumulate) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   const long g = blockIdx.x;
-  float acc = 0.f;
-  for (int i = threadIdx.x; i < DD; i += 256) acc = fmaf(S[g * DD + i], G[g * DD + i], acc);
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = threadIdx.x * 4; i < DD; i += 256 * 4 * 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = i + u * 256 * 4;
+      if (j < DD) {
+        const float4 a = *reinterpret_cast<const float4*>(S + g * DD + j);
+        const float4 c = *reinterpret_cast<const float4*>(G + g * DD + j);
+        acc[u] = fmaf(a.x, c.x, fmaf(a.y, c.y, fmaf(a.z, c.z, fmaf(a.w, c.w, acc[u]))));
+      }
+    }
   }
-  if (threadIdx.x == 0) dalpha[g] = accumulate ? dalpha[g] + red[0] : red[0];
+  const float w = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float t = (red[0] + red[1]) + (red[2] + red[3]);
+    dalpha[g] = accumulate ? dalpha[g] + t : t;
+  }
 }
 
 // bf16 copies of a float [n][128][128] matrix set, row-major and transposed
@@ -288,33 +311,33 @@ __global__ void copy_f32_k(const float* __restrict__ a, float* __restrict__ b, l
 // bf16 MFMA building blocks (d = 128)
 // ---------------------------------------------------------------------------
 
-// Y = X Bt^T: one workgroup of 4 waves per 128 rows of one g; wave w computes
-// rows 32w.. against all 128 columns (4 tiles), operands straight from memory
-// (Bt, 32 KB, stays in L2).
+// Y = X Bt^T: one workgroup of 4 waves per 32 rows of one g; wave w computes
+// the 32 x 32 tile of columns 32 w.., operands straight from memory (the rows
+// of X are shared through L1, Bt, 32 KB, stays in L2).
 __global__ void __launch_bounds__(256)
 nt_gemm_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ bt, Epi ep, int rows,
                int H, int x_per_head, int bt_per_head, int n_rblk) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, h2 = lane >> 5;
   const long g = blockIdx.x / n_rblk;
-  const int row0 = (blockIdx.x % n_rblk) * 128 + 32 * wave;
+  const int row0 = (blockIdx.x % n_rblk) * 32;
   const __bf16* xg = x + (x_per_head ? g % H : g) * (long)rows * HD;
   const __bf16* bg = bt + (bt_per_head ? g % H : g) * (long)HD * HD;
   const __bf16* xr = xg + (long)min(row0 + n, rows - 1) * HD + 8 * h2;
-  bf16x8 a[8];
+  const __bf16* br = bg + (long)(32 * wave + n) * HD + 8 * h2;
+  bf16x8 a[8], b[8];
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) a[kc] = ld8(xr + 16 * kc);
+  for (int kc = 0; kc < 8; ++kc) {
+    a[kc] = ld8(xr + 16 * kc);
+    b[kc] = ld8(br + 16 * kc);
+  }
+  f32x16 acc = zero16();
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    const __bf16* br = bg + (long)(32 * tn + n) * HD + 8 * h2;
-    f32x16 acc = zero16();
+  for (int kc = 0; kc < 8; ++kc) acc = mfma32(a[kc], b[kc], acc);
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) acc = mfma32(a[kc], ld8(br + 16 * kc), acc);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-      if (row < rows) epilogue<__bf16>(ep, ((size_t)g * rows + row) * HD + 32 * tn + n, acc[r]);
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+    if (row < rows) epilogue<__bf16>(ep, ((size_t)g * rows + row) * HD + 32 * wave + n, acc[r]);
   }
 }
 
@@ -328,21 +351,20 @@ __device__ __forceinline__ void stage_tr(char* dst, const __bf16* src, int rows,
   }
 }
 
-constexpr int XTY_CHUNK = 256;                // tokens per partial
 constexpr int XTY_SUB = 64;                   // tokens staged at a time
 
-// Partial X^T Y over one chunk of tokens of one g, as 16 tiles of 32 x 32 in
-// MFMA accumulator order: part[(g * nch + ch) * 16 + tile][lane][16].
+// Partial X^T Y over one chunk of `chunk` tokens of one g, as 16 tiles of
+// 32 x 32 in MFMA accumulator order: part[(g * nch + ch) * 16 + tile][lane][16].
 __global__ void __launch_bounds__(256)
 xty_part_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ y,
-                float* __restrict__ part, int T, int nch) {
+                float* __restrict__ part, int T, int chunk, int nch) {
   __shared__ __attribute__((aligned(16))) char lx[XTY_SUB * 256];
   __shared__ __attribute__((aligned(16))) char ly[XTY_SUB * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long g = blockIdx.x / nch;
   const int ch = blockIdx.x % nch;
   f32x16 acc[4] = {zero16(), zero16(), zero16(), zero16()};
-  for (int s0 = ch * XTY_CHUNK; s0 < min(T, (ch + 1) * XTY_CHUNK); s0 += XTY_SUB) {
+  for (int s0 = ch * chunk; s0 < min(T, (ch + 1) * chunk); s0 += XTY_SUB) {
     const int valid = min(XTY_SUB, T - s0);
     stage_tr(lx, x + ((size_t)g * T + s0) * HD, XTY_SUB, valid);
     stage_tr(ly, y + ((size_t)g * T + s0) * HD, XTY_SUB, valid);
@@ -441,6 +463,29 @@ __device__ __forceinline__ bf16x8 acc_op(const float* a, int kc) {
   return r;
 }
 
+// Tiles of 64 rows x 256 bytes move from memory to LDS by buffer-load DMA,
+// two buffers per operand: while a stage computes from one, the next stage's
+// rows land in the other. Wave w moves rows 16 w .. 16 w + 15 as four 1 KB
+// pieces; lane l's 16 bytes land at byte 16 l of its piece, so the lane loads
+// the logical chunk that the swz_v swizzle puts there. Rows past the buffer
+// resource's range (the frame's end) arrive as zeros.
+__device__ __forceinline__ int dma_lane_off(int lane) {
+  return (lane >> 4) * 256 + (((lane & 15) ^ ((lane >> 4) << 2)) << 4);
+}
+
+__device__ __forceinline__ void dma_tile64(char* dst, __amdgpu_buffer_rsrc_t src, int row0,
+                                           int lane_off, int wave) {
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + wave * 4096 + ii * 1024),
+                                             16, lane_off, row0 * 256 + wave * 4096 + ii * 1024,
+                                             0, 0);
+}
+
+// s_waitcnt for the vector-memory counter only: wait until at most n (< 16)
+// of this wave's vector-memory operations are outstanding.
+#define VMCNT_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8))
+
 // Per query row: lse2 = log2 sum_j exp2(c q.k_j) and dsum = dO . O_intra. One
 // workgroup of 4 waves per 128 queries; wave w holds queries 32 w.. as the
 // columns of S^T = K Q^T (a lane's running max and sum cover half the keys;
@@ -449,8 +494,10 @@ __global__ void __launch_bounds__(256)
 attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
                 float* __restrict__ lse2, float* __restrict__ dsum, int T, float c, int n_qblk) {
-  __shared__ __attribute__((aligned(16))) char lk[AB_STAGE * 256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char lk0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lk1[AB_STAGE * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
   const long g = blockIdx.x / n_qblk;
   const int i = (blockIdx.x % n_qblk) * 128 + 32 * wave + n;     // this lane's query
@@ -459,10 +506,11 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   bf16x8 qb[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) qb[kc] = ld8(qr + 16 * kc);
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + gbase * HD, (uint32_t)T * 256);
+  const int loff = dma_lane_off(lane);
+  const int n_st = (T + AB_STAGE - 1) / AB_STAGE;
   float m = -INFINITY, l = 0.f;
-  for (int j0 = 0; j0 < T; j0 += AB_STAGE) {
-    stage_tr(lk, k + (gbase + j0) * HD, AB_STAGE, min(AB_STAGE, T - j0));
-    __syncthreads();
+  auto compute = [&](const char* lk, int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int sub = 0; sub < AB_STAGE / 32; ++sub) {
       f32x16 acc = zero16();
@@ -479,13 +527,28 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       if (mn > -INFINITY) {
         float add = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) add += exp2f(sv[r] - mn);
+        for (int r = 0; r < 16; ++r) add += __builtin_amdgcn_exp2f(sv[r] - mn);
         l = l * exp2f(m - mn) + add;
         m = mn;
       }
     }
-    __syncthreads();
+  };
+  dma_tile64(lk0, rk, 0, loff, wave);
+  for (int st = 0;;) {
+    dma_tile64(lk1, rk, min(st + 1, n_st - 1) * AB_STAGE, loff, wave);
+    VMCNT_WAIT(4);
+    __builtin_amdgcn_s_barrier();
+    compute(lk0, st * AB_STAGE);
+    __builtin_amdgcn_s_barrier();
+    if (++st >= n_st) break;
+    dma_tile64(lk0, rk, min(st + 1, n_st - 1) * AB_STAGE, loff, wave);
+    VMCNT_WAIT(4);
+    __builtin_amdgcn_s_barrier();
+    compute(lk1, st * AB_STAGE);
+    __builtin_amdgcn_s_barrier();
+    if (++st >= n_st) break;
   }
+  VMCNT_WAIT(0);
   const float mo = swap_halves(m), lo = swap_halves(l);
   const float M = fmaxf(m, mo);
   const float L = (m > -INFINITY ? l * exp2f(m - M) : 0.f) + (mo > -INFINITY ? lo * exp2f(mo - M) : 0.f);
@@ -495,9 +558,9 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   float dd = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const bf16x8 a = ld8(dr + 8 * u), b = ld8(orr + 8 * u);
+    const bf16x8 x = ld8(dr + 8 * u), y = ld8(orr + 8 * u);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dd = fmaf((float)a[e], (float)b[e], dd);
+    for (int e = 0; e < 8; ++e) dd = fmaf((float)x[e], (float)y[e], dd);
   }
   dd += swap_halves(dd);
   if (h2 == 0 && i < T) {
@@ -506,7 +569,7 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 }
 
-// dQ = scale sum_j dS_ij K_j (+ dO M^T when mt_rows is given: the inter-frame
+// dQ = scale sum_j dS_ij K_j (+ dO M^T when m_rows is given: the inter-frame
 // branch with M = Phi_q S, bf16 row-major [e][v]). One workgroup of 4 waves
 // per 128 queries; wave w accumulates dQ^T for queries 32 w.. (lane = query,
 // registers = features), key and value tiles staged in LDS.
@@ -516,9 +579,12 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                const float* __restrict__ lse2, const float* __restrict__ dsum,
                const __bf16* __restrict__ m_rows, __bf16* __restrict__ dq, int T, float c,
                float scale, int n_qblk, int accumulate) {
-  __shared__ __attribute__((aligned(16))) char lk[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lv[AB_STAGE * 256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char lk0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lk1[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lv0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lv1[AB_STAGE * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
   const long g = blockIdx.x / n_qblk;
   const int i = (blockIdx.x % n_qblk) * 128 + 32 * wave + n;
@@ -531,12 +597,12 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     ob[kc] = ld8(d_o + qrow * HD + 16 * kc + 8 * h2);
   }
   const float li = lse2[qrow], di = dsum[qrow];
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + gbase * HD, (uint32_t)T * 256);
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + gbase * HD, (uint32_t)T * 256);
+  const int loff = dma_lane_off(lane);
+  const int n_st = (T + AB_STAGE - 1) / AB_STAGE;
   f32x16 dacc[4] = {zero16(), zero16(), zero16(), zero16()};
-  for (int j0 = 0; j0 < T; j0 += AB_STAGE) {
-    const int valid = min(AB_STAGE, T - j0);
-    stage_tr(lk, k + (gbase + j0) * HD, AB_STAGE, valid);
-    stage_tr(lv, v + (gbase + j0) * HD, AB_STAGE, valid);
-    __syncthreads();
+  auto compute = [&](const char* lk, const char* lv, int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int sub = 0; sub < AB_STAGE / 32; ++sub) {
       f32x16 st = zero16(), dp = zero16();
@@ -549,8 +615,8 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const float p = j < T ? exp2f(st[r] * c - li) : 0.f;
-        ds[r] = p * (dp[r] - di);
+        const float e = __builtin_amdgcn_exp2f(st[r] * c - li);
+        ds[r] = (j < T ? e : 0.f) * (dp[r] - di);
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
@@ -560,8 +626,27 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           dacc[te] = mfma32(tr_op_acc(lk, 32 * sub + 16 * kc, 32 * te, lane), b, dacc[te]);
       }
     }
-    __syncthreads();
+  };
+  auto issue = [&](char* lk, char* lv, int st) __attribute__((always_inline)) {
+    dma_tile64(lk, rk, st * AB_STAGE, loff, wave);
+    dma_tile64(lv, rv, st * AB_STAGE, loff, wave);
+  };
+  issue(lk0, lv0, 0);
+  for (int st = 0;;) {
+    issue(lk1, lv1, min(st + 1, n_st - 1));
+    VMCNT_WAIT(8);
+    __builtin_amdgcn_s_barrier();
+    compute(lk0, lv0, st * AB_STAGE);
+    __builtin_amdgcn_s_barrier();
+    if (++st >= n_st) break;
+    issue(lk0, lv0, min(st + 1, n_st - 1));
+    VMCNT_WAIT(8);
+    __builtin_amdgcn_s_barrier();
+    compute(lk1, lv1, st * AB_STAGE);
+    __builtin_amdgcn_s_barrier();
+    if (++st >= n_st) break;
   }
+  VMCNT_WAIT(0);
 #pragma unroll
   for (int te = 0; te < 4; ++te) dacc[te] *= scale;
   if (m_rows) {
@@ -594,17 +679,23 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // dK = scale sum_i dS_ij Q_i and dV = sum_i P_ij dO_i. One workgroup of 4
 // waves per 128 keys; wave w holds keys 32 w.. as the columns of S = Q K^T and
 // accumulates dK^T and dV^T (lane = key, registers = features); query, dO,
-// lse2 and dsum tiles staged in LDS.
+// lse2 and dsum tiles staged in LDS (waves 0 and 1 move lse2 and dsum; waves
+// 2 and 3 move lse2 once more into a spare slot, so that every wave issues the
+// same number of transfers per stage).
 __global__ void __launch_bounds__(256)
 attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                  const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
                  const float* __restrict__ lse2, const float* __restrict__ dsum,
                  __bf16* __restrict__ dk, __bf16* __restrict__ dv, int T, float c, float scale,
                  int n_kblk, int accumulate) {
-  __shared__ __attribute__((aligned(16))) char lq[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lo[AB_STAGE * 256];
-  __shared__ float ll[AB_STAGE], ld[AB_STAGE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char lq0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lq1[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lo0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lo1[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) float lr0[4 * AB_STAGE];   // lse2, dsum, spare x2
+  __shared__ __attribute__((aligned(16))) float lr1[4 * AB_STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
   const long g = blockIdx.x / n_kblk;
   const int j = (blockIdx.x % n_kblk) * 128 + 32 * wave + n;     // this lane's key
@@ -619,16 +710,16 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   f32x16 kacc[4] = {zero16(), zero16(), zero16(), zero16()};
   f32x16 vacc[4] = {zero16(), zero16(), zero16(), zero16()};
   const bool key_ok = j < T;
-  for (int i0 = 0; i0 < T; i0 += AB_STAGE) {
-    const int valid = min(AB_STAGE, T - i0);
-    stage_tr(lq, q + (gbase + i0) * HD, AB_STAGE, valid);
-    stage_tr(lo, d_o + (gbase + i0) * HD, AB_STAGE, valid);
-    if (threadIdx.x < AB_STAGE) {
-      const int t = threadIdx.x;
-      ll[t] = t < valid ? lse2[gbase + i0 + t] : 0.f;
-      ld[t] = t < valid ? dsum[gbase + i0 + t] : 0.f;
-    }
-    __syncthreads();
+  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + gbase * HD, (uint32_t)T * 256);
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(d_o + gbase * HD, (uint32_t)T * 256);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(wave == 1 ? dsum + gbase : lse2 + gbase,
+                                                (uint32_t)T * 4);
+  const int loff = dma_lane_off(lane);
+  const int n_st = (T + AB_STAGE - 1) / AB_STAGE;
+  auto compute = [&](const char* lq, const char* lo, const float* lr, int i0)
+                     __attribute__((always_inline)) {
+    const float* ll = lr;
+    const float* ld = lr + AB_STAGE;
 #pragma unroll
     for (int sub = 0; sub < AB_STAGE / 32; ++sub) {
       f32x16 sc = zero16(), dp = zero16();
@@ -641,7 +732,8 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int il = 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const float p = (key_ok && i0 + il < T) ? exp2f(sc[r] * c - ll[il]) : 0.f;
+        const float e = __builtin_amdgcn_exp2f(sc[r] * c - ll[il]);
+        const float p = (key_ok && i0 + il < T) ? e : 0.f;
         pv[r] = p;
         ds[r] = p * (dp[r] - ld[il]);
       }
@@ -655,8 +747,29 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
       }
     }
-    __syncthreads();
+  };
+  auto issue = [&](char* lq, char* lo, float* lr, int st) __attribute__((always_inline)) {
+    dma_tile64(lq, rq, st * AB_STAGE, loff, wave);
+    dma_tile64(lo, ro, st * AB_STAGE, loff, wave);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lr + wave * AB_STAGE), 4,
+                                             lane * 4, st * AB_STAGE * 4, 0, 0);
+  };
+  issue(lq0, lo0, lr0, 0);
+  for (int st = 0;;) {
+    issue(lq1, lo1, lr1, min(st + 1, n_st - 1));
+    VMCNT_WAIT(9);
+    __builtin_amdgcn_s_barrier();
+    compute(lq0, lo0, lr0, st * AB_STAGE);
+    __builtin_amdgcn_s_barrier();
+    if (++st >= n_st) break;
+    issue(lq0, lo0, lr0, min(st + 1, n_st - 1));
+    VMCNT_WAIT(9);
+    __builtin_amdgcn_s_barrier();
+    compute(lq1, lo1, lr1, st * AB_STAGE);
+    __builtin_amdgcn_s_barrier();
+    if (++st >= n_st) break;
   }
+  VMCNT_WAIT(0);
   if (key_ok) {
     __bf16* ok = dk + (gbase + j) * HD;
     __bf16* ov = dv + (gbase + j) * HD;
@@ -709,7 +822,7 @@ hipError_t nt_gemm(const Dims& d, const void* x, int rows, bool x_per_head, cons
   const long n_g = (long)d.B * d.H;
   if (use_mfma(d)) {
     if (bt_trans) return hipErrorInvalidValue;
-    const int n_rblk = (rows + 127) / 128;
+    const int n_rblk = (rows + 31) / 32;
     nt_gemm_mfma_k<<<(unsigned)(n_g * n_rblk), 256, 0, s>>>(
         static_cast<const __bf16*>(x), static_cast<const __bf16*>(bt), ep, rows, d.H,
         x_per_head ? 1 : 0, bt_per_head ? 1 : 0, n_rblk);
@@ -722,9 +835,18 @@ hipError_t nt_gemm(const Dims& d, const void* x, int rows, bool x_per_head, cons
   return hipGetLastError();
 }
 
+// Tokens per partial of the X^T Y reduction: a multiple of 64 chosen so that
+// the partial workgroups number about two per compute unit.
+int xty_chunk(const Dims& d) {
+  const long n_g = (long)d.B * d.H;
+  const long sub = (d.T + XTY_SUB - 1) / XTY_SUB;
+  const long want = std::max(1L, std::min(sub, (512 + n_g - 1) / n_g));
+  return (int)(((sub + want - 1) / want) * XTY_SUB);
+}
+
 size_t xty_ws_bytes(const Dims& d) {
   if (!use_mfma(d)) return 0;
-  const long nch = (d.T + XTY_CHUNK - 1) / XTY_CHUNK;
+  const long nch = (d.T + xty_chunk(d) - 1) / xty_chunk(d);
   return (size_t)d.B * d.H * nch * HD * HD * sizeof(float);
 }
 
@@ -735,10 +857,11 @@ hipError_t xty(const Dims& d, const void* x, const void* y, float* out, bool sum
                hipStream_t s) {
   const long n_go = sum_b ? d.H : (long)d.B * d.H;
   if (use_mfma(d)) {
-    const int nch = (d.T + XTY_CHUNK - 1) / XTY_CHUNK;
+    const int chunk = xty_chunk(d);
+    const int nch = (d.T + chunk - 1) / chunk;
     float* part = static_cast<float*>(ws);
     xty_part_mfma_k<<<(unsigned)((long)d.B * d.H * nch), 256, 0, s>>>(
-        static_cast<const __bf16*>(x), static_cast<const __bf16*>(y), part, d.T, nch);
+        static_cast<const __bf16*>(x), static_cast<const __bf16*>(y), part, d.T, chunk, nch);
     const long n_thr = n_go * 1024;
     xty_reduce_mfma_k<<<blocks(n_thr, 256), 256, 0, s>>>(part, out, base_mat, gamma, delta,
                                                          accumulate ? 1 : 0, nch, d.B, d.H,
@@ -789,19 +912,20 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
   const int acc = accumulate ? 1 : 0;
   if (use_mfma(d)) {
     const float cl = d.scale * kLog2e;
-    const int nb = (d.T + 127) / 128;
-    const unsigned grid = (unsigned)((long)d.B * d.H * nb);
     const __bf16* qb = static_cast<const __bf16*>(q);
     const __bf16* kb = static_cast<const __bf16*>(k);
     const __bf16* vb = static_cast<const __bf16*>(v);
     const __bf16* ob = static_cast<const __bf16*>(d_o);
-    attn_pre_mfma_k<<<grid, 256, 0, s>>>(qb, kb, static_cast<const __bf16*>(o_intra), ob, lse,
-                                         dsum, d.T, cl, nb);
-    attn_dq_mfma_k<<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum,
-                                        static_cast<const __bf16*>(m_rows),
-                                        static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
+    const __bf16* oi = static_cast<const __bf16*>(o_intra);
+    const __bf16* mr = static_cast<const __bf16*>(m_rows);
+    const long n_g = (long)d.B * d.H;
+    const int nb = (d.T + 127) / 128;
+    const unsigned grid = (unsigned)(n_g * nb);
+    attn_pre_mfma_k<<<grid, 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl, nb);
+    attn_dq_mfma_k<<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum, mr,
+                                           static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
     attn_dkdv_mfma_k<<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum, static_cast<__bf16*>(dk),
-                                          static_cast<__bf16*>(dv), d.T, cl, d.scale, nb, acc);
+                                             static_cast<__bf16*>(dv), d.T, cl, d.scale, nb, acc);
   } else {
     const float* qf = static_cast<const float*>(q);
     const float* kf = static_cast<const float*>(k);
@@ -894,12 +1018,12 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   if ((e = feature_map_any(d, k, phi_k, kt, false, s)) != hipSuccess) return e;
   if ((e = feature_map_any(d, v, phi_v, vp, false, s)) != hipSuccess) return e;
   if (mf) {
-    rownorm_k<__bf16><<<blocks(n_rows, 128), 128, 0, s>>>(static_cast<const __bf16*>(kt),
+    rownorm_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(static_cast<const __bf16*>(kt),
                                                           static_cast<__bf16*>(kp), nrm, d.D, n_rows);
     to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(S, Sb, Stb, (long)mat_count(d));
     to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(G, Gb, Gtb, (long)mat_count(d));
   } else {
-    rownorm_k<float><<<blocks(n_rows, 128), 128, 0, s>>>(static_cast<const float*>(kt),
+    rownorm_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(static_cast<const float*>(kt),
                                                          static_cast<float*>(kp), nrm, d.D, n_rows);
   }
   // R = V' - K' S ;  K'G
@@ -911,11 +1035,11 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   if (e != hipSuccess) return e;
   // dbeta, dV' = beta K'G
   if (mf)
-    commit_rows1_k<__bf16><<<blocks(n_rows, 128), 128, 0, s>>>(kg32, r32, beta, dbeta,
+    commit_rows1_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(kg32, r32, beta, dbeta,
                                                                static_cast<__bf16*>(dvx), d.D, acc,
                                                                n_rows);
   else
-    commit_rows1_k<float><<<blocks(n_rows, 128), 128, 0, s>>>(kg32, r32, beta, dbeta,
+    commit_rows1_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(kg32, r32, beta, dbeta,
                                                               static_cast<float*>(dvx), d.D, acc,
                                                               n_rows);
   // dKraw = R G^T - K'G S^T
@@ -927,10 +1051,10 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   if (e != hipSuccess) return e;
   // dK~ through beta and the row normalisation
   if (mf)
-    commit_rows2_k<__bf16><<<blocks(n_rows, 128), 128, 0, s>>>(
+    commit_rows2_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(
         dkr, static_cast<const __bf16*>(kp), nrm, beta, static_cast<__bf16*>(dktx), d.D, n_rows);
   else
-    commit_rows2_k<float><<<blocks(n_rows, 128), 128, 0, s>>>(
+    commit_rows2_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(
         dkr, static_cast<const float*>(kp), nrm, beta, static_cast<float*>(dktx), d.D, n_rows);
   // dK = dK~ Phi_k^T, dV = dV' Phi_v^T
   e = nt_gemm(d, dktx, d.T, false, phi_k, true, false, make_epi(nullptr, false, nullptr, dk, accumulate), s);
