@@ -26,6 +26,10 @@ namespace {
 
 constexpr float kNormFloor = 1e-12f;          // row-norm floor of the key map
 
+__device__ __forceinline__ float4 ld4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+
 template <typename Tx>
 __device__ __forceinline__ float ldf(const Tx* p, size_t i) { return (float)p[i]; }
 template <typename Tx>
@@ -435,9 +439,17 @@ __global__ void xty_reduce_mfma_k(const float* __restrict__ part, float* __restr
 // ---------------------------------------------------------------------------
 constexpr int AB_STAGE = 64;                  // keys (or queries) staged per step
 
-// Row operand (8 consecutive columns 16 kc + 8 h2 ..) of a swz_v-staged tile.
+// Chunk swizzle of the staged attention tiles: 16-byte chunk p of row r sits at
+// p ^ swz_b(r). Bits 3:2 follow r % 4 and bits 1:0 follow (r / 4) % 4, so both
+// ways the kernels read a tile are free of bank conflicts: a row read (16
+// consecutive rows, one chunk each) meets 16 distinct positions, and a
+// transposing read (4 consecutive rows, 4 aligned chunks each) meets 4
+// disjoint groups of positions.
+__device__ __forceinline__ int swz_b(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Row operand (8 consecutive columns 16 kc + 8 h2 ..) of a staged tile.
 __device__ __forceinline__ bf16x8 row_op_v(const char* base, int row, int kc, int h2) {
-  return *reinterpret_cast<const bf16x8*>(base + row * 256 + (((2 * kc + h2) ^ swz_v(row)) << 4));
+  return *reinterpret_cast<const bf16x8*>(base + row * 256 + (((2 * kc + h2) ^ swz_b(row)) << 4));
 }
 
 // A operand by transposing reads whose contraction slots follow an MFMA
@@ -450,9 +462,49 @@ __device__ __forceinline__ bf16x8 tr_op_acc(const char* base, int r0, int c0, in
   const int col = c0 + 16 * (G & 1) + 4 * j;
   const int c16 = col >> 3, sub = (col & 7) * 2;
   const int rb = r0 + 4 * (G >> 1) + c;
-  const char* a0 = base + rb * 256 + ((c16 ^ swz_v(rb)) << 4) + sub;
-  const char* a1 = base + (rb + 8) * 256 + ((c16 ^ swz_v(rb + 8)) << 4) + sub;
+  const char* a0 = base + rb * 256 + ((c16 ^ swz_b(rb)) << 4) + sub;
+  const char* a1 = base + (rb + 8) * 256 + ((c16 ^ swz_b(rb + 8)) << 4) + sub;
   return __builtin_shufflevector(tr_read(a0), tr_read(a1), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per-lane byte offsets of the two reads above and of the row operands, for a
+// tile origin r0 that is a multiple of 16 (swz_b then depends on the lane
+// alone, and r0 * 256 folds into the reads' immediate offsets). Made opaque so
+// that each stays one register instead of being re-derived per read.
+struct TileOffsets {
+  int tr[4][2];                                  // transposing reads, by column tile
+  int row[8];                                    // row operand, by 16-column step kc
+};
+
+__device__ __forceinline__ TileOffsets tile_offsets(int lane) {
+  TileOffsets t;
+  const int G = lane >> 4;
+  const int s = lane & 15, c = s >> 2, j = s & 3;
+  const int rb = 4 * (G >> 1) + c;
+#pragma unroll
+  for (int te = 0; te < 4; ++te) {
+    const int col = 32 * te + 16 * (G & 1) + 4 * j;
+    const int c16 = col >> 3, sub = (col & 7) * 2;
+    t.tr[te][0] = rb * 256 + ((c16 ^ swz_b(rb)) << 4) + sub;
+    t.tr[te][1] = (rb + 8) * 256 + ((c16 ^ swz_b(rb + 8)) << 4) + sub;
+    asm volatile("" : "+v"(t.tr[te][0]), "+v"(t.tr[te][1]));
+  }
+  const int n = lane & 31, h2 = lane >> 5;
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    t.row[kc] = n * 256 + (((2 * kc + h2) ^ swz_b(n)) << 4);
+    asm volatile("" : "+v"(t.row[kc]));
+  }
+  return t;
+}
+
+__device__ __forceinline__ bf16x8 tr_op_at(const char* base, int r0, const TileOffsets& t, int te) {
+  return __builtin_shufflevector(tr_read(base + r0 * 256 + t.tr[te][0]),
+                                 tr_read(base + r0 * 256 + t.tr[te][1]), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 row_op_at(const char* base, int r0, const TileOffsets& t, int kc) {
+  return *reinterpret_cast<const bf16x8*>(base + r0 * 256 + t.row[kc]);
 }
 
 // registers 8 kc .. 8 kc + 7 of an accumulator as a bf16 operand
@@ -465,32 +517,52 @@ __device__ __forceinline__ bf16x8 acc_op(const float* a, int kc) {
 
 // Tiles of 64 rows x 256 bytes move from memory to LDS by buffer-load DMA,
 // two buffers per operand: while a stage computes from one, the next stage's
-// rows land in the other. Wave w moves rows 16 w .. 16 w + 15 as four 1 KB
+// rows land in the other. Each of the NW waves moves 64 / NW rows as 1 KB
 // pieces; lane l's 16 bytes land at byte 16 l of its piece, so the lane loads
 // the logical chunk that the swz_v swizzle puts there. Rows past the buffer
 // resource's range (the frame's end) arrive as zeros.
-__device__ __forceinline__ int dma_lane_off(int lane) {
-  return (lane >> 4) * 256 + (((lane & 15) ^ ((lane >> 4) << 2)) << 4);
+// Byte offset that lane l loads for a piece whose first row is a multiple of
+// 4 with (first row / 4) % 4 = q: row (l / 16) of the piece, logical chunk
+// (l % 16) ^ swz_b(row).
+__device__ __forceinline__ int dma_lane_off(int lane, int q) {
+  return (lane >> 4) * 256 + (((lane & 15) ^ ((lane >> 4) << 2) ^ q) << 4);
 }
 
-__device__ __forceinline__ void dma_tile64(char* dst, __amdgpu_buffer_rsrc_t src, int row0,
-                                           int lane_off, int wave) {
+struct DmaOffsets {
+  int o[4];                                      // by q = piece % 4
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
+  DmaOffsets d;
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + wave * 4096 + ii * 1024),
-                                             16, lane_off, row0 * 256 + wave * 4096 + ii * 1024,
-                                             0, 0);
+  for (int q = 0; q < 4; ++q) d.o[q] = dma_lane_off(lane, q);
+  return d;
 }
 
-// s_waitcnt for the vector-memory counter only: wait until at most n (< 16)
-// of this wave's vector-memory operations are outstanding.
-#define VMCNT_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8))
+template <int NW>
+__device__ __forceinline__ void dma_tile64(char* dst, __amdgpu_buffer_rsrc_t src, int row0,
+                                           const DmaOffsets& lo, int wave) {
+  constexpr int PIECES = 16 / NW;               // 1 KB pieces per wave (a multiple of 4)
+#pragma unroll
+  for (int ii = 0; ii < PIECES; ++ii)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (lds_void_t*)(dst + wave * PIECES * 1024 + ii * 1024), 16, lo.o[ii & 3],
+        row0 * 256 + wave * PIECES * 1024 + ii * 1024, 0, 0);
+}
+
+// s_waitcnt for the vector-memory counter only: wait until at most n (< 64)
+// of this wave's vector-memory operations are outstanding (the count's low
+// four bits in [3:0], its high two in [15:14]; expcnt and lgkmcnt at their
+// maxima, i.e. not waited for).
+#define VMCNT_WAIT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 // Per query row: lse2 = log2 sum_j exp2(c q.k_j) and dsum = dO . O_intra. One
-// workgroup of 4 waves per 128 queries; wave w holds queries 32 w.. as the
+// workgroup of NW waves per 32 NW queries; wave w holds queries 32 w.. as the
 // columns of S^T = K Q^T (a lane's running max and sum cover half the keys;
 // the halves combine at the end).
-__global__ void __launch_bounds__(256)
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
 attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
                 float* __restrict__ lse2, float* __restrict__ dsum, int T, float c, int n_qblk) {
@@ -500,14 +572,15 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
   const long g = blockIdx.x / n_qblk;
-  const int i = (blockIdx.x % n_qblk) * 128 + 32 * wave + n;     // this lane's query
+  const int i = (blockIdx.x % n_qblk) * (32 * NW) + 32 * wave + n;   // this lane's query
   const size_t gbase = (size_t)g * T;
   const __bf16* qr = q + (gbase + min(i, T - 1)) * HD + 8 * h2;
   bf16x8 qb[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) qb[kc] = ld8(qr + 16 * kc);
   const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + gbase * HD, (uint32_t)T * 256);
-  const int loff = dma_lane_off(lane);
+  const DmaOffsets loff = dma_offsets(lane);
+  const TileOffsets to = tile_offsets(lane);
   const int n_st = (T + AB_STAGE - 1) / AB_STAGE;
   float m = -INFINITY, l = 0.f;
   auto compute = [&](const char* lk, int j0) __attribute__((always_inline)) {
@@ -515,7 +588,7 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int sub = 0; sub < AB_STAGE / 32; ++sub) {
       f32x16 acc = zero16();
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) acc = mfma32(row_op_v(lk, 32 * sub + n, kc, h2), qb[kc], acc);
+      for (int kc = 0; kc < 8; ++kc) acc = mfma32(row_op_at(lk, 32 * sub, to, kc), qb[kc], acc);
       float sv[16], mt = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -533,16 +606,16 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
     }
   };
-  dma_tile64(lk0, rk, 0, loff, wave);
+  dma_tile64<NW>(lk0, rk, 0, loff, wave);
   for (int st = 0;;) {
-    dma_tile64(lk1, rk, min(st + 1, n_st - 1) * AB_STAGE, loff, wave);
-    VMCNT_WAIT(4);
+    dma_tile64<NW>(lk1, rk, min(st + 1, n_st - 1) * AB_STAGE, loff, wave);
+    VMCNT_WAIT(16 / NW);
     __builtin_amdgcn_s_barrier();
     compute(lk0, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
     if (++st >= n_st) break;
-    dma_tile64(lk0, rk, min(st + 1, n_st - 1) * AB_STAGE, loff, wave);
-    VMCNT_WAIT(4);
+    dma_tile64<NW>(lk0, rk, min(st + 1, n_st - 1) * AB_STAGE, loff, wave);
+    VMCNT_WAIT(16 / NW);
     __builtin_amdgcn_s_barrier();
     compute(lk1, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
@@ -570,10 +643,11 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 }
 
 // dQ = scale sum_j dS_ij K_j (+ dO M^T when m_rows is given: the inter-frame
-// branch with M = Phi_q S, bf16 row-major [e][v]). One workgroup of 4 waves
-// per 128 queries; wave w accumulates dQ^T for queries 32 w.. (lane = query,
+// branch with M = Phi_q S, bf16 row-major [e][v]). One workgroup of NW waves
+// per 32 NW queries; wave w accumulates dQ^T for queries 32 w.. (lane = query,
 // registers = features), key and value tiles staged in LDS.
-__global__ void __launch_bounds__(256)
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
 attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
                const float* __restrict__ lse2, const float* __restrict__ dsum,
@@ -587,7 +661,7 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
   const long g = blockIdx.x / n_qblk;
-  const int i = (blockIdx.x % n_qblk) * 128 + 32 * wave + n;
+  const int i = (blockIdx.x % n_qblk) * (32 * NW) + 32 * wave + n;
   const size_t gbase = (size_t)g * T;
   const size_t qrow = gbase + min(i, T - 1);
   bf16x8 qb[8], ob[8];
@@ -599,7 +673,8 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const float li = lse2[qrow], di = dsum[qrow];
   const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + gbase * HD, (uint32_t)T * 256);
   const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + gbase * HD, (uint32_t)T * 256);
-  const int loff = dma_lane_off(lane);
+  const DmaOffsets loff = dma_offsets(lane);
+  const TileOffsets to = tile_offsets(lane);
   const int n_st = (T + AB_STAGE - 1) / AB_STAGE;
   f32x16 dacc[4] = {zero16(), zero16(), zero16(), zero16()};
   auto compute = [&](const char* lk, const char* lv, int j0) __attribute__((always_inline)) {
@@ -608,8 +683,8 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       f32x16 st = zero16(), dp = zero16();
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
-        st = mfma32(row_op_v(lk, 32 * sub + n, kc, h2), qb[kc], st);
-        dp = mfma32(row_op_v(lv, 32 * sub + n, kc, h2), ob[kc], dp);
+        st = mfma32(row_op_at(lk, 32 * sub, to, kc), qb[kc], st);
+        dp = mfma32(row_op_at(lv, 32 * sub, to, kc), ob[kc], dp);
       }
       float ds[16];
 #pragma unroll
@@ -623,24 +698,24 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const bf16x8 b = acc_op(ds, kc);
 #pragma unroll
         for (int te = 0; te < 4; ++te)
-          dacc[te] = mfma32(tr_op_acc(lk, 32 * sub + 16 * kc, 32 * te, lane), b, dacc[te]);
+          dacc[te] = mfma32(tr_op_at(lk, 32 * sub + 16 * kc, to, te), b, dacc[te]);
       }
     }
   };
   auto issue = [&](char* lk, char* lv, int st) __attribute__((always_inline)) {
-    dma_tile64(lk, rk, st * AB_STAGE, loff, wave);
-    dma_tile64(lv, rv, st * AB_STAGE, loff, wave);
+    dma_tile64<NW>(lk, rk, st * AB_STAGE, loff, wave);
+    dma_tile64<NW>(lv, rv, st * AB_STAGE, loff, wave);
   };
   issue(lk0, lv0, 0);
   for (int st = 0;;) {
     issue(lk1, lv1, min(st + 1, n_st - 1));
-    VMCNT_WAIT(8);
+    VMCNT_WAIT(32 / NW);
     __builtin_amdgcn_s_barrier();
     compute(lk0, lv0, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
     if (++st >= n_st) break;
     issue(lk0, lv0, min(st + 1, n_st - 1));
-    VMCNT_WAIT(8);
+    VMCNT_WAIT(32 / NW);
     __builtin_amdgcn_s_barrier();
     compute(lk1, lv1, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
@@ -676,13 +751,14 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 }
 
-// dK = scale sum_i dS_ij Q_i and dV = sum_i P_ij dO_i. One workgroup of 4
-// waves per 128 keys; wave w holds keys 32 w.. as the columns of S = Q K^T and
+// dK = scale sum_i dS_ij Q_i and dV = sum_i P_ij dO_i. One workgroup of NW
+// waves per 32 NW keys; wave w holds keys 32 w.. as the columns of S = Q K^T and
 // accumulates dK^T and dV^T (lane = key, registers = features); query, dO,
-// lse2 and dsum tiles staged in LDS (waves 0 and 1 move lse2 and dsum; waves
-// 2 and 3 move lse2 once more into a spare slot, so that every wave issues the
-// same number of transfers per stage).
-__global__ void __launch_bounds__(256)
+// lse2 and dsum tiles staged in LDS (waves 0 and 1 move lse2 and dsum; any
+// further waves move lse2 once more into a spare slot, so that every wave
+// issues the same number of transfers per stage).
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
 attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                  const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
                  const float* __restrict__ lse2, const float* __restrict__ dsum,
@@ -698,7 +774,7 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
   const long g = blockIdx.x / n_kblk;
-  const int j = (blockIdx.x % n_kblk) * 128 + 32 * wave + n;     // this lane's key
+  const int j = (blockIdx.x % n_kblk) * (32 * NW) + 32 * wave + n;   // this lane's key
   const size_t gbase = (size_t)g * T;
   const size_t krow = gbase + min(j, T - 1);
   bf16x8 kb[8], vb[8];
@@ -714,7 +790,8 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(d_o + gbase * HD, (uint32_t)T * 256);
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(wave == 1 ? dsum + gbase : lse2 + gbase,
                                                 (uint32_t)T * 4);
-  const int loff = dma_lane_off(lane);
+  const DmaOffsets loff = dma_offsets(lane);
+  const TileOffsets to = tile_offsets(lane);
   const int n_st = (T + AB_STAGE - 1) / AB_STAGE;
   auto compute = [&](const char* lq, const char* lo, const float* lr, int i0)
                      __attribute__((always_inline)) {
@@ -725,45 +802,55 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
-        sc = mfma32(row_op_v(lq, 32 * sub + n, kc, h2), kb[kc], sc);
-        dp = mfma32(row_op_v(lo, 32 * sub + n, kc, h2), vb[kc], dp);
+        sc = mfma32(row_op_at(lq, 32 * sub, to, kc), kb[kc], sc);
+        dp = mfma32(row_op_at(lo, 32 * sub, to, kc), vb[kc], dp);
+      }
+      // lse2 and dsum of this lane's 16 query rows: 4 runs of 4 consecutive rows
+      float lv[16], dv4[16];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const float4 a = ld4(ll + 32 * sub + 8 * rg + 4 * h2);
+        const float4 b = ld4(ld + 32 * sub + 8 * rg + 4 * h2);
+        lv[4 * rg] = a.x; lv[4 * rg + 1] = a.y; lv[4 * rg + 2] = a.z; lv[4 * rg + 3] = a.w;
+        dv4[4 * rg] = b.x; dv4[4 * rg + 1] = b.y; dv4[4 * rg + 2] = b.z; dv4[4 * rg + 3] = b.w;
       }
       float pv[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int il = 32 * sub + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const float e = __builtin_amdgcn_exp2f(sc[r] * c - ll[il]);
-        const float p = (key_ok && i0 + il < T) ? e : 0.f;
+        const float e = __builtin_amdgcn_exp2f(sc[r] * c - lv[r]);
+        const bool ok = key_ok & (i0 + il < T);
+        const float p = ok ? e : 0.f;
         pv[r] = p;
-        ds[r] = p * (dp[r] - ld[il]);
+        ds[r] = p * (dp[r] - dv4[r]);
       }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const bf16x8 pb = acc_op(pv, kc), db = acc_op(ds, kc);
 #pragma unroll
         for (int te = 0; te < 4; ++te) {
-          vacc[te] = mfma32(tr_op_acc(lo, 32 * sub + 16 * kc, 32 * te, lane), pb, vacc[te]);
-          kacc[te] = mfma32(tr_op_acc(lq, 32 * sub + 16 * kc, 32 * te, lane), db, kacc[te]);
+          vacc[te] = mfma32(tr_op_at(lo, 32 * sub + 16 * kc, to, te), pb, vacc[te]);
+          kacc[te] = mfma32(tr_op_at(lq, 32 * sub + 16 * kc, to, te), db, kacc[te]);
         }
       }
     }
   };
   auto issue = [&](char* lq, char* lo, float* lr, int st) __attribute__((always_inline)) {
-    dma_tile64(lq, rq, st * AB_STAGE, loff, wave);
-    dma_tile64(lo, ro, st * AB_STAGE, loff, wave);
+    dma_tile64<NW>(lq, rq, st * AB_STAGE, loff, wave);
+    dma_tile64<NW>(lo, ro, st * AB_STAGE, loff, wave);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lr + wave * AB_STAGE), 4,
                                              lane * 4, st * AB_STAGE * 4, 0, 0);
   };
   issue(lq0, lo0, lr0, 0);
   for (int st = 0;;) {
     issue(lq1, lo1, lr1, min(st + 1, n_st - 1));
-    VMCNT_WAIT(9);
+    VMCNT_WAIT(32 / NW + 1);
     __builtin_amdgcn_s_barrier();
     compute(lq0, lo0, lr0, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
     if (++st >= n_st) break;
     issue(lq0, lo0, lr0, min(st + 1, n_st - 1));
-    VMCNT_WAIT(9);
+    VMCNT_WAIT(32 / NW + 1);
     __builtin_amdgcn_s_barrier();
     compute(lq1, lo1, lr1, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
@@ -919,13 +1006,30 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
     const __bf16* oi = static_cast<const __bf16*>(o_intra);
     const __bf16* mr = static_cast<const __bf16*>(m_rows);
     const long n_g = (long)d.B * d.H;
-    const int nb = (d.T + 127) / 128;
-    const unsigned grid = (unsigned)(n_g * nb);
-    attn_pre_mfma_k<<<grid, 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl, nb);
-    attn_dq_mfma_k<<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum, mr,
-                                           static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
-    attn_dkdv_mfma_k<<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum, static_cast<__bf16*>(dk),
-                                             static_cast<__bf16*>(dv), d.T, cl, d.scale, nb, acc);
+    // dQ and dK/dV: 4-wave workgroups (128 rows) when they fill the chip twice
+    // over, else 2-wave ones (64 rows) for twice as many; the row statistics
+    // always in 4-wave workgroups
+    if (n_g * ((d.T + 127) / 128) >= 512) {
+      const int nb = (d.T + 127) / 128;
+      const unsigned grid = (unsigned)(n_g * nb);
+      attn_pre_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl, nb);
+      attn_dq_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum, mr,
+                                             static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
+      attn_dkdv_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum,
+                                               static_cast<__bf16*>(dk), static_cast<__bf16*>(dv),
+                                               d.T, cl, d.scale, nb, acc);
+    } else {
+      const int nb = (d.T + 63) / 64;
+      const unsigned grid = (unsigned)(n_g * nb);
+      const int nb4 = (d.T + 127) / 128;
+      attn_pre_mfma_k<4><<<(unsigned)(n_g * nb4), 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl,
+                                                              nb4);
+      attn_dq_mfma_k<2><<<grid, 128, 0, s>>>(qb, kb, vb, ob, lse, dsum, mr,
+                                             static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
+      attn_dkdv_mfma_k<2><<<grid, 128, 0, s>>>(qb, kb, vb, ob, lse, dsum,
+                                               static_cast<__bf16*>(dk), static_cast<__bf16*>(dv),
+                                               d.T, cl, d.scale, nb, acc);
+    }
   } else {
     const float* qf = static_cast<const float*>(q);
     const float* kf = static_cast<const float*>(k);
