@@ -447,27 +447,13 @@ constexpr int AB_STAGE = 64;                  // keys (or queries) staged per st
 // disjoint groups of positions.
 __device__ __forceinline__ int swz_b(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// Row operand (8 consecutive columns 16 kc + 8 h2 ..) of a staged tile.
-__device__ __forceinline__ bf16x8 row_op_v(const char* base, int row, int kc, int h2) {
-  return *reinterpret_cast<const bf16x8*>(base + row * 256 + (((2 * kc + h2) ^ swz_b(row)) << 4));
-}
-
-// A operand by transposing reads whose contraction slots follow an MFMA
-// accumulator's register order: lane (n, h2) receives M[r0 + 4 h2 + u][c0 + n]
-// for u = 0..3 and M[r0 + 8 + 4 h2 + u - 4][c0 + n] for u = 4..7, i.e. the rows
-// that registers 8 kc .. 8 kc + 7 of a 32 x 32 accumulator hold (r0 = 32 t + 16 kc).
-__device__ __forceinline__ bf16x8 tr_op_acc(const char* base, int r0, int c0, int lane) {
-  const int G = lane >> 4;
-  const int s = lane & 15, c = s >> 2, j = s & 3;
-  const int col = c0 + 16 * (G & 1) + 4 * j;
-  const int c16 = col >> 3, sub = (col & 7) * 2;
-  const int rb = r0 + 4 * (G >> 1) + c;
-  const char* a0 = base + rb * 256 + ((c16 ^ swz_b(rb)) << 4) + sub;
-  const char* a1 = base + (rb + 8) * 256 + ((c16 ^ swz_b(rb + 8)) << 4) + sub;
-  return __builtin_shufflevector(tr_read(a0), tr_read(a1), 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Per-lane byte offsets of the two reads above and of the row operands, for a
+// Operand reads from a staged tile. A operands by transposing reads follow an
+// MFMA accumulator's register order in their contraction slots: lane (n, h2)
+// receives M[r0 + 4 h2 + u][c0 + n] for u = 0..3 and M[r0 + 8 + 4 h2 + u - 4]
+// [c0 + n] for u = 4..7, the rows that registers 8 kc .. 8 kc + 7 of a 32 x 32
+// accumulator hold (r0 = 32 t + 16 kc). Row operands take 8 consecutive columns
+// 16 kc + 8 h2 .. of row r0 + n.
+// Per-lane byte offsets of the transposing reads and of the row operands, for a
 // tile origin r0 that is a multiple of 16 (swz_b then depends on the lane
 // alone, and r0 * 256 folds into the reads' immediate offsets). Made opaque so
 // that each stays one register instead of being re-derived per read.
