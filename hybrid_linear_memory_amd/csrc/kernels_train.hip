@@ -357,77 +357,79 @@ __device__ __forceinline__ void stage_tr(char* dst, const __bf16* src, int rows,
 
 constexpr int XTY_SUB = 64;                   // tokens staged at a time
 
-// Partial X^T Y over one chunk of `chunk` tokens of one g, as 16 tiles of
-// 32 x 32 in MFMA accumulator order: part[(g * nch + ch) * 16 + tile][lane][16].
+// Partial X^T Y over one chunk of `chunk` tokens of one g, for one 64 x 64
+// quadrant (qe, qv) of the 128 x 128 result: wave w computes the 32 x 32 tile
+// (2 qe + w / 2, 2 qv + w % 2), stored in MFMA accumulator order:
+// part[(g * nch + ch) * 16 + tile][lane][16], tile = 4 te + tv.
 __global__ void __launch_bounds__(256)
 xty_part_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ y,
                 float* __restrict__ part, int T, int chunk, int nch) {
   __shared__ __attribute__((aligned(16))) char lx[XTY_SUB * 256];
   __shared__ __attribute__((aligned(16))) char ly[XTY_SUB * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long g = blockIdx.x / nch;
-  const int ch = blockIdx.x % nch;
-  f32x16 acc[4] = {zero16(), zero16(), zero16(), zero16()};
+  const int quad = blockIdx.x & 3;
+  const long gc = blockIdx.x >> 2;
+  const long g = gc / nch;
+  const int ch = gc % nch;
+  const int te = 2 * (quad >> 1) + (wave >> 1), tv = 2 * (quad & 1) + (wave & 1);
+  f32x16 acc = zero16();
   for (int s0 = ch * chunk; s0 < min(T, (ch + 1) * chunk); s0 += XTY_SUB) {
     const int valid = min(XTY_SUB, T - s0);
     stage_tr(lx, x + ((size_t)g * T + s0) * HD, XTY_SUB, valid);
     stage_tr(ly, y + ((size_t)g * T + s0) * HD, XTY_SUB, valid);
     __syncthreads();
 #pragma unroll
-    for (int kc = 0; kc < XTY_SUB / 16; ++kc) {
-      const bf16x8 a = tr_op(lx, 16 * kc, 8, 32 * wave, lane);   // X^T rows e
-#pragma unroll
-      for (int tv = 0; tv < 4; ++tv)
-        acc[tv] = mfma32(a, tr_op(ly, 16 * kc, 8, 32 * tv, lane), acc[tv]);
-    }
+    for (int kc = 0; kc < XTY_SUB / 16; ++kc)
+      acc = mfma32(tr_op(lx, 16 * kc, 8, 32 * te, lane), tr_op(ly, 16 * kc, 8, 32 * tv, lane), acc);
     __syncthreads();
   }
+  float* p = part + (((size_t)g * nch + ch) * 16 + 4 * te + tv) * 1024 + lane * 16;
 #pragma unroll
-  for (int tv = 0; tv < 4; ++tv) {
-    float* p = part + (((size_t)g * nch + ch) * 16 + 4 * wave + tv) * 1024 + lane * 16;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<float4*>(p + 4 * q4) =
-          make_float4(acc[tv][4 * q4], acc[tv][4 * q4 + 1], acc[tv][4 * q4 + 2], acc[tv][4 * q4 + 3]);
-  }
+  for (int q4 = 0; q4 < 4; ++q4)
+    *reinterpret_cast<float4*>(p + 4 * q4) =
+        make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
 }
 
 // out[go][e][v] (+)= gamma[go] base[go][e][v] + delta * sum_b sum_ch part:
-// one thread per (go, tile, lane), 16 outputs each, chunks summed in order.
-__global__ void xty_reduce_mfma_k(const float* __restrict__ part, float* __restrict__ out,
-                                  const float* __restrict__ base_mat,
-                                  const float* __restrict__ gamma, float delta, int accumulate,
-                                  int nch, int B, int H, int sum_b, long n_thr) {
+// one thread per (go, tile, lane, 4 registers), chunks summed in order with
+// the loads of 4 chunks issued ahead of their sums.
+__global__ void __launch_bounds__(256)
+xty_reduce_mfma_k(const float* __restrict__ part, float* __restrict__ out,
+                  const float* __restrict__ base_mat, const float* __restrict__ gamma,
+                  float delta, int accumulate, int nch, int B, int H, int sum_b, long n_thr) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n_thr) return;
-  const int lane = (int)(idx & 63);
-  const int tile = (int)((idx >> 6) & 15);
-  const long go = idx >> 10;
-  float acc[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int q4 = (int)(idx & 3);
+  const int lane = (int)((idx >> 2) & 63);
+  const int tile = (int)((idx >> 8) & 15);
+  const long go = idx >> 12;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int nb = sum_b ? B : 1;
+  const size_t inner = ((size_t)tile * 1024 + lane * 16 + 4 * q4);
   for (int b = 0; b < nb; ++b) {
     const long g = sum_b ? (long)b * H + go : go;
-    for (int ch = 0; ch < nch; ++ch) {
-      const float* p = part + (((size_t)g * nch + ch) * 16 + tile) * 1024 + lane * 16;
+    const float* pg = part + (size_t)g * nch * 16 * 1024 + inner;
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+      float4 xs[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 x = *reinterpret_cast<const float4*>(p + 4 * q4);
-        acc[4 * q4] += x.x;
-        acc[4 * q4 + 1] += x.y;
-        acc[4 * q4 + 2] += x.z;
-        acc[4 * q4 + 3] += x.w;
-      }
+      for (int u = 0; u < 4; ++u)
+        if (c0 + u < nch) xs[u] = *reinterpret_cast<const float4*>(pg + (size_t)(c0 + u) * 16 * 1024);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c0 + u < nch) {
+          acc.x += xs[u].x; acc.y += xs[u].y; acc.z += xs[u].z; acc.w += xs[u].w;
+        }
     }
   }
   const int n = lane & 31, h2 = lane >> 5;
   const int v = 32 * (tile & 3) + n;
+  const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * q4 + u;
     const int e = 32 * (tile >> 2) + 8 * (r >> 2) + 4 * h2 + (r & 3);
     const size_t o = (size_t)go * HD * HD + (size_t)e * HD + v;
-    float val = delta * acc[r];
+    float val = delta * a4[u];
     if (base_mat) val += gamma[go] * base_mat[o];
     out[o] = accumulate ? out[o] + val : val;
   }
@@ -909,11 +911,12 @@ hipError_t nt_gemm(const Dims& d, const void* x, int rows, bool x_per_head, cons
 }
 
 // Tokens per partial of the X^T Y reduction: a multiple of 64 chosen so that
-// the partial workgroups number about two per compute unit.
+// the partial workgroups (four quadrants per chunk) number about two per
+// compute unit.
 int xty_chunk(const Dims& d) {
   const long n_g = (long)d.B * d.H;
   const long sub = (d.T + XTY_SUB - 1) / XTY_SUB;
-  const long want = std::max(1L, std::min(sub, (512 + n_g - 1) / n_g));
+  const long want = std::max(1L, std::min(sub, (512 + 4 * n_g - 1) / (4 * n_g)));
   return (int)(((sub + want - 1) / want) * XTY_SUB);
 }
 
@@ -933,9 +936,9 @@ hipError_t xty(const Dims& d, const void* x, const void* y, float* out, bool sum
     const int chunk = xty_chunk(d);
     const int nch = (d.T + chunk - 1) / chunk;
     float* part = static_cast<float*>(ws);
-    xty_part_mfma_k<<<(unsigned)((long)d.B * d.H * nch), 256, 0, s>>>(
+    xty_part_mfma_k<<<(unsigned)((long)d.B * d.H * nch * 4), 256, 0, s>>>(
         static_cast<const __bf16*>(x), static_cast<const __bf16*>(y), part, d.T, chunk, nch);
-    const long n_thr = n_go * 1024;
+    const long n_thr = n_go * 4096;
     xty_reduce_mfma_k<<<blocks(n_thr, 256), 256, 0, s>>>(part, out, base_mat, gamma, delta,
                                                          accumulate ? 1 : 0, nch, d.B, d.H,
                                                          sum_b ? 1 : 0, n_thr);
