@@ -335,6 +335,27 @@ def cpu_baseline(seconds: float):
             est = busy / frames
             if busy + est > 2.5 * seconds:
                 break
+    # beside it: one BLAS thread (one whole frame), the commit alone at all
+    # cores (frames/s of the clean pass's state write), the tiny fp32 workload
+    # end to end
+    fr = synth.oracle_frame(w, 0)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.rollout([fr], *phis, S0=np.zeros((w.B, w.H, w.D, w.D)))
+        one_thread = 1.0 / (time.perf_counter() - t0)
+    with threadpool_limits(limits=cores):
+        _, kc, vc = fr["passes"][-1]
+        n_c, t0 = 0, time.perf_counter()
+        while n_c < 3 or time.perf_counter() - t0 < 1.0:
+            oracle.commit(kc, vc, phis[1], phis[2], fr["beta"], fr["alpha"],
+                          np.zeros((w.B, w.H, w.D, w.D)))
+            n_c += 1
+        commit_only = n_c / (time.perf_counter() - t0)
+        w0 = synth.WORKLOADS[0]
+        frames0 = [synth.oracle_frame(w0, f) for f in range(w0.frames)]
+        t0 = time.perf_counter()
+        oracle.rollout(frames0, *synth.phi_maps(w0))
+        tiny_s = time.perf_counter() - t0
     threads = max((n for _, n in blas if n), default=1)
     cpu_model = ""
     try:
@@ -353,6 +374,9 @@ def cpu_baseline(seconds: float):
         "sample": f"{frames} whole frames of the 1x12x128, T=1560 layer (4 reads + clean pass "
                   f"each), fp64 numpy, {busy:.1f} s",
         "tokens_per_s": frames * w.T / busy,
+        "one_thread_frames_per_s": one_thread,
+        "commit_only_frames_per_s": commit_only,
+        "tiny_fp32_rollout_s": tiny_s,
         "cpu_model": cpu_model,
         "blas": blas,
     }
