@@ -134,6 +134,37 @@ def _ptr(t, name, dtype=None, optional=False):
     return t.data_ptr()
 
 
+_ACT = ("q", "k", "v", "o", "o_intra", "o_inter", "x", "x_out", "q_prime", "k_prime", "v_prime",
+        "d_o", "dq", "dk", "dv")
+_PHI = ("phi", "phi_q", "phi_k", "phi_v", "dphi_q", "dphi_k", "dphi_v")
+_STATE = ("S", "S_prev", "S_next", "dS", "dS_next", "dS_prev", "S0", "states")
+
+
+def _checker(shape: "Shape", frames: int = 1, state_frames: int = 1):
+    """_ptr that also checks each tensor's element count against the shape
+    (the library sees only pointers: a short tensor would be read past its
+    end). `frames` multiplies the per-frame inputs (k, v, beta, alpha) of a
+    multi-frame call, `state_frames` the state-shaped tensors."""
+    B, H, T, D = shape.B, shape.H, shape.T, shape.D
+    sizes = {}
+    sizes.update({n: B * H * T * D * frames for n in _ACT})
+    sizes.update({n: H * D * D for n in _PHI})
+    sizes.update({n: B * H * D * D * state_frames for n in _STATE})
+    sizes.update({"beta": B * H * T * frames, "dbeta": B * H * T, "alpha": B * H * frames,
+                  "dalpha": B * H})
+    min_bytes = {"prepared": prepared_bytes(shape), "prepared_next": prepared_bytes(shape)}
+
+    def ck(t, name, dtype=None, optional=False):
+        ptr = _ptr(t, name, dtype, optional)
+        if t is not None and name in sizes and t.numel() != sizes[name]:
+            raise ValueError(f"{name} has {t.numel()} elements, the shape needs {sizes[name]}")
+        if t is not None and name in min_bytes and t.numel() * t.element_size() < min_bytes[name]:
+            raise ValueError(f"{name} has {t.numel() * t.element_size()} bytes, the shape needs "
+                             f"{min_bytes[name]}")
+        return ptr
+    return ck
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -161,42 +192,47 @@ def alloc_workspace(shape: Shape, op: int, device=None) -> torch.Tensor:
 
 
 def feature_map(shape: Shape, x, phi, x_out, normalize_rows=False, stream=None):
+    ck = _checker(shape)
     a = shape.torch_dtype
-    _check(_lib.arl2_feature_map(ctypes.byref(shape.c()), _ptr(x, "x", a), _ptr(phi, "phi", a),
-                                 _ptr(x_out, "x_out", a), int(bool(normalize_rows)),
+    _check(_lib.arl2_feature_map(ctypes.byref(shape.c()), ck(x, "x", a), ck(phi, "phi", a),
+                                 ck(x_out, "x_out", a), int(bool(normalize_rows)),
                                  _stream(stream)))
 
 
 def intra_attn(shape: Shape, q, k, v, o_intra, stream=None):
+    ck = _checker(shape)
     a = shape.torch_dtype
-    _check(_lib.arl2_intra_attn(ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a),
-                                _ptr(v, "v", a), _ptr(o_intra, "o_intra", a), _stream(stream)))
+    _check(_lib.arl2_intra_attn(ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a),
+                                ck(v, "v", a), ck(o_intra, "o_intra", a), _stream(stream)))
 
 
 def inter_read(shape: Shape, q_prime, S, o_intra, o, stream=None):
+    ck = _checker(shape)
     a = shape.torch_dtype
-    _check(_lib.arl2_inter_read(ctypes.byref(shape.c()), _ptr(q_prime, "q_prime", a),
-                                _ptr(S, "S", torch.float32),
-                                _ptr(o_intra, "o_intra", a, optional=True), _ptr(o, "o", a),
+    _check(_lib.arl2_inter_read(ctypes.byref(shape.c()), ck(q_prime, "q_prime", a),
+                                ck(S, "S", torch.float32),
+                                ck(o_intra, "o_intra", a, optional=True), ck(o, "o", a),
                                 _stream(stream)))
 
 
 def state_commit(shape: Shape, k_prime, v_prime, beta, alpha, S_prev, S_next, ws, stream=None):
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_state_commit(
-        ctypes.byref(shape.c()), _ptr(k_prime, "k_prime", a), _ptr(v_prime, "v_prime", a),
-        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
-        _ptr(S_next, "S_next", f), _ptr(ws, "ws", optional=True),
+        ctypes.byref(shape.c()), ck(k_prime, "k_prime", a), ck(v_prime, "v_prime", a),
+        ck(beta, "beta", f), ck(alpha, "alpha", f), ck(S_prev, "S_prev", f),
+        ck(S_next, "S_next", f), ck(ws, "ws", optional=True),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
 def read(shape: Shape, q, k, v, phi_q, S, o, o_intra=None, o_inter=None, ws=None, stream=None):
+    ck = _checker(shape)
     a = shape.torch_dtype
     _check(_lib.arl2_read(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(phi_q, "phi_q", a), _ptr(S, "S", torch.float32), _ptr(o, "o", a),
-        _ptr(o_intra, "o_intra", a, optional=True), _ptr(o_inter, "o_inter", a, optional=True),
-        _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(phi_q, "phi_q", a), ck(S, "S", torch.float32), ck(o, "o", a),
+        ck(o_intra, "o_intra", a, optional=True), ck(o_inter, "o_inter", a, optional=True),
+        ck(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
         _stream(stream)))
 
 
@@ -209,80 +245,87 @@ def alloc_prepared(shape: Shape, device=None) -> torch.Tensor:
 
 
 def read_prepare(shape: Shape, phi_q, S, prepared, stream=None):
-    _check(_lib.arl2_read_prepare(ctypes.byref(shape.c()), _ptr(phi_q, "phi_q", shape.torch_dtype),
-                                  _ptr(S, "S", torch.float32), _ptr(prepared, "prepared"),
+    ck = _checker(shape)
+    _check(_lib.arl2_read_prepare(ctypes.byref(shape.c()), ck(phi_q, "phi_q", shape.torch_dtype),
+                                  ck(S, "S", torch.float32), ck(prepared, "prepared"),
                                   _stream(stream)))
 
 
 def read_prepared(shape: Shape, q, k, v, prepared, o, o_intra=None, o_inter=None, ws=None,
                   stream=None):
+    ck = _checker(shape)
     a = shape.torch_dtype
     _check(_lib.arl2_read_prepared(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(prepared, "prepared"), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
-        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(prepared, "prepared"), ck(o, "o", a), ck(o_intra, "o_intra", a, optional=True),
+        ck(o_inter, "o_inter", a, optional=True), ck(ws, "ws", optional=True),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
 def clean_pass_prepared(shape: Shape, q, k, v, prepared, phi_k, phi_v, beta, alpha, S_prev,
                         S_next, o, o_intra=None, o_inter=None, ws=None, stream=None, phi_q=None,
                         prepared_next=None):
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_clean_pass_prepared(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(prepared, "prepared"), _ptr(phi_q, "phi_q", a, optional=True),
-        _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f),
-        _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f), _ptr(S_next, "S_next", f),
-        _ptr(prepared_next, "prepared_next", optional=True), _ptr(o, "o", a),
-        _ptr(o_intra, "o_intra", a, optional=True), _ptr(o_inter, "o_inter", a, optional=True),
-        _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(prepared, "prepared"), ck(phi_q, "phi_q", a, optional=True),
+        ck(phi_k, "phi_k", a), ck(phi_v, "phi_v", a), ck(beta, "beta", f),
+        ck(alpha, "alpha", f), ck(S_prev, "S_prev", f), ck(S_next, "S_next", f),
+        ck(prepared_next, "prepared_next", optional=True), ck(o, "o", a),
+        ck(o_intra, "o_intra", a, optional=True), ck(o_inter, "o_inter", a, optional=True),
+        ck(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
         _stream(stream)))
 
 
 def commit(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, stream=None):
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_commit(
-        ctypes.byref(shape.c()), _ptr(k, "k", a), _ptr(v, "v", a), _ptr(phi_k, "phi_k", a),
-        _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f), _ptr(alpha, "alpha", f),
-        _ptr(S_prev, "S_prev", f), _ptr(S_next, "S_next", f), _ptr(ws, "ws", optional=True),
+        ctypes.byref(shape.c()), ck(k, "k", a), ck(v, "v", a), ck(phi_k, "phi_k", a),
+        ck(phi_v, "phi_v", a), ck(beta, "beta", f), ck(alpha, "alpha", f),
+        ck(S_prev, "S_prev", f), ck(S_next, "S_next", f), ck(ws, "ws", optional=True),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
 def clean_pass(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, S_next, o,
                o_intra=None, o_inter=None, ws=None, stream=None):
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_clean_pass(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(phi_q, "phi_q", a), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
-        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
-        _ptr(S_next, "S_next", f), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
-        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(phi_q, "phi_q", a), ck(phi_k, "phi_k", a), ck(phi_v, "phi_v", a),
+        ck(beta, "beta", f), ck(alpha, "alpha", f), ck(S_prev, "S_prev", f),
+        ck(S_next, "S_next", f), ck(o, "o", a), ck(o_intra, "o_intra", a, optional=True),
+        ck(o_inter, "o_inter", a, optional=True), ck(ws, "ws", optional=True),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
 def token_read(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, S, o, o_intra=None,
                o_inter=None, ws=None, stream=None):
     """Read under token-level access (token t sees the frame's earlier tokens)."""
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_token_read(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(phi_q, "phi_q", a), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
-        _ptr(beta, "beta", f), _ptr(S, "S", f), _ptr(o, "o", a),
-        _ptr(o_intra, "o_intra", a, optional=True), _ptr(o_inter, "o_inter", a, optional=True),
-        _ptr(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(phi_q, "phi_q", a), ck(phi_k, "phi_k", a), ck(phi_v, "phi_v", a),
+        ck(beta, "beta", f), ck(S, "S", f), ck(o, "o", a),
+        ck(o_intra, "o_intra", a, optional=True), ck(o_inter, "o_inter", a, optional=True),
+        ck(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
         _stream(stream)))
 
 
 def token_clean_pass(shape: Shape, q, k, v, phi_q, phi_k, phi_v, beta, alpha, S_prev, S_next, o,
                      o_intra=None, o_inter=None, ws=None, stream=None):
     """Clean pass under token-level access: the read, then S_next from its end state."""
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_token_clean_pass(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(phi_q, "phi_q", a), _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a),
-        _ptr(beta, "beta", f), _ptr(alpha, "alpha", f), _ptr(S_prev, "S_prev", f),
-        _ptr(S_next, "S_next", f), _ptr(o, "o", a), _ptr(o_intra, "o_intra", a, optional=True),
-        _ptr(o_inter, "o_inter", a, optional=True), _ptr(ws, "ws", optional=True),
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(phi_q, "phi_q", a), ck(phi_k, "phi_k", a), ck(phi_v, "phi_v", a),
+        ck(beta, "beta", f), ck(alpha, "alpha", f), ck(S_prev, "S_prev", f),
+        ck(S_next, "S_next", f), ck(o, "o", a), ck(o_intra, "o_intra", a, optional=True),
+        ck(o_inter, "o_inter", a, optional=True), ck(ws, "ws", optional=True),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
@@ -293,22 +336,24 @@ def _ws(ws):
 def intra_attn_backward(shape: Shape, q, k, v, o_intra, d_o, dq, dk, dv, accumulate=False,
                         ws=None, stream=None):
     """dq, dk, dv of the intra-frame softmax from its output o_intra and dL/dO_intra."""
+    ck = _checker(shape)
     a = shape.torch_dtype
     _check(_lib.arl2_intra_attn_backward(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(o_intra, "o_intra", a), _ptr(d_o, "d_o", a), _ptr(dq, "dq", a), _ptr(dk, "dk", a),
-        _ptr(dv, "dv", a), 1 if accumulate else 0, *_ws(ws), _stream(stream)))
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(o_intra, "o_intra", a), ck(d_o, "d_o", a), ck(dq, "dq", a), ck(dk, "dk", a),
+        ck(dv, "dv", a), 1 if accumulate else 0, *_ws(ws), _stream(stream)))
 
 
 def read_backward(shape: Shape, q, k, v, phi_q, S, o_intra, d_o, dq, dk, dv, dphi_q, dS,
                   accumulate=False, ws=None, stream=None):
     """Gradients of a read O = O_intra + (Q Phi_q) S given dL/dO."""
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_read_backward(
-        ctypes.byref(shape.c()), _ptr(q, "q", a), _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(phi_q, "phi_q", a), _ptr(S, "S", f), _ptr(o_intra, "o_intra", a),
-        _ptr(d_o, "d_o", a), _ptr(dq, "dq", a), _ptr(dk, "dk", a), _ptr(dv, "dv", a),
-        _ptr(dphi_q, "dphi_q", f), _ptr(dS, "dS", f), 1 if accumulate else 0, *_ws(ws),
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(phi_q, "phi_q", a), ck(S, "S", f), ck(o_intra, "o_intra", a),
+        ck(d_o, "d_o", a), ck(dq, "dq", a), ck(dk, "dk", a), ck(dv, "dv", a),
+        ck(dphi_q, "dphi_q", f), ck(dS, "dS", f), 1 if accumulate else 0, *_ws(ws),
         _stream(stream)))
 
 
@@ -316,37 +361,40 @@ def commit_backward(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S_prev, dS_ne
                     dphi_k, dphi_v, dbeta, dalpha, dS_prev, accumulate=False, ws=None,
                     stream=None):
     """Gradients of the commit given dL/dS_next."""
+    ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_commit_backward(
-        ctypes.byref(shape.c()), _ptr(k, "k", a), _ptr(v, "v", a), _ptr(phi_k, "phi_k", a),
-        _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f), _ptr(alpha, "alpha", f),
-        _ptr(S_prev, "S_prev", f), _ptr(dS_next, "dS_next", f), _ptr(dk, "dk", a),
-        _ptr(dv, "dv", a), _ptr(dphi_k, "dphi_k", f), _ptr(dphi_v, "dphi_v", f),
-        _ptr(dbeta, "dbeta", f), _ptr(dalpha, "dalpha", f), _ptr(dS_prev, "dS_prev", f),
+        ctypes.byref(shape.c()), ck(k, "k", a), ck(v, "v", a), ck(phi_k, "phi_k", a),
+        ck(phi_v, "phi_v", a), ck(beta, "beta", f), ck(alpha, "alpha", f),
+        ck(S_prev, "S_prev", f), ck(dS_next, "dS_next", f), ck(dk, "dk", a),
+        ck(dv, "dv", a), ck(dphi_k, "dphi_k", f), ck(dphi_v, "dphi_v", f),
+        ck(dbeta, "dbeta", f), ck(dalpha, "dalpha", f), ck(dS_prev, "dS_prev", f),
         1 if accumulate else 0, *_ws(ws), _stream(stream)))
 
 
 def state_scan(shape: Shape, k, v, phi_k, phi_v, beta, alpha, S0, states, ws=None, stream=None):
     """states[0] = S0 and states[f + 1] = the commit of frame f (k, v: [F, B, H, T, D])."""
+    ck = _checker(shape, frames=int(k.shape[0]), state_frames=int(k.shape[0]) + 1)
     a, f = shape.torch_dtype, torch.float32
     n_frames = int(k.shape[0])
     if tuple(states.shape[:1]) != (n_frames + 1,):
         raise ValueError("states needs n_frames + 1 entries")
     _check(_lib.arl2_state_scan(
-        ctypes.byref(shape.c()), n_frames, _ptr(k, "k", a), _ptr(v, "v", a),
-        _ptr(phi_k, "phi_k", a), _ptr(phi_v, "phi_v", a), _ptr(beta, "beta", f),
-        _ptr(alpha, "alpha", f), _ptr(S0, "S0", f), _ptr(states, "states", f), *_ws(ws),
+        ctypes.byref(shape.c()), n_frames, ck(k, "k", a), ck(v, "v", a),
+        ck(phi_k, "phi_k", a), ck(phi_v, "phi_v", a), ck(beta, "beta", f),
+        ck(alpha, "alpha", f), _checker(shape)(S0, "S0", f), ck(states, "states", f), *_ws(ws),
         _stream(stream)))
 
 
 def fullkv_attn(shape: Shape, q, k_cache, v_cache, n_kv: int, o, stream=None):
+    ck = _checker(shape)
     a = shape.torch_dtype
     cap = k_cache.shape[2]
     if tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache and v_cache shapes differ")
-    _check(_lib.arl2_fullkv_attn(ctypes.byref(shape.c()), _ptr(q, "q", a),
-                                 _ptr(k_cache, "k_cache", a), _ptr(v_cache, "v_cache", a),
-                                 int(n_kv), int(cap), _ptr(o, "o", a), _stream(stream)))
+    _check(_lib.arl2_fullkv_attn(ctypes.byref(shape.c()), ck(q, "q", a),
+                                 ck(k_cache, "k_cache", a), ck(v_cache, "v_cache", a),
+                                 int(n_kv), int(cap), ck(o, "o", a), _stream(stream)))
 
 
 def raw_call(name: str, *args):

@@ -279,3 +279,25 @@ def test_read_paths_agree(case):
     assert_close(host(o2), ref["o"], TOL[w.dtype], "o")
     assert_close(host(oi), ref["o_intra"], TOL[w.dtype], "o_intra")
     assert_close(host(oe), ref["o_inter"], TOL[w.dtype], "o_inter")
+
+
+def test_binding_rejects_wrong_sizes():
+    """The binding checks every tensor's element count against the shape
+    before calling the library (which sees only pointers): a tensor one
+    element short, or a map of the wrong head count, raises without a launch."""
+    import torch
+    from hybrid_linear_memory_amd import arl2
+    sh = arl2.Shape(1, 2, 64, 128, arl2.BF16)
+    act = dict(dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 2, 64, 128), **act)
+    short = torch.zeros(1 * 2 * 64 * 128 - 1, **act)
+    o = torch.zeros_like(q)
+    with pytest.raises(ValueError, match="elements"):
+        arl2.intra_attn(sh, q, short, q, o)
+    phi = torch.zeros((3, 128, 128), **act)
+    S = torch.zeros((1, 2, 128, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="phi_q"):
+        arl2.read(sh, q, q, q, phi, S, o, ws=arl2.alloc_workspace(sh, arl2.OP_READ))
+    small = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="prepared"):
+        arl2.read_prepared(sh, q, q, q, small, o)
