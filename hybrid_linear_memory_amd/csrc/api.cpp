@@ -104,7 +104,8 @@ size_t prepared_bytes(const arl2::Dims& d) {
   return (size_t)d.B * d.H * d.D * d.D * (arl2::use_mfma(d) ? 2 : 4);
 }
 size_t ws_read_prepared(const arl2::Dims& d) {
-  return arl2::use_mfma(d) ? 0 : arl2::round_up(arl2::act_bytes(d), 256);
+  return arl2::use_mfma(d) ? arl2::mfma_read_prepared_ws_bytes(d)
+                           : arl2::round_up(arl2::act_bytes(d), 256);
 }
 size_t ws_commit(const arl2::Dims& d) {
   if (arl2::use_mfma(d)) return arl2::round_up(arl2::mfma_commit_ws_bytes(d), 256);
@@ -453,7 +454,8 @@ arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q, const voi
   OPTIONAL_PTR(o_intra);
   OPTIONAL_PTR(o_inter);
   const size_t need = ws_read_prepared(d);
-  if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
+  // bf16: the workspace is optional (without it the read runs on the plain grid)
+  if ((ws || !arl2::use_mfma(d)) && (st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
   const size_t ab = arl2::act_bytes(d);
   const Range outs[3] = {{o, ab}, {o_intra, ab}, {o_inter, ab}};
   const Range ins[5] = {{q, ab}, {k, ab}, {v, ab}, {prepared, prepared_bytes(d)}, {ws, need}};
@@ -464,7 +466,8 @@ arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q, const voi
     return fail(ARL2_E_ALIAS, "outputs o, o_intra, o_inter overlap");
   hipStream_t s = (hipStream_t)stream;
   if (arl2::use_mfma(d))
-    return hip_status(arl2::mfma_read_prepared(d, q, k, v, prepared, o, o_intra, o_inter, s),
+    return hip_status(arl2::mfma_read_prepared(d, q, k, v, prepared, o, o_intra, o_inter, ws,
+                                               ws ? ws_bytes : 0, s),
                       "prepared read");
   void* oi = o_intra ? o_intra : ws;
   hipError_t e = run_attention(d, q, k, v, oi, d.T, d.T, s);

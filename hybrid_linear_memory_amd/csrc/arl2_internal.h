@@ -45,14 +45,19 @@ hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
                            const void* o_intra, void* o, void* o_inter,
                            hipStream_t s);
 // Fused read (bf16, D = 128): M = Phi_q S per head into `ws`, then the
-// attention kernel with the epilogue O = O_intra + Q M.
+// attention kernel with the epilogue O = O_intra + Q M (the split read's
+// workspace follows M).
 size_t mfma_read_ws_bytes(const Dims& d);
 // Prepared reads: M^T = (Phi_q S)^T once per frame, then attention + Q M.
 hipError_t mfma_read_prepare(const Dims& d, const void* phi_q, const float* S, void* mt,
                              hipStream_t s);
+// With a workspace of mfma_read_prepared_ws_bytes (0: never used for this
+// shape), shapes whose grid would leave compute units idle split key ranges
+// over one workgroup per compute unit; ws may be null (plain grid).
+size_t mfma_read_prepared_ws_bytes(const Dims& d);
 hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const void* v,
-                              const void* mt, void* o, void* o_intra, void* o_inter,
-                              hipStream_t s);
+                              const void* mt, void* o, void* o_intra, void* o_inter, void* ws,
+                              size_t ws_bytes, hipStream_t s);
 // Clean pass from a prepared map in one launch (fused read workgroups plus the
 // fused commit's workgroups), then the chunk reduction, which also forms the
 // map of S_next into mt_next when mt_next is given (phi_q then required); ws

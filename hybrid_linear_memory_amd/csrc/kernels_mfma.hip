@@ -10,6 +10,9 @@
 // layout is described in mfma_common.h.
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "arl2_internal.h"
 #include "mfma_common.h"
 
@@ -198,6 +201,50 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
   __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
 }
 
+// Split key ranges ("stream-K"): when a shape's query blocks are too few to
+// fill the chip, the key tiles of all query blocks are laid end to end and
+// dealt evenly to one workgroup per compute unit, so a workgroup may hold the
+// end of one query block's keys and the start of the next's (a segment each).
+// A segment that is not a whole block publishes its unnormalised output, its
+// reference maximum and its row sums in a slot of the workspace; the last of a
+// block's segments to arrive (a per-block counter) merges them in key order.
+// No workgroup waits for another.
+constexpr int kSkSlotFloats = 8 * 2048 + 2 * 512;   // output, then (maximum, sum) pairs
+constexpr int kSkStatOff = 8 * 2048 * 4;              // byte offset of the pairs
+constexpr int kCoherent = 16;                         // cache policy: device scope (sc1)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct SkSeg {
+  float* slots;                  // [2 * grid] slots of kSkSlotFloats
+  unsigned long long* ctr;       // one counter per query block
+  unsigned long long tag;        // this call's tag, in bits 16..63
+  int nseg, iseg;                // the block's segment count, this segment's index
+  int my_slot;                   // this segment's slot
+  int wf, first_local;           // workgroup of the block's first segment, its slot parity
+  __device__ int slot_of(int i) const { return i == 0 ? 2 * wf + first_local : 2 * (wf + i); }
+};
+
+// Counts one arrival at a block's counter; true for the block's last segment.
+// The counter holds (tag << 16 | count) while a call is under way and is left
+// at 0 by the last arrival; a value from another call (or any other content of
+// the workspace) carries a different tag and counts as 0, so the workspace
+// needs no clearing between calls. Each failed exchange means another arrival
+// succeeded, so the loop ends after at most nseg attempts.
+__device__ __forceinline__ bool sk_arrive(unsigned long long* ctr, unsigned long long tag,
+                                          int nseg) {
+  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const unsigned c = (old >> 16) == (tag >> 16) ? (unsigned)(old & 0xFFFFu) : 0u;
+    const bool last = (int)c + 1 == nseg;
+    const unsigned long long nw = last ? 0ull : (tag | (c + 1u));
+    if (__hip_atomic_compare_exchange_strong(ctr, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return last;
+  }
+}
+
 // With INTER (the fused read), the epilogue adds the inter-frame branch
 // O_inter = Q M, M = Phi_q S (given transposed in `mt`, bf16 [B, H, D_v,
 // D_in]); the two branches can also be written separately to o_intra /
@@ -205,13 +252,14 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
 // One workgroup (logical block `blk`) of the attention; the LDS arrays are the
 // kernel's (see AKV) and reach here as parameters so that, once inlined, every
 // access still names its own array.
-template <bool INTER>
+template <bool INTER, bool SK = false>
 __device__ __forceinline__ void attn_block(
     int blk, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv, long kv_cap,
     float sl2, int n_qblk, const __bf16* __restrict__ mt, __bf16* __restrict__ o_intra,
     __bf16* __restrict__ o_inter, char* lk0, char* lk1, char* lv0, char* lv1,
-    float (*mlx)[2][64], int& redo_flag) {
+    float (*mlx)[2][64], int& redo_flag, int t0 = 0, int nt = -1,
+    const SkSeg* sk = nullptr, int* sk_last = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -231,7 +279,9 @@ __device__ __forceinline__ void attn_block(
 
   // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s.
   // Wave 4s + w loads rows [16w, 16w + 16) of the stream's K and V tiles.
-  const int n_tiles = (n_kv + AKT - 1) / AKT;
+  // this workgroup's key tiles: [t0, t0 + n_tiles) (all of them unless SK)
+  const int n_tiles = SK ? nt : (n_kv + AKT - 1) / AKT;
+  if (!SK) t0 = 0;
   const int my_cnt = (n_tiles - stream + 1) / 2;
   const uint32_t kv_bytes = (uint32_t)n_kv * (HD * 2);
   const __amdgpu_buffer_rsrc_t k_src = buffer_rsrc(k + (size_t)bh * kv_cap * HD, kv_bytes);
@@ -248,12 +298,12 @@ __device__ __forceinline__ void attn_block(
   auto load_k = [&](char* dst, int j) __attribute__((always_inline)) {
     int qoff = (wave & 3) * 4096;       // opaque: offsets formed in place
     asm volatile("" : "+s"(qoff));
-    tile_quarter<false>(dst, k_src, (2 * j + stream) * TILE_B, qoff, k_off);
+    tile_quarter<false>(dst, k_src, (t0 + 2 * j + stream) * TILE_B, qoff, k_off);
   };
   auto load_v = [&](char* dst, int j) __attribute__((always_inline)) {
     int qoff = (wave & 3) * 4096;
     asm volatile("" : "+s"(qoff));
-    tile_quarter<true>(dst, v_src, (2 * j + stream) * TILE_B, qoff, v_off);
+    tile_quarter<true>(dst, v_src, (t0 + 2 * j + stream) * TILE_B, qoff, v_off);
   };
   // M^T (the inter-frame map, 32 KB) is loaded during the last iteration into
   // the K buffers that iteration leaves idle (rows under the swz_r swizzle),
@@ -302,7 +352,7 @@ __device__ __forceinline__ void attn_block(
     f32x16 s[2];
     auto scores = [&](int j, const char* Kb) __attribute__((always_inline)) {
       attn_qk(s, Kb, off, qreg);
-      const int valid = n_kv - (2 * j + stream) * AKT;
+      const int valid = n_kv - (t0 + 2 * j + stream) * AKT;
       if (valid < AKT) attn_mask(s, valid, lane);
       if (mode == 1) m_ref = fmaxf(m_ref, attn_tile_max(s));
       if (mode == 0 && j == 0) m_ref = attn_tile_max(s);
@@ -396,8 +446,11 @@ __device__ __forceinline__ void attn_block(
   const float m = fmaxf(m_ref, mb);
   const float fa = __builtin_amdgcn_exp2f((m_ref - m) * sl2);
   const float fb = __builtin_amdgcn_exp2f((mb - m) * sl2);
-  const float inv = 1.f / halves_sum(l * fa + lb * fb);
-  if (t < T) {
+  const float lsum = halves_sum(l * fa + lb * fb);
+  // Writes this wave's 32 queries x 64 output columns: intra(b2, r) is the
+  // normalised softmax branch of accumulator register r of column block b2.
+  auto store = [&](auto intra_of) __attribute__((always_inline)) {
+    if (t >= T) return;
     const size_t row = ((size_t)bh * T + t) * HD + 4 * h2;
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
@@ -408,8 +461,7 @@ __device__ __forceinline__ void attn_block(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * jj + i;
-          const float vb = ex_r[(b2 * 16 + r) * 64 + lane];
-          const float intra = (keep[b2][r] * fa + vb * fb) * inv;
+          const float intra = intra_of(b2, r);
           const float inter = INTER ? oi[b2][r] : 0.f;
           w[i] = (__bf16)(intra + inter);
           wi[i] = (__bf16)intra;
@@ -421,7 +473,88 @@ __device__ __forceinline__ void attn_block(
         if (o_inter) *reinterpret_cast<bf16x4*>(o_inter + off_o) = we;
       }
     }
+  };
+  if (SK && sk->nseg > 1) {
+    // A part of the query block's keys: publish the unnormalised output, the
+    // reference maximum and the row sum; the segment that arrives last merges
+    // every segment's results, in key order, and writes the output. Slots are
+    // written and read with the device-scope coherence bit (what agent-scope
+    // atomic accesses compile to: coherent across the XCDs' L2 caches without
+    // writing back or invalidating them); each wave waits for its stores to
+    // complete before the workgroup counts its arrival, and the last arrival
+    // reads the slots only after that.
+    f32x4 c[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b2 = g >> 2, r = 4 * (g & 3) + e;
+        c[g][e] = keep[b2][r] * fa + ex_r[(b2 * 16 + r) * 64 + lane] * fb;
+      }
+    const __amdgpu_buffer_rsrc_t mine =
+        buffer_rsrc(sk->slots + (size_t)sk->my_slot * kSkSlotFloats, kSkSlotFloats * 4);
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c[g]), mine,
+                                             ((wave * 8 + g) * 64 + lane) * 16, 0, kCoherent);
+    const f32x2 ml = {m, lsum};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), mine,
+                                          kSkStatOff + (wave * 64 + lane) * 8, 0, kCoherent);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) *sk_last = sk_arrive(sk->ctr + blk, sk->tag, sk->nseg) ? 1 : 0;
+    __syncthreads();
+    if (*sk_last == 0) return;
+    // The other segments (at most two: the host plans only grids whose
+    // workgroup ranges cover at least half a block), all loads issued before
+    // the first use (an index past nseg reads an empty range: zeros, no access).
+    f32x2 om[2];
+    f32x4 od[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = j < sk->iseg ? j : j + 1;
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(sk->slots + (size_t)sk->slot_of(i < sk->nseg ? i : 0) * kSkSlotFloats,
+                      i < sk->nseg ? kSkSlotFloats * 4 : 0);
+      om[j] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rs, kSkStatOff + (wave * 64 + lane) * 8, 0, kCoherent));
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        od[j][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, ((wave * 8 + g) * 64 + lane) * 16, 0,
+                                                 kCoherent));
+    }
+    float mx = m;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j + 1 < sk->nseg) mx = fmaxf(mx, om[j][0]);
+    f32x4 acc2[8];
+    float lt = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) acc2[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // key order: segment i is this one (i == iseg) or other j = i - (i > iseg)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (i >= sk->nseg) break;
+      const bool own = i == sk->iseg;
+      const bool j1 = i > sk->iseg ? i - 1 == 1 : i == 1;
+      const float mi = own ? m : (j1 ? om[1][0] : om[0][0]);
+      const float li = own ? lsum : (j1 ? om[1][1] : om[0][1]);
+      const float wi = __builtin_amdgcn_exp2f((mi - mx) * sl2);
+      lt += wi * li;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) acc2[g] += wi * (own ? c[g] : (j1 ? od[1][g] : od[0][g]));
+    }
+    const float inv = 1.f / lt;
+    store([&](int b2, int r) __attribute__((always_inline)) {
+      return acc2[b2 * 4 + (r >> 2)][r & 3] * inv;
+    });
+    return;
   }
+  const float inv = 1.f / lsum;
+  store([&](int b2, int r) __attribute__((always_inline)) {
+    return (keep[b2][r] * fa + ex_r[(b2 * 16 + r) * 64 + lane] * fb) * inv;
+  });
 }
 
 // L2 warm-up by a workgroup on an otherwise idle compute unit: block i of the
@@ -483,6 +616,58 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   else if (b >= n_attn_pad)
     attn_l2_warm(b - n_attn_pad, ((int)gridDim.x - n_attn_pad) / 8, n_attn, n_qblk, k, v, n_kv,
                  kv_cap, lk0);
+}
+
+// Split-key attention grid: one workgroup per compute unit (gridDim.x = G).
+// Block qb's tiles sit at [qb L + pad, (qb + 1) L) of a line of n_blk L slots
+// (L = tiles per block + pad); workgroup w takes [w V / G, (w + 1) V / G),
+// V = n_blk L. The pad slots before each block make a workgroup that crosses
+// a block boundary (and pays a second ramp and a merge) take fewer tiles.
+// With n_blk <= G a workgroup meets at most two blocks.
+__device__ __forceinline__ int sk_wg_of(long x, long V, int G) {
+  return (int)(((x + 1) * G - 1) / V);
+}
+
+template <bool INTER>
+__global__ void __launch_bounds__(512, 1)
+attn_sk_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+          const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, float sl2, int n_qblk,
+          const __bf16* __restrict__ mt, __bf16* __restrict__ o_intra,
+          __bf16* __restrict__ o_inter, int n_blk, int pad, float* __restrict__ slots,
+          unsigned long long* __restrict__ ctr, unsigned long long tag) {
+  __shared__ __attribute__((aligned(1024))) char lk0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lk1[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv0[AKV];
+  __shared__ __attribute__((aligned(1024))) char lv1[AKV];
+  __shared__ float mlx[8][2][64];
+  __shared__ int redo_flag;
+  __shared__ int sk_last;
+  const int G = (int)gridDim.x;
+  const int w = xcd_remap(blockIdx.x, G);
+  const int n_tiles = (T + AKT - 1) / AKT;
+  const long L = n_tiles + pad, V = (long)n_blk * L;
+  const long v0 = (long)w * V / G, v1 = (long)(w + 1) * V / G;
+  int local = 0;
+  for (int qb = (int)(v0 / L); qb < n_blk && (long)qb * L < v1; ++qb) {
+    const long rs = (long)qb * L + pad;
+    const long a = v0 > rs ? v0 : rs;
+    const long b = v1 < rs + n_tiles ? v1 : rs + n_tiles;
+    if (a >= b) continue;
+    SkSeg sg;
+    sg.slots = slots;
+    sg.ctr = ctr;
+    sg.tag = tag;
+    sg.wf = sk_wg_of(rs, V, G);
+    sg.nseg = sk_wg_of(rs + n_tiles - 1, V, G) - sg.wf + 1;
+    sg.iseg = w - sg.wf;
+    sg.first_local = (long)sg.wf * V / G < (long)qb * L ? 1 : 0;
+    sg.my_slot = 2 * w + local;
+    if (local > 0) __syncthreads();      // the previous segment's LDS reads are done
+    attn_block<INTER, true>(qb, q, k, v, o, T, T, T, sl2, n_qblk, mt, o_intra, o_inter, lk0,
+                            lk1, lv0, lv1, mlx, redo_flag, (int)(a - rs), (int)(b - a), &sg,
+                            &sk_last);
+    ++local;
+  }
 }
 
 // ===========================================================================
@@ -1202,7 +1387,52 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const voi
   return hipGetLastError();
 }
 
-size_t mfma_read_ws_bytes(const Dims& d) { return (size_t)d.B * d.H * HD * HD * 2; }
+// Split-key fused read (attn_sk_k): used when the plain grid (one workgroup
+// per 128 queries of a head) leaves compute units idle and the longest split
+// workgroup is estimated to finish at least 10% before a whole query block
+// does. Measured on MI355X: a segment boundary costs about 12 key tiles, so
+// the split pays off for long frames with few heads (4 x 4096 tokens: 60 ->
+// 45 us; 1 x 16384: 233 -> 134 us) and not at 12 heads x 1560 tokens (25
+// tiles per block).
+constexpr int kSkMaxGrid = 256;
+constexpr int kSkPad = 2;
+constexpr int kSkBoundaryTiles = 12;
+struct SkPlan {
+  bool use;
+  int G, pad;
+};
+static SkPlan sk_plan(const Dims& d, int n_cu) {
+  SkPlan p{false, 0, kSkPad};
+  const int n_tiles = (d.T + AKT - 1) / AKT;
+  const long n_blk = (long)d.B * d.H * ((d.T + AQ - 1) / AQ);
+  const int G = std::min(n_cu, kSkMaxGrid);
+  if (G <= 0 || n_blk > G || n_tiles < 4) return p;
+  const long L = n_tiles + p.pad, V = n_blk * L;
+  // each workgroup's range covers at least half a block, so a block meets at
+  // most three workgroups (the merge reads at most two other segments at once)
+  if (V < G || V / G < (L + 1) / 2) return p;
+  // key tiles on the longest workgroup's path: a whole block on the plain
+  // grid; on the split grid its range plus the cost of a segment boundary
+  // (publishing a partial, the counter, the merge: about kSkBoundaryTiles)
+  p.use = 10 * ((V + G - 1) / G + kSkBoundaryTiles) < 9 * n_tiles;
+  p.G = G;
+  return p;
+}
+static long sk_ctr_bytes(const Dims& d) {
+  return (long)round_up((size_t)d.B * d.H * ((d.T + AQ - 1) / AQ) * 8, 256);
+}
+
+size_t mfma_read_prepared_ws_bytes(const Dims& d) {
+  if (!sk_plan(d, kSkMaxGrid).use) return 0;
+  return (size_t)sk_ctr_bytes(d) + (size_t)2 * kSkMaxGrid * kSkSlotFloats * sizeof(float);
+}
+
+size_t mfma_read_ws_bytes(const Dims& d) {
+  return round_up((size_t)d.B * d.H * HD * HD * 2, 256) + mfma_read_prepared_ws_bytes(d);
+}
+
+// Per-call tags of the split read's block counters (48 bits, never 0).
+static std::atomic<unsigned long long> g_sk_tag{0};
 
 hipError_t mfma_read_prepare(const Dims& d, const void* phi_q, const float* S, void* mt,
                              hipStream_t s) {
@@ -1212,10 +1442,31 @@ hipError_t mfma_read_prepare(const Dims& d, const void* phi_q, const float* S, v
 }
 
 hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const void* v,
-                              const void* mt, void* o, void* o_intra, void* o_inter,
-                              hipStream_t s) {
+                              const void* mt, void* o, void* o_intra, void* o_inter, void* ws,
+                              size_t ws_bytes, hipStream_t s) {
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long nblk = (long)d.B * d.H * n_qblk;
+  const size_t sk_need = mfma_read_prepared_ws_bytes(d);
+  if (ws && sk_need > 0 && ws_bytes >= sk_need) {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 0;
+    const SkPlan p = sk_plan(d, n_cu);
+    if (p.use) {
+      unsigned long long tag = 0;
+      while (tag == 0) tag = (++g_sk_tag) & 0xFFFFFFFFFFFFull;
+      char* w = static_cast<char*>(ws);
+      attn_sk_k<true><<<(unsigned)p.G, 512, 0, s>>>(
+          static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+          static_cast<const __bf16*>(v), static_cast<__bf16*>(o), d.T, d.scale * kLog2e, n_qblk,
+          static_cast<const __bf16*>(mt), static_cast<__bf16*>(o_intra),
+          static_cast<__bf16*>(o_inter), (int)nblk, p.pad,
+          reinterpret_cast<float*>(w + sk_ctr_bytes(d)),
+          reinterpret_cast<unsigned long long*>(w), tag << 16);
+      return hipGetLastError();
+    }
+  }
   long n_pad, total;
   attn_grid(nblk, d.T, &n_pad, &total);
   attn_mfma_k<true><<<(unsigned)total, 512, 0, s>>>(
@@ -1263,7 +1514,9 @@ hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
                      void* ws, hipStream_t s) {
   hipError_t e = mfma_read_prepare(d, phi_q, S, ws, s);
   if (e != hipSuccess) return e;
-  return mfma_read_prepared(d, q, k, v, ws, o, o_intra, o_inter, s);
+  const size_t mb = round_up((size_t)d.B * d.H * HD * HD * 2, 256);
+  return mfma_read_prepared(d, q, k, v, ws, o, o_intra, o_inter, static_cast<char*>(ws) + mb,
+                            mfma_read_prepared_ws_bytes(d), s);
 }
 
 hipError_t mfma_feature_map(const Dims& d, const void* x, const void* phi, void* out,

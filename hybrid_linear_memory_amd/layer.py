@@ -90,7 +90,8 @@ class Arl2Layer:
                    torch.zeros(st, dtype=torch.float32, device=self.device)]
         self._cur = 0
         ops = ((arl2.OP_TOKEN_LEVEL,) if access == "token" else
-               (arl2.OP_CLEAN_PASS, arl2.OP_CLEAN_PASS_PREPARED, arl2.OP_COMMIT))
+               (arl2.OP_READ, arl2.OP_READ_PREPARED, arl2.OP_CLEAN_PASS,
+                arl2.OP_CLEAN_PASS_PREPARED, arl2.OP_COMMIT))
         ws_bytes = max(arl2.workspace_bytes(shape, op) for op in ops)
         self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.device)
         self.fused_clean = fused_clean

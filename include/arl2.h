@@ -147,7 +147,9 @@ arl2_status arl2_state_commit(const arl2_shape* shape, const void* k_prime,
 /* Denoising-step read: Q' = Q Phi_q[h], o_intra = softmax(QK^T*scale)V,
  * o = o_intra + Q' S. S is const: a read never writes the state.
  * o_intra and o_inter are optional extra outputs (NULL to skip) holding the
- * two branches separately. Needs arl2_workspace_bytes(shape, ARL2_OP_READ). */
+ * two branches separately. Needs arl2_workspace_bytes(shape, ARL2_OP_READ)
+ * (bf16: the map of arl2_read_prepare, then the split read's workspace of
+ * arl2_read_prepared when the shape takes it). */
 arl2_status arl2_read(const arl2_shape* shape, const void* q, const void* k,
                       const void* v, const void* phi_q, const float* S,
                       void* o, void* o_intra, void* o_inter, void* ws,
@@ -166,9 +168,18 @@ arl2_status arl2_read_prepare(const arl2_shape* shape, const void* phi_q,
 
 /* Denoising-step read from a prepared map: o = softmax(Q K^T * scale) V + Q M,
  * identical in meaning to arl2_read with the (Phi_q, S) the map was prepared
- * from. o_intra / o_inter are optional extra outputs. Needs
- * arl2_workspace_bytes(shape, ARL2_OP_READ_PREPARED) bytes of workspace (0 for
- * bf16 shapes). */
+ * from. o_intra / o_inter are optional extra outputs.
+ * Workspace: float32 shapes need arl2_workspace_bytes(shape,
+ * ARL2_OP_READ_PREPARED) bytes. For bf16 shapes it is optional: with ws NULL
+ * the read runs one workgroup per 128 queries of a head; with a workspace of
+ * at least that many bytes (a non-NULL ws smaller than that is
+ * ARL2_E_WORKSPACE), shapes whose query blocks leave compute units idle and
+ * whose frames are long (the size is 0 for other shapes) split each block's
+ * keys over several workgroups and merge their partial softmax results in
+ * key order. Results of the two agree to fp32 rounding order; each is
+ * deterministic. The workspace needs no clearing (its block counters carry a
+ * per-call tag and are left at zero); calls that share a workspace must not
+ * overlap in time. */
 arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q,
                                const void* k, const void* v,
                                const void* prepared, void* o, void* o_intra,

@@ -50,7 +50,24 @@ def test_workspace_sizes(arl2):
     # one-launch clean pass (bf16): the commit partials only
     assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED) == arl2.workspace_bytes(
         s, arl2.OP_COMMIT)
+    # the plain grid at 12 heads x 1560 tokens: no workspace
     assert arl2.workspace_bytes(s, arl2.OP_READ_PREPARED) == 0
+    assert arl2.workspace_bytes(s, arl2.OP_READ) == 12 * 128 * 128 * 2
+    # split-key read (4 heads x 4096 tokens: 128 query blocks of 64 key tiles):
+    # one 8-byte counter per query block, then two slots per workgroup (256)
+    # of 8 x 2048 output floats and 512 (maximum, sum) pairs; the one-call
+    # read puts M^T first
+    s4 = arl2.Shape(1, 4, 4096, 128, arl2.BF16)
+    split = (128 * 8 + 255) // 256 * 256 + 2 * 256 * (8 * 2048 + 1024) * 4
+    assert arl2.workspace_bytes(s4, arl2.OP_READ_PREPARED) == split
+    assert arl2.workspace_bytes(s4, arl2.OP_READ) == 4 * 128 * 128 * 2 + split
+    # no split where the plain grid fills the chip, or at most 10% would be won
+    for B, H, T in ((8, 12, 1560), (1, 3, 300), (1, 6, 4096), (1, 8, 3000)):
+        assert arl2.workspace_bytes(arl2.Shape(B, H, T, 128, arl2.BF16),
+                                    arl2.OP_READ_PREPARED) == 0, (B, H, T)
+    for B, H, T in ((2, 2, 4096), (1, 5, 4000), (1, 3, 8192), (1, 1, 16384)):
+        assert arl2.workspace_bytes(arl2.Shape(B, H, T, 128, arl2.BF16),
+                                    arl2.OP_READ_PREPARED) > 0, (B, H, T)
     assert arl2.workspace_bytes(s, 17) == 0
     assert arl2.workspace_bytes(arl2.Shape(0, 1, 1, 128), arl2.OP_READ) == 0
     f = arl2.Shape(1, 1, 64, 16, arl2.F32)
