@@ -9,7 +9,7 @@ read, combine, state commit. Inputs are seeded synthetic tensors resident in
 HBM before timing starts (a pool of frames is cycled); the state carries over
 from frame to frame. Each frame's calls are launched on the stream as the layer
 driver issues them (replays of a HIP graph of the same launches are timed
-beside, or instead with --graph; on this stack the graph replays run slower).
+beside, or instead with --graph; on this stack both run at about the same rate).
 
 Printed (one JSON line): frames/s (value) and tokens/s, the roofline of the
 dominant kernel (the fused read: intra-frame attention plus the inter-frame
@@ -19,6 +19,12 @@ a bounded sample, and the flatness of per-frame time and memory over a long
 rollout beside the full-KV-cache softmax comparator.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+    python bench.py --workload batched_streams   # 8 videos (8 x 12 heads)
+    python bench.py --workload large_model       # 40 heads
+
+The two other workloads time the same step at their shapes (without the
+traffic counters, the rollout and the oracle baseline, which are taken on the
+one-layer shape).
 """
 from __future__ import annotations
 
@@ -43,8 +49,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="timed frames")
     ap.add_argument("--warmup", type=int, default=20, help="untimed frames")
-    ap.add_argument("--pool", type=int, default=8,
-                    help="distinct resident input frames (even; one graph covers them all)")
+    ap.add_argument("--workload", default="wan13b_layer",
+                    choices=["wan13b_layer", "batched_streams", "large_model"],
+                    help="the one-layer shape (the reported metric), 8 videos of it, or 40 heads")
+    ap.add_argument("--pool", type=int, default=None,
+                    help="distinct resident input frames (even; one graph covers them all; "
+                         "default: enough frames for >= 512 MB of inputs, at least 2)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of the pool's frames instead of launching "
                          "each frame's calls on the stream")
@@ -96,8 +106,12 @@ class Bench:
 
         self.torch, self.arl2, self.synth = torch, arl2, synth
         self.args = args
-        self.w = synth.WORKLOADS[1]
+        self.w = next(x for x in synth.WORKLOADS.values() if x.name == args.workload)
         w = self.w
+        if args.pool is None:
+            per_frame = w.passes * 3 * w.B * w.H * w.T * w.D * 2
+            args.pool = max(2, -(-(512 << 20) // per_frame))
+            args.pool += args.pool % 2
         self.shape = arl2.Shape(w.B, w.H, w.T, w.D, arl2.BF16)
         self.stream = torch.cuda.current_stream()
         bf = torch.bfloat16
@@ -427,6 +441,11 @@ def main():
         "state_commit_algorithmic_bytes": commit_bytes,
         "copy_calibration": calib,
     }
+    one_layer = args.workload == "wan13b_layer"
+    if not one_layer:
+        # the traffic counters, the flatness rollout and the oracle baseline are
+        # taken on the one-layer shape only
+        traffic, args.skip_rollout, args.skip_cpu = None, True, True
     flat = None
     if not args.skip_rollout:
         print("[bench] rollout flatness", file=sys.stderr, flush=True)
@@ -436,7 +455,9 @@ def main():
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(args.cpu_seconds)
     res = {
-        "metric": "ARL2 layer frames/sec (12x128 heads, 1560 tok/frame)",
+        "metric": ("ARL2 layer frames/sec (12x128 heads, 1560 tok/frame)" if one_layer else
+                   f"ARL2 layer frames/sec ({w.B} video{'s' if w.B > 1 else ''} x {w.H}x{w.D} "
+                   f"heads, {w.T} tok/frame)"),
         "value": fps,
         "unit": "frames/s",
         "n_gpus": 1,
@@ -448,9 +469,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "wan13b_layer: 1 video x 12 heads x d128, T=1560 tokens/frame, "
-                               "4 denoising reads + clean pass (read + state commit) per frame, "
-                               "bf16 activations, fp32 state",
+        "config": {"workload": f"{w.name}: {w.B} video{'s' if w.B > 1 else ''} x {w.H} heads "
+                               f"x d{w.D}, T={w.T} tokens/frame, {w.n_denoise} denoising reads + "
+                               "clean pass (read + state commit) per frame, bf16 activations, "
+                               "fp32 state",
                    "B": w.B, "H": w.H, "D": w.D, "T": w.T, "passes_per_frame": w.passes,
                    "hip_graph": args.graph},
         "tokens_per_s": fps * w.T,
