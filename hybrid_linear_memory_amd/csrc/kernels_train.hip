@@ -268,11 +268,10 @@ commit_rows2_k(const float* __restrict__ dkraw, const Tx* __restrict__ kp,
 }
 
 // dalpha[g] (+)= <S[g], G[g]>  (one workgroup of 256 per (b, h), fixed order)
-__global__ void __launch_bounds__(256)
-dalpha_k(const float* __restrict__ S, const float* __restrict__ G, float* __restrict__ dalpha,
-         int DD, int accumulate) {
+__device__ __forceinline__ void dalpha_block(long g, const float* __restrict__ S,
+                                             const float* __restrict__ G,
+                                             float* __restrict__ dalpha, int DD, int accumulate) {
   __shared__ float red[4];
-  const long g = blockIdx.x;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int i = threadIdx.x * 4; i < DD; i += 256 * 4 * 4) {
 #pragma unroll
@@ -294,11 +293,33 @@ dalpha_k(const float* __restrict__ S, const float* __restrict__ G, float* __rest
   }
 }
 
-// bf16 copies of a float [n][128][128] matrix set, row-major and transposed
-__global__ void to_bf16_pair_k(const float* __restrict__ m, __bf16* __restrict__ mb,
-                               __bf16* __restrict__ mtb, long n_out) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void __launch_bounds__(256)
+dalpha_k(const float* __restrict__ S, const float* __restrict__ G, float* __restrict__ dalpha,
+         int DD, int accumulate) {
+  dalpha_block(blockIdx.x, S, G, dalpha, DD, accumulate);
+}
+
+// bf16 copies of a float [n][128][128] matrix set, row-major and transposed;
+// threads from n_out take a second set (m1, mb1, mtb1) when the grid covers it
+// (workgroups from n_cast_blocks on: dalpha_block over (m0, m1) when dalpha
+// is given, one per matrix)
+__global__ void __launch_bounds__(256)
+to_bf16_pair_k(const float* __restrict__ m0, __bf16* __restrict__ mb0,
+               __bf16* __restrict__ mtb0, const float* __restrict__ m1,
+               __bf16* __restrict__ mb1, __bf16* __restrict__ mtb1, long n_out,
+               float* __restrict__ dalpha = nullptr, long n_cast_blocks = 0,
+               int accumulate = 0) {
+  if (dalpha && (long)blockIdx.x >= n_cast_blocks) {
+    dalpha_block((long)blockIdx.x - n_cast_blocks, m0, m1, dalpha, HD * HD, accumulate);
+    return;
+  }
+  long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool second = idx >= n_out;
+  if (second) idx -= n_out;
   if (idx >= n_out) return;
+  const float* m = second ? m1 : m0;
+  __bf16* mb = second ? mb1 : mb0;
+  __bf16* mtb = second ? mtb1 : mtb0;
   const int c = (int)(idx % HD), r = (int)((idx / HD) % HD);
   const long g = idx / (HD * HD);
   const __bf16 x = (__bf16)m[idx];
@@ -315,16 +336,28 @@ __global__ void copy_f32_k(const float* __restrict__ a, float* __restrict__ b, l
 // bf16 MFMA building blocks (d = 128)
 // ---------------------------------------------------------------------------
 
+// One problem of a batched Y = X Bt^T launch: with x2 set, Y = X Bt^T -
+// X2 Bt2^T (both products in fp32, then one subtraction).
+struct NtProb {
+  const __bf16* x;
+  const __bf16* bt;
+  const __bf16* x2;
+  const __bf16* bt2;
+  Epi ep;
+  int x_per_head, bt_per_head;
+};
+struct NtBatch {
+  NtProb p0, p1;
+};
+
 // Y = X Bt^T: one workgroup of 4 waves per 32 rows of one g; wave w computes
 // the 32 x 32 tile of columns 32 w.., operands straight from memory (the rows
-// of X are shared through L1, Bt, 32 KB, stays in L2).
-__global__ void __launch_bounds__(256)
-nt_gemm_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ bt, Epi ep, int rows,
-               int H, int x_per_head, int bt_per_head, int n_rblk) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// of X are shared through L1, Bt, 32 KB, stays in L2). Workgroups from
+// per_prob on take the batch's second problem (same shapes).
+__device__ __forceinline__ f32x16 nt_tile(const __bf16* x, const __bf16* bt, int x_per_head,
+                                          int bt_per_head, long g, int H, int rows, int row0,
+                                          int lane, int wave) {
   const int n = lane & 31, h2 = lane >> 5;
-  const long g = blockIdx.x / n_rblk;
-  const int row0 = (blockIdx.x % n_rblk) * 32;
   const __bf16* xg = x + (x_per_head ? g % H : g) * (long)rows * HD;
   const __bf16* bg = bt + (bt_per_head ? g % H : g) * (long)HD * HD;
   const __bf16* xr = xg + (long)min(row0 + n, rows - 1) * HD + 8 * h2;
@@ -338,10 +371,25 @@ nt_gemm_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ bt, Epi 
   f32x16 acc = zero16();
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) acc = mfma32(a[kc], b[kc], acc);
+  return acc;
+}
+
+__global__ void __launch_bounds__(256)
+nt_gemm_mfma_k(NtBatch nb, int rows, int H, int n_rblk, long per_prob) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const bool second = (long)blockIdx.x >= per_prob;
+  const long bid = second ? (long)blockIdx.x - per_prob : (long)blockIdx.x;
+  const NtProb& P = second ? nb.p1 : nb.p0;
+  const long g = bid / n_rblk;
+  const int row0 = (int)(bid % n_rblk) * 32;
+  f32x16 acc = nt_tile(P.x, P.bt, P.x_per_head, P.bt_per_head, g, H, rows, row0, lane, wave);
+  if (P.x2)
+    acc = acc - nt_tile(P.x2, P.bt2, P.x_per_head, P.bt_per_head, g, H, rows, row0, lane, wave);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-    if (row < rows) epilogue<__bf16>(ep, ((size_t)g * rows + row) * HD + 32 * wave + n, acc[r]);
+    if (row < rows) epilogue<__bf16>(P.ep, ((size_t)g * rows + row) * HD + 32 * wave + n, acc[r]);
   }
 }
 
@@ -361,14 +409,31 @@ constexpr int XTY_SUB = 64;                   // tokens staged at a time
 // quadrant (qe, qv) of the 128 x 128 result: wave w computes the 32 x 32 tile
 // (2 qe + w / 2, 2 qv + w % 2), stored in MFMA accumulator order:
 // part[(g * nch + ch) * 16 + tile][lane][16], tile = 4 te + tv.
+// Up to three X^T Y problems of one shape per launch: workgroups
+// [j per_prob, (j + 1) per_prob) take problem j, whose partials follow the
+// previous problem's (part + j * per_prob * 4096 floats).
+struct XtyBatch {
+  const __bf16* x0;
+  const __bf16* y0;
+  const __bf16* x1;
+  const __bf16* y1;
+  const __bf16* x2;
+  const __bf16* y2;
+};
+
 __global__ void __launch_bounds__(256)
-xty_part_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ y,
-                float* __restrict__ part, int T, int chunk, int nch) {
+xty_part_mfma_k(XtyBatch xb, float* __restrict__ part_all, int T, int chunk, int nch,
+                long per_prob) {
   __shared__ __attribute__((aligned(16))) char lx[XTY_SUB * 256];
   __shared__ __attribute__((aligned(16))) char ly[XTY_SUB * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int quad = blockIdx.x & 3;
-  const long gc = blockIdx.x >> 2;
+  const int j = (int)((long)blockIdx.x / per_prob);
+  const long bid = (long)blockIdx.x - j * per_prob;
+  const __bf16* x = j == 0 ? xb.x0 : j == 1 ? xb.x1 : xb.x2;
+  const __bf16* y = j == 0 ? xb.y0 : j == 1 ? xb.y1 : xb.y2;
+  float* part = part_all + (size_t)j * per_prob * 4096;
+  const int quad = (int)(bid & 3);
+  const long gc = bid >> 2;
   const long g = gc / nch;
   const int ch = gc % nch;
   const int te = 2 * (quad >> 1) + (wave >> 1), tv = 2 * (quad & 1) + (wave & 1);
@@ -393,12 +458,39 @@ xty_part_mfma_k(const __bf16* __restrict__ x, const __bf16* __restrict__ y,
 // out[go][e][v] (+)= gamma[go] base[go][e][v] + delta * sum_b sum_ch part:
 // one thread per (go, tile, lane, 4 registers), chunks summed in order with
 // the loads of 4 chunks issued ahead of their sums.
+struct XtyRed {
+  float* out;
+  const float* base_mat;
+  const float* gamma;
+  float delta;
+  int sum_b;
+  long n_thr;                     // go count x 4096
+};
+struct XtyRedBatch {
+  XtyRed r0, r1, r2;
+};
+
 __global__ void __launch_bounds__(256)
-xty_reduce_mfma_k(const float* __restrict__ part, float* __restrict__ out,
-                  const float* __restrict__ base_mat, const float* __restrict__ gamma,
-                  float delta, int accumulate, int nch, int B, int H, int sum_b, long n_thr) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n_thr) return;
+xty_reduce_mfma_k(const float* __restrict__ part_all, XtyRedBatch rb, int accumulate, int nch,
+                  int B, int H, long part_stride) {
+  long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  int j = 0;
+  if (idx >= rb.r0.n_thr) {
+    idx -= rb.r0.n_thr;
+    j = 1;
+    if (idx >= rb.r1.n_thr) {
+      idx -= rb.r1.n_thr;
+      j = 2;
+    }
+  }
+  const XtyRed& R = j == 0 ? rb.r0 : j == 1 ? rb.r1 : rb.r2;
+  if (idx >= R.n_thr) return;
+  const float* part = part_all + (size_t)j * part_stride;
+  float* out = R.out;
+  const float* base_mat = R.base_mat;
+  const float* gamma = R.gamma;
+  const float delta = R.delta;
+  const int sum_b = R.sum_b;
   const int q4 = (int)(idx & 3);
   const int lane = (int)((idx >> 2) & 63);
   const int tile = (int)((idx >> 8) & 15);
@@ -890,6 +982,31 @@ Epi make_epi(const void* z, bool z_f32, float* y32, void* yx, bool accumulate) {
   return e;
 }
 
+NtProb nt_prob(const void* x, bool x_per_head, const void* bt, bool bt_per_head, const Epi& ep,
+               const void* x2 = nullptr, const void* bt2 = nullptr) {
+  NtProb p;
+  p.x = static_cast<const __bf16*>(x);
+  p.bt = static_cast<const __bf16*>(bt);
+  p.x2 = static_cast<const __bf16*>(x2);
+  p.bt2 = static_cast<const __bf16*>(bt2);
+  p.ep = ep;
+  p.x_per_head = x_per_head ? 1 : 0;
+  p.bt_per_head = bt_per_head ? 1 : 0;
+  return p;
+}
+
+// bf16 MFMA: one or two independent Y = X B^T problems of `rows` rows per g in
+// one launch.
+hipError_t nt_gemm_batch(const Dims& d, int rows, const NtProb& p0, const NtProb* p1,
+                         hipStream_t s) {
+  const long n_g = (long)d.B * d.H;
+  const int n_rblk = (rows + 31) / 32;
+  const long per = n_g * n_rblk;
+  const NtBatch nb{p0, p1 ? *p1 : p0};
+  nt_gemm_mfma_k<<<(unsigned)(per * (p1 ? 2 : 1)), 256, 0, s>>>(nb, rows, d.H, n_rblk, per);
+  return hipGetLastError();
+}
+
 // Y = X B^T per g over n_g = B*H matrices of `rows` rows; bt_trans (float32
 // only) reads B^T from a row-major B instead.
 hipError_t nt_gemm(const Dims& d, const void* x, int rows, bool x_per_head, const void* bt,
@@ -897,10 +1014,7 @@ hipError_t nt_gemm(const Dims& d, const void* x, int rows, bool x_per_head, cons
   const long n_g = (long)d.B * d.H;
   if (use_mfma(d)) {
     if (bt_trans) return hipErrorInvalidValue;
-    const int n_rblk = (rows + 31) / 32;
-    nt_gemm_mfma_k<<<(unsigned)(n_g * n_rblk), 256, 0, s>>>(
-        static_cast<const __bf16*>(x), static_cast<const __bf16*>(bt), ep, rows, d.H,
-        x_per_head ? 1 : 0, bt_per_head ? 1 : 0, n_rblk);
+    return nt_gemm_batch(d, rows, nt_prob(x, x_per_head, bt, bt_per_head, ep), nullptr, s);
   } else {
     const long n_out = n_g * rows * d.D;
     nt_gemm_f32_k<<<blocks(n_out, 256), 256, 0, s>>>(
@@ -926,6 +1040,61 @@ size_t xty_ws_bytes(const Dims& d) {
   return (size_t)d.B * d.H * nch * HD * HD * sizeof(float);
 }
 
+// One X^T Y reduction: out (+)= gamma * base + delta * sum_t X^T Y, per
+// (b, h) or summed over b into per-head outputs.
+struct XtyJob {
+  const void* x;
+  const void* y;
+  float* out;
+  bool sum_b;
+  const float* base_mat;
+  const float* gamma;
+  float delta;
+};
+
+hipError_t xty(const Dims& d, const void* x, const void* y, float* out, bool sum_b,
+               const float* base_mat, const float* gamma, float delta, bool accumulate, void* ws,
+               hipStream_t s);
+
+// Up to three reductions of one shape in two launches (bf16 MFMA; ws holds
+// n_jobs x xty_ws_bytes); float32 runs them one after the other.
+hipError_t xty_batch(const Dims& d, const XtyJob* jobs, int n_jobs, bool accumulate, void* ws,
+                     hipStream_t s) {
+  if (!use_mfma(d)) {
+    for (int j = 0; j < n_jobs; ++j) {
+      const XtyJob& J = jobs[j];
+      hipError_t e = xty(d, J.x, J.y, J.out, J.sum_b, J.base_mat, J.gamma, J.delta, accumulate,
+                         ws, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const int chunk = xty_chunk(d);
+  const int nch = (d.T + chunk - 1) / chunk;
+  const long per = (long)d.B * d.H * nch * 4;
+  auto bx = [&](int j) { return static_cast<const __bf16*>(jobs[j < n_jobs ? j : 0].x); };
+  auto by = [&](int j) { return static_cast<const __bf16*>(jobs[j < n_jobs ? j : 0].y); };
+  const XtyBatch xb{bx(0), by(0), bx(1), by(1), bx(2), by(2)};
+  float* part = static_cast<float*>(ws);
+  xty_part_mfma_k<<<(unsigned)(per * n_jobs), 256, 0, s>>>(xb, part, d.T, chunk, nch, per);
+  XtyRed r[3];
+  long total = 0;
+  for (int j = 0; j < 3; ++j) {
+    if (j < n_jobs) {
+      const XtyJob& J = jobs[j];
+      r[j] = XtyRed{J.out, J.base_mat, J.gamma, J.delta, J.sum_b ? 1 : 0,
+                    (J.sum_b ? (long)d.H : (long)d.B * d.H) * 4096};
+    } else {
+      r[j] = XtyRed{nullptr, nullptr, nullptr, 0.f, 0, 0};
+    }
+    total += r[j].n_thr;
+  }
+  xty_reduce_mfma_k<<<blocks(total, 256), 256, 0, s>>>(part, XtyRedBatch{r[0], r[1], r[2]},
+                                                       accumulate ? 1 : 0, nch, d.B, d.H,
+                                                       per * 4096);
+  return hipGetLastError();
+}
+
 // out (+)= gamma * base + delta * sum_t X^T Y, per (b, h) or summed over b
 // into per-head outputs.
 hipError_t xty(const Dims& d, const void* x, const void* y, float* out, bool sum_b,
@@ -933,15 +1102,8 @@ hipError_t xty(const Dims& d, const void* x, const void* y, float* out, bool sum
                hipStream_t s) {
   const long n_go = sum_b ? d.H : (long)d.B * d.H;
   if (use_mfma(d)) {
-    const int chunk = xty_chunk(d);
-    const int nch = (d.T + chunk - 1) / chunk;
-    float* part = static_cast<float*>(ws);
-    xty_part_mfma_k<<<(unsigned)((long)d.B * d.H * nch * 4), 256, 0, s>>>(
-        static_cast<const __bf16*>(x), static_cast<const __bf16*>(y), part, d.T, chunk, nch);
-    const long n_thr = n_go * 4096;
-    xty_reduce_mfma_k<<<blocks(n_thr, 256), 256, 0, s>>>(part, out, base_mat, gamma, delta,
-                                                         accumulate ? 1 : 0, nch, d.B, d.H,
-                                                         sum_b ? 1 : 0, n_thr);
+    const XtyJob job{x, y, out, sum_b, base_mat, gamma, delta};
+    return xty_batch(d, &job, 1, accumulate, ws, s);
   } else {
     const long n_out = n_go * d.D * d.D;
     xty_f32_k<<<blocks(n_out, 256), 256, 0, s>>>(
@@ -1049,11 +1211,12 @@ hipError_t read_backward_steps(const Dims& d, const void* q, const void* k, cons
   void* Mm = c.take<char>(mat_count(d) * (mf ? 2 : 4));     // M = Phi_q S per (b, h)
   void* qp = c.take<char>(ab);
   void* dqp = c.take<char>(ab);
-  void* part = c.take<char>(xty_ws_bytes(d));
+  void* part = c.take<char>(2 * xty_ws_bytes(d));
   hipError_t e;
   if (c.base) {
     if (mf) {
-      to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(S, Sb, Stb, (long)mat_count(d));
+      to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(
+          S, Sb, Stb, nullptr, nullptr, nullptr, (long)mat_count(d));
       // M[e][v] = sum_d Phi_q[e][d] S[d][v]: rows of Phi_q against S^T
       e = nt_gemm(d, phi_q, HD, true, Stb, false, false, make_epi(nullptr, false, nullptr, Mm, false), s);
     } else {
@@ -1069,15 +1232,14 @@ hipError_t read_backward_steps(const Dims& d, const void* q, const void* k, cons
     e = nt_gemm(d, d_o, d.T, false, Mm, false, false, make_epi(nullptr, false, nullptr, dq, true), s);
     if (e != hipSuccess) return e;
   }
-  // dS (+)= Q'^T dO
+  // Q' = Q Phi_q, dQ' = dO S^T; then dS (+)= Q'^T dO and dPhi_q (+)= sum_b Q^T dQ'
   if ((e = feature_map_any(d, q, phi_q, qp, false, s)) != hipSuccess) return e;
-  if ((e = xty(d, qp, d_o, dS, false, nullptr, nullptr, 1.f, accumulate, part, s)) != hipSuccess)
-    return e;
-  // dQ' = dO S^T, dPhi_q (+)= sum_b Q^T dQ'
   e = nt_gemm(d, d_o, d.T, false, mf ? (const void*)Sb : (const void*)S, false, false,
               make_epi(nullptr, false, nullptr, dqp, false), s);
   if (e != hipSuccess) return e;
-  return xty(d, q, dqp, dphi_q, true, nullptr, nullptr, 1.f, accumulate, part, s);
+  const XtyJob jobs[2] = {{qp, d_o, dS, false, nullptr, nullptr, 1.f},
+                          {q, dqp, dphi_q, true, nullptr, nullptr, 1.f}};
+  return xty_batch(d, jobs, 2, accumulate, part, s);
 }
 
 hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, const void* phi_k,
@@ -1103,7 +1265,7 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   __bf16* Stb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
   __bf16* Gb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
   __bf16* Gtb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
-  void* part = c.take<char>(xty_ws_bytes(d));
+  void* part = c.take<char>(3 * xty_ws_bytes(d));
   if (!c.base) return hipSuccess;
   const long n_rows = (long)row_count(d);
   const int acc = accumulate ? 1 : 0;
@@ -1113,8 +1275,10 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   if (mf) {
     rownorm_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(static_cast<const __bf16*>(kt),
                                                           static_cast<__bf16*>(kp), nrm, d.D, n_rows);
-    to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(S, Sb, Stb, (long)mat_count(d));
-    to_bf16_pair_k<<<blocks((long)mat_count(d), 256), 256, 0, s>>>(G, Gb, Gtb, (long)mat_count(d));
+    // bf16 copies of S and G, and dalpha = <S, G> per (b, h), in one launch
+    const long cast_blocks = blocks(2 * (long)mat_count(d), 256);
+    to_bf16_pair_k<<<(unsigned)(cast_blocks + (long)d.B * d.H), 256, 0, s>>>(
+        S, Sb, Stb, G, Gb, Gtb, (long)mat_count(d), dalpha, cast_blocks, acc);
   } else {
     rownorm_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(static_cast<const float*>(kt),
                                                          static_cast<float*>(kp), nrm, d.D, n_rows);
@@ -1122,9 +1286,15 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   // R = V' - K' S ;  K'G
   const void* bS_t = mf ? (const void*)Stb : (const void*)S;
   const void* bG_t = mf ? (const void*)Gtb : (const void*)G;
-  e = nt_gemm(d, kp, d.T, false, bS_t, false, !mf, make_epi(vp, false, r32, rx, false), s);
-  if (e != hipSuccess) return e;
-  e = nt_gemm(d, kp, d.T, false, bG_t, false, !mf, make_epi(nullptr, false, kg32, kgx, false), s);
+  if (mf) {
+    const NtProb p1 = nt_prob(kp, false, bG_t, false, make_epi(nullptr, false, kg32, kgx, false));
+    e = nt_gemm_batch(d, d.T, nt_prob(kp, false, bS_t, false, make_epi(vp, false, r32, rx, false)),
+                      &p1, s);
+  } else {
+    e = nt_gemm(d, kp, d.T, false, bS_t, false, true, make_epi(vp, false, r32, rx, false), s);
+    if (e != hipSuccess) return e;
+    e = nt_gemm(d, kp, d.T, false, bG_t, false, true, make_epi(nullptr, false, kg32, kgx, false), s);
+  }
   if (e != hipSuccess) return e;
   // dbeta, dV' = beta K'G
   if (mf)
@@ -1138,9 +1308,17 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   // dKraw = R G^T - K'G S^T
   const void* bG = mf ? (const void*)Gb : (const void*)G;
   const void* bS = mf ? (const void*)Sb : (const void*)S;
-  e = nt_gemm(d, rx, d.T, false, bG, false, false, make_epi(nullptr, false, dkr, nullptr, false), s);
-  if (e != hipSuccess) return e;
-  e = nt_gemm(d, kgx, d.T, false, bS, false, false, make_epi(dkr, true, dkr, nullptr, false), s);
+  if (mf) {
+    // both products in one launch, the second subtracted from the first in fp32
+    e = nt_gemm_batch(d, d.T,
+                      nt_prob(rx, false, bG, false, make_epi(nullptr, false, dkr, nullptr, false),
+                              kgx, bS),
+                      nullptr, s);
+  } else {
+    e = nt_gemm(d, rx, d.T, false, bG, false, false, make_epi(nullptr, false, dkr, nullptr, false), s);
+    if (e != hipSuccess) return e;
+    e = nt_gemm(d, kgx, d.T, false, bS, false, false, make_epi(dkr, true, dkr, nullptr, false), s);
+  }
   if (e != hipSuccess) return e;
   // dK~ through beta and the row normalisation
   if (mf)
@@ -1150,19 +1328,24 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
     commit_rows2_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(
         dkr, static_cast<const float*>(kp), nrm, beta, static_cast<float*>(dktx), d.D, n_rows);
   // dK = dK~ Phi_k^T, dV = dV' Phi_v^T
-  e = nt_gemm(d, dktx, d.T, false, phi_k, true, false, make_epi(nullptr, false, nullptr, dk, accumulate), s);
+  if (mf) {
+    const NtProb p1 = nt_prob(dvx, false, phi_v, true,
+                              make_epi(nullptr, false, nullptr, dv, accumulate));
+    e = nt_gemm_batch(d, d.T, nt_prob(dktx, false, phi_k, true,
+                                      make_epi(nullptr, false, nullptr, dk, accumulate)),
+                      &p1, s);
+  } else {
+    e = nt_gemm(d, dktx, d.T, false, phi_k, true, false, make_epi(nullptr, false, nullptr, dk, accumulate), s);
+    if (e != hipSuccess) return e;
+    e = nt_gemm(d, dvx, d.T, false, phi_v, true, false, make_epi(nullptr, false, nullptr, dv, accumulate), s);
+  }
   if (e != hipSuccess) return e;
-  e = nt_gemm(d, dvx, d.T, false, phi_v, true, false, make_epi(nullptr, false, nullptr, dv, accumulate), s);
-  if (e != hipSuccess) return e;
-  // dPhi_k = sum_b K^T dK~, dPhi_v = sum_b V^T dV'
-  if ((e = xty(d, k, dktx, dphi_k, true, nullptr, nullptr, 1.f, accumulate, part, s)) != hipSuccess)
-    return e;
-  if ((e = xty(d, v, dvx, dphi_v, true, nullptr, nullptr, 1.f, accumulate, part, s)) != hipSuccess)
-    return e;
-  // dS_prev = alpha G - K'^T dV'
-  if ((e = xty(d, kp, dvx, dS_prev, false, G, alpha, -1.f, accumulate, part, s)) != hipSuccess)
-    return e;
-  dalpha_k<<<(unsigned)((long)d.B * d.H), 256, 0, s>>>(S, G, dalpha, d.D * d.D, acc);
+  // dPhi_k = sum_b K^T dK~, dPhi_v = sum_b V^T dV', dS_prev = alpha G - K'^T dV'
+  const XtyJob jobs[3] = {{k, dktx, dphi_k, true, nullptr, nullptr, 1.f},
+                          {v, dvx, dphi_v, true, nullptr, nullptr, 1.f},
+                          {kp, dvx, dS_prev, false, G, alpha, -1.f}};
+  if ((e = xty_batch(d, jobs, 3, accumulate, part, s)) != hipSuccess) return e;
+  if (!mf) dalpha_k<<<(unsigned)((long)d.B * d.H), 256, 0, s>>>(S, G, dalpha, d.D * d.D, acc);
   return hipGetLastError();
 }
 
