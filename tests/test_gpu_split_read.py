@@ -118,3 +118,16 @@ def test_split_read_workspace_too_small():
     small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(arl2.Arl2Error, match="workspace"):
         arl2.read_prepared(sh, x, x, x, M, torch.empty_like(x), ws=small)
+
+
+def test_split_read_layer_rollout():
+    """Three frames of a 4-head, 4096-token layer through Arl2Layer (whose
+    denoising reads take the split-key grid): every pass's outputs on sampled
+    rows and the state after every commit against the oracle."""
+    from gpu_helpers import lockstep_rollout
+    from hybrid_linear_memory_amd import arl2
+    w = synth.WORKLOADS[1].replace(H=4, T=4096, frames=3)
+    assert arl2.workspace_bytes(shape_of(w), arl2.OP_READ_PREPARED) > 0
+    log("split read layer rollout 1x4x4096")
+    worst = lockstep_rollout(w, read_frames={0, 1, 2}, row_sample=_rows(w.T))
+    log(f"worst relative errors {worst}")
