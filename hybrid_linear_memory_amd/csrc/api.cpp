@@ -208,12 +208,20 @@ arl2_status do_token(const arl2::Dims& d, const void* q, const void* k, const vo
   void* kp = w + ab;
   void* vp = w + 2 * ab;
   void* oi = o_intra ? o_intra : (void*)(w + 3 * ab);
-  hipError_t e = run_feature_map(d, q, phi_q, qp, false, s);
-  if (e != hipSuccess) return hip_status(e, "feature map (phi_q)");
-  e = run_feature_map(d, k, phi_k, kp, true, s);
-  if (e != hipSuccess) return hip_status(e, "feature map (phi_k)");
-  e = run_feature_map(d, v, phi_v, vp, false, s);
-  if (e != hipSuccess) return hip_status(e, "feature map (phi_v)");
+  hipError_t e;
+  if (arl2::use_mfma(d)) {
+    const arl2::FeatureMapJob jobs[3] = {
+        {q, phi_q, qp, false}, {k, phi_k, kp, true}, {v, phi_v, vp, false}};
+    e = arl2::mfma_feature_maps(d, jobs, 3, s);
+    if (e != hipSuccess) return hip_status(e, "feature maps");
+  } else {
+    e = run_feature_map(d, q, phi_q, qp, false, s);
+    if (e != hipSuccess) return hip_status(e, "feature map (phi_q)");
+    e = run_feature_map(d, k, phi_k, kp, true, s);
+    if (e != hipSuccess) return hip_status(e, "feature map (phi_k)");
+    e = run_feature_map(d, v, phi_v, vp, false, s);
+    if (e != hipSuccess) return hip_status(e, "feature map (phi_v)");
+  }
   e = run_attention(d, q, k, v, oi, d.T, d.T, s);
   if (e != hipSuccess) return hip_status(e, "intra-frame attention");
   e = arl2::token_level_scan(d, qp, kp, vp, beta, S_prev, alpha, S_next, oi, o, o_inter,

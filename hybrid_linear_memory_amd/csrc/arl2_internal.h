@@ -36,6 +36,14 @@ hipError_t generic_state_commit(const Dims& d, const void* k_prime,
                                 const float* alpha, const float* S_prev,
                                 float* S_next, void* ws, hipStream_t s);
 
+// Up to three feature maps of one shape in one launch.
+struct FeatureMapJob {
+  const void* x;
+  const void* phi;
+  void* out;
+  bool normalize;
+};
+hipError_t mfma_feature_maps(const Dims& d, const FeatureMapJob* jobs, int n_jobs, hipStream_t s);
 hipError_t mfma_feature_map(const Dims& d, const void* x, const void* phi,
                             void* out, bool normalize, hipStream_t s);
 hipError_t mfma_attention(const Dims& d, const void* q, const void* k,

@@ -721,16 +721,48 @@ constexpr int MAP_ROWS = 128;         // rows per workgroup
 
 enum MapMode { MAP_PHI = 0, MAP_STATE = 1 };
 
+// Feature maps of up to three inputs of one shape in one launch (the
+// token-level pass's Q', K', V'; the commit backward's K~, V'): workgroups
+// [j per_prob, (j + 1) per_prob) map input j; input 0 is the kernel's x /
+// mat / out / normalize.
+struct MapMore {
+  const __bf16* x1;
+  const void* m1;
+  __bf16* o1;
+  int n1;
+  const __bf16* x2;
+  const void* m2;
+  __bf16* o2;
+  int n2;
+};
+
 template <int MODE>
 __global__ void __launch_bounds__(256)
 rowmap_mfma_k(const __bf16* __restrict__ x, const void* __restrict__ mat,
               const __bf16* o_intra, __bf16* out, __bf16* __restrict__ o_inter, int H,
-              int T, int n_rblk, int normalize) {
+              int T, int n_rblk, int normalize, MapMore more = MapMore{}, int per_prob = 0) {
   __shared__ __attribute__((aligned(16))) __bf16 MT[HD * MS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  int bid = blockIdx.x, nb = gridDim.x;
+  if (MODE == MAP_PHI && per_prob > 0) {
+    const int j = bid / per_prob;
+    bid -= j * per_prob;
+    nb = per_prob;
+    if (j == 1) {
+      x = more.x1;
+      mat = more.m1;
+      out = more.o1;
+      normalize = more.n1;
+    } else if (j == 2) {
+      x = more.x2;
+      mat = more.m2;
+      out = more.o2;
+      normalize = more.n2;
+    }
+  }
+  const int blk = xcd_remap(bid, nb);
   const long bh = blk / n_rblk;
   const int rblk = blk % n_rblk;
 
@@ -1526,6 +1558,24 @@ hipError_t mfma_feature_map(const Dims& d, const void* x, const void* phi, void*
   rowmap_mfma_k<MAP_PHI><<<(unsigned)nblk, 256, 0, s>>>(
       static_cast<const __bf16*>(x), phi, nullptr, static_cast<__bf16*>(out), nullptr, d.H, d.T,
       n_rblk, normalize ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t mfma_feature_maps(const Dims& d, const FeatureMapJob* jobs, int n_jobs, hipStream_t s) {
+  if (n_jobs < 1 || n_jobs > 3) return hipErrorInvalidValue;
+  if (n_jobs == 1)
+    return mfma_feature_map(d, jobs[0].x, jobs[0].phi, jobs[0].out, jobs[0].normalize, s);
+  const int n_rblk = (d.T + MAP_ROWS - 1) / MAP_ROWS;
+  const long nblk = (long)d.B * d.H * n_rblk;
+  const FeatureMapJob& j1 = jobs[1];
+  const FeatureMapJob& j2 = jobs[n_jobs > 2 ? 2 : 1];
+  const MapMore more{static_cast<const __bf16*>(j1.x), j1.phi, static_cast<__bf16*>(j1.out),
+                     j1.normalize ? 1 : 0, static_cast<const __bf16*>(j2.x), j2.phi,
+                     static_cast<__bf16*>(j2.out), j2.normalize ? 1 : 0};
+  rowmap_mfma_k<MAP_PHI><<<(unsigned)(nblk * n_jobs), 256, 0, s>>>(
+      static_cast<const __bf16*>(jobs[0].x), jobs[0].phi, nullptr,
+      static_cast<__bf16*>(jobs[0].out), nullptr, d.H, d.T, n_rblk, jobs[0].normalize ? 1 : 0,
+      more, (int)nblk);
   return hipGetLastError();
 }
 

@@ -1270,8 +1270,13 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   const long n_rows = (long)row_count(d);
   const int acc = accumulate ? 1 : 0;
   hipError_t e;
-  if ((e = feature_map_any(d, k, phi_k, kt, false, s)) != hipSuccess) return e;
-  if ((e = feature_map_any(d, v, phi_v, vp, false, s)) != hipSuccess) return e;
+  if (mf) {
+    const FeatureMapJob jobs[2] = {{k, phi_k, kt, false}, {v, phi_v, vp, false}};
+    if ((e = mfma_feature_maps(d, jobs, 2, s)) != hipSuccess) return e;
+  } else {
+    if ((e = feature_map_any(d, k, phi_k, kt, false, s)) != hipSuccess) return e;
+    if ((e = feature_map_any(d, v, phi_v, vp, false, s)) != hipSuccess) return e;
+  }
   if (mf) {
     rownorm_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(static_cast<const __bf16*>(kt),
                                                           static_cast<__bf16*>(kp), nrm, d.D, n_rows);
