@@ -46,6 +46,7 @@ _SP = ctypes.POINTER(_Shape)
 SIGNATURES = {
     "arl2_feature_map": (_i32, [_SP, _vp, _vp, _vp, _i32, _vp]),
     "arl2_intra_attn": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp]),
+    "arl2_intra_attn_lse": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp]),
     "arl2_inter_read": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp]),
     "arl2_state_commit": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_read": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -62,8 +63,8 @@ SIGNATURES = {
                                _sz, _vp]),
     "arl2_token_clean_pass": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _sz, _vp]),
-    "arl2_intra_attn_backward": (_i32, [_SP] + [_vp] * 8 + [_i32, _vp, _sz, _vp]),
-    "arl2_read_backward": (_i32, [_SP] + [_vp] * 12 + [_i32, _vp, _sz, _vp]),
+    "arl2_intra_attn_backward": (_i32, [_SP] + [_vp] * 9 + [_i32, _vp, _sz, _vp]),
+    "arl2_read_backward": (_i32, [_SP] + [_vp] * 13 + [_i32, _vp, _sz, _vp]),
     "arl2_commit_backward": (_i32, [_SP] + [_vp] * 15 + [_i32, _vp, _sz, _vp]),
     "arl2_state_scan": (_i32, [_SP, _i32] + [_vp] * 9 + [_sz, _vp]),
     "arl2_workspace_bytes": (_sz, [_SP, _i32]),
@@ -151,7 +152,7 @@ def _checker(shape: "Shape", frames: int = 1, state_frames: int = 1):
     sizes.update({n: H * D * D for n in _PHI})
     sizes.update({n: B * H * D * D * state_frames for n in _STATE})
     sizes.update({"beta": B * H * T * frames, "dbeta": B * H * T, "alpha": B * H * frames,
-                  "dalpha": B * H})
+                  "dalpha": B * H, "lse": B * H * T})
     min_bytes = {"prepared": prepared_bytes(shape), "prepared_next": prepared_bytes(shape)}
 
     def ck(t, name, dtype=None, optional=False):
@@ -204,6 +205,16 @@ def intra_attn(shape: Shape, q, k, v, o_intra, stream=None):
     a = shape.torch_dtype
     _check(_lib.arl2_intra_attn(ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a),
                                 ck(v, "v", a), ck(o_intra, "o_intra", a), _stream(stream)))
+
+
+def intra_attn_lse(shape: Shape, q, k, v, o_intra, lse, stream=None):
+    """intra_attn, plus each row's log-sum-exp of the scaled scores (natural
+    log, float32 [B, H, T]) for the backward calls."""
+    ck = _checker(shape)
+    a = shape.torch_dtype
+    _check(_lib.arl2_intra_attn_lse(ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a),
+                                    ck(v, "v", a), ck(o_intra, "o_intra", a),
+                                    ck(lse, "lse", torch.float32), _stream(stream)))
 
 
 def inter_read(shape: Shape, q_prime, S, o_intra, o, stream=None):
@@ -334,24 +345,28 @@ def _ws(ws):
 
 
 def intra_attn_backward(shape: Shape, q, k, v, o_intra, d_o, dq, dk, dv, accumulate=False,
-                        ws=None, stream=None):
-    """dq, dk, dv of the intra-frame softmax from its output o_intra and dL/dO_intra."""
+                        ws=None, stream=None, lse=None):
+    """dq, dk, dv of the intra-frame softmax from its output o_intra and
+    dL/dO_intra (lse: the rows' log-sum-exp from intra_attn_lse, or None)."""
     ck = _checker(shape)
     a = shape.torch_dtype
     _check(_lib.arl2_intra_attn_backward(
         ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
-        ck(o_intra, "o_intra", a), ck(d_o, "d_o", a), ck(dq, "dq", a), ck(dk, "dk", a),
-        ck(dv, "dv", a), 1 if accumulate else 0, *_ws(ws), _stream(stream)))
+        ck(o_intra, "o_intra", a), ck(lse, "lse", torch.float32, optional=True),
+        ck(d_o, "d_o", a), ck(dq, "dq", a), ck(dk, "dk", a), ck(dv, "dv", a),
+        1 if accumulate else 0, *_ws(ws), _stream(stream)))
 
 
 def read_backward(shape: Shape, q, k, v, phi_q, S, o_intra, d_o, dq, dk, dv, dphi_q, dS,
-                  accumulate=False, ws=None, stream=None):
-    """Gradients of a read O = O_intra + (Q Phi_q) S given dL/dO."""
+                  accumulate=False, ws=None, stream=None, lse=None):
+    """Gradients of a read O = O_intra + (Q Phi_q) S given dL/dO (lse: the
+    rows' log-sum-exp from intra_attn_lse, or None)."""
     ck = _checker(shape)
     a, f = shape.torch_dtype, torch.float32
     _check(_lib.arl2_read_backward(
         ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
         ck(phi_q, "phi_q", a), ck(S, "S", f), ck(o_intra, "o_intra", a),
+        ck(lse, "lse", f, optional=True),
         ck(d_o, "d_o", a), ck(dq, "dq", a), ck(dk, "dk", a), ck(dv, "dv", a),
         ck(dphi_q, "dphi_q", f), ck(dS, "dS", f), 1 if accumulate else 0, *_ws(ws),
         _stream(stream)))

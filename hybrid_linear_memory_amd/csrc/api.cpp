@@ -359,6 +359,30 @@ arl2_status arl2_intra_attn(const arl2_shape* shape, const void* q, const void* 
                     "intra-frame attention");
 }
 
+arl2_status arl2_intra_attn_lse(const arl2_shape* shape, const void* q, const void* k,
+                                const void* v, void* o_intra, float* lse, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o_intra);
+  REQUIRE_PTR(lse);
+  const size_t ab = arl2::act_bytes(d);
+  const size_t lb = (size_t)d.B * d.H * d.T * sizeof(float);
+  const Range outs[2] = {{o_intra, ab}, {lse, lb}};
+  const Range ins[3] = {{q, ab}, {k, ab}, {v, ab}};
+  if ((st = check_disjoint(outs, 2, ins, 3)) != ARL2_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (arl2::use_mfma(d))
+    return hip_status(arl2::mfma_attention_lse(d, q, k, v, o_intra, lse, s),
+                      "intra-frame attention");
+  hipError_t e = run_attention(d, q, k, v, o_intra, d.T, d.T, s);
+  if (e != hipSuccess) return hip_status(e, "intra-frame attention");
+  return hip_status(arl2::attn_lse_f32(d, q, k, lse, s), "row log-sum-exp");
+}
+
 arl2_status arl2_inter_read(const arl2_shape* shape, const void* q_prime, const float* S,
                             const void* o_intra, void* o, void* stream) {
   arl2::Dims d;
@@ -644,9 +668,10 @@ arl2_status arl2_token_clean_pass(const arl2_shape* shape, const void* q, const 
 // ------------------------------------------------------------- training side
 
 arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q, const void* k,
-                                     const void* v, const void* o_intra, const void* d_o,
-                                     void* dq, void* dk, void* dv, int32_t accumulate, void* ws,
-                                     size_t ws_bytes, void* stream) {
+                                     const void* v, const void* o_intra, const float* lse,
+                                     const void* d_o, void* dq, void* dk, void* dv,
+                                     int32_t accumulate, void* ws, size_t ws_bytes,
+                                     void* stream) {
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
@@ -661,19 +686,23 @@ arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q, con
   const size_t need = arl2::attn_backward_ws_bytes(d);
   if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
   const size_t ab = arl2::act_bytes(d);
+  OPTIONAL_PTR(lse);
+  const size_t lb = (size_t)d.B * d.H * d.T * sizeof(float);
   const Range outs[3] = {{dq, ab}, {dk, ab}, {dv, ab}};
-  const Range ins[6] = {{q, ab}, {k, ab}, {v, ab}, {o_intra, ab}, {d_o, ab}, {ws, need}};
-  if ((st = check_disjoint(outs, 3, ins, 6)) != ARL2_OK) return st;
-  return hip_status(arl2::attn_backward(d, q, k, v, o_intra, d_o, dq, dk, dv, accumulate != 0,
-                                        ws, (hipStream_t)stream),
+  const Range ins[7] = {{q, ab},   {k, ab},    {v, ab},  {o_intra, ab},
+                        {d_o, ab}, {ws, need}, {lse, lb}};
+  if ((st = check_disjoint(outs, 3, ins, 7)) != ARL2_OK) return st;
+  if (overlap({lse, lb}, {ws, need})) return fail(ARL2_E_ALIAS, "lse overlaps the workspace");
+  return hip_status(arl2::attn_backward(d, q, k, v, o_intra, lse, d_o, dq, dk, dv,
+                                        accumulate != 0, ws, (hipStream_t)stream),
                     "attention backward");
 }
 
 arl2_status arl2_read_backward(const arl2_shape* shape, const void* q, const void* k,
                                const void* v, const void* phi_q, const float* S,
-                               const void* o_intra, const void* d_o, void* dq, void* dk,
-                               void* dv, float* dphi_q, float* dS, int32_t accumulate, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               const void* o_intra, const float* lse, const void* d_o, void* dq,
+                               void* dk, void* dv, float* dphi_q, float* dS, int32_t accumulate,
+                               void* ws, size_t ws_bytes, void* stream) {
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
@@ -693,12 +722,15 @@ arl2_status arl2_read_backward(const arl2_shape* shape, const void* q, const voi
   if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
   const size_t ab = arl2::act_bytes(d);
   const size_t pb = (size_t)d.H * d.D * d.D * 4;
+  OPTIONAL_PTR(lse);
+  const size_t lb = (size_t)d.B * d.H * d.T * sizeof(float);
   const Range outs[5] = {{dq, ab}, {dk, ab}, {dv, ab}, {dphi_q, pb}, {dS, state_bytes(d)}};
-  const Range ins[8] = {{q, ab},       {k, ab},   {v, ab},   {phi_q, phi_bytes(d)},
-                        {S, state_bytes(d)}, {o_intra, ab}, {d_o, ab}, {ws, need}};
-  if ((st = check_disjoint(outs, 5, ins, 8)) != ARL2_OK) return st;
-  return hip_status(arl2::read_backward(d, q, k, v, phi_q, S, o_intra, d_o, dq, dk, dv, dphi_q,
-                                        dS, accumulate != 0, ws, (hipStream_t)stream),
+  const Range ins[9] = {{q, ab},       {k, ab},   {v, ab},   {phi_q, phi_bytes(d)},
+                        {S, state_bytes(d)}, {o_intra, ab}, {d_o, ab}, {ws, need}, {lse, lb}};
+  if ((st = check_disjoint(outs, 5, ins, 9)) != ARL2_OK) return st;
+  if (overlap({lse, lb}, {ws, need})) return fail(ARL2_E_ALIAS, "lse overlaps the workspace");
+  return hip_status(arl2::read_backward(d, q, k, v, phi_q, S, o_intra, lse, d_o, dq, dk, dv,
+                                        dphi_q, dS, accumulate != 0, ws, (hipStream_t)stream),
                     "read backward");
 }
 

@@ -49,6 +49,10 @@ hipError_t mfma_feature_map(const Dims& d, const void* x, const void* phi,
 hipError_t mfma_attention(const Dims& d, const void* q, const void* k,
                           const void* v, void* o, int64_t n_kv, int64_t kv_cap,
                           hipStream_t s);
+// Intra-frame attention that also writes each row's log-sum-exp of the
+// scaled scores (natural log, fp32 [B, H, T]).
+hipError_t mfma_attention_lse(const Dims& d, const void* q, const void* k, const void* v,
+                              void* o, float* lse, hipStream_t s);
 hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
                            const void* o_intra, void* o, void* o_inter,
                            hipStream_t s);
@@ -108,13 +112,17 @@ hipError_t token_level_scan(const Dims& d, const void* q_prime, const void* k_pr
 size_t attn_backward_ws_bytes(const Dims& d);
 size_t read_backward_ws_bytes(const Dims& d);
 size_t commit_backward_ws_bytes(const Dims& d);
+// lse: the rows' log-sum-exp from the forward (natural log), or null to
+// compute it here.
 hipError_t attn_backward(const Dims& d, const void* q, const void* k, const void* v,
-                         const void* o_intra, const void* d_o, void* dq, void* dk, void* dv,
-                         bool accumulate, void* ws, hipStream_t s);
+                         const void* o_intra, const float* lse, const void* d_o, void* dq,
+                         void* dk, void* dv, bool accumulate, void* ws, hipStream_t s);
 hipError_t read_backward(const Dims& d, const void* q, const void* k, const void* v,
-                         const void* phi_q, const float* S, const void* o_intra, const void* d_o,
-                         void* dq, void* dk, void* dv, float* dphi_q, float* dS, bool accumulate,
-                         void* ws, hipStream_t s);
+                         const void* phi_q, const float* S, const void* o_intra, const float* lse,
+                         const void* d_o, void* dq, void* dk, void* dv, float* dphi_q, float* dS,
+                         bool accumulate, void* ws, hipStream_t s);
+// float32 shapes: the rows' log-sum-exp of scale Q K^T (natural log).
+hipError_t attn_lse_f32(const Dims& d, const void* q, const void* k, float* lse, hipStream_t s);
 hipError_t commit_backward(const Dims& d, const void* k, const void* v, const void* phi_k,
                            const void* phi_v, const float* beta, const float* alpha,
                            const float* S_prev, const float* dS_next, void* dk, void* dv,

@@ -51,6 +51,7 @@ constexpr int AQ = 128;                     // queries per workgroup
 constexpr int AKT = 64;                     // keys per tile
 constexpr int TILE_B = AKT * HD * 2;        // one 64 x 128 bf16 tile (16 KB)
 constexpr float kRedoSum = 18446744073709551616.0f;   // 2^64: largest accepted l
+constexpr float kLn2 = 0.6931471805599453f;
 // LDS: the tiles of parity p (local tile index & 1) sit in arrays of their
 // own: lk[p] = [stream A K, stream B K] of parity p and lv[p] = [stream A V of
 // parity p, stream B V of parity 1-p] (stream B's V tiles are loaded one
@@ -252,14 +253,14 @@ __device__ __forceinline__ bool sk_arrive(unsigned long long* ctr, unsigned long
 // One workgroup (logical block `blk`) of the attention; the LDS arrays are the
 // kernel's (see AKV) and reach here as parameters so that, once inlined, every
 // access still names its own array.
-template <bool INTER, bool SK = false>
+template <bool INTER, bool SK = false, bool LSE = false>
 __device__ __forceinline__ void attn_block(
     int blk, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv, long kv_cap,
     float sl2, int n_qblk, const __bf16* __restrict__ mt, __bf16* __restrict__ o_intra,
     __bf16* __restrict__ o_inter, char* lk0, char* lk1, char* lv0, char* lv1,
     float (*mlx)[2][64], int& redo_flag, int t0 = 0, int nt = -1,
-    const SkSeg* sk = nullptr, int* sk_last = nullptr) {
+    const SkSeg* sk = nullptr, int* sk_last = nullptr, float* __restrict__ lse = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -551,6 +552,11 @@ __device__ __forceinline__ void attn_block(
     });
     return;
   }
+  // with LSE: the row's log-sum-exp of the scaled scores (natural log): the
+  // weights are 2^((s - m) sl2) / lsum, so log sum_j e^(scale s_j) =
+  // (m sl2 + log2(lsum)) ln 2
+  if (LSE && stream == 0 && h2 == 0 && t < T)
+    lse[(size_t)bh * T + t] = (m * sl2 + log2f(lsum)) * kLn2;
   const float inv = 1.f / lsum;
   store([&](int b2, int r) __attribute__((always_inline)) {
     return (keep[b2][r] * fa + ex_r[(b2 * 16 + r) * 64 + lane] * fb) * inv;
@@ -596,13 +602,13 @@ __device__ __forceinline__ void attn_l2_warm(int i, int per_xcd, int n_attn, int
 // Blocks [0, n_attn): attention workgroups; blocks from n_attn_pad (n_attn
 // rounded up to the XCD count): the L2 warm-up role (when the grid leaves
 // compute units idle).
-template <bool INTER>
+template <bool INTER, bool LSE = false>
 __global__ void __launch_bounds__(512, 1)
 attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, int n_kv,
             long kv_cap, float sl2, int n_qblk, const __bf16* __restrict__ mt,
             __bf16* __restrict__ o_intra, __bf16* __restrict__ o_inter, int n_attn,
-            int n_attn_pad) {
+            int n_attn_pad, float* __restrict__ lse = nullptr) {
   __shared__ __attribute__((aligned(1024))) char lk0[AKV];
   __shared__ __attribute__((aligned(1024))) char lk1[AKV];
   __shared__ __attribute__((aligned(1024))) char lv0[AKV];
@@ -611,8 +617,9 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   __shared__ int redo_flag;
   const int b = blockIdx.x;
   if (b < n_attn)
-    attn_block<INTER>(xcd_remap(b, n_attn), q, k, v, o, T, n_kv, kv_cap, sl2, n_qblk, mt,
-                      o_intra, o_inter, lk0, lk1, lv0, lv1, mlx, redo_flag);
+    attn_block<INTER, false, LSE>(xcd_remap(b, n_attn), q, k, v, o, T, n_kv, kv_cap, sl2,
+                                  n_qblk, mt, o_intra, o_inter, lk0, lk1, lv0, lv1, mlx,
+                                  redo_flag, 0, -1, nullptr, nullptr, lse);
   else if (b >= n_attn_pad)
     attn_l2_warm(b - n_attn_pad, ((int)gridDim.x - n_attn_pad) / 8, n_attn, n_qblk, k, v, n_kv,
                  kv_cap, lk0);
@@ -1457,6 +1464,19 @@ static long sk_ctr_bytes(const Dims& d) {
 size_t mfma_read_prepared_ws_bytes(const Dims& d) {
   if (!sk_plan(d, kSkMaxGrid).use) return 0;
   return (size_t)sk_ctr_bytes(d) + (size_t)2 * kSkMaxGrid * kSkSlotFloats * sizeof(float);
+}
+
+hipError_t mfma_attention_lse(const Dims& d, const void* q, const void* k, const void* v,
+                              void* o, float* lse, hipStream_t s) {
+  const int n_qblk = (d.T + AQ - 1) / AQ;
+  const long nblk = (long)d.B * d.H * n_qblk;
+  long n_pad, total;
+  attn_grid(nblk, d.T, &n_pad, &total);
+  attn_mfma_k<false, true><<<(unsigned)total, 512, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<__bf16*>(o), d.T, d.T, (long)d.T, d.scale * kLog2e, n_qblk, nullptr, nullptr,
+      nullptr, (int)nblk, (int)n_pad, lse);
+  return hipGetLastError();
 }
 
 size_t mfma_read_ws_bytes(const Dims& d) {

@@ -117,24 +117,28 @@ __global__ void attn_pre_f32_k(const float* __restrict__ q, const float* __restr
   const long r = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= n_rows) return;
   const long g = r / T;
-  const float* qr = q + r * D;
-  const float* kg = k + g * (long)T * D;
-  float m = -INFINITY;
-  for (int j = 0; j < T; ++j) {
-    float s = 0.f;
-    for (int e = 0; e < D; ++e) s = fmaf(qr[e], kg[(long)j * D + e], s);
-    m = fmaxf(m, s * scale);
+  if (q) {                       // (without q: dsum only, lse given)
+    const float* qr = q + r * D;
+    const float* kg = k + g * (long)T * D;
+    float m = -INFINITY;
+    for (int j = 0; j < T; ++j) {
+      float s = 0.f;
+      for (int e = 0; e < D; ++e) s = fmaf(qr[e], kg[(long)j * D + e], s);
+      m = fmaxf(m, s * scale);
+    }
+    float l = 0.f;
+    for (int j = 0; j < T; ++j) {
+      float s = 0.f;
+      for (int e = 0; e < D; ++e) s = fmaf(qr[e], kg[(long)j * D + e], s);
+      l += expf(s * scale - m);
+    }
+    lse[r] = m + logf(l);
   }
-  float l = 0.f;
-  for (int j = 0; j < T; ++j) {
-    float s = 0.f;
-    for (int e = 0; e < D; ++e) s = fmaf(qr[e], kg[(long)j * D + e], s);
-    l += expf(s * scale - m);
+  if (d_o) {                     // (without d_o: lse only)
+    float dd = 0.f;
+    for (int e = 0; e < D; ++e) dd = fmaf(d_o[r * D + e], o[r * D + e], dd);
+    dsum[r] = dd;
   }
-  lse[r] = m + logf(l);
-  float dd = 0.f;
-  for (int e = 0; e < D; ++e) dd = fmaf(d_o[r * D + e], o[r * D + e], dd);
-  dsum[r] = dd;
 }
 
 // P_ij = exp(scale q_i.k_j - lse_i), dS_ij = P_ij (dO_i.v_j - dsum_i).
@@ -1138,16 +1142,44 @@ hipError_t feature_map_any(const Dims& d, const void* x, const void* phi, void* 
                      : generic_feature_map(d, x, phi, out, norm, s);
 }
 
+// With the rows' log-sum-exp given (natural log, from the forward): lse2 =
+// lse log2(e) and dsum = dO . O_intra, 16 rows per workgroup (16 lanes of 8
+// features per row).
+__global__ void __launch_bounds__(256)
+attn_dsum_mfma_k(const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
+                 const float* __restrict__ lse_in, float* __restrict__ lse2,
+                 float* __restrict__ dsum, long n_rows) {
+  const long r = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int p = threadIdx.x & 15;
+  float dd = 0.f;
+  if (r < n_rows) {
+    const bf16x8 x = ld8(d_o + r * HD + 8 * p), y = ld8(o + r * HD + 8 * p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dd = fmaf((float)x[e], (float)y[e], dd);
+  }
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) dd += __shfl_xor(dd, w, 16);
+  if (r < n_rows && p == 0) {
+    dsum[r] = dd;
+    lse2[r] = lse_in[r] * kLog2e;
+  }
+}
+
 // lse, dsum, then dQ (with the inter term dO M^T on bf16 shapes when m_rows is
 // given), dK and dV.
 hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, const void* v,
                                const void* o_intra, const void* d_o, void* dq, void* dk, void* dv,
-                               const void* m_rows, bool accumulate, Carve& c, hipStream_t s) {
+                               const void* m_rows, bool accumulate, Carve& c, hipStream_t s,
+                               const float* lse_in = nullptr) {
   const long n_rows = (long)row_count(d);
   float* lse = c.take<float>(n_rows * sizeof(float));
   float* dsum = c.take<float>(n_rows * sizeof(float));
   if (!c.base) return hipSuccess;
   const int acc = accumulate ? 1 : 0;
+  if (lse_in && use_mfma(d))
+    attn_dsum_mfma_k<<<blocks(n_rows, 16), 256, 0, s>>>(
+        static_cast<const __bf16*>(o_intra), static_cast<const __bf16*>(d_o), lse_in, lse, dsum,
+        n_rows);
   if (use_mfma(d)) {
     const float cl = d.scale * kLog2e;
     const __bf16* qb = static_cast<const __bf16*>(q);
@@ -1163,7 +1195,7 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
     if (n_g * ((d.T + 127) / 128) >= 512) {
       const int nb = (d.T + 127) / 128;
       const unsigned grid = (unsigned)(n_g * nb);
-      attn_pre_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl, nb);
+      if (!lse_in) attn_pre_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl, nb);
       attn_dq_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum, mr,
                                              static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
       attn_dkdv_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, vb, ob, lse, dsum,
@@ -1173,8 +1205,9 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
       const int nb = (d.T + 63) / 64;
       const unsigned grid = (unsigned)(n_g * nb);
       const int nb4 = (d.T + 127) / 128;
-      attn_pre_mfma_k<4><<<(unsigned)(n_g * nb4), 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl,
-                                                              nb4);
+      if (!lse_in)
+        attn_pre_mfma_k<4><<<(unsigned)(n_g * nb4), 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T,
+                                                                cl, nb4);
       attn_dq_mfma_k<2><<<grid, 128, 0, s>>>(qb, kb, vb, ob, lse, dsum, mr,
                                              static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
       attn_dkdv_mfma_k<2><<<grid, 128, 0, s>>>(qb, kb, vb, ob, lse, dsum,
@@ -1187,8 +1220,10 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
     const float* vf = static_cast<const float*>(v);
     const float* of = static_cast<const float*>(d_o);
     const long n_el = n_rows * d.D;
-    attn_pre_f32_k<<<blocks(n_rows, 128), 128, 0, s>>>(qf, kf, static_cast<const float*>(o_intra),
-                                                       of, lse, dsum, d.T, d.D, d.scale, n_rows);
+    if (lse_in) lse = const_cast<float*>(lse_in);     // read only below
+    attn_pre_f32_k<<<blocks(n_rows, 128), 128, 0, s>>>(lse_in ? nullptr : qf, kf,
+                                                       static_cast<const float*>(o_intra), of,
+                                                       lse, dsum, d.T, d.D, d.scale, n_rows);
     attn_dq_f32_k<<<blocks(n_el, 128), 128, 0, s>>>(qf, kf, vf, of, lse, dsum,
                                                     static_cast<float*>(dq), d.T, d.D, d.scale,
                                                     acc, n_el);
@@ -1203,7 +1238,8 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
 hipError_t read_backward_steps(const Dims& d, const void* q, const void* k, const void* v,
                                const void* phi_q, const float* S, const void* o_intra,
                                const void* d_o, void* dq, void* dk, void* dv, float* dphi_q,
-                               float* dS, bool accumulate, Carve& c, hipStream_t s) {
+                               float* dS, bool accumulate, Carve& c, hipStream_t s,
+                               const float* lse_in = nullptr) {
   const size_t ab = act_bytes(d);
   const bool mf = use_mfma(d);
   __bf16* Sb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
@@ -1225,7 +1261,8 @@ hipError_t read_backward_steps(const Dims& d, const void* q, const void* k, cons
     }
     if (e != hipSuccess) return e;
   }
-  e = attn_backward_steps(d, q, k, v, o_intra, d_o, dq, dk, dv, mf ? Mm : nullptr, accumulate, c, s);
+  e = attn_backward_steps(d, q, k, v, o_intra, d_o, dq, dk, dv, mf ? Mm : nullptr, accumulate, c, s,
+                          lse_in);
   if (e != hipSuccess || !c.base) return e;
   if (!mf) {
     // dQ += dO M^T
@@ -1377,19 +1414,28 @@ size_t commit_backward_ws_bytes(const Dims& d) {
 }
 
 hipError_t attn_backward(const Dims& d, const void* q, const void* k, const void* v,
-                         const void* o_intra, const void* d_o, void* dq, void* dk, void* dv,
-                         bool accumulate, void* ws, hipStream_t s) {
+                         const void* o_intra, const float* lse, const void* d_o, void* dq,
+                         void* dk, void* dv, bool accumulate, void* ws, hipStream_t s) {
   Carve c(ws);
-  return attn_backward_steps(d, q, k, v, o_intra, d_o, dq, dk, dv, nullptr, accumulate, c, s);
+  return attn_backward_steps(d, q, k, v, o_intra, d_o, dq, dk, dv, nullptr, accumulate, c, s, lse);
+}
+
+hipError_t attn_lse_f32(const Dims& d, const void* q, const void* k, float* lse, hipStream_t s) {
+  const long n_rows = (long)row_count(d);
+  attn_pre_f32_k<<<blocks(n_rows, 128), 128, 0, s>>>(static_cast<const float*>(q),
+                                                     static_cast<const float*>(k), nullptr,
+                                                     nullptr, lse, nullptr, d.T, d.D, d.scale,
+                                                     n_rows);
+  return hipGetLastError();
 }
 
 hipError_t read_backward(const Dims& d, const void* q, const void* k, const void* v,
-                         const void* phi_q, const float* S, const void* o_intra, const void* d_o,
-                         void* dq, void* dk, void* dv, float* dphi_q, float* dS, bool accumulate,
-                         void* ws, hipStream_t s) {
+                         const void* phi_q, const float* S, const void* o_intra, const float* lse,
+                         const void* d_o, void* dq, void* dk, void* dv, float* dphi_q, float* dS,
+                         bool accumulate, void* ws, hipStream_t s) {
   Carve c(ws);
   return read_backward_steps(d, q, k, v, phi_q, S, o_intra, d_o, dq, dk, dv, dphi_q, dS,
-                             accumulate, c, s);
+                             accumulate, c, s, lse);
 }
 
 hipError_t commit_backward(const Dims& d, const void* k, const void* v, const void* phi_k,

@@ -60,6 +60,7 @@ def rollout_backward(shape: arl2.Shape, frames, phi_q, phi_k, phi_v, d_outputs, 
     G = torch.zeros((B, H, D, D), **f32) if dS_final is None else dS_final.clone()
     G2 = torch.zeros_like(G)
     o_intra = torch.empty((B, H, T, D), dtype=a, device=dev)
+    lse = torch.empty((B, H, T), **f32)
     for f in range(len(frames) - 1, -1, -1):
         fr = frames[f]
         grads = [tuple(torch.zeros((B, H, T, D), dtype=a, device=dev) for _ in range(3))
@@ -76,9 +77,10 @@ def rollout_backward(shape: arl2.Shape, frames, phi_q, phi_k, phi_v, d_outputs, 
             if (f, p) not in d_outputs:
                 continue
             dq, dk, dv = grads[p]
-            arl2.intra_attn(shape, q, k, v, o_intra, stream)
+            arl2.intra_attn_lse(shape, q, k, v, o_intra, lse, stream)
             arl2.read_backward(shape, q, k, v, phi_q, states[f], o_intra, d_outputs[(f, p)], dq,
-                               dk, dv, out["dphi_q"], G2, accumulate=True, ws=ws, stream=stream)
+                               dk, dv, out["dphi_q"], G2, accumulate=True, ws=ws, stream=stream,
+                               lse=lse)
         for p, g in enumerate(grads):
             out["d_passes"][(f, p)] = g
         G, G2 = G2, G

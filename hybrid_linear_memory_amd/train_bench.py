@@ -5,12 +5,14 @@
 Measures, with HIP events around back-to-back calls on one stream, the
 forward read (arl2_read) and commit (arl2_commit) beside their backward calls
 (arl2_read_backward, arl2_commit_backward), the intra-frame attention
-backward alone (arl2_intra_attn_backward), and the clean-state scan over 21
-frames (arl2_state_scan). bf16 activations, fp32 state, seeded synthetic
+backward alone (arl2_intra_attn_backward), the same backward calls given the
+rows' log-sum-exp by the forward (arl2_intra_attn_lse, timed too), and the
+clean-state scan over 21 frames (arl2_state_scan). bf16 activations, fp32 state, seeded synthetic
 inputs resident in HBM. The attention backward's algorithmic work is counted
 as the five T x T x d products of its definition (S, dP, dV, dQ, dK:
 10 T^2 d FLOP per head); the kernels recompute S for the log-sum-exp pass and
-S, dP once more so that no accumulation crosses workgroups (16 T^2 d).
+S, dP once more so that no accumulation crosses workgroups (16 T^2 d; 14 when
+the log-sum-exp comes from the forward).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -59,7 +61,8 @@ def main(argv=None):
                          (arl2.OP_READ, arl2.OP_COMMIT, arl2.OP_READ_BACKWARD,
                           arl2.OP_COMMIT_BACKWARD, arl2.OP_INTRA_ATTN_BACKWARD)),
                      dtype=torch.uint8, device="cuda")
-    arl2.intra_attn(sh, q, k, v, o_intra)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    arl2.intra_attn_lse(sh, q, k, v, o_intra, lse)
 
     calls = {
         "read": lambda: arl2.read(sh, q, k, v, phis[0], S, o, None, None, ws),
@@ -68,6 +71,12 @@ def main(argv=None):
                                                                 dv, ws=ws),
         "read_backward": lambda: arl2.read_backward(sh, q, k, v, phis[0], S, o_intra, d_o, dq, dk,
                                                     dv, dphi[0], dS, ws=ws),
+        # with the rows' log-sum-exp from the forward (no pass to recompute it)
+        "intra_attn_lse": lambda: arl2.intra_attn_lse(sh, q, k, v, o_intra, lse),
+        "intra_attn_backward_lse": lambda: arl2.intra_attn_backward(sh, q, k, v, o_intra, d_o, dq,
+                                                                    dk, dv, ws=ws, lse=lse),
+        "read_backward_lse": lambda: arl2.read_backward(sh, q, k, v, phis[0], S, o_intra, d_o, dq,
+                                                        dk, dv, dphi[0], dS, ws=ws, lse=lse),
         "commit_backward": lambda: arl2.commit_backward(sh, k, v, phis[1], phis[2], beta, alpha, S,
                                                         G, dk, dv, dphi[1], dphi[2], dbeta,
                                                         dalpha, dS_prev, ws=ws),
@@ -107,6 +116,8 @@ def main(argv=None):
     res["intra_attn_backward_tflops_algorithmic"] = alg / (res["intra_attn_backward_us"] * 1e-6) / 1e12
     res["intra_attn_backward_tflops_executed"] = 1.6 * res["intra_attn_backward_tflops_algorithmic"]
     res["intra_attn_backward_frac_of_bf16_peak"] = res["intra_attn_backward_tflops_algorithmic"] / 2500.0
+    res["intra_attn_backward_lse_tflops_algorithmic"] = (
+        alg / (res["intra_attn_backward_lse_us"] * 1e-6) / 1e12)
     out = {"workload": f"{B} x {H} heads x 128, T={T}, bf16 activations, fp32 state", **{
         key: round(val, 3) for key, val in res.items()}}
     print(json.dumps(out), flush=True)

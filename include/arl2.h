@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define ARL2_ABI_VERSION 1
+#define ARL2_ABI_VERSION 2
 
 typedef enum arl2_status {
   ARL2_OK = 0,
@@ -281,28 +281,40 @@ arl2_status arl2_token_clean_pass(const arl2_shape* shape, const void* q,
  *   identical inputs give bit-identical gradients.
  * ------------------------------------------------------------------------ */
 
+/* Intra-frame attention for training: arl2_intra_attn's o_intra, and lse =
+ * each row's log-sum-exp of the scaled scores, lse[b,h,t] = log sum_j
+ * exp(scale q_t . k_j) (natural log, float32 [B,H,T], caller-owned), which the
+ * backward calls below take so as not to recompute Q K^T for it. */
+arl2_status arl2_intra_attn_lse(const arl2_shape* shape, const void* q,
+                                const void* k, const void* v, void* o_intra,
+                                float* lse, void* stream);
+
 /* Backward of the intra-frame softmax (arl2_intra_attn): from the forward's
  * o_intra and d_o = dL/dO_intra,
  *   P = softmax(Q K^T * scale), dV = P^T dO, dP = dO V^T,
  *   dZ = P * (dP - rowsum(dO * O_intra)), dQ = scale dZ K, dK = scale dZ^T Q.
+ * lse: NULL, or the rows' log-sum-exp from arl2_intra_attn_lse on the same
+ * q and k (then P = exp(scale Q K^T - lse) without a pass to find it).
  * Needs arl2_workspace_bytes(shape, ARL2_OP_INTRA_ATTN_BACKWARD). */
 arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q,
                                      const void* k, const void* v,
-                                     const void* o_intra, const void* d_o,
-                                     void* dq, void* dk, void* dv,
-                                     int32_t accumulate, void* ws,
+                                     const void* o_intra, const float* lse,
+                                     const void* d_o, void* dq, void* dk,
+                                     void* dv, int32_t accumulate, void* ws,
                                      size_t ws_bytes, void* stream);
 
 /* Backward of a read, O = softmax(Q K^T * scale) V + (Q Phi_q) S, from the
  * read's o_intra and d_o = dL/dO: dq, dk, dv, dphi_q and dS, with
  *   dQ += dO (Phi_q S)^T, dS = (Q Phi_q)^T dO, dPhi_q = sum_b Q^T dO S^T.
+ * lse as in arl2_intra_attn_backward (NULL or from arl2_intra_attn_lse).
  * Needs arl2_workspace_bytes(shape, ARL2_OP_READ_BACKWARD). */
 arl2_status arl2_read_backward(const arl2_shape* shape, const void* q,
                                const void* k, const void* v, const void* phi_q,
                                const float* S, const void* o_intra,
-                               const void* d_o, void* dq, void* dk, void* dv,
-                               float* dphi_q, float* dS, int32_t accumulate,
-                               void* ws, size_t ws_bytes, void* stream);
+                               const float* lse, const void* d_o, void* dq,
+                               void* dk, void* dv, float* dphi_q, float* dS,
+                               int32_t accumulate, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Backward of the commit (arl2_commit) from dS_next = dL/dS_next = G, with
  * K' = rownorm(K Phi_k), V' = V Phi_v, R = V' - K' S_prev:

@@ -6,6 +6,7 @@ with the HIP path and imports nothing from it.
 """
 from .arl2_oracle import (  # noqa: F401
     L2_EPS,
+    attention_logsumexp,
     attention_weights,
     commit,
     commit_backward,

@@ -125,6 +125,22 @@ def attention_weights(q, k, scale: float | None = None) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
+def attention_logsumexp(q, k, scale: float | None = None) -> np.ndarray:
+    """Each query row's log-sum-exp of its scaled scores over the frame's keys,
+    log sum_j exp(scale q . k_j) (natural log): the normaliser of the weights
+    of attention_weights, exp(scale q . k_j - lse) = weight j (ARL2 summary
+    §2.1, intra-frame branch; the quantity a backward pass reuses).
+
+    q: [..., Tq, d], k: [..., Tk, d] -> [..., Tq]."""
+    q = _f64(q)
+    k = _f64(k)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    a = np.matmul(q, _t(k)) * scale
+    m = np.max(a, axis=-1)
+    return m + np.log(np.sum(np.exp(a - m[..., None]), axis=-1))
+
+
 def intra_attention(q, k, v, scale: float | None = None) -> np.ndarray:
     """O_intra = softmax(Q K^T * scale) V over one frame (ARL2 summary §2.1).
 

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(arl2):
 
 
 def test_version_and_status_strings(arl2):
-    assert arl2.abi_version() == 1
+    assert arl2.abi_version() == 2
     for code, name in arl2.STATUS_NAMES.items():
         assert arl2.status_string(code) == name
     assert arl2.status_string(99) == "ARL2_E_UNKNOWN"
@@ -158,8 +158,13 @@ def test_alias_and_workspace_errors(arl2):
                B + (4 << 20), B + (5 << 20), B + (6 << 20), B + (7 << 20), S2, 0, WS, cb,
                None) == 5
     rb = arl2.workspace_bytes(s, arl2.OP_READ_BACKWARD)
-    assert _st(arl2, "arl2_read_backward", cs(s), A, A, A, A, S1, A, A, B, B, B + (4 << 20),
+    assert _st(arl2, "arl2_read_backward", cs(s), A, A, A, A, S1, A, None, A, B, B, B + (4 << 20),
                B + (6 << 20), S2, 0, WS, rb, None) == 5
+    # the rows' log-sum-exp (optional input) must not overlap an output
+    ab = arl2.workspace_bytes(s, arl2.OP_INTRA_ATTN_BACKWARD)
+    assert _st(arl2, "arl2_intra_attn_backward", cs(s), A, A, A, A, B, A, B, B + (4 << 20),
+               B + (6 << 20), 0, WS, ab, None) == 5
+    assert _st(arl2, "arl2_intra_attn_lse", cs(s), A, A, A, B, B, None) == 5
     assert _st(arl2, "arl2_state_scan", cs(s), 0, A, A, A, A, A, A, S1, S2, WS, need, None) == 2
     # fullkv: n_kv beyond capacity
     assert _st(arl2, "arl2_fullkv_attn", cs(s), A, B, S1, 200, 100, WS, None) == 2

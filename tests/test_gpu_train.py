@@ -62,30 +62,63 @@ def _zeros(shape, dtype="f32"):
                        device="cuda")
 
 
+def _forward(arl2, sh, w, q, k, v, with_lse):
+    """o_intra, and the rows' log-sum-exp when with_lse (else None)."""
+    o = _zeros((w.B, w.H, w.T, w.D), w.dtype)
+    if not with_lse:
+        arl2.intra_attn(sh, q, k, v, o)
+        return o, None
+    lse = _zeros((w.B, w.H, w.T))
+    arl2.intra_attn_lse(sh, q, k, v, o, lse)
+    return o, lse
+
+
 @pytest.mark.parametrize("case", CASES, ids=_ids)
-def test_intra_attn_backward(case):
+def test_intra_attn_lse(case):
+    """The forward with the rows' log-sum-exp: o_intra identical to
+    arl2_intra_attn's, lse against the oracle's (absolute: it is a logarithm;
+    bf16 inputs, and the kernel's sum of bf16-rounded weights, leave ~1e-3)."""
+    import torch
     from hybrid_linear_memory_amd import arl2
     w = _w(*case)
-    log(f"intra_attn_backward {_ids(case)}")
+    log(f"intra_attn_lse {_ids(case)}")
+    sh = shape_of(w)
+    q, k, v = synth.qkv(w, 0, 1)
+    dq_, dk_, dv_ = (dev(x, w.dtype) for x in (q, k, v))
+    o1, _ = _forward(arl2, sh, w, dq_, dk_, dv_, False)
+    o2, lse = _forward(arl2, sh, w, dq_, dk_, dv_, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    ref = oracle.attention_logsumexp(q, k)
+    err = np.abs(host(lse) - ref).max()
+    assert err <= (2e-2 if w.dtype == "bf16" else 1e-5), f"lse: max |err| {err:.3e}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+@pytest.mark.parametrize("with_lse", [False, True])
+def test_intra_attn_backward(case, with_lse):
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"intra_attn_backward {_ids(case)} lse={with_lse}")
     sh = shape_of(w)
     q, k, v = synth.qkv(w, 0, 1)
     d_o = _grad_out(w, 20)
     dq_, dk_, dv_ = (dev(x, w.dtype) for x in (q, k, v))
-    o = _zeros((w.B, w.H, w.T, w.D), w.dtype)
-    arl2.intra_attn(sh, dq_, dk_, dv_, o)
+    o, lse = _forward(arl2, sh, w, dq_, dk_, dv_, with_lse)
     grads = [_zeros((w.B, w.H, w.T, w.D), w.dtype) for _ in range(3)]
     ws = arl2.alloc_workspace(sh, arl2.OP_INTRA_ATTN_BACKWARD)
-    arl2.intra_attn_backward(sh, dq_, dk_, dv_, o, dev(d_o, w.dtype), *grads, ws=ws)
+    arl2.intra_attn_backward(sh, dq_, dk_, dv_, o, dev(d_o, w.dtype), *grads, ws=ws, lse=lse)
     ref = oracle.intra_attention_backward(q, k, v, d_o)
     for name, got in zip(("dq", "dk", "dv"), grads):
         _close(host(got), ref[name], TOL[w.dtype], name, floor=np.abs(ref["dv"]).max())
 
 
 @pytest.mark.parametrize("case", CASES, ids=_ids)
-def test_read_backward(case):
+@pytest.mark.parametrize("with_lse", [False, True])
+def test_read_backward(case, with_lse):
     from hybrid_linear_memory_amd import arl2
     w = _w(*case)
-    log(f"read_backward {_ids(case)}")
+    log(f"read_backward {_ids(case)} lse={with_lse}")
     sh = shape_of(w)
     q, k, v = synth.qkv(w, 0, 1)
     phis = synth.phi_maps(w)
@@ -93,14 +126,13 @@ def test_read_backward(case):
     S = (g.standard_normal((w.B, w.H, w.D, w.D)) * 0.05).astype(np.float32)
     d_o = _grad_out(w, 22)
     dq_, dk_, dv_ = (dev(x, w.dtype) for x in (q, k, v))
-    o = _zeros((w.B, w.H, w.T, w.D), w.dtype)
-    arl2.intra_attn(sh, dq_, dk_, dv_, o)
+    o, lse = _forward(arl2, sh, w, dq_, dk_, dv_, with_lse)
     grads = [_zeros((w.B, w.H, w.T, w.D), w.dtype) for _ in range(3)]
     dphi = _zeros((w.H, w.D, w.D))
     dS = _zeros((w.B, w.H, w.D, w.D))
     ws = arl2.alloc_workspace(sh, arl2.OP_READ_BACKWARD)
     arl2.read_backward(sh, dq_, dk_, dv_, dev(phis[0], w.dtype), dev32(S), o, dev(d_o, w.dtype),
-                       *grads, dphi, dS, ws=ws)
+                       *grads, dphi, dS, ws=ws, lse=lse)
     ref = oracle.read_backward(q, k, v, phis[0], S, d_o)
     for name, got in zip(("dq", "dk", "dv", "dphi_q", "dS"), grads + [dphi, dS]):
         _close(host(got), ref[name], TOL[w.dtype], name, floor=np.abs(ref["dv"]).max())

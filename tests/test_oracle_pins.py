@@ -121,6 +121,31 @@ def test_softmax_shift_invariance_large_logits():
     np.testing.assert_allclose(w2, w, rtol=1e-12, atol=0)
 
 
+def test_logsumexp_closed_forms():
+    """The rows' log-sum-exp: log 4 for the golden example's scores (0, ln 3)
+    (4 = e^0 + e^ln3), log T for Q = 0, the single score for one key, and
+    log T plus the common score for T equal keys; catches a base-2 or
+    unscaled sum, a dropped max shift or a sum over the wrong axis."""
+    gd = _load_golden("softmax_ln3.txt")
+    q, k = _as_array(gd["q"]), _as_array(gd["k"])
+    lse = oracle.attention_logsumexp(q[None, None], k[None, None], scale=1.0)[0, 0]
+    np.testing.assert_allclose(lse, math.log(4.0), rtol=0, atol=1e-14)
+    g = _rs(11)
+    k = g.standard_normal((2, 3, 9, 8))
+    np.testing.assert_allclose(oracle.attention_logsumexp(np.zeros((2, 3, 5, 8)), k),
+                               np.log(9.0), rtol=0, atol=1e-14)
+    q1, k1 = g.standard_normal((1, 2, 4, 8)), g.standard_normal((1, 2, 1, 8))
+    one = (q1 @ np.swapaxes(k1, -1, -2))[..., 0] * 0.5
+    np.testing.assert_allclose(oracle.attention_logsumexp(q1, k1, 0.5), one, rtol=1e-14)
+    kr = np.repeat(k1, 6, axis=2)
+    np.testing.assert_allclose(oracle.attention_logsumexp(q1, kr, 0.5), one + math.log(6.0),
+                               rtol=0, atol=1e-13)
+    # far beyond exp's range: the max shift keeps it finite and exact
+    big = oracle.attention_logsumexp(np.full((1, 1, 1, 1), 30.0), np.full((1, 1, 2, 1), 40.0),
+                                     1.0)
+    np.testing.assert_allclose(big, 1200.0 + math.log(2.0), rtol=1e-15)
+
+
 # ----------------------------------------------------------- feature maps (a1)
 
 def test_feature_map_orientation_and_heads():
