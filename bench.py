@@ -400,7 +400,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer shards "
-              "by (video, head) with no exchange inside the step, and this build measures "
+              "by (video, head) with no exchange inside the step, and this program measures "
               "the one-GPU share.", file=sys.stderr)
         sys.exit(2)
     import torch
