@@ -629,8 +629,9 @@ attn_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // Block qb's tiles sit at [qb L + pad, (qb + 1) L) of a line of n_blk L slots
 // (L = tiles per block + pad); workgroup w takes [w V / G, (w + 1) V / G),
 // V = n_blk L. The pad slots before each block make a workgroup that crosses
-// a block boundary (and pays a second ramp and a merge) take fewer tiles.
-// With n_blk <= G a workgroup meets at most two blocks.
+// a block boundary (and pays a second ramp and a merge) take fewer tiles. A
+// workgroup's segments between its first and its last are whole blocks, so
+// only those two can be partial: two slots per workgroup.
 __device__ __forceinline__ int sk_wg_of(long x, long V, int G) {
   return (int)(((x + 1) * G - 1) / V);
 }
@@ -654,7 +655,7 @@ attn_sk_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int n_tiles = (T + AKT - 1) / AKT;
   const long L = n_tiles + pad, V = (long)n_blk * L;
   const long v0 = (long)w * V / G, v1 = (long)(w + 1) * V / G;
-  int local = 0;
+  int local = 0;        // segments of this workgroup so far
   for (int qb = (int)(v0 / L); qb < n_blk && (long)qb * L < v1; ++qb) {
     const long rs = (long)qb * L + pad;
     const long a = v0 > rs ? v0 : rs;
@@ -668,7 +669,7 @@ attn_sk_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     sg.nseg = sk_wg_of(rs + n_tiles - 1, V, G) - sg.wf + 1;
     sg.iseg = w - sg.wf;
     sg.first_local = (long)sg.wf * V / G < (long)qb * L ? 1 : 0;
-    sg.my_slot = 2 * w + local;
+    sg.my_slot = 2 * w + (local > 0 ? 1 : 0);    // only a first or a last segment is partial
     if (local > 0) __syncthreads();      // the previous segment's LDS reads are done
     attn_block<INTER, true>(qb, q, k, v, o, T, T, T, sl2, n_qblk, mt, o_intra, o_inter, lk0,
                             lk1, lv0, lv1, mlx, redo_flag, (int)(a - rs), (int)(b - a), &sg,
@@ -1431,8 +1432,10 @@ hipError_t mfma_attention(const Dims& d, const void* q, const void* k, const voi
 // workgroup is estimated to finish at least 10% before a whole query block
 // does. Measured on MI355X: a segment boundary costs about 12 key tiles, so
 // the split pays off for long frames with few heads (4 x 4096 tokens: 60 ->
-// 45 us; 1 x 16384: 233 -> 134 us) and not at 12 heads x 1560 tokens (25
-// tiles per block).
+// 45 us; 1 x 16384: 233 -> 134 us) and where the plain grid's last round is
+// mostly idle (40 heads x 1560: 83 -> 76 us; 12 heads x 3600: 116 -> 102 us),
+// and not at 12 heads x 1560 tokens (25 tiles per block) nor with the chip
+// full.
 constexpr int kSkMaxGrid = 256;
 constexpr int kSkPad = 2;
 constexpr int kSkBoundaryTiles = 12;
@@ -1445,15 +1448,17 @@ static SkPlan sk_plan(const Dims& d, int n_cu) {
   const int n_tiles = (d.T + AKT - 1) / AKT;
   const long n_blk = (long)d.B * d.H * ((d.T + AQ - 1) / AQ);
   const int G = std::min(n_cu, kSkMaxGrid);
-  if (G <= 0 || n_blk > G || n_tiles < 4) return p;
+  if (G <= 0 || n_tiles < 4) return p;
   const long L = n_tiles + p.pad, V = n_blk * L;
   // each workgroup's range covers at least half a block, so a block meets at
   // most three workgroups (the merge reads at most two other segments at once)
   if (V < G || V / G < (L + 1) / 2) return p;
-  // key tiles on the longest workgroup's path: a whole block on the plain
-  // grid; on the split grid its range plus the cost of a segment boundary
-  // (publishing a partial, the counter, the merge: about kSkBoundaryTiles)
-  p.use = 10 * ((V + G - 1) / G + kSkBoundaryTiles) < 9 * n_tiles;
+  // key tiles on the longest workgroup's path: one whole block per round of
+  // the plain grid (one workgroup per compute unit at a time); on the split
+  // grid its range plus the cost of its segment boundaries (publishing a
+  // partial, the counter, the merge: about kSkBoundaryTiles)
+  const long plain = (n_blk + G - 1) / G * n_tiles;
+  p.use = 10 * ((V + G - 1) / G + kSkBoundaryTiles) < 9 * plain;
   p.G = G;
   return p;
 }

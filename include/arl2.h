@@ -173,10 +173,11 @@ arl2_status arl2_read_prepare(const arl2_shape* shape, const void* phi_q,
  * ARL2_OP_READ_PREPARED) bytes. For bf16 shapes it is optional: with ws NULL
  * the read runs one workgroup per 128 queries of a head; with a workspace of
  * at least that many bytes (a non-NULL ws smaller than that is
- * ARL2_E_WORKSPACE), shapes whose query blocks leave compute units idle and
- * whose frames are long (the size is 0 for other shapes) split each block's
- * keys over several workgroups and merge their partial softmax results in
- * key order. Results of the two agree to fp32 rounding order; each is
+ * ARL2_E_WORKSPACE), shapes whose query blocks would leave many compute units
+ * idle (too few blocks, or a last round of blocks that fills few units) and
+ * whose frames are long enough (the size is 0 for other shapes) split each
+ * block's keys over several workgroups and merge their partial softmax
+ * results in key order. Results of the two agree to fp32 rounding order; each is
  * deterministic. The workspace needs no clearing (its block counters carry a
  * per-call tag and are left at zero); calls that share a workspace must not
  * overlap in time. */

@@ -65,7 +65,8 @@ def test_workspace_sizes(arl2):
     for B, H, T in ((8, 12, 1560), (1, 3, 300), (1, 6, 4096), (1, 8, 3000)):
         assert arl2.workspace_bytes(arl2.Shape(B, H, T, 128, arl2.BF16),
                                     arl2.OP_READ_PREPARED) == 0, (B, H, T)
-    for B, H, T in ((2, 2, 4096), (1, 5, 4000), (1, 3, 8192), (1, 1, 16384)):
+    for B, H, T in ((2, 2, 4096), (1, 5, 4000), (1, 3, 8192), (1, 1, 16384), (1, 40, 1560),
+                    (1, 12, 3600)):
         assert arl2.workspace_bytes(arl2.Shape(B, H, T, 128, arl2.BF16),
                                     arl2.OP_READ_PREPARED) > 0, (B, H, T)
     assert arl2.workspace_bytes(s, 17) == 0

@@ -15,8 +15,11 @@ pytestmark = pytest.mark.gpu
 
 # (B, H, T): long frames with few heads (the plain grid holds at most 128
 # workgroups of 64 or 128 key tiles); a ragged last key tile and query block;
-# two videos; three heads of 8192 tokens
-CASES = [(1, 4, 4096), (1, 2, 8192), (1, 5, 4000), (2, 2, 4096), (1, 3, 8192)]
+# two videos; three heads of 8192 tokens; more query blocks than compute
+# units (workgroups then hold whole blocks between their first and last
+# segments): 40 heads of 1560 tokens, 12 heads of 3600
+CASES = [(1, 4, 4096), (1, 2, 8192), (1, 5, 4000), (2, 2, 4096), (1, 3, 8192), (1, 40, 1560),
+         (1, 12, 3600)]
 
 
 def _ids(c):
@@ -63,7 +66,7 @@ def test_split_read_matches_oracle(case):
     assert_close(host(o), host(o_plain), TOL["bf16"], "split vs plain grid")
 
 
-@pytest.mark.parametrize("case", [(1, 4, 4096), (1, 5, 4000)], ids=_ids)
+@pytest.mark.parametrize("case", [(1, 4, 4096), (1, 5, 4000), (1, 40, 1560)], ids=_ids)
 def test_split_read_deterministic_on_any_workspace(case):
     """Per-call counter tags: a workspace left by earlier calls, or filled
     with arbitrary bytes, needs no clearing, and every call gives the same
