@@ -18,6 +18,9 @@ import torch  # loaded first: libarl2 then binds to the HIP runtime torch carrie
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarl2.so")
 
+# ARL2_ABI_VERSION of include/arl2.h that these signatures follow
+ABI_VERSION = 2
+
 F32 = 0
 BF16 = 1
 OP_READ, OP_CLEAN_PASS, OP_COMMIT, OP_STATE_COMMIT, OP_READ_PREPARED = 0, 1, 2, 3, 4
@@ -84,6 +87,10 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    got = lib.arl2_abi_version()
+    if got != ABI_VERSION:
+        raise ImportError(f"{_LIB_PATH} has ABI version {got}, the binding expects "
+                          f"{ABI_VERSION}; rebuild with `python -m hybrid_linear_memory_amd.build`")
     return lib
 
 

@@ -34,7 +34,9 @@ def test_every_declared_symbol_is_exported(arl2):
 
 
 def test_version_and_status_strings(arl2):
-    assert arl2.abi_version() == 2
+    assert arl2.abi_version() == arl2.ABI_VERSION == 2
+    hdr = open(os.path.join(os.path.dirname(arl2._LIB_PATH), "..", "include", "arl2.h")).read()
+    assert re.search(r"#define ARL2_ABI_VERSION (\d+)", hdr).group(1) == str(arl2.ABI_VERSION)
     for code, name in arl2.STATUS_NAMES.items():
         assert arl2.status_string(code) == name
     assert arl2.status_string(99) == "ARL2_E_UNKNOWN"
