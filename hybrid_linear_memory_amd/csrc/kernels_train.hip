@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "arl2_internal.h"
 #include "mfma_common.h"
@@ -730,22 +731,20 @@ attn_pre_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // branch with M = Phi_q S, bf16 row-major [e][v]). One workgroup of NW waves
 // per 32 NW queries; wave w accumulates dQ^T for queries 32 w.. (lane = query,
 // registers = features), key and value tiles staged in LDS.
+// (Workgroup `blk` of the dQ grid; the LDS arrays are the kernel's and reach
+// here as parameters, so that, once inlined, every access names its array.)
 template <int NW>
-__global__ void __launch_bounds__(64 * NW)
-attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-               const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
-               const float* __restrict__ lse2, const float* __restrict__ dsum,
-               const __bf16* __restrict__ m_rows, __bf16* __restrict__ dq, int T, float c,
-               float scale, int n_qblk, int accumulate) {
-  __shared__ __attribute__((aligned(16))) char lk0[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lk1[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lv0[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lv1[AB_STAGE * 256];
+__device__ __forceinline__ void attn_dq_block(
+    int blk, char* lk0, char* lk1, char* lv0, char* lv1, const __bf16* __restrict__ q,
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+    const float* __restrict__ lse2, const float* __restrict__ dsum,
+    const __bf16* __restrict__ m_rows, __bf16* __restrict__ dq, int T, float c, float scale,
+    int n_qblk, int accumulate) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  const long g = blockIdx.x / n_qblk;
-  const int i = (blockIdx.x % n_qblk) * (32 * NW) + 32 * wave + n;
+  const long g = blk / n_qblk;
+  const int i = (blk % n_qblk) * (32 * NW) + 32 * wave + n;
   const size_t gbase = (size_t)g * T;
   const size_t qrow = gbase + min(i, T - 1);
   bf16x8 qb[8], ob[8];
@@ -835,30 +834,67 @@ attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 }
 
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
+attn_dq_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+               const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+               const float* __restrict__ lse2, const float* __restrict__ dsum,
+               const __bf16* __restrict__ m_rows, __bf16* __restrict__ dq, int T, float c,
+               float scale, int n_qblk, int accumulate) {
+  __shared__ __attribute__((aligned(16))) char lk0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lk1[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lv0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lv1[AB_STAGE * 256];
+  attn_dq_block<NW>(blockIdx.x, lk0, lk1, lv0, lv1, q, k, v, d_o, lse2, dsum, m_rows, dq, T, c,
+                    scale, n_qblk, accumulate);
+}
+
+// A key block's dK and dV summed over two halves of the queries, each half a
+// workgroup of its own: both publish their fp32 sums (kacc, then vacc, in
+// 16-byte pieces, lane-interleaved) in their slot with device-scope (sc1)
+// stores, wait for them to complete and count their arrival on the block's
+// counter; the second to arrive adds the other's sums to its own (a + b, the
+// same value whichever half is second) and writes dK and dV.
+struct PairSplit {
+  float* slots;                  // 2 per key block (slot 2 blk + half), NW * 8192 floats each
+  unsigned long long* ctr;       // one per key block
+  unsigned long long tag;        // this call's tag (bit 63 set, so never 0)
+};
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCoherentAux = 16;   // cache policy bits of the slot accesses: device scope (sc1)
+
+// Two-party arrival: false for the first of a pair, true for the second, which
+// leaves the counter at 0 again. The first leaves this call's tag there; any
+// other content (0 after a completed call, or whatever a fresh workspace holds)
+// counts as no arrival, so the workspace needs no clearing between calls.
+__device__ __forceinline__ bool pair_arrive(unsigned long long* ctr, unsigned long long tag) {
+  const unsigned long long old =
+      __hip_atomic_exchange(ctr, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old != tag) return false;
+  __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // dK = scale sum_i dS_ij Q_i and dV = sum_i P_ij dO_i. One workgroup of NW
 // waves per 32 NW keys; wave w holds keys 32 w.. as the columns of S = Q K^T and
 // accumulates dK^T and dV^T (lane = key, registers = features); query, dO,
 // lse2 and dsum tiles staged in LDS (waves 0 and 1 move lse2 and dsum; any
 // further waves move lse2 once more into a spare slot, so that every wave
-// issues the same number of transfers per stage).
+// issues the same number of transfers per stage). With a PairSplit (half 0
+// or 1), the workgroup covers that half of the query stages.
 template <int NW>
-__global__ void __launch_bounds__(64 * NW)
-attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                 const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
-                 const float* __restrict__ lse2, const float* __restrict__ dsum,
-                 __bf16* __restrict__ dk, __bf16* __restrict__ dv, int T, float c, float scale,
-                 int n_kblk, int accumulate) {
-  __shared__ __attribute__((aligned(16))) char lq0[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lq1[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lo0[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) char lo1[AB_STAGE * 256];
-  __shared__ __attribute__((aligned(16))) float lr0[4 * AB_STAGE];   // lse2, dsum, spare x2
-  __shared__ __attribute__((aligned(16))) float lr1[4 * AB_STAGE];
+__device__ __forceinline__ void attn_dkdv_block(
+    int blk, int half, char* lq0, char* lq1, char* lo0, char* lo1, float* lr0, float* lr1,
+    int* flag, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+    const float* __restrict__ lse2, const float* __restrict__ dsum, __bf16* __restrict__ dk,
+    __bf16* __restrict__ dv, int T, float c, float scale, int n_kblk, int accumulate,
+    const PairSplit* ps) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  const long g = blockIdx.x / n_kblk;
-  const int j = (blockIdx.x % n_kblk) * (32 * NW) + 32 * wave + n;   // this lane's key
+  const long g = blk / n_kblk;
+  const int j = (blk % n_kblk) * (32 * NW) + 32 * wave + n;   // this lane's key
   const size_t gbase = (size_t)g * T;
   const size_t krow = gbase + min(j, T - 1);
   bf16x8 kb[8], vb[8];
@@ -925,22 +961,63 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lr + wave * AB_STAGE), 4,
                                              lane * 4, st * AB_STAGE * 4, 0, 0);
   };
-  issue(lq0, lo0, lr0, 0);
-  for (int st = 0;;) {
-    issue(lq1, lo1, lr1, min(st + 1, n_st - 1));
+  // query stages [s_begin, s_end): all, or this half's (the host splits only
+  // frames of at least 4 stages, so both halves are non-empty)
+  const int s_mid = n_st / 2;
+  const int s_begin = ps && half ? s_mid : 0;
+  const int s_end = ps && !half ? s_mid : n_st;
+  issue(lq0, lo0, lr0, s_begin);
+  for (int st = s_begin;;) {
+    issue(lq1, lo1, lr1, min(st + 1, s_end - 1));
     VMCNT_WAIT(32 / NW + 1);
     __builtin_amdgcn_s_barrier();
     compute(lq0, lo0, lr0, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
-    if (++st >= n_st) break;
-    issue(lq0, lo0, lr0, min(st + 1, n_st - 1));
+    if (++st >= s_end) break;
+    issue(lq0, lo0, lr0, min(st + 1, s_end - 1));
     VMCNT_WAIT(32 / NW + 1);
     __builtin_amdgcn_s_barrier();
     compute(lq1, lo1, lr1, st * AB_STAGE);
     __builtin_amdgcn_s_barrier();
-    if (++st >= n_st) break;
+    if (++st >= s_end) break;
   }
   VMCNT_WAIT(0);
+  if (ps) {
+    constexpr int kSlotFloats = NW * 8192;
+    const __amdgpu_buffer_rsrc_t mine =
+        buffer_rsrc(ps->slots + (size_t)(2 * blk + half) * kSlotFloats, kSlotFloats * 4);
+#pragma unroll
+    for (int gp = 0; gp < 32; ++gp) {
+      const f32x16& a = gp < 16 ? kacc[gp >> 2] : vacc[(gp >> 2) & 3];
+      const f32x4 x = {a[4 * (gp & 3)], a[4 * (gp & 3) + 1], a[4 * (gp & 3) + 2],
+                       a[4 * (gp & 3) + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), mine,
+                                             ((wave * 32 + gp) * 64 + lane) * 16, 0,
+                                             kCoherentAux);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) *flag = pair_arrive(ps->ctr + blk, ps->tag) ? 1 : 0;
+    __syncthreads();
+    if (*flag == 0) return;
+    const __amdgpu_buffer_rsrc_t other =
+        buffer_rsrc(ps->slots + (size_t)(2 * blk + 1 - half) * kSlotFloats, kSlotFloats * 4);
+    f32x4 od[32];
+#pragma unroll
+    for (int gp = 0; gp < 32; ++gp)
+      od[gp] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             other, ((wave * 32 + gp) * 64 + lane) * 16, 0,
+                                             kCoherentAux));
+#pragma unroll
+    for (int gp = 0; gp < 32; ++gp)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gp < 16)
+          kacc[gp >> 2][4 * (gp & 3) + e] += od[gp][e];
+        else
+          vacc[(gp >> 2) & 3][4 * (gp & 3) + e] += od[gp][e];
+      }
+  }
   if (key_ok) {
     __bf16* ok = dk + (gbase + j) * HD;
     __bf16* ov = dv + (gbase + j) * HD;
@@ -964,6 +1041,57 @@ attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         *pv4 = wv;
       }
     }
+  }
+}
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
+attn_dkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                 const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+                 const float* __restrict__ lse2, const float* __restrict__ dsum,
+                 __bf16* __restrict__ dk, __bf16* __restrict__ dv, int T, float c, float scale,
+                 int n_kblk, int accumulate) {
+  __shared__ __attribute__((aligned(16))) char lq0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lq1[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lo0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char lo1[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) float lr0[4 * AB_STAGE];   // lse2, dsum, spare x2
+  __shared__ __attribute__((aligned(16))) float lr1[4 * AB_STAGE];
+  attn_dkdv_block<NW>(blockIdx.x, 0, lq0, lq1, lo0, lo1, lr0, lr1, nullptr, q, k, v, d_o, lse2,
+                      dsum, dk, dv, T, c, scale, n_kblk, accumulate, nullptr);
+}
+
+// dQ and dK/dV in one grid, for shapes whose separate grids would each leave
+// most SIMDs idle (both kernels hold one wave per SIMD): the n_dq dQ
+// workgroups first (the longer ones), then the dK/dV workgroups, two per key
+// block (query halves) when a PairSplit is given. The two share one set of
+// LDS arrays.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
+attn_dqdkdv_mfma_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                   const __bf16* __restrict__ v, const __bf16* __restrict__ d_o,
+                   const float* __restrict__ lse2, const float* __restrict__ dsum,
+                   const __bf16* __restrict__ m_rows, __bf16* __restrict__ dq,
+                   __bf16* __restrict__ dk, __bf16* __restrict__ dv, int T, float c, float scale,
+                   int n_blk, int n_dq, int accumulate, PairSplit split) {
+  __shared__ __attribute__((aligned(16))) char l0[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char l1[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char l2[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) char l3[AB_STAGE * 256];
+  __shared__ __attribute__((aligned(16))) float lr0[4 * AB_STAGE];
+  __shared__ __attribute__((aligned(16))) float lr1[4 * AB_STAGE];
+  __shared__ int flag;
+  const int b = blockIdx.x;
+  if (b < n_dq) {
+    attn_dq_block<NW>(b, l0, l1, l2, l3, q, k, v, d_o, lse2, dsum, m_rows, dq, T, c, scale,
+                      n_blk, accumulate);
+  } else if (split.slots) {
+    const int u = b - n_dq;
+    attn_dkdv_block<NW>(u >> 1, u & 1, l0, l1, l2, l3, lr0, lr1, &flag, q, k, v, d_o, lse2,
+                        dsum, dk, dv, T, c, scale, n_blk, accumulate, &split);
+  } else {
+    attn_dkdv_block<NW>(b - n_dq, 0, l0, l1, l2, l3, lr0, lr1, &flag, q, k, v, d_o, lse2, dsum,
+                        dk, dv, T, c, scale, n_blk, accumulate, nullptr);
   }
 }
 
@@ -1174,6 +1302,18 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
   const long n_rows = (long)row_count(d);
   float* lse = c.take<float>(n_rows * sizeof(float));
   float* dsum = c.take<float>(n_rows * sizeof(float));
+  // One-grid dQ + dK/dV (2-wave workgroups of 64 rows) on shapes with fewer
+  // than 512 blocks of 128 rows; its dK/dV split over query halves from 4
+  // query stages up, with two fp32 slots and a counter per key block.
+  const long n_g = (long)d.B * d.H;
+  const bool small_grid = use_mfma(d) && n_g * ((d.T + 127) / 128) < 512;
+  const long n_kb = n_g * ((d.T + 63) / 64);
+  const bool split = small_grid && (d.T + AB_STAGE - 1) / AB_STAGE >= 4;
+  PairSplit ps{nullptr, nullptr, 0};
+  if (split) {
+    ps.slots = c.take<float>((size_t)2 * n_kb * 2 * 8192 * sizeof(float));
+    ps.ctr = c.take<unsigned long long>((size_t)n_kb * sizeof(unsigned long long));
+  }
   if (!c.base) return hipSuccess;
   const int acc = accumulate ? 1 : 0;
   if (lse_in && use_mfma(d))
@@ -1188,11 +1328,10 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
     const __bf16* ob = static_cast<const __bf16*>(d_o);
     const __bf16* oi = static_cast<const __bf16*>(o_intra);
     const __bf16* mr = static_cast<const __bf16*>(m_rows);
-    const long n_g = (long)d.B * d.H;
     // dQ and dK/dV: 4-wave workgroups (128 rows) when they fill the chip twice
-    // over, else 2-wave ones (64 rows) for twice as many; the row statistics
-    // always in 4-wave workgroups
-    if (n_g * ((d.T + 127) / 128) >= 512) {
+    // over, else 2-wave ones (64 rows) for twice as many, in one grid; the row
+    // statistics always in 4-wave workgroups
+    if (!small_grid) {
       const int nb = (d.T + 127) / 128;
       const unsigned grid = (unsigned)(n_g * nb);
       if (!lse_in) attn_pre_mfma_k<4><<<grid, 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T, cl, nb);
@@ -1208,11 +1347,14 @@ hipError_t attn_backward_steps(const Dims& d, const void* q, const void* k, cons
       if (!lse_in)
         attn_pre_mfma_k<4><<<(unsigned)(n_g * nb4), 256, 0, s>>>(qb, kb, oi, ob, lse, dsum, d.T,
                                                                 cl, nb4);
-      attn_dq_mfma_k<2><<<grid, 128, 0, s>>>(qb, kb, vb, ob, lse, dsum, mr,
-                                             static_cast<__bf16*>(dq), d.T, cl, d.scale, nb, acc);
-      attn_dkdv_mfma_k<2><<<grid, 128, 0, s>>>(qb, kb, vb, ob, lse, dsum,
-                                               static_cast<__bf16*>(dk), static_cast<__bf16*>(dv),
-                                               d.T, cl, d.scale, nb, acc);
+      if (split) {
+        static std::atomic<unsigned long long> g_pair_tag{0};
+        ps.tag = (++g_pair_tag) | (1ull << 63);
+      }
+      const unsigned grid2 = grid + (split ? 2u : 1u) * grid;
+      attn_dqdkdv_mfma_k<2><<<grid2, 128, 0, s>>>(
+          qb, kb, vb, ob, lse, dsum, mr, static_cast<__bf16*>(dq), static_cast<__bf16*>(dk),
+          static_cast<__bf16*>(dv), d.T, cl, d.scale, nb, (int)grid, acc, ps);
     }
   } else {
     const float* qf = static_cast<const float*>(q);

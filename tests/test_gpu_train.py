@@ -113,6 +113,42 @@ def test_intra_attn_backward(case, with_lse):
         _close(host(got), ref[name], TOL[w.dtype], name, floor=np.abs(ref["dv"]).max())
 
 
+@pytest.mark.parametrize("case", [("bf16", 1, 2, 513, 128), ("bf16", 1, 3, 256, 128)], ids=_ids)
+def test_attn_backward_split_halves(case):
+    """Shapes whose dK/dV key blocks are split over two query halves (the
+    second half to finish adds the first's fp32 sums): identical bits over
+    repeated calls on a workspace refilled with arbitrary bytes (the pair
+    counters need no clearing), accumulate = 1 doubles, and the oracle agrees
+    (513 tokens: 9 query stages, halves of 4 and 5)."""
+    import torch
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"attention backward split halves {_ids(case)}")
+    sh = shape_of(w)
+    q, k, v = synth.qkv(w, 0, 1)
+    d_o = _grad_out(w, 21)
+    dq_, dk_, dv_, do_ = (dev(x, w.dtype) for x in (q, k, v, d_o))
+    o, lse = _forward(arl2, sh, w, dq_, dk_, dv_, True)
+    ws = arl2.alloc_workspace(sh, arl2.OP_INTRA_ATTN_BACKWARD)
+    runs = []
+    for fill in (0xA5, 0x00, 0xFF):
+        ws.fill_(fill)
+        grads = [_zeros((w.B, w.H, w.T, w.D), w.dtype) for _ in range(3)]
+        arl2.intra_attn_backward(sh, dq_, dk_, dv_, o, do_, *grads, ws=ws, lse=lse)
+        runs.append(grads)
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for name, x, y in zip(("dq", "dk", "dv"), runs[0], r):
+            assert torch.equal(x, y), f"{name} not reproducible"
+    twice = [x.clone() for x in runs[0]]
+    arl2.intra_attn_backward(sh, dq_, dk_, dv_, o, do_, *twice, accumulate=True, ws=ws, lse=lse)
+    for name, x, y in zip(("dq", "dk", "dv"), runs[0], twice):
+        assert_close(host(y), 2 * host(x), 1e-2, name)
+    ref = oracle.intra_attention_backward(q, k, v, d_o)
+    for name, got in zip(("dq", "dk", "dv"), runs[0]):
+        _close(host(got), ref[name], TOL[w.dtype], name, floor=np.abs(ref["dv"]).max())
+
+
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 @pytest.mark.parametrize("with_lse", [False, True])
 def test_read_backward(case, with_lse):
