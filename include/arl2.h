@@ -296,7 +296,11 @@ arl2_status arl2_intra_attn_lse(const arl2_shape* shape, const void* q,
  *   dZ = P * (dP - rowsum(dO * O_intra)), dQ = scale dZ K, dK = scale dZ^T Q.
  * lse: NULL, or the rows' log-sum-exp from arl2_intra_attn_lse on the same
  * q and k (then P = exp(scale Q K^T - lse) without a pass to find it).
- * Needs arl2_workspace_bytes(shape, ARL2_OP_INTRA_ATTN_BACKWARD). */
+ * Needs arl2_workspace_bytes(shape, ARL2_OP_INTRA_ATTN_BACKWARD). On shapes
+ * with fewer than 512 blocks of 128 rows (bf16, d = 128) the workspace also
+ * holds per-key-block partial sums and counters: it needs no clearing (the
+ * counters carry a per-call tag and are left at zero), and calls that share a
+ * workspace must not run concurrently. */
 arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q,
                                      const void* k, const void* v,
                                      const void* o_intra, const float* lse,
@@ -308,7 +312,8 @@ arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q,
  * read's o_intra and d_o = dL/dO: dq, dk, dv, dphi_q and dS, with
  *   dQ += dO (Phi_q S)^T, dS = (Q Phi_q)^T dO, dPhi_q = sum_b Q^T dO S^T.
  * lse as in arl2_intra_attn_backward (NULL or from arl2_intra_attn_lse).
- * Needs arl2_workspace_bytes(shape, ARL2_OP_READ_BACKWARD). */
+ * Needs arl2_workspace_bytes(shape, ARL2_OP_READ_BACKWARD) (with the same
+ * sharing rule as arl2_intra_attn_backward's). */
 arl2_status arl2_read_backward(const arl2_shape* shape, const void* q,
                                const void* k, const void* v, const void* phi_q,
                                const float* S, const void* o_intra,
