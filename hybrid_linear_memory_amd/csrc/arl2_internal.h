@@ -42,6 +42,7 @@ struct FeatureMapJob {
   const void* phi;
   void* out;
   bool normalize;
+  float* norms = nullptr;   // first job only, with normalize: each row's norm before the floor
 };
 hipError_t mfma_feature_maps(const Dims& d, const FeatureMapJob* jobs, int n_jobs, hipStream_t s);
 hipError_t mfma_feature_map(const Dims& d, const void* x, const void* phi,

@@ -730,9 +730,9 @@ constexpr int MAP_ROWS = 128;         // rows per workgroup
 enum MapMode { MAP_PHI = 0, MAP_STATE = 1 };
 
 // Feature maps of up to three inputs of one shape in one launch (the
-// token-level pass's Q', K', V'; the commit backward's K~, V'): workgroups
-// [j per_prob, (j + 1) per_prob) map input j; input 0 is the kernel's x /
-// mat / out / normalize.
+// token-level pass's Q', K', V'; the commit backward's K' with its rows'
+// norms, and V'): workgroups [j per_prob, (j + 1) per_prob) map input j;
+// input 0 is the kernel's x / mat / out / normalize / norms.
 struct MapMore {
   const __bf16* x1;
   const void* m1;
@@ -748,7 +748,8 @@ template <int MODE>
 __global__ void __launch_bounds__(256)
 rowmap_mfma_k(const __bf16* __restrict__ x, const void* __restrict__ mat,
               const __bf16* o_intra, __bf16* out, __bf16* __restrict__ o_inter, int H,
-              int T, int n_rblk, int normalize, MapMore more = MapMore{}, int per_prob = 0) {
+              int T, int n_rblk, int normalize, MapMore more = MapMore{}, int per_prob = 0,
+              float* __restrict__ norms = nullptr) {
   __shared__ __attribute__((aligned(16))) __bf16 MT[HD * MS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -758,6 +759,7 @@ rowmap_mfma_k(const __bf16* __restrict__ x, const void* __restrict__ mat,
     const int j = bid / per_prob;
     bid -= j * per_prob;
     nb = per_prob;
+    if (j > 0) norms = nullptr;    // (the norms belong to input 0)
     if (j == 1) {
       x = more.x1;
       mat = more.m1;
@@ -831,7 +833,9 @@ rowmap_mfma_k(const __bf16* __restrict__ x, const void* __restrict__ mat,
 #pragma unroll
       for (int r = 0; r < 16; ++r) ss = fmaf(acc[ob][r], acc[ob][r], ss);
     ss += swap_halves(ss);
-    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+    const float nr = sqrtf(ss);
+    if (norms && h2 == 0 && t < T) norms[row] = nr;
+    const float inv = 1.f / fmaxf(nr, 1e-12f);
 #pragma unroll
     for (int ob = 0; ob < 4; ++ob)
 #pragma unroll
@@ -1588,7 +1592,10 @@ hipError_t mfma_feature_map(const Dims& d, const void* x, const void* phi, void*
 
 hipError_t mfma_feature_maps(const Dims& d, const FeatureMapJob* jobs, int n_jobs, hipStream_t s) {
   if (n_jobs < 1 || n_jobs > 3) return hipErrorInvalidValue;
-  if (n_jobs == 1)
+  for (int j = 1; j < n_jobs; ++j)
+    if (jobs[j].norms) return hipErrorInvalidValue;
+  if (jobs[0].norms && !jobs[0].normalize) return hipErrorInvalidValue;
+  if (n_jobs == 1 && !jobs[0].norms)
     return mfma_feature_map(d, jobs[0].x, jobs[0].phi, jobs[0].out, jobs[0].normalize, s);
   const int n_rblk = (d.T + MAP_ROWS - 1) / MAP_ROWS;
   const long nblk = (long)d.B * d.H * n_rblk;
@@ -1600,7 +1607,7 @@ hipError_t mfma_feature_maps(const Dims& d, const FeatureMapJob* jobs, int n_job
   rowmap_mfma_k<MAP_PHI><<<(unsigned)(nblk * n_jobs), 256, 0, s>>>(
       static_cast<const __bf16*>(jobs[0].x), jobs[0].phi, nullptr,
       static_cast<__bf16*>(jobs[0].out), nullptr, d.H, d.T, n_rblk, jobs[0].normalize ? 1 : 0,
-      more, (int)nblk);
+      more, (int)nblk, jobs[0].norms);
   return hipGetLastError();
 }
 

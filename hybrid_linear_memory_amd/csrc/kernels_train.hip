@@ -1429,7 +1429,7 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   const size_t ab = act_bytes(d);
   const size_t fb = row_count(d) * d.D * sizeof(float);
   const bool mf = use_mfma(d);
-  void* kt = c.take<char>(ab);            // K Phi_k
+  void* kt = mf ? nullptr : c.take<char>(ab);   // K Phi_k (the MFMA map normalises in place)
   void* kp = c.take<char>(ab);            // K'
   float* nrm = c.take<float>(row_count(d) * sizeof(float));
   void* vp = c.take<char>(ab);            // V'
@@ -1450,15 +1450,14 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   const int acc = accumulate ? 1 : 0;
   hipError_t e;
   if (mf) {
-    const FeatureMapJob jobs[2] = {{k, phi_k, kt, false}, {v, phi_v, vp, false}};
+    // K' = rownorm(K Phi_k) with its rows' norms, and V' = V Phi_v, in one launch
+    const FeatureMapJob jobs[2] = {{k, phi_k, kp, true, nrm}, {v, phi_v, vp, false}};
     if ((e = mfma_feature_maps(d, jobs, 2, s)) != hipSuccess) return e;
   } else {
     if ((e = feature_map_any(d, k, phi_k, kt, false, s)) != hipSuccess) return e;
     if ((e = feature_map_any(d, v, phi_v, vp, false, s)) != hipSuccess) return e;
   }
   if (mf) {
-    rownorm_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(static_cast<const __bf16*>(kt),
-                                                          static_cast<__bf16*>(kp), nrm, d.D, n_rows);
     // bf16 copies of S and G, and dalpha = <S, G> per (b, h), in one launch
     const long cast_blocks = blocks(2 * (long)mat_count(d), 256);
     to_bf16_pair_k<<<(unsigned)(cast_blocks + (long)d.B * d.H), 256, 0, s>>>(
