@@ -10,10 +10,14 @@
 //   nt_gemm   Y = X Bt^T per (b, h) with an elementwise epilogue
 //   xty       C = X^T Y summed over tokens (and over videos for the maps'
 //             gradients), in fixed-order chunk partials
-//   row kernels for the row normalisation, beta and the norm's backward
+//   row steps (the row normalisation, beta and the norm's backward): in the
+//             epilogues of the products that feed them on MFMA, row kernels
+//             on the float path
 //   attention backward: per-row log-sum-exp and dO.O, then dK, dV (one
-//             workgroup per key block) and dQ (one per query block), each
-//             recomputing the scores, so no accumulation crosses workgroups.
+//             workgroup per key block; on small grids two, over the query
+//             halves, the second adding the first's sums) and dQ (one per
+//             query block), each recomputing the scores; no atomic
+//             accumulation, so the gradients are deterministic.
 #include <math.h>
 
 #include <algorithm>
@@ -395,6 +399,115 @@ nt_gemm_mfma_k(NtBatch nb, int rows, int H, int n_rblk, long per_prob) {
   for (int r = 0; r < 16; ++r) {
     const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
     if (row < rows) epilogue<__bf16>(P.ep, ((size_t)g * rows + row) * HD + 32 * wave + n, acc[r]);
+  }
+}
+
+// The commit backward's row steps fused into the products that feed them. A
+// workgroup holds 32 whole rows (4 waves x 32 columns), so the per-row sums
+// go through LDS: value v[r] of lane (n, h2) of wave w sits at row
+// 8 (r / 4) + 4 h2 + r % 4 and column 32 w + n (the accumulator's order).
+constexpr int RS_LD = 132;                     // row stride of the reduction tile (floats)
+
+// Row sums of the 32 x 128 tile, in a fixed order (8 runs of 16 columns, then
+// a pairwise tree over the runs); every lane receives its 16 rows' sums.
+__device__ __forceinline__ void tile_row_sums(const float (&v)[16], float (&sum)[16], float* red,
+                                              float* rs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[(8 * (r >> 2) + 4 * h2 + (r & 3)) * RS_LD + 32 * wave + n] = v[r];
+  __syncthreads();
+  const int row = threadIdx.x >> 3, part = threadIdx.x & 7;
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a += red[row * RS_LD + 16 * part + j];
+  a += __shfl_xor(a, 1);
+  a += __shfl_xor(a, 2);
+  a += __shfl_xor(a, 4);
+  if (part == 0) rs[row] = a;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sum[r] = rs[8 * (r >> 2) + 4 * h2 + (r & 3)];
+}
+
+// Per 32 rows of one g: R = V' - K'S and K'G (both products in the workgroup),
+// then dbeta_t (+)= sum_v K'G[t][v] R[t][v] and dV' = beta K'G; R, K'G and dV'
+// leave as bf16 (the operands of the next products).
+__global__ void __launch_bounds__(256)
+commit_resid_rows_k(const __bf16* __restrict__ kp, const __bf16* __restrict__ st,
+                    const __bf16* __restrict__ gt, const __bf16* __restrict__ vp,
+                    const float* __restrict__ beta, __bf16* __restrict__ rx,
+                    __bf16* __restrict__ kgx, __bf16* __restrict__ dvx,
+                    float* __restrict__ dbeta, int T, int H, int n_rblk, int accumulate) {
+  __shared__ float red[32 * RS_LD];
+  __shared__ float rs[32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long g = blockIdx.x / n_rblk;
+  const int row0 = (int)(blockIdx.x % n_rblk) * 32;
+  const f32x16 as = nt_tile(kp, st, 0, 0, g, H, T, row0, lane, wave);
+  const f32x16 ag = nt_tile(kp, gt, 0, 0, g, H, T, row0, lane, wave);
+  float prod[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+    prod[r] = 0.f;
+    if (row < T) {
+      const size_t idx = ((size_t)g * T + row) * HD + 32 * wave + n;
+      const float R = (float)vp[idx] - as[r];
+      const float kg = ag[r];
+      prod[r] = kg * R;
+      rx[idx] = (__bf16)R;
+      kgx[idx] = (__bf16)kg;
+      dvx[idx] = (__bf16)(beta[(size_t)g * T + row] * kg);
+    }
+  }
+  float sum[16];
+  tile_row_sums(prod, sum, red, rs);
+  const int t = threadIdx.x;
+  if (t < 32 && row0 + t < T) {
+    const size_t i = (size_t)g * T + row0 + t;
+    dbeta[i] = accumulate ? dbeta[i] + rs[t] : rs[t];
+  }
+}
+
+// Per 32 rows of one g: dKraw = R G^T - K'G S^T, then through beta and the row
+// normalisation K' = K~ / max(||K~||, floor): dK~ = beta (dKraw - K' (K'.dKraw))
+// / ||K~|| above the floor, beta dKraw / floor below it (bf16 out).
+__global__ void __launch_bounds__(256)
+commit_dkt_rows_k(const __bf16* __restrict__ rx, const __bf16* __restrict__ gb,
+                  const __bf16* __restrict__ kgx, const __bf16* __restrict__ sb,
+                  const __bf16* __restrict__ kp, const float* __restrict__ nrm,
+                  const float* __restrict__ beta, __bf16* __restrict__ dkt, int T, int H,
+                  int n_rblk) {
+  __shared__ float red[32 * RS_LD];
+  __shared__ float rs[32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+  const long g = blockIdx.x / n_rblk;
+  const int row0 = (int)(blockIdx.x % n_rblk) * 32;
+  const f32x16 d = nt_tile(rx, gb, 0, 0, g, H, T, row0, lane, wave) -
+                   nt_tile(kgx, sb, 0, 0, g, H, T, row0, lane, wave);
+  float kv[16], prod[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+    kv[r] = row < T ? (float)kp[((size_t)g * T + row) * HD + 32 * wave + n] : 0.f;
+    prod[r] = kv[r] * d[r];
+  }
+  float dot[16];
+  tile_row_sums(prod, dot, red, rs);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = row0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+    if (row < T) {
+      const size_t i = (size_t)g * T + row;
+      const float nr = nrm[i];
+      const bool above = nr > kNormFloor;
+      const float inv = above ? 1.f / nr : 1.f / kNormFloor;
+      const float pr = above ? dot[r] : 0.f;
+      dkt[i * HD + 32 * wave + n] = (__bf16)(beta[i] * (d[r] - kv[r] * pr) * inv);
+    }
   }
 }
 
@@ -1433,12 +1546,14 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
   void* kp = c.take<char>(ab);            // K'
   float* nrm = c.take<float>(row_count(d) * sizeof(float));
   void* vp = c.take<char>(ab);            // V'
-  float* r32 = c.take<float>(fb);         // R = V' - K'S
+  // (the fp32 intermediates only on the float path: the MFMA path keeps them
+  // in the workgroups that form them)
+  float* r32 = mf ? nullptr : c.take<float>(fb);    // R = V' - K'S
   void* rx = c.take<char>(ab);
-  float* kg32 = c.take<float>(fb);        // K'G
+  float* kg32 = mf ? nullptr : c.take<float>(fb);   // K'G
   void* kgx = c.take<char>(ab);
   void* dvx = c.take<char>(ab);           // dV'
-  float* dkr = c.take<float>(fb);         // R G^T - K'G S^T
+  float* dkr = mf ? nullptr : c.take<float>(fb);    // R G^T - K'G S^T
   void* dktx = c.take<char>(ab);          // dK~
   __bf16* Sb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
   __bf16* Stb = mf ? c.take<__bf16>(mat_count(d) * 2) : nullptr;
@@ -1466,50 +1581,38 @@ hipError_t commit_backward_steps(const Dims& d, const void* k, const void* v, co
     rownorm_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(static_cast<const float*>(kt),
                                                          static_cast<float*>(kp), nrm, d.D, n_rows);
   }
-  // R = V' - K' S ;  K'G
-  const void* bS_t = mf ? (const void*)Stb : (const void*)S;
-  const void* bG_t = mf ? (const void*)Gtb : (const void*)G;
+  const int n_rblk = (d.T + 31) / 32;
+  const unsigned row_grid = (unsigned)((long)d.B * d.H * n_rblk);
   if (mf) {
-    const NtProb p1 = nt_prob(kp, false, bG_t, false, make_epi(nullptr, false, kg32, kgx, false));
-    e = nt_gemm_batch(d, d.T, nt_prob(kp, false, bS_t, false, make_epi(vp, false, r32, rx, false)),
-                      &p1, s);
+    // R = V' - K'S and K'G, then dbeta and dV' = beta K'G, in one launch
+    commit_resid_rows_k<<<row_grid, 256, 0, s>>>(
+        static_cast<const __bf16*>(kp), Stb, Gtb, static_cast<const __bf16*>(vp), beta,
+        static_cast<__bf16*>(rx), static_cast<__bf16*>(kgx), static_cast<__bf16*>(dvx), dbeta,
+        d.T, d.H, n_rblk, acc);
+    // dKraw = R G^T - K'G S^T and dK~ through beta and the row normalisation
+    commit_dkt_rows_k<<<row_grid, 256, 0, s>>>(
+        static_cast<const __bf16*>(rx), Gb, static_cast<const __bf16*>(kgx), Sb,
+        static_cast<const __bf16*>(kp), nrm, beta, static_cast<__bf16*>(dktx), d.T, d.H, n_rblk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
-    e = nt_gemm(d, kp, d.T, false, bS_t, false, true, make_epi(vp, false, r32, rx, false), s);
+    // R = V' - K' S ;  K'G
+    e = nt_gemm(d, kp, d.T, false, S, false, true, make_epi(vp, false, r32, rx, false), s);
     if (e != hipSuccess) return e;
-    e = nt_gemm(d, kp, d.T, false, bG_t, false, true, make_epi(nullptr, false, kg32, kgx, false), s);
-  }
-  if (e != hipSuccess) return e;
-  // dbeta, dV' = beta K'G
-  if (mf)
-    commit_rows1_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(kg32, r32, beta, dbeta,
-                                                               static_cast<__bf16*>(dvx), d.D, acc,
-                                                               n_rows);
-  else
+    e = nt_gemm(d, kp, d.T, false, G, false, true, make_epi(nullptr, false, kg32, kgx, false), s);
+    if (e != hipSuccess) return e;
+    // dbeta, dV' = beta K'G
     commit_rows1_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(kg32, r32, beta, dbeta,
                                                               static_cast<float*>(dvx), d.D, acc,
                                                               n_rows);
-  // dKraw = R G^T - K'G S^T
-  const void* bG = mf ? (const void*)Gb : (const void*)G;
-  const void* bS = mf ? (const void*)Sb : (const void*)S;
-  if (mf) {
-    // both products in one launch, the second subtracted from the first in fp32
-    e = nt_gemm_batch(d, d.T,
-                      nt_prob(rx, false, bG, false, make_epi(nullptr, false, dkr, nullptr, false),
-                              kgx, bS),
-                      nullptr, s);
-  } else {
-    e = nt_gemm(d, rx, d.T, false, bG, false, false, make_epi(nullptr, false, dkr, nullptr, false), s);
+    // dKraw = R G^T - K'G S^T
+    e = nt_gemm(d, rx, d.T, false, G, false, false, make_epi(nullptr, false, dkr, nullptr, false), s);
     if (e != hipSuccess) return e;
-    e = nt_gemm(d, kgx, d.T, false, bS, false, false, make_epi(dkr, true, dkr, nullptr, false), s);
-  }
-  if (e != hipSuccess) return e;
-  // dK~ through beta and the row normalisation
-  if (mf)
-    commit_rows2_k<__bf16><<<blocks(n_rows, 4), 256, 0, s>>>(
-        dkr, static_cast<const __bf16*>(kp), nrm, beta, static_cast<__bf16*>(dktx), d.D, n_rows);
-  else
+    e = nt_gemm(d, kgx, d.T, false, S, false, false, make_epi(dkr, true, dkr, nullptr, false), s);
+    if (e != hipSuccess) return e;
+    // dK~ through beta and the row normalisation
     commit_rows2_k<float><<<blocks(n_rows, 4), 256, 0, s>>>(
         dkr, static_cast<const float*>(kp), nrm, beta, static_cast<float*>(dktx), d.D, n_rows);
+  }
   // dK = dK~ Phi_k^T, dV = dV' Phi_v^T
   if (mf) {
     const NtProb p1 = nt_prob(dvx, false, phi_v, true,
