@@ -59,10 +59,8 @@ arl2_status check_shape(const arl2_shape* sh, arl2::Dims* d) {
   if (sh->B < 1 || sh->H < 1 || sh->T < 1)
     return fail(ARL2_E_SHAPE, "B, H, T must be >= 1 (got %d, %d, %d)", sh->B, sh->H, sh->T);
   const bool bf16 = sh->act_dtype == ARL2_BF16;
-  if (bf16 && sh->D != 128)
-    return fail(ARL2_E_SHAPE, "bf16 activations need D = 128 (got %d)", sh->D);
-  if (!bf16 && sh->D != 16 && sh->D != 32 && sh->D != 64 && sh->D != 128)
-    return fail(ARL2_E_SHAPE, "float32 activations need D in {16, 32, 64, 128} (got %d)", sh->D);
+  if (sh->D != 16 && sh->D != 32 && sh->D != 64 && sh->D != 128)
+    return fail(ARL2_E_SHAPE, "D must be one of 16, 32, 64, 128 (got %d)", sh->D);
   const double elems = (double)sh->B * sh->H * sh->T * sh->D;
   if (elems >= 2147483648.0)
     return fail(ARL2_E_SHAPE, "B*H*T*D = %.0f exceeds 2^31 - 1", elems);
@@ -74,6 +72,14 @@ arl2_status check_shape(const arl2_shape* sh, arl2::Dims* d) {
   d->D = sh->D;
   d->bf16 = bf16;
   d->scale = sh->softmax_scale > 0.f ? sh->softmax_scale : 1.0f / sqrtf((float)sh->D);
+  return ARL2_OK;
+}
+
+// The token-level and training calls run bf16 activations at D = 128 only
+// (their smaller-D kernels are float32).
+arl2_status require_d128_for_bf16(const arl2::Dims& d, const char* what) {
+  if (d.bf16 && d.D != 128)
+    return fail(ARL2_E_SHAPE, "%s with bf16 activations needs D = 128 (got %d)", what, d.D);
   return ARL2_OK;
 }
 
@@ -364,6 +370,7 @@ arl2_status arl2_intra_attn_lse(const arl2_shape* shape, const void* q, const vo
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
+  if ((st = require_d128_for_bf16(d, "arl2_intra_attn_lse")) != ARL2_OK) return st;
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
@@ -415,6 +422,17 @@ arl2_status arl2_state_commit(const arl2_shape* shape, const void* k_prime, cons
   REQUIRE_PTR(S_next);
   if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
   if ((st = check_ws(ws, ws_bytes, commit_ws(d))) != ARL2_OK) return st;
+  {
+    const size_t ab = arl2::act_bytes(d);
+    const Range outs[1] = {{S_next, state_bytes(d)}};
+    const Range ins[6] = {{k_prime, ab},
+                          {v_prime, ab},
+                          {beta, (size_t)d.B * d.H * d.T * 4},
+                          {alpha, (size_t)d.B * d.H * 4},
+                          {S_prev, state_bytes(d)},
+                          {ws, commit_ws(d)}};
+    if ((st = check_disjoint(outs, 1, ins, 6)) != ARL2_OK) return st;
+  }
   return hip_status(run_state_commit(d, k_prime, v_prime, beta, alpha, S_prev, S_next, ws,
                                      (hipStream_t)stream),
                     "state commit");
@@ -526,8 +544,19 @@ arl2_status arl2_commit(const arl2_shape* shape, const void* k, const void* v, c
   REQUIRE_PTR(S_next);
   if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
   if ((st = check_ws(ws, ws_bytes, ws_commit(d))) != ARL2_OK) return st;
-  if (overlap({S_next, state_bytes(d)}, {ws, ws_commit(d)}))
-    return fail(ARL2_E_ALIAS, "S_next overlaps the workspace");
+  {
+    const size_t ab = arl2::act_bytes(d);
+    const Range outs[1] = {{S_next, state_bytes(d)}};
+    const Range ins[8] = {{k, ab},
+                          {v, ab},
+                          {phi_k, phi_bytes(d)},
+                          {phi_v, phi_bytes(d)},
+                          {beta, (size_t)d.B * d.H * d.T * 4},
+                          {alpha, (size_t)d.B * d.H * 4},
+                          {S_prev, state_bytes(d)},
+                          {ws, ws_commit(d)}};
+    if ((st = check_disjoint(outs, 1, ins, 8)) != ARL2_OK) return st;
+  }
   return do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, (hipStream_t)stream);
 }
 
@@ -557,14 +586,17 @@ arl2_status arl2_clean_pass(const arl2_shape* shape, const void* q, const void* 
   if ((st = check_ws(ws, ws_bytes, need)) != ARL2_OK) return st;
   const size_t ab = arl2::act_bytes(d);
   const Range outs[4] = {{o, ab}, {o_intra, ab}, {o_inter, ab}, {S_next, state_bytes(d)}};
-  const Range ins[7] = {{q, ab}, {k, ab}, {v, ab}, {phi_q, phi_bytes(d)}, {S_prev, state_bytes(d)},
-                        {ws, need}, {beta, (size_t)d.B * d.H * d.T * 4}};
-  for (const Range& a : outs)
-    for (const Range& b : ins)
-      if (overlap(a, b)) return fail(ARL2_E_ALIAS, "an output overlaps an input or the workspace");
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return fail(ARL2_E_ALIAS, "two outputs overlap");
+  const Range ins[10] = {{q, ab},
+                         {k, ab},
+                         {v, ab},
+                         {phi_q, phi_bytes(d)},
+                         {phi_k, phi_bytes(d)},
+                         {phi_v, phi_bytes(d)},
+                         {S_prev, state_bytes(d)},
+                         {ws, need},
+                         {beta, (size_t)d.B * d.H * d.T * 4},
+                         {alpha, (size_t)d.B * d.H * 4}};
+  if ((st = check_disjoint(outs, 4, ins, 10)) != ARL2_OK) return st;
   st = do_read(d, q, k, v, phi_q, S_prev, o, o_intra, o_inter, ws, (hipStream_t)stream);
   if (st != ARL2_OK) return st;
   return do_commit(d, k, v, phi_k, phi_v, beta, alpha, S_prev, S_next, ws, (hipStream_t)stream);
@@ -640,6 +672,7 @@ arl2_status arl2_token_read(const arl2_shape* shape, const void* q, const void* 
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
+  if ((st = require_d128_for_bf16(d, "token-level access")) != ARL2_OK) return st;
   st = check_token(d, q, k, v, phi_q, phi_k, phi_v, beta, nullptr, S, nullptr, o, o_intra,
                    o_inter, ws, ws_bytes);
   if (st != ARL2_OK) return st;
@@ -655,6 +688,7 @@ arl2_status arl2_token_clean_pass(const arl2_shape* shape, const void* q, const 
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
+  if ((st = require_d128_for_bf16(d, "token-level access")) != ARL2_OK) return st;
   REQUIRE_PTR(alpha);
   REQUIRE_PTR(S_next);
   if ((st = check_state_pair(d, S_prev, S_next)) != ARL2_OK) return st;
@@ -675,6 +709,7 @@ arl2_status arl2_intra_attn_backward(const arl2_shape* shape, const void* q, con
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
+  if ((st = require_d128_for_bf16(d, "the attention backward")) != ARL2_OK) return st;
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
@@ -706,6 +741,7 @@ arl2_status arl2_read_backward(const arl2_shape* shape, const void* q, const voi
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
+  if ((st = require_d128_for_bf16(d, "the read backward")) != ARL2_OK) return st;
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
@@ -743,6 +779,7 @@ arl2_status arl2_commit_backward(const arl2_shape* shape, const void* k, const v
   arl2::Dims d;
   arl2_status st = check_shape(shape, &d);
   if (st != ARL2_OK) return st;
+  if ((st = require_d128_for_bf16(d, "the commit backward")) != ARL2_OK) return st;
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
   REQUIRE_PTR(phi_k);

@@ -21,6 +21,19 @@ class SequenceError(RuntimeError):
     """A pass was issued out of the read* -> clean pass order."""
 
 
+class NonFiniteInput(ValueError):
+    """An input of a pass holds a NaN or an infinity (debug check)."""
+
+
+def check_finite(**tensors):
+    """Raise NonFiniteInput naming the first given tensor that holds a NaN or
+    an infinity (None entries are skipped). Reads every element, and on a
+    device tensor waits for the stream: a debug aid, off by default."""
+    for name, t in tensors.items():
+        if t is not None and not bool(torch.isfinite(t).all()):
+            raise NonFiniteInput(f"{name} holds non-finite values")
+
+
 class PassSequencer:
     """Frame / pass bookkeeping. With ``n_denoise`` set (strict mode) each
     frame must have exactly that many reads before its clean pass."""
@@ -71,14 +84,19 @@ class Arl2Layer:
     (the summary's §4): within each pass token t reads the state updated by
     the frame's earlier tokens (arl2_token_read / arl2_token_clean_pass); the
     state is still written once per frame, by the clean pass.
+
+    ``check_finite=True`` (debug) checks every input of a pass for NaN and
+    infinity before anything is launched and raises NonFiniteInput, leaving
+    the state and the pass order untouched.
     """
 
     def __init__(self, shape: arl2.Shape, phi_q, phi_k, phi_v, n_denoise: int | None = None,
                  device=None, prepared: bool = True, fused_clean: bool = True,
-                 access: str = "frame"):
+                 access: str = "frame", check_finite: bool = False):
         if access not in ("frame", "token"):
             raise ValueError(f"access must be 'frame' or 'token' (got {access!r})")
         self.access = access
+        self.check_finite = check_finite
         if access == "token":
             prepared = False
         self.shape = shape
@@ -142,6 +160,8 @@ class Arl2Layer:
         if self.access == "token" and beta is None:
             raise ValueError("token-level reads need the frame's beta")
         self.seq.before_read()
+        if self.check_finite:
+            check_finite(q=q, k=k, v=v, beta=beta)
         o = self.new_output() if o is None else o
         if self.access == "token":
             arl2.token_read(self.shape, q, k, v, *self.phi, beta, self.S, o, o_intra, o_inter,
@@ -157,6 +177,8 @@ class Arl2Layer:
     def clean_pass(self, q, k, v, beta, alpha, o=None, o_intra=None, o_inter=None, stream=None):
         """Read against S_{N-1}, commit S_N into the other buffer, swap."""
         self.seq.before_clean_pass()
+        if self.check_finite:
+            check_finite(q=q, k=k, v=v, beta=beta, alpha=alpha)
         o = self.new_output() if o is None else o
         nxt = 1 - self._cur
         if self.access == "token":
@@ -188,6 +210,8 @@ class Arl2Layer:
     def commit(self, k, v, beta, alpha, stream=None):
         """State write of the clean pass without its read."""
         self.seq.before_clean_pass()
+        if self.check_finite:
+            check_finite(k=k, v=v, beta=beta, alpha=alpha)
         nxt = 1 - self._cur
         if self.access == "token":
             # the end state depends on K, V and beta only: any query will do,

@@ -31,9 +31,12 @@
  *     contiguous.
  *   - beta is float32 [B, H, T]; alpha is float32 [B, H].
  *   - Every pointer is a device pointer, 16-byte aligned, owned by the
- *     caller. The library allocates no memory and keeps no state between
- *     calls. Scratch memory comes from the caller's workspace (ws, ws_bytes),
- *     sized by arl2_workspace_bytes().
+ *     caller. The library allocates no memory. Scratch memory comes from the
+ *     caller's workspace (ws, ws_bytes), sized by arl2_workspace_bytes().
+ *     Its only state between calls is a process-wide host counter that gives
+ *     each call of the split-key read and of the attention backward's split
+ *     a distinct tag for its workspace block counters (so that a workspace
+ *     needs no clearing); results never depend on the counter's value.
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).
  *     All work is enqueued asynchronously on it; stream order alone makes a
  *     read of frame N+1 see the S_N written by frame N's commit.
@@ -41,9 +44,12 @@
  *     is enqueued and a status other than ARL2_OK is returned, with detail
  *     text available from arl2_last_error() on the calling thread.
  *     ARL2_E_HIP reports a launch failure (hipGetLastError after launch).
- *   - Supported shapes: act_dtype ARL2_F32 with D in {16, 32, 64, 128};
- *     ARL2_BF16 with D = 128. Any T >= 1, B >= 1, H >= 1 with
- *     B*H*T*D < 2^31.
+ *   - Supported shapes: act_dtype ARL2_F32 or ARL2_BF16 with D in
+ *     {16, 32, 64, 128}; any T >= 1, B >= 1, H >= 1 with B*H*T*D < 2^31.
+ *     bf16 at D = 128 runs on the MFMA kernels, other shapes on plain
+ *     per-thread kernels. Token-level access and the training calls (from
+ *     arl2_intra_attn_lse on) take bf16 only at D = 128 (ARL2_E_SHAPE
+ *     otherwise).
  *   - Results are deterministic: no floating-point atomics, fixed reduction
  *     order, so identical inputs give bit-identical outputs.
  */

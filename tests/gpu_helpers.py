@@ -53,24 +53,40 @@ def shape_of(w: synth.Workload):
 
 
 def lockstep_rollout(w: synth.Workload, read_frames, row_sample=None, check_state=True,
-                     frames=None, **layer_kwargs):
+                     frames=None, commit_via="commit", clean_rows=None, full_every=1,
+                     **layer_kwargs):
     """Drive Arl2Layer and the oracle frame by frame.
 
     Frames in ``read_frames`` run every denoising read and the clean pass, and
     their outputs (o, o_intra, o_inter) are compared on ``row_sample`` query
-    rows (all rows if None). Other frames run the commit only: reads never
-    change the state, so the state trajectory is the same. The state is
-    compared after every commit. Returns the worst relative errors seen."""
+    rows (all rows if None). Other frames write the state without the
+    denoising reads: with ``commit_via="commit"`` through the commit-only call
+    (reads never change the state, so the state trajectory is the same); with
+    ``commit_via="clean_pass"`` through the layer's clean pass, whose outputs
+    are compared on every row on every ``full_every``-th frame and on
+    ``clean_rows`` rows (all rows if None) on the others. The state is compared
+    after every commit. Returns the worst relative errors seen."""
     import torch
     from hybrid_linear_memory_amd.layer import Arl2Layer
 
+    if commit_via not in ("commit", "clean_pass"):
+        raise ValueError(commit_via)
     tol = TOL[w.dtype]
     phis = synth.phi_maps(w)
     layer = Arl2Layer(shape_of(w), *[dev(p, w.dtype) for p in phis], **layer_kwargs)
     S_ref = np.zeros((w.B, w.H, w.D, w.D))
     worst = {"S": 0.0, "o": 0.0, "o_intra": 0.0, "o_inter": 0.0}
     n_frames = w.frames if frames is None else frames
-    rows = slice(None) if row_sample is None else np.asarray(row_sample)
+
+    def _compare(o, o_i, o_e, q, k, v, rows, what):
+        sel = slice(None) if rows is None else np.asarray(rows)
+        ref = oracle.read(q[:, :, sel], k, v, phis[0], S_ref)
+        got = {"o": host(o)[:, :, sel], "o_intra": host(o_i)[:, :, sel],
+               "o_inter": host(o_e)[:, :, sel]}
+        for name in ("o", "o_intra", "o_inter"):
+            r = assert_close(got[name], ref[name], tol, f"{what} {name}")
+            worst[name] = max(worst[name], r)
+
     for f in range(n_frames):
         beta, alpha = synth.gates(w, f)
         if f in read_frames:
@@ -84,13 +100,16 @@ def lockstep_rollout(w: synth.Workload, read_frames, row_sample=None, check_stat
                 else:
                     o = layer.clean_pass(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype),
                                          dev32(beta), dev32(alpha), o_intra=o_i, o_inter=o_e)
-                ref = oracle.read(q[:, :, rows], k, v, phis[0], S_ref)
-                got = {"o": host(o)[:, :, rows], "o_intra": host(o_i)[:, :, rows],
-                       "o_inter": host(o_e)[:, :, rows]}
-                for name in ("o", "o_intra", "o_inter"):
-                    r = assert_close(got[name], ref[name], tol, f"frame {f} pass {p} {name}")
-                    worst[name] = max(worst[name], r)
+                _compare(o, o_i, o_e, q, k, v, row_sample, f"frame {f} pass {p}")
             kc, vc = k, v                      # the clean pass's keys and values
+        elif commit_via == "clean_pass":
+            q, kc, vc = synth.qkv(w, f, w.passes - 1)
+            o_i = layer.new_output()
+            o_e = layer.new_output()
+            o = layer.clean_pass(dev(q, w.dtype), dev(kc, w.dtype), dev(vc, w.dtype),
+                                 dev32(beta), dev32(alpha), o_intra=o_i, o_inter=o_e)
+            rows = None if f % full_every == 0 or f == n_frames - 1 else clean_rows
+            _compare(o, o_i, o_e, q, kc, vc, rows, f"frame {f} clean pass")
         else:
             kc, vc = synth.kv(w, f, w.passes - 1)
             layer.commit(dev(kc, w.dtype), dev(vc, w.dtype), dev32(beta), dev32(alpha))

@@ -97,8 +97,13 @@ def test_null_shape_dtype_layout_errors(arl2):
     assert _st(arl2, "arl2_intra_attn", None, A, A, A, B, None) == 1
     assert _st(arl2, "arl2_intra_attn", cs(good), None, A, A, B, None) == 1
     assert "'q'" in arl2.last_error()
-    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, 64, arl2.BF16)), A, A, A, B,
+    # bf16 runs at D in {16, 32, 64, 128}: an unsupported D is a shape error, a
+    # supported one reaches the alias check (o over q) before any launch
+    assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, 48, arl2.BF16)), A, A, A, B,
                None) == 2
+    for D in (16, 32, 64):
+        assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, D, arl2.BF16)), A, B, B, A,
+                   None) == 5
     assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 0, 128, arl2.BF16)), A, A, A, B,
                None) == 2
     assert _st(arl2, "arl2_intra_attn", cs(arl2.Shape(1, 2, 64, 48, arl2.F32)), A, A, A, B,
@@ -169,6 +174,26 @@ def test_alias_and_workspace_errors(arl2):
                B + (6 << 20), 0, WS, ab, None) == 5
     assert _st(arl2, "arl2_intra_attn_lse", cs(s), A, A, A, B, B, None) == 5
     assert _st(arl2, "arl2_state_scan", cs(s), 0, A, A, A, A, A, A, S1, S2, WS, need, None) == 2
+    # S_next over an input or the workspace (state commit, commit, clean pass)
+    sneed = arl2.workspace_bytes(s, arl2.OP_STATE_COMMIT)
+    assert sneed > 0
+    assert _st(arl2, "arl2_state_commit", cs(s), A, A, A, A, S1, WS, WS, sneed, None) == 5
+    assert _st(arl2, "arl2_state_commit", cs(s), B, A, A, A, S1, B + 4096, WS, sneed,
+               None) == 5
+    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, A + 4096, WS, need, None) == 5
+    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, B, S1, B, WS, need, None) == 5
+    clneed = arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS)
+    for phi_k, alpha in ((S2, A), (A, S2)):
+        assert _st(arl2, "arl2_clean_pass", cs(s), A, A, A, A, phi_k, A, A, alpha, S1, S2, B,
+                   None, None, WS, clneed, None) == 5
+    # token-level and training calls keep bf16 at D = 128
+    s64 = arl2.Shape(1, 2, 300, 64, arl2.BF16)
+    assert _st(arl2, "arl2_token_read", cs(s64), A, A, A, A, A, A, A, S1, B, None, None, WS,
+               1 << 20, None) == 2
+    assert "D = 128" in arl2.last_error()
+    assert _st(arl2, "arl2_intra_attn_lse", cs(s64), A, A, A, B, S1, None) == 2
+    assert _st(arl2, "arl2_intra_attn_backward", cs(s64), A, A, A, A, None, A, B, B + (4 << 20),
+               B + (6 << 20), 0, WS, 1 << 20, None) == 2
     # fullkv: n_kv beyond capacity
     assert _st(arl2, "arl2_fullkv_attn", cs(s), A, B, S1, 200, 100, WS, None) == 2
 
@@ -193,3 +218,45 @@ def test_sequencer_host_logic():
         free.before_read(); free.after_read()
     with pytest.raises(ValueError):
         PassSequencer(-1)
+
+
+def test_validation_under_host_sanitizers(tmp_path):
+    """The C-ABI layer (csrc/api.cpp) built with g++ under AddressSanitizer and
+    UndefinedBehaviorSanitizer, its kernel launchers replaced by host stubs
+    (tests/abi_asan/launch_stubs.cpp), and driven through every entry point
+    with valid and invalid arguments (tests/abi_asan/abi_check.cpp): every
+    status as documented, no sanitizer report."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    here = os.path.join(ROOT, "tests", "abi_asan")
+    exe = str(tmp_path / "abi_check")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           os.path.join(ROOT, "hybrid_linear_memory_amd", "csrc", "api.cpp"),
+           os.path.join(here, "launch_stubs.cpp"), os.path.join(here, "abi_check.cpp"),
+           "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert b.returncode == 0, b.stdout + b.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
+
+
+def test_finiteness_check_host_logic():
+    """The layer's debug check (run before any launch) names the first input
+    holding a NaN or an infinity and passes finite inputs and None."""
+    import torch
+    from hybrid_linear_memory_amd.layer import NonFiniteInput, check_finite
+    ok = torch.randn(4, 8)
+    check_finite(q=ok, k=ok.to(torch.bfloat16), beta=None)
+    for bad_value in (float("nan"), float("inf"), float("-inf")):
+        bad = ok.clone()
+        bad[2, 5] = bad_value
+        with pytest.raises(NonFiniteInput, match="^k "):
+            check_finite(q=ok, k=bad, v=bad)
+        with pytest.raises(NonFiniteInput, match="alpha"):
+            check_finite(q=ok, alpha=bad.to(torch.bfloat16))

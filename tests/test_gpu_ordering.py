@@ -141,3 +141,39 @@ def test_g6_checkpoint_resume(w):
     for f in range(2, w.frames):
         resumed.clean_pass(*_frame(w, f, w.passes - 1), *_gates(w, f))
     assert np.array_equal(_bytes(resumed.S), _bytes(full.S))
+
+
+@pytest.mark.parametrize("w", CASES, ids=_ids)
+def test_debug_check_refuses_non_finite_inputs(w):
+    """With check_finite, a NaN or an infinity in any input of a pass raises
+    before anything is launched: the state bytes, the frame index and the
+    pass count stay as they were, and the next good pass runs normally."""
+    import torch
+    from hybrid_linear_memory_amd.layer import Arl2Layer, NonFiniteInput
+    log(f"debug finiteness check {_ids(w)}")
+    layer = Arl2Layer(shape_of(w), *[dev(p, w.dtype) for p in synth.phi_maps(w)],
+                      check_finite=True)
+    _warm_state(layer, w)
+    torch.cuda.synchronize()
+    before = _bytes(layer.S)
+    frame, reads = layer.frame, layer.seq.reads
+    q, k, v = _frame(w, 5, 0)
+    beta, alpha = _gates(w, 5)
+    bad_q = q.clone()
+    bad_q[0, 0, 3, 1] = float("nan")
+    with pytest.raises(NonFiniteInput, match="q"):
+        layer.read(bad_q, k, v)
+    bad_alpha = alpha.clone()
+    bad_alpha[0, 0] = float("inf")
+    with pytest.raises(NonFiniteInput, match="alpha"):
+        layer.clean_pass(q, k, v, beta, bad_alpha)
+    bad_v = v.clone()
+    bad_v[0, -1, -1, -1] = float("-inf")
+    with pytest.raises(NonFiniteInput, match="v"):
+        layer.commit(k, bad_v, beta, alpha)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bytes(layer.S), before)
+    assert (layer.frame, layer.seq.reads) == (frame, reads)
+    layer.read(q, k, v)
+    layer.clean_pass(q, k, v, beta, alpha)
+    assert layer.frame == frame + 1

@@ -149,6 +149,39 @@ def test_attn_backward_split_halves(case):
         _close(host(got), ref[name], TOL[w.dtype], name, floor=np.abs(ref["dv"]).max())
 
 
+@pytest.mark.parametrize("case", [("bf16", 1, 2, 513, 128), ("bf16", 1, 4, 1560, 128)], ids=_ids)
+def test_attn_backward_split_reused_workspace_new_inputs(case):
+    """One workspace across attention backward calls whose inputs all differ:
+    each call's gradients equal, bit for bit, those of the same inputs on a
+    fresh workspace, and match the oracle. A pair merge that added sums left
+    in a slot by the previous call would fail both."""
+    import torch
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"attention backward, reused workspace, new inputs {_ids(case)}")
+    sh = shape_of(w)
+    ws = arl2.alloc_workspace(sh, arl2.OP_INTRA_ATTN_BACKWARD)
+    for call, frame in enumerate((0, 1, 2)):
+        q, k, v = synth.qkv(w, frame, 1)
+        d_o = _grad_out(w, 30 + frame)
+        dq_, dk_, dv_, do_ = (dev(x, w.dtype) for x in (q, k, v, d_o))
+        o, lse = _forward(arl2, sh, w, dq_, dk_, dv_, True)
+        grads = [_zeros((w.B, w.H, w.T, w.D), w.dtype) for _ in range(3)]
+        arl2.intra_attn_backward(sh, dq_, dk_, dv_, o, do_, *grads, ws=ws, lse=lse)
+        fresh = arl2.alloc_workspace(sh, arl2.OP_INTRA_ATTN_BACKWARD)
+        fresh.fill_(0x3C)
+        again = [_zeros((w.B, w.H, w.T, w.D), w.dtype) for _ in range(3)]
+        arl2.intra_attn_backward(sh, dq_, dk_, dv_, o, do_, *again, ws=fresh, lse=lse)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dq", "dk", "dv"), grads, again):
+            assert torch.equal(x, y), f"call {call}: {name} differs from a fresh workspace"
+        ref = oracle.intra_attention_backward(q, k, v, d_o)
+        for name, got in zip(("dq", "dk", "dv"), grads):
+            _close(host(got), ref[name], TOL[w.dtype], f"call {call} {name}",
+                   floor=np.abs(ref["dv"]).max())
+        del fresh
+
+
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 @pytest.mark.parametrize("with_lse", [False, True])
 def test_read_backward(case, with_lse):
