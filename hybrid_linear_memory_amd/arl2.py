@@ -53,6 +53,7 @@ SIGNATURES = {
     "arl2_inter_read": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp]),
     "arl2_state_commit": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_read": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "arl2_read_noalloc": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "arl2_commit": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "arl2_clean_pass": (_i32, [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _sz, _vp]),
@@ -251,6 +252,22 @@ def read(shape: Shape, q, k, v, phi_q, S, o, o_intra=None, o_inter=None, ws=None
         ck(phi_q, "phi_q", a), ck(S, "S", torch.float32), ck(o, "o", a),
         ck(o_intra, "o_intra", a, optional=True), ck(o_inter, "o_inter", a, optional=True),
         ck(ws, "ws", optional=True), ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(stream)))
+
+
+# bytes of the library's fixed scratch that arl2_read_noalloc uses
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def read_noalloc(shape: Shape, q, k, v, phi_q, S, o, o_intra=None, o_inter=None, stream=None):
+    """read() without a workspace: the library's fixed device scratch holds
+    its intermediates (for callers that cannot allocate)."""
+    ck = _checker(shape)
+    a = shape.torch_dtype
+    _check(_lib.arl2_read_noalloc(
+        ctypes.byref(shape.c()), ck(q, "q", a), ck(k, "k", a), ck(v, "v", a),
+        ck(phi_q, "phi_q", a), ck(S, "S", torch.float32), ck(o, "o", a),
+        ck(o_intra, "o_intra", a, optional=True), ck(o_inter, "o_inter", a, optional=True),
         _stream(stream)))
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libarl2.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "kernels_generic.hip", "kernels_mfma.hip", "kernels_token.hip",
-           "kernels_train.hip"]
+           "kernels_train.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

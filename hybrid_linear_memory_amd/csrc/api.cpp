@@ -466,6 +466,47 @@ arl2_status arl2_read(const arl2_shape* shape, const void* q, const void* k, con
   return do_read(d, q, k, v, phi_q, S, o, o_intra, o_inter, ws, (hipStream_t)stream);
 }
 
+arl2_status arl2_read_noalloc(const arl2_shape* shape, const void* q, const void* k,
+                              const void* v, const void* phi_q, const float* S, void* o,
+                              void* o_intra, void* o_inter, void* stream) {
+  arl2::Dims d;
+  arl2_status st = check_shape(shape, &d);
+  if (st != ARL2_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(phi_q);
+  REQUIRE_PTR(S);
+  REQUIRE_PTR(o);
+  OPTIONAL_PTR(o_intra);
+  OPTIONAL_PTR(o_inter);
+  const size_t ab = arl2::act_bytes(d);
+  const Range outs[3] = {{o, ab}, {o_intra, ab}, {o_inter, ab}};
+  const Range ins[5] = {{q, ab}, {k, ab}, {v, ab}, {phi_q, phi_bytes(d)}, {S, state_bytes(d)}};
+  if ((st = check_disjoint(outs, 3, ins, 5)) != ARL2_OK) return st;
+  // bf16 at D = 128: the map M^T = (Phi_q S)^T, then the fused read on the
+  // plain grid (one workgroup per 128 queries of a head, no split-key
+  // workspace); other shapes: Q' and o_intra as in arl2_read
+  const bool mf = arl2::use_mfma(d);
+  const size_t need = mf ? arl2::round_up(prepared_bytes(d), 256) : ws_read(d);
+  const size_t have = arl2::noalloc_scratch_bytes();
+  if (need > have)
+    return fail(ARL2_E_WORKSPACE,
+                "arl2_read_noalloc needs %zu bytes of scratch for this shape; the library's "
+                "fixed scratch holds %zu (use arl2_read with a workspace)",
+                need, have);
+  void* scratch_ptr = nullptr;
+  if ((st = hip_status(arl2::noalloc_scratch(&scratch_ptr), "scratch address")) != ARL2_OK)
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (!mf) return do_read(d, q, k, v, phi_q, S, o, o_intra, o_inter, scratch_ptr, s);
+  hipError_t e = arl2::mfma_read_prepare(d, phi_q, S, scratch_ptr, s);
+  if (e != hipSuccess) return hip_status(e, "read preparation");
+  return hip_status(arl2::mfma_read_prepared(d, q, k, v, scratch_ptr, o, o_intra, o_inter,
+                                             nullptr, 0, s),
+                    "prepared read");
+}
+
 size_t arl2_prepared_bytes(const arl2_shape* shape) {
   arl2::Dims d;
   if (check_shape(shape, &d) != ARL2_OK) return 0;

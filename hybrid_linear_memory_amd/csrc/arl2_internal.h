@@ -131,6 +131,11 @@ hipError_t commit_backward(const Dims& d, const void* k, const void* v, const vo
                            float* dS_prev, bool accumulate, void* ws, hipStream_t s);
 hipError_t copy_state(const float* src, float* dst, size_t n, hipStream_t s);
 
+// The library's fixed device scratch (noalloc.hip): its size, and the device
+// address of the current device's copy (looked up on first use per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
+
 inline bool use_mfma(const Dims& d) { return d.bf16 && d.D == 128; }
 
 }  // namespace arl2

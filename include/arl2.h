@@ -161,6 +161,25 @@ arl2_status arl2_read(const arl2_shape* shape, const void* q, const void* k,
                       void* o, void* o_intra, void* o_inter, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): arl2_read without
+ * a workspace argument. Same meaning, arguments and errors as arl2_read; its
+ * scratch memory (the map M = Phi_q S on bf16 D = 128 shapes, where the read
+ * then always runs on the plain grid; Q' and o_intra on other shapes) is a
+ * fixed device array inside the library, ARL2_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on a GPU until the process ends. A shape that
+ * needs more (bf16 D = 128: B*H*D*D*2 bytes; other shapes: 2*B*H*T*D*elem
+ * bytes, each rounded up to 256) returns ARL2_E_WORKSPACE before anything is
+ * enqueued. The call itself allocates nothing. Every call on one GPU uses
+ * that GPU's one array (each call rewrites all it reads, so no state carries
+ * over): calls that overlap in time on one GPU (different streams, or
+ * different host threads) race on it and must be serialised by the caller. */
+#define ARL2_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+arl2_status arl2_read_noalloc(const arl2_shape* shape, const void* q,
+                              const void* k, const void* v,
+                              const void* phi_q, const float* S, void* o,
+                              void* o_intra, void* o_inter, void* stream);
+
 /* Read preparation. Every token and every pass of a frame reads the same
  * S_{N-1} (frame-level access, §2.2), and Q' S = Q (Phi_q S), so the map
  * M = Phi_q[h] S[b,h] (D x D per head) can be formed once per frame, after the

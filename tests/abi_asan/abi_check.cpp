@@ -86,6 +86,11 @@ static void run_shape(const arl2_shape& sh, bool full_kernels) {
   REFUSES(arl2_read(s, q, k, v, pq, S0, o, o, nullptr, ws, rd, nullptr), ARL2_E_ALIAS);
   REFUSES(arl2_read(s, q, k, v, pq, S0, o, oi, oe, ws, rd - 1, nullptr), ARL2_E_WORKSPACE);
 
+  LAUNCHES(arl2_read_noalloc(s, q, k, v, pq, S0, o, oi, oe, nullptr));
+  REFUSES(arl2_read_noalloc(s, q, k, v, pq, S0, o, o, nullptr, nullptr), ARL2_E_ALIAS);
+  REFUSES(arl2_read_noalloc(s, q, k, v, pq, S0, q, nullptr, nullptr, nullptr), ARL2_E_ALIAS);
+  REFUSES(arl2_read_noalloc(s, q, k, v, nullptr, S0, o, nullptr, nullptr, nullptr), ARL2_E_NULL);
+
   EXPECT(arl2_prepared_bytes(s) > 0, 1);
   LAUNCHES(arl2_read_prepare(s, pq, S0, M0, nullptr));
   REFUSES(arl2_read_prepare(s, pq, S0, S0, nullptr), ARL2_E_ALIAS);
@@ -173,6 +178,11 @@ int main() {
   for (int i = 0; i < 5; ++i)
     REFUSES(arl2_intra_attn(&bad[i], P(0), P(1), P(2), P(3), nullptr), bad_status[i]);
   REFUSES(arl2_intra_attn(nullptr, P(0), P(1), P(2), P(3), nullptr), ARL2_E_NULL);
+  // more than the fixed scratch of the allocation-free read holds
+  const arl2_shape wide = {1, 300, 64, 128, ARL2_BF16, 0.f};
+  REFUSES(arl2_read_noalloc(&wide, P(0), P(1), P(2), P(3), F(4), P(5), nullptr, nullptr,
+                            nullptr),
+          ARL2_E_WORKSPACE);
   if (strlen(arl2_last_error()) == 0) {
     fprintf(stderr, "no detail text after a failed call\n");
     ++g_fail;
