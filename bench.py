@@ -21,6 +21,7 @@ rollout beside the full-KV-cache softmax comparator.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
     python bench.py --workload batched_streams   # 8 videos (8 x 12 heads)
     python bench.py --workload large_model       # 40 heads
+    python bench.py --sweep-read                 # the fused read across shapes
 
 The two other workloads time the same step at their shapes (without the
 traffic counters, the rollout and the oracle baseline, which are taken on the
@@ -65,6 +66,9 @@ def parse():
     ap.add_argument("--skip-rollout", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sweep-read", action="store_true",
+                    help="instead of the step: time the fused read (arl2_read_prepared) across "
+                         "frame lengths, heads and videos, one JSON line per shape")
     return ap.parse_args()
 
 
@@ -343,6 +347,61 @@ class Bench:
         }
 
 
+SWEEP_SHAPES = [(1, 12, 1560), (1, 12, 3600), (1, 12, 6240), (2, 12, 1560), (4, 12, 1560),
+                (8, 12, 1560), (1, 40, 1560), (1, 4, 4096), (1, 2, 8192)]
+
+
+def sweep_read(base_iters: int):
+    """The fused read (arl2_read_prepared, with a workspace so that the shapes
+    that take the split-key grid do) at d = 128 across (B, H, T): launches back
+    to back on one stream over a pool of resident inputs of at least 512 MB
+    (so that they come from HBM), each shape warmed up for as many launches as
+    it times, timed with HIP events. Inputs follow the workloads' recipe (Q, K,
+    V standard normal, keys L2-normalised row by row). Work per launch: 4 T^2 d
+    (Q K^T and P V) plus 2 T d^2 (Q M) FLOP per head, against the dense bf16
+    MFMA peak."""
+    import torch
+
+    from hybrid_linear_memory_amd import arl2
+    for B, H, T in SWEEP_SHAPES:
+        sh = arl2.Shape(B, H, T, 128, arl2.BF16)
+        g = torch.Generator(device="cuda").manual_seed(0)
+        n_sets = max(2, -(-(512 << 20) // (3 * B * H * T * 128 * 2)))
+
+        def qkv():
+            q, k, v = (torch.randn(B, H, T, 128, generator=g, device="cuda") for _ in range(3))
+            k = k / k.norm(dim=-1, keepdim=True)
+            return tuple(x.to(torch.bfloat16) for x in (q, k, v))
+
+        sets = [qkv() for _ in range(n_sets)]
+        M = arl2.alloc_prepared(sh)
+        phi = (torch.randn(H, 128, 128, generator=g, device="cuda") * 128 ** -0.5).to(
+            torch.bfloat16)
+        arl2.read_prepare(sh, phi, torch.randn(B, H, 128, 128, generator=g, device="cuda") * 0.05,
+                          M)
+        o = torch.empty(B, H, T, 128, dtype=torch.bfloat16, device="cuda")
+        ws = arl2.alloc_workspace(sh, arl2.OP_READ_PREPARED)
+        split = arl2.workspace_bytes(sh, arl2.OP_READ_PREPARED) > 0
+        iters = max(20, base_iters * 1560 * 12 // (T * H * B))
+        for i in range(iters):
+            arl2.read_prepared(sh, *sets[i % n_sets], M, o, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            arl2.read_prepared(sh, *sets[i % n_sets], M, o, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        flop = B * H * (4.0 * T * T * 128 + 2.0 * T * 128 * 128)
+        print(json.dumps({"B": B, "H": H, "T": T, "split_key_grid": split,
+                          "query_blocks": B * H * (-(-T // 128)), "us": round(us, 2),
+                          "tflops": round(flop / us / 1e6, 1),
+                          "frac_of_bf16_peak": round(flop / (us * 1e-6) / PEAK_BF16_MFMA, 4)}),
+              flush=True)
+        del sets
+
+
 def cpu_baseline(seconds: float):
     """The fp64 oracle, as it stands, on this host: whole frames of the same
     workload (4 reads + clean pass, all heads) until ~`seconds` of CPU time,
@@ -426,6 +485,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep_read:
+        sweep_read(4 * args.steps)
+        return
     print("[bench] building the pool of input frames", file=sys.stderr, flush=True)
     b = Bench(args)
     print(f"[bench] pool of {args.pool} frames resident", file=sys.stderr, flush=True)
