@@ -71,10 +71,10 @@ size_t mfma_read_prepared_ws_bytes(const Dims& d);
 hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const void* v,
                               const void* mt, void* o, void* o_intra, void* o_inter, void* ws,
                               size_t ws_bytes, hipStream_t s);
-// Clean pass from a prepared map in one launch (fused read workgroups plus the
-// fused commit's workgroups), then the chunk reduction, which also forms the
-// map of S_next into mt_next when mt_next is given (phi_q then required); ws
-// holds the commit partials (mfma_commit_ws_bytes).
+// Clean pass from a prepared map in one launch: the fused read's workgroups
+// plus the column-split commit's (four per (b, h), no workspace), which also
+// form the map of S_next into mt_next when mt_next is given (phi_q then
+// required). The workspace argument is unused.
 hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k, const void* v,
                                     const void* mt, const void* phi_q, const void* phi_k,
                                     const void* phi_v, const float* beta, const float* alpha,
@@ -87,7 +87,8 @@ hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
                      const void* phi_q, const float* S, void* o, void* o_intra, void* o_inter,
                      void* ws, hipStream_t s);
 // Fused commit (bf16, D = 128) from the raw K, V: feature maps, row norm and
-// the gated delta update in one kernel (+ a fixed-order chunk reduction).
+// the gated delta update in one launch, one workgroup per (b, h, 32 state
+// columns); needs no workspace (mfma_commit_ws_bytes is 0).
 size_t mfma_commit_ws_bytes(const Dims& d);
 hipError_t mfma_commit(const Dims& d, const void* k, const void* v, const void* phi_k,
                        const void* phi_v, const float* beta, const float* alpha,

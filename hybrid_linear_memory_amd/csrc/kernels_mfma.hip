@@ -1010,37 +1010,6 @@ commit_mfma_k(const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
   }
 }
 
-// ===========================================================================
-// Fused commit from the clean pass's raw K and V: the feature maps
-// K' = rownorm(K Phi_k), V' = V Phi_v and the gated delta update in one pass
-// over the frame's tokens, so K' and V' never leave the chip.
-//
-// One workgroup = 4 waves per (b, h, token chunk); wave w owns output columns
-// [32w, 32w + 32). Phi_k and Phi_v are staged once (row-major, read as MFMA
-// operands with transposing reads). Per 32-token slice:
-//   K~^T = Phi_k^T K^T   (column block w; lane = token, registers = columns,
-//                          so the row norm is an in-lane sum, one half
-//                          exchange and a 4-wave exchange through LDS)
-//   V'   = V Phi_v       (column block w, laid out like P^ below)
-//   K'   = K~ / max(|K~|, 1e-12) -> LDS (two swizzles)
-//   P^   = K' S_prev[:, w]; W = beta (V' - P^); U[:, w] += K'^T W
-// With one chunk the workgroup writes S_next = alpha S_prev + U; otherwise a
-// partial, summed in chunk order by commit_reduce_k.
-// ===========================================================================
-constexpr int FT = 32;                          // tokens per slice
-constexpr int F_PHI_B = HD * HD * 2;            // 32 KB per map
-constexpr int F_SLICE_B = FT * HD * 2;          // 8 KB per 32-token slice
-// LDS: four regions, each within one 32 KB array: Phi_k, Phi_v, the raw
-// slices ([buf][K, V]) and the K' region below.
-constexpr int F_RAW_B = 4 * F_SLICE_B;          // 32 KB
-constexpr int F_KPA = 0;                        // K' rows, row-read swizzle (swz_k)
-constexpr int F_KPB = F_KPA + F_SLICE_B;        // K' rows, transposing-read swizzle (swz_v)
-constexpr int F_SS = F_KPB + F_SLICE_B;         // [4 waves][32 tokens] partial sums of squares
-constexpr int F_BETA = F_SS + 4 * FT * 4;       // [buf][32] beta
-constexpr int F_KP_B = F_BETA + 2 * FT * 4;
-static_assert(F_KP_B <= AKV && F_RAW_B <= AKV && F_PHI_B <= AKV, "commit regions fit the arrays");
-
-
 // Wave-wide DMA of `n_inst` x 4 rows (256-byte rows) starting at row r_begin of
 // a row-major bf16 matrix into LDS under chunk swizzle `swz` (rows past
 // `rows_valid` are clamped to the last valid row).
@@ -1058,174 +1027,285 @@ __device__ __forceinline__ void rows_load(char* dst, const char* src, int r_begi
   }
 }
 
-// One workgroup (logical block `blk`, threads 0-255) of the fused commit, on
-// the LDS regions l_phik, l_phiv (32 KB each), l_raw (F_RAW_B) and l_kp
-// (F_KP_B).
-__device__ __forceinline__ void commit_block(
+// ===========================================================================
+// Column-split commit from the clean pass's raw K and V: the feature maps
+// K' = rownorm(K Phi_k), V' = V Phi_v and the gated delta update, one
+// workgroup (8 waves) per (b, h, 32-column block `cb` of the state) over all of
+// the frame's tokens. A column block of the update needs only the same
+// columns of S and V':
+//   S_N[:, cols] = alpha S_{N-1}[:, cols] + K'^T diag(beta) (V'[:, cols] - K' S_{N-1}[:, cols]),
+// so no workgroup needs another's results: the workgroup writes S_N[:, cols]
+// and, when asked, the next frame's map for those columns,
+// M^T[cols, :] = (Phi_q S_N[:, cols])^T. K' rows need all of K~ = K Phi_k (the
+// row norm), so each of a head's four workgroups forms the whole of K~; they
+// sit on one XCD and share the K and V reads in its L2.
+//
+// Wave w takes the 32-token slices w, w + 8, ... Per slice (all in registers
+// except one transposition of K' through the wave's own LDS buffer):
+//   K~^T = Phi_k^T K^T  (A = Phi_k^T by transposing LDS reads, B = K rows
+//                        straight from global memory; lane = token, so the
+//                        row norm is an in-lane sum and one half exchange)
+//   V'   = V Phi_v[:, cols] (A = V rows from global memory, B from LDS)
+//   P^   = K' S[:, cols]    (A = K' from the K~^T registers, B = S held in
+//                        registers with its rows in the order those registers
+//                        give the contraction index)
+//   W    = beta (V' - P^);  U[:, cols] += K'^T W  (A = K' transposed via LDS)
+// Tokens are loaded in the perm32 order, so that the accumulators of P^ and V'
+// hold W in the register order that U's contraction takes. At the end the
+// eight per-wave sums of U are added in wave order through LDS.
+// ===========================================================================
+constexpr int CC_WAVES = 8;
+constexpr int CC_SLICE = 32;                    // tokens per slice
+constexpr int CC_KP_B = CC_SLICE * HD * 2;      // one wave's K' slice (8 KB)
+constexpr int CC_RED_B = HD * 32 * 4;           // one wave's U column block (16 KB)
+constexpr int CC_ST_LD = HD + 8;                // row of the transposed S_N block (bf16)
+constexpr int CC_OPS_B = 8 * 64 * 16;           // one fixed B operand in lane order (8 KB)
+static_assert(4 * CC_KP_B <= AKV && 2 * CC_RED_B <= AKV && HD * HD * 2 <= AKV &&
+                  2 * CC_OPS_B + CC_WAVES * 128 <= AKV,
+              "column-split commit regions fit the arrays");
+
+// The LDS arrays l0..l3 (32 KB each): Phi_k; the fixed B operands (Phi_v and
+// S columns); the K' buffers of waves 0-3 and of waves 4-7; then the per-wave
+// U sums (two waves per array).
+__device__ __forceinline__ void commit_col_block(
     int blk, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
-    const float* __restrict__ beta, const float* __restrict__ alpha,
-    const float* __restrict__ S_prev, float* __restrict__ S_next, float* __restrict__ partial,
-    int H, int T, int chunk_tokens, int n_chunks, long n_bh, char* l_phik, char* l_phiv,
-    char* l_raw, char* l_kp) {
+    const __bf16* __restrict__ phi_q, const float* __restrict__ beta,
+    const float* __restrict__ alpha, const float* __restrict__ S_prev,
+    float* __restrict__ S_next, __bf16* __restrict__ mt_next, int H, int T, char* l0, char* l1,
+    char* l2, char* l3) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  const long bh = blk / n_chunks;
-  const int chunk = blk % n_chunks;
+  const long bh = blk >> 2;
+  const int cb = blk & 3;
   const int h = (int)(bh % H);
-  const int t_begin = chunk * chunk_tokens;
-  const int t_end = min(T, t_begin + chunk_tokens);
-  const int n_slices = (t_end - t_begin + FT - 1) / FT;
-  const int cb = wave;
   const int col = 32 * cb + n;
-  const char* kh = reinterpret_cast<const char*>(k + (size_t)bh * T * HD);
-  const char* vh = reinterpret_cast<const char*>(v + (size_t)bh * T * HD);
-  const float* bt = beta + (size_t)bh * T;
-  float* fbeta = reinterpret_cast<float*>(l_kp + F_BETA);
-  float* fss = reinterpret_cast<float*>(l_kp + F_SS);
 
-  // maps: waves 0-1 stage Phi_k, waves 2-3 Phi_v (64 rows each)
-  {
-    const char* src = reinterpret_cast<const char*>((wave < 2 ? phi_k : phi_v) + (size_t)h * HD * HD);
-    rows_load<1>(wave < 2 ? l_phik : l_phiv, src, 64 * (wave & 1), 16, HD, lane);
-  }
-  // raw slice s: waves 0-1 load K rows [16w, 16w + 16), waves 2-3 V rows
-  auto issue = [&](int sl) {
-    const int t0 = t_begin + sl * FT;
-    char* dst = l_raw + (sl & 1) * 2 * F_SLICE_B + (wave < 2 ? 0 : F_SLICE_B);
-    const char* src = (wave < 2 ? kh : vh) + (size_t)t0 * 256;
-    if (wave < 2) rows_load<2>(dst, src, 16 * (wave & 1), 4, t_end - t0, lane);
-    else rows_load<0>(dst, src, 16 * (wave & 1), 4, t_end - t0, lane);
-    if (tid < FT) fbeta[(sl & 1) * FT + tid] = t0 + tid < t_end ? bt[t0 + tid] : 0.f;
-  };
-  issue(0);
-
-  // S_prev[:, col] as the B operand of P^ = K' S (k = state row)
+  // Phi_k into l0 (waves 0-3, 32 rows each), row-major under the swz_v
+  // swizzle for the transposing reads. The two B operands that stay fixed over
+  // the frame go to l1 in MFMA lane order (16 bytes per lane and step, read
+  // back without conflicts): Phi_v[:, cols] for V' = V Phi_v[:, cols], step kc
+  // giving lane (c, h2) Phi_v[16 kc + 8 h2 + u][32 cb + c]; and S_{N-1}[:, cols]
+  // for P^ = K' S, step j giving lane (c, h2) S[d][32 cb + c] with
+  // d = 32 (j / 2) + 16 (j % 2) + 8 (u / 4) + 4 h2 + u % 4, the K~ columns that
+  // the K~^T registers of block j / 2, registers 8 (j % 2) .. + 7 hold.
+  if (wave < 4)
+    rows_load<1>(l0, reinterpret_cast<const char*>(phi_k + (size_t)h * HD * HD), 32 * wave, 8,
+                 HD, lane);
   const float* Sp = S_prev + (size_t)bh * HD * HD;
-  bf16x8 sreg[8];
+  {
+    const int st = tid >> 6, sl_lane = tid & 63;
+    const int c = 32 * cb + (sl_lane & 31), g2 = sl_lane >> 5;
+    const __bf16* pv = phi_v + (size_t)h * HD * HD;
+    bf16x8 a, b;
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) sreg[kc][u] = (__bf16)Sp[(size_t)(16 * kc + 8 * h2 + u) * HD + col];
+    for (int u = 0; u < 8; ++u) {
+      a[u] = pv[(size_t)(16 * st + 8 * g2 + u) * HD + c];
+      const int d = 32 * (st >> 1) + 16 * (st & 1) + 8 * (u >> 2) + 4 * g2 + (u & 3);
+      b[u] = (__bf16)Sp[(size_t)d * HD + c];
+    }
+    *reinterpret_cast<bf16x8*>(l1 + tid * 16) = a;
+    *reinterpret_cast<bf16x8*>(l1 + CC_OPS_B + tid * 16) = b;
+  }
+  const uint32_t act_b = (uint32_t)T * (HD * 2);
+  const __amdgpu_buffer_rsrc_t k_src = buffer_rsrc(k + (size_t)bh * T * HD, act_b);
+  const __amdgpu_buffer_rsrc_t v_src = buffer_rsrc(v + (size_t)bh * T * HD, act_b);
+  const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(beta + (size_t)bh * T, (uint32_t)T * 4);
+  char* kpb = (wave < 4 ? l2 : l3) + (wave & 3) * CC_KP_B;
+  const int krow = perm32(n);
+  const char* pv_op = l1 + lane * 16;                 // + kc * 1024
+  const char* s_op = l1 + CC_OPS_B + lane * 16;       // + j * 1024
+  float* bslot = reinterpret_cast<float*>(l1 + 2 * CC_OPS_B + wave * 128);
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();                                      // maps and operands are in LDS
 
   f32x16 uacc[4];
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) uacc[ib] = zero16();
-  const int krow = perm32(n);
-
-  for (int sl = 0; sl < n_slices; ++sl) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();                                    // slice sl and beta visible
-    if (sl + 1 < n_slices) issue(sl + 1);
-    const char* Kr = l_raw + (sl & 1) * 2 * F_SLICE_B;
-    const char* Vr = Kr + F_SLICE_B;
-
-    // K~^T column block: kt[r] = K~[token n][32cb + 8(r/4) + 4h2 + r%4]
-    f32x16 kt = zero16();
-    // V' block in the P^ layout: vp[r] = V'[token 16h2 + r][col]
+  const int n_slices = (T + CC_SLICE - 1) / CC_SLICE;
+  // Operands of slice sl: lane n holds token 32 sl + perm32(n) of K and V,
+  // lane n < 32 the beta of token 32 sl + n, each a load of its own (rows past
+  // T read as zeros; a slice past the last reads zeros only). The next slice's
+  // are loaded while the current one computes; beta passes through the wave's
+  // LDS slot, from which lane (c, h2) reads those of tokens 32 sl + 16 h2 + r.
+  bf16x8 kop[8], vop[8];
+  float bnext;
+  auto load_slice = [&](int sl) __attribute__((always_inline)) {
+    bnext = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                          b_src, (sl * CC_SLICE + n) * 4, 0, 0));
+    const int roff = (sl * CC_SLICE + krow) * (HD * 2) + 16 * h2;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      kop[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               k_src, roff + 32 * kc, 0, 0));
+      vop[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               v_src, roff + 32 * kc, 0, 0));
+    }
+  };
+  load_slice(wave);
+  for (int sl = wave; sl < n_slices; sl += CC_WAVES) {
+    if (h2 == 0) bslot[n] = bnext;
+    // K~^T: kt[b][r] = K~[token][32 b + 8 (r / 4) + 4 h2 + r % 4]
+    f32x16 kt[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      kt[b] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        kt[b] = mfma32(tr_op(l0, 16 * kc, 8, 32 * b, lane), kop[kc], kt[b]);
+    }
+    // V'[:, cols]: vp[r] = V'[token 16 h2 + r][col]
     f32x16 vp = zero16();
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kr + n * 256 + (((2 * kc + h2) ^ swz_r(n)) << 4));
-      kt = mfma32(tr_op(l_phik, 16 * kc, 8, 32 * cb, lane), kb, kt);
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vr + krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4));
-      vp = mfma32(va, tr_op(l_phiv, 16 * kc, 8, 32 * cb, lane), vp);
-    }
+    for (int kc = 0; kc < 8; ++kc)
+      vp = mfma32(vop[kc], *reinterpret_cast<const bf16x8*>(pv_op + kc * 1024), vp);
+    load_slice(sl + CC_WAVES);
+
     float ss = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ss = fmaf(kt[r], kt[r], ss);
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss = fmaf(kt[b][r], kt[b][r], ss);
     ss = halves_sum(ss);
-    if (h2 == 0) fss[cb * FT + n] = ss;
-    __syncthreads();                                    // partial norms visible
-    const float inv = 1.f / fmaxf(sqrtf(fss[n] + fss[FT + n] + fss[2 * FT + n] + fss[3 * FT + n]),
-                                  1e-12f);
+    const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+    bf16x8 kp[8];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      bf16x4 w4;
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w4[i] = (__bf16)(kt[4 * jj + i] * inv);
-      const int d = 32 * cb + 8 * jj + 4 * h2;         // 4 consecutive columns of row n
-      const int c16 = d >> 3, sub = (d & 7) * 2;
-      *reinterpret_cast<bf16x4*>(l_kp + F_KPA + n * 256 + ((c16 ^ swz_k(n)) << 4) + sub) = w4;
-      *reinterpret_cast<bf16x4*>(l_kp + F_KPB + n * 256 + ((c16 ^ swz_v(n)) << 4) + sub) = w4;
-    }
-    __syncthreads();                                    // K' of the slice visible
+      for (int u = 0; u < 8; ++u) kp[j][u] = (__bf16)(kt[j >> 1][8 * (j & 1) + u] * inv);
 
-    // P^ = K' S[:, col]; register r <-> token 16*h2 + r
+    // K' rows into this wave's buffer (row = token within the slice, swz_v)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bf16x4 w4 = {kp[2 * b + (jj >> 1)][4 * (jj & 1)],
+                           kp[2 * b + (jj >> 1)][4 * (jj & 1) + 1],
+                           kp[2 * b + (jj >> 1)][4 * (jj & 1) + 2],
+                           kp[2 * b + (jj >> 1)][4 * (jj & 1) + 3]};
+        *reinterpret_cast<bf16x4*>(kpb + krow * 256 + (((4 * b + jj) ^ swz_v(krow)) << 4) +
+                                   8 * h2) = w4;
+      }
+    // P^ = K' S[:, col]: p[r] = P^[token 16 h2 + r][col]
     f32x16 p = zero16();
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(l_kp + F_KPA + krow * 256 + (((2 * kc + h2) ^ swz_k(krow)) << 4));
-      p = mfma32(a, sreg[kc], p);
-    }
-    bf16x8 wb[2];
-    const float* bsl = fbeta + (sl & 1) * FT + 16 * h2;
+    for (int j = 0; j < 8; ++j)
+      p = mfma32(kp[j], *reinterpret_cast<const bf16x8*>(s_op + j * 1024), p);
+    // the wave's own LDS writes (beta, K') are done before its reads
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    f32x4 bq[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) wb[r >> 3][r & 7] = (__bf16)(bsl[r] * (vp[r] - p[r]));
-    // U[:, col] += K'^T W  (A = K'^T rows d, k = tokens 16*h2 + 8*cc + u)
+    for (int i = 0; i < 4; ++i) bq[i] = *reinterpret_cast<const f32x4*>(bslot + 16 * h2 + 4 * i);
+    bf16x8 wb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wb[r >> 3][r & 7] = (__bf16)(bq[r >> 2][r & 3] * (vp[r] - p[r]));
+    // U[:, col] += K'^T W (A = K'^T: tokens 8 cc + 16 h2 + u, as W's registers)
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
-        uacc[ib] = mfma32(tr_op(l_kp + F_KPB, 8 * cc, 16, 32 * ib, lane), wb[cc], uacc[ib]);
+        uacc[ib] = mfma32(tr_op(kpb, 8 * cc, 16, 32 * ib, lane), wb[cc], uacc[ib]);
+    // the next slice's K' writes follow this slice's reads in LDS order
   }
 
-  // uacc[ib][r] = U[row 32*ib + 8*(r/4) + 4*h2 + (r%4)][col]
-  if (n_chunks == 1) {
-    const float a = alpha[bh];
-    float* Sn = S_next + (size_t)bh * HD * HD;
+  // Sum of the eight per-wave U blocks, in wave order, through LDS:
+  // red_w[d][c] (fp32, 32 columns per row), uacc[ib][r] = U[32 ib + 8 (r / 4) +
+  // 4 h2 + r % 4][col]
+  __syncthreads();                                      // every wave is done with l0-l3
+  {
+    char* arr = wave < 2 ? l0 : wave < 4 ? l1 : wave < 6 ? l2 : l3;
+    float* red = reinterpret_cast<float*>(arr + (wave & 1) * CC_RED_B);
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const size_t e = (size_t)(32 * ib + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + col;
-        Sn[e] = fmaf(a, Sp[e], uacc[ib][r]);
-      }
-  } else {
-    float* P = partial + ((size_t)chunk * n_bh + bh) * HD * HD;
+      for (int r = 0; r < 16; ++r)
+        red[(32 * ib + 8 * (r >> 2) + 4 * h2 + (r & 3)) * 32 + n] = uacc[ib][r];
+  }
+  __syncthreads();
+  const float a = alpha[bh];
+  float* Sn = S_next + (size_t)bh * HD * HD;
+  float sv[8];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 512 * i;                        // (d, c) = (e / 32, e % 32)
+    float acc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const size_t e = (size_t)(32 * ib + 8 * (r >> 2) + 4 * h2 + (r & 3)) * HD + col;
-        P[e] = uacc[ib][r];
-      }
+    for (int w = 0; w < CC_WAVES; ++w) {
+      const char* arr = w < 2 ? l0 : w < 4 ? l1 : w < 6 ? l2 : l3;
+      const float x = reinterpret_cast<const float*>(arr + (w & 1) * CC_RED_B)[e];
+      acc = w == 0 ? x : acc + x;
+    }
+    const size_t g = (size_t)(e >> 5) * HD + 32 * cb + (e & 31);
+    sv[i] = fmaf(a, Sp[g], acc);
+    Sn[g] = sv[i];
+  }
+  if (!mt_next) return;
+  // The next frame's map for these columns, as read_prep_k forms it: the block
+  // S_N[:, cols] goes through LDS transposed (bf16) as the B operand of
+  // M = Phi_q S_N; wave ib < 4 computes rows [32 ib, 32 ib + 32) of M.
+  __syncthreads();                                      // every U sum is read
+  __bf16* st = reinterpret_cast<__bf16*>(l0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 512 * i;
+    st[(e & 31) * CC_ST_LD + (e >> 5)] = (__bf16)sv[i];
+  }
+  __syncthreads();
+  if (wave >= 4) return;
+  const __bf16* P = phi_q + (size_t)h * HD * HD + (size_t)(32 * wave + n) * HD + 8 * h2;
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+    acc = mfma32(ld8(P + 16 * kc),
+                 *reinterpret_cast<const bf16x8*>(st + n * CC_ST_LD + 16 * kc + 8 * h2), acc);
+  // acc[r] = M[i = 32 wave + 8 (r / 4) + 4 h2 + r % 4][j = col]  ->  M^T[j][i]
+  __bf16* out = mt_next + (size_t)bh * HD * HD + (size_t)col * HD + 32 * wave + 4 * h2;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    bf16x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (__bf16)acc[4 * jj + i];
+    *reinterpret_cast<bf16x4*>(out + 8 * jj) = w;
   }
 }
 
-__global__ void __launch_bounds__(256)
-commit_fused_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-               const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
-               const float* __restrict__ beta, const float* __restrict__ alpha,
-               const float* __restrict__ S_prev, float* __restrict__ S_next,
-               float* __restrict__ partial, int H, int T, int chunk_tokens, int n_chunks,
-               long n_bh) {
-  __shared__ __attribute__((aligned(1024))) char l_phik[F_PHI_B];
-  __shared__ __attribute__((aligned(1024))) char l_phiv[F_PHI_B];
-  __shared__ __attribute__((aligned(1024))) char l_raw[F_RAW_B];
-  __shared__ __attribute__((aligned(1024))) char l_kp[F_KP_B];
-  commit_block(xcd_remap(blockIdx.x, gridDim.x), k, v, phi_k, phi_v, beta, alpha, S_prev, S_next,
-               partial, H, T, chunk_tokens, n_chunks, n_bh, l_phik, l_phiv, l_raw, l_kp);
+__global__ void __launch_bounds__(512, 1)
+commit_col_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+             const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
+             const __bf16* __restrict__ phi_q, const float* __restrict__ beta,
+             const float* __restrict__ alpha, const float* __restrict__ S_prev,
+             float* __restrict__ S_next, __bf16* __restrict__ mt_next, int H, int T) {
+  __shared__ __attribute__((aligned(1024))) char l0[AKV];
+  __shared__ __attribute__((aligned(1024))) char l1[AKV];
+  __shared__ __attribute__((aligned(1024))) char l2[AKV];
+  __shared__ __attribute__((aligned(1024))) char l3[AKV];
+  commit_col_block(xcd_remap(blockIdx.x, gridDim.x), k, v, phi_k, phi_v, phi_q, beta, alpha,
+                   S_prev, S_next, mt_next, H, T, l0, l1, l2, l3);
 }
 
 // The clean pass of the prepared read in one launch: blocks [0, n_attn) are
 // the fused read's workgroups (dispatched first, they take their compute units
-// first), the next n_warm blocks (from n_attn_pad) the attention's L2 warm-up
-// role (short-lived), then the commit's blocks (threads 0-255; the other four
-// waves leave), which run on the compute units the read leaves idle. The
-// commit reuses the read's LDS arrays; n_attn_pad and n_warm are multiples of
-// 8, so each role's blocks are dealt round-robin over the XCDs from XCD 0.
+// first), the next n_commit blocks (from n_attn_pad) the column-split commit's
+// four workgroups per (b, h), which run on the compute units the read leaves
+// idle, reuse its LDS arrays, and also write the next frame's map when
+// mt_next is given; then n_warm blocks of the attention's L2 warm-up role
+// (short-lived, on whatever compute units remain). n_attn_pad and
+// n_commit_pad are multiples of 8, so each role's blocks are dealt
+// round-robin over the XCDs from XCD 0.
 __global__ void __launch_bounds__(512, 1)
 clean_fused_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const __bf16* __restrict__ v, __bf16* __restrict__ o, int T, float sl2,
               int n_qblk, const __bf16* __restrict__ mt, __bf16* __restrict__ o_intra,
-              __bf16* __restrict__ o_inter, int n_attn, int n_attn_pad, int n_warm,
-              const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
+              __bf16* __restrict__ o_inter, int n_attn, int n_attn_pad, int n_commit,
+              int n_commit_pad, int n_warm, const __bf16* __restrict__ phi_k,
+              const __bf16* __restrict__ phi_v, const __bf16* __restrict__ phi_q,
               const float* __restrict__ beta, const float* __restrict__ alpha,
               const float* __restrict__ S_prev, float* __restrict__ S_next,
-              float* __restrict__ partial, int H, int chunk_tokens, int n_chunks, long n_bh) {
+              __bf16* __restrict__ mt_next, int H) {
   __shared__ __attribute__((aligned(1024))) char lk0[AKV];
   __shared__ __attribute__((aligned(1024))) char lk1[AKV];
   __shared__ __attribute__((aligned(1024))) char lv0[AKV];
@@ -1237,13 +1317,13 @@ clean_fused_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (b < n_attn)
       attn_block<true>(xcd_remap(b, n_attn), q, k, v, o, T, T, T, sl2, n_qblk, mt, o_intra,
                        o_inter, lk0, lk1, lv0, lv1, mlx, redo_flag);
-  } else if (b < n_attn_pad + n_warm) {
-    attn_l2_warm(b - n_attn_pad, n_warm / 8, n_attn, n_qblk, k, v, T, T, lk0);
-  } else if (threadIdx.x < 256) {
-    const int c = b - n_attn_pad - n_warm;
-    commit_block(xcd_remap(c, (int)gridDim.x - n_attn_pad - n_warm), k, v, phi_k, phi_v, beta,
-                 alpha, S_prev, S_next, partial, H, T, chunk_tokens, n_chunks, n_bh, lk0, lk1,
-                 lv0, lv1);
+  } else if (b < n_attn_pad + n_commit_pad) {
+    const int c = b - n_attn_pad;
+    if (c < n_commit)
+      commit_col_block(xcd_remap(c, n_commit), k, v, phi_k, phi_v, phi_q, beta, alpha, S_prev,
+                       S_next, mt_next, H, T, lk0, lk1, lv0, lv1);
+  } else {
+    attn_l2_warm(b - n_attn_pad - n_commit_pad, n_warm / 8, n_attn, n_qblk, k, v, T, T, lk0);
   }
 }
 
@@ -1281,120 +1361,11 @@ commit_reduce_k(const float* __restrict__ partial, const float* __restrict__ alp
   reinterpret_cast<float4*>(S_next)[q4] = r;
 }
 
-// End of the clean pass when the next frame's map is wanted: S_next = alpha
-// S_prev + the chunk partials summed in chunk order (as commit_reduce_k; with a
-// single chunk the commit has written S_next already), then the prepared map of
-// S_next, M^T[j][i] = sum_k Phi_q[i][k] S_next[k][j] in bf16 (as read_prep_k).
-// One workgroup of 512 threads per (b, h, 32-column block jb): thread t sums
-// row t / 4, columns 32 jb + 8 (t % 4) + 0..7; the block goes through LDS
-// transposed (column-major, bf16) as the B operand of M = Phi_q S.
-constexpr int FIN_LD = HD + 8;                  // padded row of the transposed block
-__global__ void __launch_bounds__(512)
-commit_finish_k(const float* __restrict__ partial, const float* __restrict__ alpha,
-                const float* __restrict__ S_prev, float* __restrict__ S_next, int n_chunks,
-                long n_bh, const __bf16* __restrict__ phi_q, __bf16* __restrict__ mt, int H) {
-  __shared__ __attribute__((aligned(16))) __bf16 st[32 * FIN_LD];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, h2 = lane >> 5;
-  const long bh = blockIdx.x >> 2;
-  const int jb = blockIdx.x & 3;
-  const int kr = tid >> 2, cq = 8 * (tid & 3);
-  const size_t e = ((size_t)bh * HD + kr) * HD + 32 * jb + cq;
-  // waves 0-3 fetch their Phi_q rows first, so that the fetch overlaps the sum
-  bf16x8 pq[8];
-  if (wave < 4) {
-    const __bf16* P = phi_q + (size_t)(bh % H) * HD * HD + (size_t)(32 * wave + n) * HD + 8 * h2;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) pq[kc] = ld8(P + 16 * kc);
-  }
-  float r[8];
-  if (n_chunks > 1) {
-    const size_t stride = (size_t)n_bh * HD * HD;
-    float4 a0 = *reinterpret_cast<const float4*>(partial + e);
-    float4 a1 = *reinterpret_cast<const float4*>(partial + e + 4);
-    // chunks in order; the loads of 8 chunks are issued before their sums
-    for (int c0 = 1; c0 < n_chunks; c0 += 8) {
-      float4 x0[8], x1[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < n_chunks) {
-          x0[u] = *reinterpret_cast<const float4*>(partial + (c0 + u) * stride + e);
-          x1[u] = *reinterpret_cast<const float4*>(partial + (c0 + u) * stride + e + 4);
-        }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < n_chunks) {
-          a0.x += x0[u].x; a0.y += x0[u].y; a0.z += x0[u].z; a0.w += x0[u].w;
-          a1.x += x1[u].x; a1.y += x1[u].y; a1.z += x1[u].z; a1.w += x1[u].w;
-        }
-    }
-    const float al = alpha[bh];
-    const float4 s0 = *reinterpret_cast<const float4*>(S_prev + e);
-    const float4 s1 = *reinterpret_cast<const float4*>(S_prev + e + 4);
-    const float4 r0 = {fmaf(al, s0.x, a0.x), fmaf(al, s0.y, a0.y), fmaf(al, s0.z, a0.z),
-                       fmaf(al, s0.w, a0.w)};
-    const float4 r1 = {fmaf(al, s1.x, a1.x), fmaf(al, s1.y, a1.y), fmaf(al, s1.z, a1.z),
-                       fmaf(al, s1.w, a1.w)};
-    *reinterpret_cast<float4*>(S_next + e) = r0;
-    *reinterpret_cast<float4*>(S_next + e + 4) = r1;
-    r[0] = r0.x; r[1] = r0.y; r[2] = r0.z; r[3] = r0.w;
-    r[4] = r1.x; r[5] = r1.y; r[6] = r1.z; r[7] = r1.w;
-  } else {
-    const float4 r0 = *reinterpret_cast<const float4*>(S_next + e);
-    const float4 r1 = *reinterpret_cast<const float4*>(S_next + e + 4);
-    r[0] = r0.x; r[1] = r0.y; r[2] = r0.z; r[3] = r0.w;
-    r[4] = r1.x; r[5] = r1.y; r[6] = r1.z; r[7] = r1.w;
-  }
-#pragma unroll
-  for (int u = 0; u < 8; ++u) st[(cq + u) * FIN_LD + kr] = (__bf16)r[u];
-  __syncthreads();
-  if (wave >= 4) return;
-  // wave w: rows i in [32w, 32w + 32) of M, columns j = 32 jb + n
-  f32x16 acc = zero16();
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc)
-    acc = mfma32(pq[kc], *reinterpret_cast<const bf16x8*>(st + n * FIN_LD + 16 * kc + 8 * h2),
-                 acc);
-  // acc[r] = M[i = 32w + 8(r/4) + 4h2 + r%4][j]  ->  MT[j][i]
-  __bf16* out = mt + (size_t)bh * HD * HD + (size_t)(32 * jb + n) * HD + 32 * wave + 4 * h2;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    bf16x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (__bf16)acc[4 * jj + i];
-    *reinterpret_cast<bf16x4*>(out + 8 * jj) = w;
-  }
-}
-
 void commit_split(const Dims& d, int* chunk_tokens, int* n_chunks) {
   const long bh = (long)d.B * d.H;
   const int max_chunks = (d.T + 127) / 128;
   long want = (512 + bh - 1) / bh;
   int c = (int)std::min<long>(std::max<long>(want, 1), max_chunks);
-  int ct = (d.T + c - 1) / c;
-  ct = (ct + CT - 1) / CT * CT;
-  *chunk_tokens = ct;
-  *n_chunks = (d.T + ct - 1) / ct;
-}
-
-// Token chunks of the commit inside the one-launch clean pass: as many as the
-// compute units the read leaves idle hold at once (fewer partials to sum than
-// the standalone split), else the standalone split.
-void clean_commit_split(const Dims& d, long n_attn, int* chunk_tokens, int* n_chunks) {
-  const long bh = (long)d.B * d.H;
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    n_cu = 0;
-  const long idle = (long)n_cu - n_attn;
-  if (idle < bh) {
-    commit_split(d, chunk_tokens, n_chunks);
-    return;
-  }
-  int ct0, nc0;
-  commit_split(d, &ct0, &nc0);              // never more chunks than its workspace holds
-  const int c = (int)std::min<long>(idle / bh, nc0);
   int ct = (d.T + c - 1) / c;
   ct = (ct + CT - 1) / CT * CT;
   *chunk_tokens = ct;
@@ -1542,31 +1513,28 @@ hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k,
                                     const void* mt, const void* phi_q, const void* phi_k,
                                     const void* phi_v, const float* beta, const float* alpha,
                                     const float* S_prev, float* S_next, void* mt_next, void* o,
-                                    void* o_intra, void* o_inter, void* ws, hipStream_t s) {
+                                    void* o_intra, void* o_inter, void*, hipStream_t s) {
   const long n_bh = (long)d.B * d.H;
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long n_attn = n_bh * n_qblk;
-  int ct, nc;
-  clean_commit_split(d, n_attn, &ct, &nc);
-  long n_pad, total;
-  attn_grid(n_attn, d.T, &n_pad, &total);
-  const long n_warm = total > n_attn ? total - n_pad : 0;
-  float* partial = static_cast<float*>(ws);
-  clean_fused_k<<<(unsigned)(n_pad + n_warm + n_bh * nc), 512, 0, s>>>(
+  const long n_pad = (n_attn + 7) / 8 * 8;
+  const long n_commit = 4 * n_bh, n_commit_pad = (n_commit + 7) / 8 * 8;
+  // the L2 warm-up role on the compute units that the read and the commit
+  // leave idle (up to 8 per XCD), for frames short enough to stay in L2
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 0;
+  const long n_warm =
+      d.T <= kWarmMaxKeys ? 8 * std::min<long>(8, std::max<long>(0, n_cu - n_pad - n_commit_pad) / 8)
+                          : 0;
+  clean_fused_k<<<(unsigned)(n_pad + n_commit_pad + n_warm), 512, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), d.T, d.scale * kLog2e, n_qblk, static_cast<const __bf16*>(mt),
       static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter), (int)n_attn, (int)n_pad,
-      (int)n_warm, static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), beta, alpha, S_prev,
-      S_next, partial, d.H, ct, nc, n_bh);
-  if (mt_next) {
-    commit_finish_k<<<(unsigned)(n_bh * 4), 512, 0, s>>>(partial, alpha, S_prev, S_next, nc, n_bh,
-                                                        static_cast<const __bf16*>(phi_q),
-                                                        static_cast<__bf16*>(mt_next), d.H);
-  } else if (nc > 1) {
-    const long total4 = n_bh * HD * HD / 4;
-    commit_reduce_k<<<(unsigned)((total4 + 255) / 256), 256, 0, s>>>(partial, alpha, S_prev,
-                                                                     S_next, nc, n_bh);
-  }
+      (int)n_commit, (int)n_commit_pad, (int)n_warm, static_cast<const __bf16*>(phi_k),
+      static_cast<const __bf16*>(phi_v), static_cast<const __bf16*>(phi_q), beta, alpha, S_prev,
+      S_next, static_cast<__bf16*>(mt_next), d.H);
   return hipGetLastError();
 }
 
@@ -1621,24 +1589,15 @@ hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
   return hipGetLastError();
 }
 
-size_t mfma_commit_ws_bytes(const Dims& d) { return mfma_state_commit_ws_bytes(d); }
+size_t mfma_commit_ws_bytes(const Dims&) { return 0; }
 
 hipError_t mfma_commit(const Dims& d, const void* k, const void* v, const void* phi_k,
                        const void* phi_v, const float* beta, const float* alpha,
-                       const float* S_prev, float* S_next, void* ws, hipStream_t s) {
-  int ct, nc;
-  commit_split(d, &ct, &nc);
-  const long n_bh = (long)d.B * d.H;
-  float* partial = static_cast<float*>(ws);
-  commit_fused_k<<<(unsigned)(n_bh * nc), 256, 0, s>>>(
+                       const float* S_prev, float* S_next, void*, hipStream_t s) {
+  commit_col_k<<<(unsigned)(4 * (long)d.B * d.H), 512, 0, s>>>(
       static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-      static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), beta, alpha, S_prev,
-      S_next, partial, d.H, d.T, ct, nc, n_bh);
-  if (nc > 1) {
-    const long total4 = n_bh * HD * HD / 4;
-    commit_reduce_k<<<(unsigned)((total4 + 255) / 256), 256, 0, s>>>(partial, alpha, S_prev,
-                                                                     S_next, nc, n_bh);
-  }
+      static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), nullptr, beta, alpha,
+      S_prev, S_next, nullptr, d.H, d.T);
   return hipGetLastError();
 }
 

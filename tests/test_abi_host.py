@@ -46,12 +46,14 @@ def test_workspace_sizes(arl2):
     s = arl2.Shape(1, 12, 1560, 128, arl2.BF16)
     act = 1 * 12 * 1560 * 128 * 2
     assert arl2.workspace_bytes(s, arl2.OP_READ) >= 12 * 128 * 128 * 2
-    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) >= arl2.workspace_bytes(s, arl2.OP_STATE_COMMIT)
+    # the bf16 commit (one workgroup per 32 state columns of a head) and the
+    # one-launch clean pass need no workspace; the commit from given K', V'
+    # sums fp32 partials of its token chunks
+    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) == 0
+    assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED) == 0
+    assert arl2.workspace_bytes(s, arl2.OP_STATE_COMMIT) > 0
     assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS) == max(
         arl2.workspace_bytes(s, arl2.OP_READ), arl2.workspace_bytes(s, arl2.OP_COMMIT))
-    # one-launch clean pass (bf16): the commit partials only
-    assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED) == arl2.workspace_bytes(
-        s, arl2.OP_COMMIT)
     # the plain grid at 12 heads x 1560 tokens: no workspace
     assert arl2.workspace_bytes(s, arl2.OP_READ_PREPARED) == 0
     assert arl2.workspace_bytes(s, arl2.OP_READ) == 12 * 128 * 128 * 2
@@ -118,30 +120,32 @@ def test_null_shape_dtype_layout_errors(arl2):
 
 
 def test_alias_and_workspace_errors(arl2):
-    # T long enough that the commit splits its tokens and needs a workspace, so
-    # every call below fails validation before anything could be launched
+    # float32: the commit maps K and V into its workspace, so every commit call
+    # below fails validation before anything could be launched
     s = arl2.Shape(1, 2, 1560, 128, arl2.BF16)
+    f = arl2.Shape(1, 2, 1560, 64, arl2.F32)
     cs = arl2.c_shape
-    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) > 0
+    assert arl2.workspace_bytes(f, arl2.OP_COMMIT) > 0
     S1, S2, WS = 8 << 20, 16 << 20, 32 << 20
-    need = arl2.workspace_bytes(s, arl2.OP_COMMIT)
+    need = arl2.workspace_bytes(f, arl2.OP_COMMIT)
     # S_prev == S_next
-    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S1, WS, need, None) == 5
+    assert _st(arl2, "arl2_commit", cs(f), A, A, A, A, A, A, S1, S1, WS, need, None) == 5
     # overlapping by one element
-    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S1 + 16, WS, need, None) == 5
+    assert _st(arl2, "arl2_commit", cs(f), A, A, A, A, A, A, S1, S1 + 16, WS, need, None) == 5
     # workspace missing / too small
-    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S2, None, 0, None) == 6
-    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, S2, WS, need - 1, None) == 6
+    assert _st(arl2, "arl2_commit", cs(f), A, A, A, A, A, A, S1, S2, None, 0, None) == 6
+    assert _st(arl2, "arl2_commit", cs(f), A, A, A, A, A, A, S1, S2, WS, need - 1, None) == 6
     assert "needed" in arl2.last_error()
     # read outputs overlapping inputs
     rneed = arl2.workspace_bytes(s, arl2.OP_READ)
     assert _st(arl2, "arl2_read", cs(s), A, B, B, B, S1, A, None, None, WS, rneed, None) == 5
-    # one-launch clean pass: S_next aliasing S_prev, missing workspace
+    # one-launch clean pass: S_next aliasing S_prev; float32 (read and commit
+    # one after the other in the workspace): missing workspace
     cneed = arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED)
-    assert cneed > 0
     assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, None, A, A, A, A, S1, S1,
                None, B, None, None, WS, cneed, None) == 5
-    assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, None, A, A, A, A, S1, S2,
+    assert arl2.workspace_bytes(f, arl2.OP_CLEAN_PASS_PREPARED) > 0
+    assert _st(arl2, "arl2_clean_pass_prepared", cs(f), A, A, A, A, None, A, A, A, A, S1, S2,
                None, B, None, None, None, 0, None) == 6
     # the next map wanted without phi_q
     assert _st(arl2, "arl2_clean_pass_prepared", cs(s), A, A, A, A, None, A, A, A, A, S1, S2,
@@ -173,15 +177,15 @@ def test_alias_and_workspace_errors(arl2):
     assert _st(arl2, "arl2_intra_attn_backward", cs(s), A, A, A, A, B, A, B, B + (4 << 20),
                B + (6 << 20), 0, WS, ab, None) == 5
     assert _st(arl2, "arl2_intra_attn_lse", cs(s), A, A, A, B, B, None) == 5
-    assert _st(arl2, "arl2_state_scan", cs(s), 0, A, A, A, A, A, A, S1, S2, WS, need, None) == 2
+    assert _st(arl2, "arl2_state_scan", cs(f), 0, A, A, A, A, A, A, S1, S2, WS, need, None) == 2
     # S_next over an input or the workspace (state commit, commit, clean pass)
     sneed = arl2.workspace_bytes(s, arl2.OP_STATE_COMMIT)
     assert sneed > 0
     assert _st(arl2, "arl2_state_commit", cs(s), A, A, A, A, S1, WS, WS, sneed, None) == 5
     assert _st(arl2, "arl2_state_commit", cs(s), B, A, A, A, S1, B + 4096, WS, sneed,
                None) == 5
-    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, A, S1, A + 4096, WS, need, None) == 5
-    assert _st(arl2, "arl2_commit", cs(s), A, A, A, A, A, B, S1, B, WS, need, None) == 5
+    assert _st(arl2, "arl2_commit", cs(f), A, A, A, A, A, A, S1, A + 4096, WS, need, None) == 5
+    assert _st(arl2, "arl2_commit", cs(f), A, A, A, A, A, B, S1, B, WS, need, None) == 5
     clneed = arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS)
     for phi_k, alpha in ((S2, A), (A, S2)):
         assert _st(arl2, "arl2_clean_pass", cs(s), A, A, A, A, phi_k, A, A, alpha, S1, S2, B,
