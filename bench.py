@@ -196,6 +196,7 @@ class Bench:
             wall = time.perf_counter() - w0
             frames = steps
         gpu_ms = t0.elapsed_time(t1)
+        self.last_host_s = wall
         return frames, max(gpu_ms / 1e3, wall), gpu_ms / 1e3
 
     def kernel_times(self, iters):
@@ -495,6 +496,7 @@ def main():
     calib = b.copy_calibration()
     print("[bench] timing frames", file=sys.stderr, flush=True)
     frames, secs, gpu_secs = b.timed(args.steps, args.warmup, use_graph=args.graph)
+    host_secs = b.last_host_s
     fps = w.B * frames / secs
     other = None
     if not args.no_graph_compare:
@@ -560,6 +562,10 @@ def main():
                    "B": w.B, "H": w.H, "D": w.D, "T": w.T, "passes_per_frame": w.passes,
                    "hip_graph": args.graph},
         "tokens_per_s": fps * w.T,
+        # the step's two clocks: GPU events around the timed frames, and the
+        # host's wall time to issue them (value uses the larger)
+        "gpu_ms_per_step": gpu_secs / frames * 1e3,
+        "host_ms_per_step": host_secs / frames * 1e3,
         ("frames_per_s_stream" if args.graph else "frames_per_s_graph"): other,
         "roofline": {"bound": "mfma",
                      "kernel": "attn_mfma_k<true> (fused read: intra-frame softmax + Q M)",

@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
+import functools
 import os
 
 import torch  # loaded first: libarl2 then binds to the HIP runtime torch carries
@@ -115,7 +116,13 @@ class Shape:
     softmax_scale: float = 0.0
 
     def c(self) -> _Shape:
-        return _Shape(self.B, self.H, self.T, self.D, self.act_dtype, self.softmax_scale)
+        # one C struct per Shape object, kept on it (the library only reads it)
+        try:
+            return self.__dict__["_c"]
+        except KeyError:
+            c = _c_shape_cached(self)
+            object.__setattr__(self, "_c", c)
+            return c
 
     @property
     def torch_dtype(self):
@@ -149,11 +156,14 @@ _PHI = ("phi", "phi_q", "phi_k", "phi_v", "dphi_q", "dphi_k", "dphi_v")
 _STATE = ("S", "S_prev", "S_next", "dS", "dS_next", "dS_prev", "S0", "states")
 
 
-def _checker(shape: "Shape", frames: int = 1, state_frames: int = 1):
-    """_ptr that also checks each tensor's element count against the shape
-    (the library sees only pointers: a short tensor would be read past its
-    end). `frames` multiplies the per-frame inputs (k, v, beta, alpha) of a
-    multi-frame call, `state_frames` the state-shaped tensors."""
+@functools.lru_cache(maxsize=256)
+def _c_shape_cached(shape: "Shape") -> _Shape:
+    # one C struct per shape, never modified (the library only reads it)
+    return _Shape(shape.B, shape.H, shape.T, shape.D, shape.act_dtype, shape.softmax_scale)
+
+
+@functools.lru_cache(maxsize=256)
+def _sizes(shape: "Shape", frames: int, state_frames: int):
     B, H, T, D = shape.B, shape.H, shape.T, shape.D
     sizes = {}
     sizes.update({n: B * H * T * D * frames for n in _ACT})
@@ -162,21 +172,48 @@ def _checker(shape: "Shape", frames: int = 1, state_frames: int = 1):
     sizes.update({"beta": B * H * T * frames, "dbeta": B * H * T, "alpha": B * H * frames,
                   "dalpha": B * H, "lse": B * H * T})
     min_bytes = {"prepared": prepared_bytes(shape), "prepared_next": prepared_bytes(shape)}
+    return sizes, min_bytes
+
+
+def _checker(shape: "Shape", frames: int = 1, state_frames: int = 1):
+    """_ptr that also checks each tensor's element count against the shape
+    (the library sees only pointers: a short tensor would be read past its
+    end). `frames` multiplies the per-frame inputs (k, v, beta, alpha) of a
+    multi-frame call, `state_frames` the state-shaped tensors."""
+    memo = shape.__dict__.get("_sizes")
+    if memo is None:
+        memo = {}
+        object.__setattr__(shape, "_sizes", memo)
+    key = (frames, state_frames)
+    got = memo.get(key)
+    if got is None:
+        got = memo[key] = _sizes(shape, frames, state_frames)
+    sizes, min_bytes = got
 
     def ck(t, name, dtype=None, optional=False):
         ptr = _ptr(t, name, dtype, optional)
-        if t is not None and name in sizes and t.numel() != sizes[name]:
-            raise ValueError(f"{name} has {t.numel()} elements, the shape needs {sizes[name]}")
-        if t is not None and name in min_bytes and t.numel() * t.element_size() < min_bytes[name]:
-            raise ValueError(f"{name} has {t.numel() * t.element_size()} bytes, the shape needs "
-                             f"{min_bytes[name]}")
+        if t is not None:
+            want = sizes.get(name)
+            if want is not None and t.numel() != want:
+                raise ValueError(f"{name} has {t.numel()} elements, the shape needs {want}")
+            mb = min_bytes.get(name)
+            if mb is not None and t.numel() * t.element_size() < mb:
+                raise ValueError(f"{name} has {t.numel() * t.element_size()} bytes, the shape "
+                                 f"needs {mb}")
         return ptr
     return ck
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def abi_version() -> int:
