@@ -1067,19 +1067,38 @@ static_assert(4 * CC_KP_B <= AKV && 2 * CC_RED_B <= AKV && HD * HD * 2 <= AKV &&
 // The LDS arrays l0..l3 (32 KB each): Phi_k; the fixed B operands (Phi_v and
 // S columns); the K' buffers of waves 0-3 and of waves 4-7; then the per-wave
 // U sums (two waves per array).
+// Token halves: the frame's 32-token slices are split into two halves, one
+// workgroup each (logical blocks 2 c and 2 c + 1 of column block c = 4 bh +
+// cb). Each publishes its fp32 sum U_half[:, cols] (16 KB, lane order e = tid +
+// 512 i) in its slot of the workspace with device-scope stores, waits for
+// them to complete and counts its arrival on the column block's counter
+// (pair_arrive); the second to arrive loads the other's sum with device-scope
+// loads and finishes the column block with U = U_0 + U_1 (the same sum
+// whichever half arrives second). Device-scope accesses are served at the
+// point where the XCDs' L2 caches are coherent, so neither side can see a
+// stale copy of the slot.
+struct CommitPair {
+  float* slots;                  // [4 B H][2][4096] floats
+  unsigned long long* ctr;       // one per (b, h, column block)
+  unsigned long long tag;        // this call's tag (bit 63 set)
+};
+constexpr int kScopeDevice = 16;   // cache policy bits: device scope (sc1)
+
 __device__ __forceinline__ void commit_col_block(
     int blk, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
     const __bf16* __restrict__ phi_q, const float* __restrict__ beta,
     const float* __restrict__ alpha, const float* __restrict__ S_prev,
     float* __restrict__ S_next, __bf16* __restrict__ mt_next, int H, int T, char* l0, char* l1,
-    char* l2, char* l3) {
+    char* l2, char* l3, const CommitPair* pair, int* flag) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  const long bh = blk >> 2;
-  const int cb = blk & 3;
+  const int half = pair ? (blk & 1) : 0;
+  const int cblk = pair ? (blk >> 1) : blk;             // 4 bh + cb
+  const long bh = cblk >> 2;
+  const int cb = cblk & 3;
   const int h = (int)(bh % H);
   const int col = 32 * cb + n;
 
@@ -1125,7 +1144,9 @@ __device__ __forceinline__ void commit_col_block(
   f32x16 uacc[4];
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) uacc[ib] = zero16();
-  const int n_slices = (T + CC_SLICE - 1) / CC_SLICE;
+  const int n_all = (T + CC_SLICE - 1) / CC_SLICE;
+  const int s_begin = pair && half ? (n_all + 1) / 2 : 0;
+  const int n_slices = pair && !half ? (n_all + 1) / 2 : n_all;
   // Operands of slice sl: lane n holds token 32 sl + perm32(n) of K and V,
   // lane n < 32 the beta of token 32 sl + n, each a load of its own (rows past
   // T read as zeros; a slice past the last reads zeros only). The next slice's
@@ -1145,8 +1166,8 @@ __device__ __forceinline__ void commit_col_block(
                                                v_src, roff + 32 * kc, 0, 0));
     }
   };
-  load_slice(wave);
-  for (int sl = wave; sl < n_slices; sl += CC_WAVES) {
+  load_slice(s_begin + wave);
+  for (int sl = s_begin + wave; sl < n_slices; sl += CC_WAVES) {
     if (h2 == 0) bslot[n] = bnext;
     // K~^T: kt[b][r] = K~[token][32 b + 8 (r / 4) + 4 h2 + r % 4]
     f32x16 kt[4];
@@ -1226,8 +1247,6 @@ __device__ __forceinline__ void commit_col_block(
         red[(32 * ib + 8 * (r >> 2) + 4 * h2 + (r & 3)) * 32 + n] = uacc[ib][r];
   }
   __syncthreads();
-  const float a = alpha[bh];
-  float* Sn = S_next + (size_t)bh * HD * HD;
   float sv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -1239,8 +1258,37 @@ __device__ __forceinline__ void commit_col_block(
       const float x = reinterpret_cast<const float*>(arr + (w & 1) * CC_RED_B)[e];
       acc = w == 0 ? x : acc + x;
     }
+    sv[i] = acc;
+  }
+  if (pair) {
+    const __amdgpu_buffer_rsrc_t mine =
+        buffer_rsrc(pair->slots + ((size_t)cblk * 2 + half) * 4096, 4096 * 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, sv[i]), mine,
+                                            (tid + 512 * i) * 4, 0, kScopeDevice);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) *flag = pair_arrive(pair->ctr + cblk, pair->tag) ? 1 : 0;
+    __syncthreads();
+    if (*flag == 0) return;
+    const __amdgpu_buffer_rsrc_t other =
+        buffer_rsrc(pair->slots + ((size_t)cblk * 2 + (1 - half)) * 4096, 4096 * 4);
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            other, (tid + 512 * i) * 4, 0, kScopeDevice));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = half ? pv[i] + sv[i] : sv[i] + pv[i];
+  }
+  const float a = alpha[bh];
+  float* Sn = S_next + (size_t)bh * HD * HD;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 512 * i;
     const size_t g = (size_t)(e >> 5) * HD + 32 * cb + (e & 31);
-    sv[i] = fmaf(a, Sp[g], acc);
+    sv[i] = fmaf(a, Sp[g], sv[i]);
     Sn[g] = sv[i];
   }
   if (!mt_next) return;
@@ -1278,21 +1326,23 @@ commit_col_k(const __bf16* __restrict__ k, const __bf16* __restrict__ v,
              const __bf16* __restrict__ phi_k, const __bf16* __restrict__ phi_v,
              const __bf16* __restrict__ phi_q, const float* __restrict__ beta,
              const float* __restrict__ alpha, const float* __restrict__ S_prev,
-             float* __restrict__ S_next, __bf16* __restrict__ mt_next, int H, int T) {
+             float* __restrict__ S_next, __bf16* __restrict__ mt_next, int H, int T,
+             CommitPair pair) {
   __shared__ __attribute__((aligned(1024))) char l0[AKV];
   __shared__ __attribute__((aligned(1024))) char l1[AKV];
   __shared__ __attribute__((aligned(1024))) char l2[AKV];
   __shared__ __attribute__((aligned(1024))) char l3[AKV];
+  __shared__ int flag;
   commit_col_block(xcd_remap(blockIdx.x, gridDim.x), k, v, phi_k, phi_v, phi_q, beta, alpha,
-                   S_prev, S_next, mt_next, H, T, l0, l1, l2, l3);
+                   S_prev, S_next, mt_next, H, T, l0, l1, l2, l3, &pair, &flag);
 }
 
 // The clean pass of the prepared read in one launch: blocks [0, n_attn) are
 // the fused read's workgroups (dispatched first, they take their compute units
 // first), the next n_commit blocks (from n_attn_pad) the column-split commit's
-// four workgroups per (b, h), which run on the compute units the read leaves
-// idle, reuse its LDS arrays, and also write the next frame's map when
-// mt_next is given; then n_warm blocks of the attention's L2 warm-up role
+// eight workgroups per (b, h) (four column blocks x two token halves), which
+// run on the compute units the read leaves idle, reuse its LDS arrays, and
+// also write the next frame's map when mt_next is given; then n_warm blocks of the attention's L2 warm-up role
 // (short-lived, on whatever compute units remain). n_attn_pad and
 // n_commit_pad are multiples of 8, so each role's blocks are dealt
 // round-robin over the XCDs from XCD 0.
@@ -1305,13 +1355,14 @@ clean_fused_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
               const __bf16* __restrict__ phi_v, const __bf16* __restrict__ phi_q,
               const float* __restrict__ beta, const float* __restrict__ alpha,
               const float* __restrict__ S_prev, float* __restrict__ S_next,
-              __bf16* __restrict__ mt_next, int H) {
+              __bf16* __restrict__ mt_next, int H, CommitPair pair) {
   __shared__ __attribute__((aligned(1024))) char lk0[AKV];
   __shared__ __attribute__((aligned(1024))) char lk1[AKV];
   __shared__ __attribute__((aligned(1024))) char lv0[AKV];
   __shared__ __attribute__((aligned(1024))) char lv1[AKV];
   __shared__ float mlx[8][2][64];
   __shared__ int redo_flag;
+  __shared__ int flag;
   const int b = blockIdx.x;
   if (b < n_attn_pad) {
     if (b < n_attn)
@@ -1321,7 +1372,7 @@ clean_fused_k(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int c = b - n_attn_pad;
     if (c < n_commit)
       commit_col_block(xcd_remap(c, n_commit), k, v, phi_k, phi_v, phi_q, beta, alpha, S_prev,
-                       S_next, mt_next, H, T, lk0, lk1, lv0, lv1);
+                       S_next, mt_next, H, T, lk0, lk1, lv0, lv1, &pair, &flag);
   } else {
     attn_l2_warm(b - n_attn_pad - n_commit_pad, n_warm / 8, n_attn, n_qblk, k, v, T, T, lk0);
   }
@@ -1509,16 +1560,28 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
   return hipGetLastError();
 }
 
+// The commit's pair-split workspace (mfma_commit_ws_bytes): the two halves'
+// slots per column block, then one counter per column block; each call gets
+// its own tag.
+static CommitPair commit_pair(const Dims& d, void* ws) {
+  static std::atomic<unsigned long long> g_commit_tag{0};
+  const size_t n_cb = (size_t)4 * d.B * d.H;
+  char* w = static_cast<char*>(ws);
+  return CommitPair{reinterpret_cast<float*>(w),
+                    reinterpret_cast<unsigned long long*>(w + n_cb * 2 * 4096 * sizeof(float)),
+                    (++g_commit_tag) | (1ull << 63)};
+}
+
 hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k, const void* v,
                                     const void* mt, const void* phi_q, const void* phi_k,
                                     const void* phi_v, const float* beta, const float* alpha,
                                     const float* S_prev, float* S_next, void* mt_next, void* o,
-                                    void* o_intra, void* o_inter, void*, hipStream_t s) {
+                                    void* o_intra, void* o_inter, void* ws, hipStream_t s) {
   const long n_bh = (long)d.B * d.H;
   const int n_qblk = (d.T + AQ - 1) / AQ;
   const long n_attn = n_bh * n_qblk;
   const long n_pad = (n_attn + 7) / 8 * 8;
-  const long n_commit = 4 * n_bh, n_commit_pad = (n_commit + 7) / 8 * 8;
+  const long n_commit = 8 * n_bh, n_commit_pad = (n_commit + 7) / 8 * 8;
   // the L2 warm-up role on the compute units that the read and the commit
   // leave idle (up to 8 per XCD), for frames short enough to stay in L2
   int dev = 0, n_cu = 0;
@@ -1534,7 +1597,7 @@ hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k,
       static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter), (int)n_attn, (int)n_pad,
       (int)n_commit, (int)n_commit_pad, (int)n_warm, static_cast<const __bf16*>(phi_k),
       static_cast<const __bf16*>(phi_v), static_cast<const __bf16*>(phi_q), beta, alpha, S_prev,
-      S_next, static_cast<__bf16*>(mt_next), d.H);
+      S_next, static_cast<__bf16*>(mt_next), d.H, commit_pair(d, ws));
   return hipGetLastError();
 }
 
@@ -1589,15 +1652,18 @@ hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
   return hipGetLastError();
 }
 
-size_t mfma_commit_ws_bytes(const Dims&) { return 0; }
+size_t mfma_commit_ws_bytes(const Dims& d) {
+  const size_t n_cb = (size_t)4 * d.B * d.H;
+  return n_cb * 2 * 4096 * sizeof(float) + round_up(n_cb * 8, 256);
+}
 
 hipError_t mfma_commit(const Dims& d, const void* k, const void* v, const void* phi_k,
                        const void* phi_v, const float* beta, const float* alpha,
-                       const float* S_prev, float* S_next, void*, hipStream_t s) {
-  commit_col_k<<<(unsigned)(4 * (long)d.B * d.H), 512, 0, s>>>(
+                       const float* S_prev, float* S_next, void* ws, hipStream_t s) {
+  commit_col_k<<<(unsigned)(8 * (long)d.B * d.H), 512, 0, s>>>(
       static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), nullptr, beta, alpha,
-      S_prev, S_next, nullptr, d.H, d.T);
+      S_prev, S_next, nullptr, d.H, d.T, commit_pair(d, ws));
   return hipGetLastError();
 }
 

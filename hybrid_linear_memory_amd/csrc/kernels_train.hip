@@ -976,18 +976,6 @@ struct PairSplit {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCoherentAux = 16;   // cache policy bits of the slot accesses: device scope (sc1)
 
-// Two-party arrival: false for the first of a pair, true for the second, which
-// leaves the counter at 0 again. The first leaves this call's tag there; any
-// other content (0 after a completed call, or whatever a fresh workspace holds)
-// counts as no arrival, so the workspace needs no clearing between calls.
-__device__ __forceinline__ bool pair_arrive(unsigned long long* ctr, unsigned long long tag) {
-  const unsigned long long old =
-      __hip_atomic_exchange(ctr, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (old != tag) return false;
-  __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return true;
-}
-
 // dK = scale sum_i dS_ij Q_i and dV = sum_i P_ij dO_i. One workgroup of NW
 // waves per 32 NW keys; wave w holds keys 32 w.. as the columns of S = Q K^T and
 // accumulates dK^T and dV^T (lane = key, registers = features); query, dO,

@@ -123,5 +123,19 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Two-party arrival on a per-pair counter in a workspace: false for the first
+// of a pair, true for the second, which leaves the counter at 0 again. The
+// first leaves this call's tag there (per-call, bit 63 set, so never 0); any
+// other content (0 after a completed call, or whatever a fresh workspace holds)
+// counts as no arrival, so the workspace needs no clearing between calls. The
+// exchange is a device-scope atomic: both parties see one modification order.
+__device__ __forceinline__ bool pair_arrive(unsigned long long* ctr, unsigned long long tag) {
+  const unsigned long long old =
+      __hip_atomic_exchange(ctr, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old != tag) return false;
+  __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 }  // namespace
 }  // namespace arl2

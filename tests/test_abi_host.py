@@ -46,11 +46,13 @@ def test_workspace_sizes(arl2):
     s = arl2.Shape(1, 12, 1560, 128, arl2.BF16)
     act = 1 * 12 * 1560 * 128 * 2
     assert arl2.workspace_bytes(s, arl2.OP_READ) >= 12 * 128 * 128 * 2
-    # the bf16 commit (one workgroup per 32 state columns of a head) and the
-    # one-launch clean pass need no workspace; the commit from given K', V'
-    # sums fp32 partials of its token chunks
-    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) == 0
-    assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED) == 0
+    # the bf16 commit and the one-launch clean pass: per (video, head, 32 state
+    # columns) two fp32 half-sums of 128 x 32 and one 8-byte counter; the commit
+    # from given K', V' sums fp32 partials of its token chunks
+    cblocks = 1 * 12 * 4
+    pair_ws = cblocks * 2 * 4096 * 4 + (cblocks * 8 + 255) // 256 * 256
+    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) == pair_ws
+    assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED) == pair_ws
     assert arl2.workspace_bytes(s, arl2.OP_STATE_COMMIT) > 0
     assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS) == max(
         arl2.workspace_bytes(s, arl2.OP_READ), arl2.workspace_bytes(s, arl2.OP_COMMIT))
