@@ -513,7 +513,11 @@ def main():
     achieved = flops / attn_s
     src_hash = kernel_source_hash()
     traffic = load_traffic("attn_mfma_k<true>", src_hash)
+    # the state write's algorithmic bytes: K and V (bf16; K', V' for the
+    # commit from mapped inputs), beta (fp32), S_prev read and S_next written
+    # (fp32); the commit from raw K, V also reads the two feature maps per head
     commit_bytes = w.B * w.H * (2 * w.T * w.D * 2 + 4 * w.T + 2 * w.D * w.D * 4)
+    commit_raw_bytes = commit_bytes + w.H * 2 * w.D * w.D * 2
     kernels = {
         "intra_attn_us": kt["intra_attn"],
         "intra_attn_tflops": flops_intra / (kt["intra_attn"] * 1e-6) / 1e12,
@@ -521,8 +525,16 @@ def main():
         "read_prepare_us": kt["read_prepare"],
         "read_prepared_us": kt["read_prepared"],
         "feature_map_us": kt["feature_map"],
-        "state_commit_us": kt["state_commit"],
+        # the commit on the step: commit_col_k (arl2_commit; the clean pass
+        # runs the same code on the compute units its read leaves idle)
         "commit_us": kt["commit"],
+        "commit_kernel": "commit_col_k",
+        "commit_hbm_frac": commit_raw_bytes / (kt["commit"] * 1e-6) / PEAK_HBM,
+        "commit_algorithmic_bytes": commit_raw_bytes,
+        # arl2_state_commit from mapped K', V' (commit_mfma_k + commit_reduce_k;
+        # not on the step)
+        "state_commit_us": kt["state_commit"],
+        "state_commit_kernels": "commit_mfma_k+commit_reduce_k",
         "state_commit_hbm_frac": commit_bytes / (kt["state_commit"] * 1e-6) / PEAK_HBM,
         "state_commit_algorithmic_bytes": commit_bytes,
         "copy_calibration": calib,

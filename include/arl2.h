@@ -214,7 +214,13 @@ arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q,
 
 /* Commit only (the clean pass's state write without its read):
  * K' = rownorm(K Phi_k[h]), V' = V Phi_v[h], then arl2_state_commit.
- * Needs arl2_workspace_bytes(shape, ARL2_OP_COMMIT). */
+ * Needs arl2_workspace_bytes(shape, ARL2_OP_COMMIT). On bf16 shapes (D = 128)
+ * one launch: each (video, head, 32 state columns) is split over two token
+ * halves whose fp32 products the second half to finish adds in a fixed order
+ * (the first half's first), so results are deterministic. The workspace holds
+ * those products and one counter per column block; the counters carry a
+ * per-call tag and are left at zero, so the workspace needs no clearing, and
+ * calls that share a workspace must not overlap in time. */
 arl2_status arl2_commit(const arl2_shape* shape, const void* k, const void* v,
                         const void* phi_k, const void* phi_v,
                         const float* beta, const float* alpha,
@@ -238,10 +244,10 @@ arl2_status arl2_clean_pass(const arl2_shape* shape, const void* q,
  * from K, V, beta, alpha and S_prev as in arl2_commit. When prepared_next is
  * not NULL it also receives the map of S_next (what arl2_read_prepare(phi_q,
  * S_next) would write; phi_q is then required), ready for the next frame's
- * reads; it must be a different buffer from `prepared`. On bf16 shapes the
- * read and the commit run in one launch, the commit on the compute units the
- * read leaves idle, followed by one launch that sums the commit's token chunks
- * and forms the next map. Needs arl2_workspace_bytes(shape,
+ * reads; it must be a different buffer from `prepared`. On bf16 shapes (D =
+ * 128) the read and the commit run in one launch, the commit (as in
+ * arl2_commit, also forming the next map) on the compute units the read leaves
+ * idle. Needs arl2_workspace_bytes(shape,
  * ARL2_OP_CLEAN_PASS_PREPARED) bytes of workspace. Outputs must not overlap
  * each other, the inputs or the workspace. */
 arl2_status arl2_clean_pass_prepared(const arl2_shape* shape, const void* q,
