@@ -138,12 +138,14 @@ __device__ __forceinline__ void attn_qk(f32x16 (&s)[2], const char* Kb, const At
 }
 
 __device__ __forceinline__ void attn_mask(f32x16 (&s)[2], int valid, int lane) {
-  const int h2 = lane >> 5;
+  // key kb*32 + 16*h2 + r is past the end when the constant kb*32 + r reaches
+  // lim (one register, no per-key index registers)
+  const int lim = valid - 16 * (lane >> 5);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (kb * 32 + 16 * h2 + r >= valid) s[kb][r] = -INFINITY;
+      if (kb * 32 + r >= lim) s[kb][r] = -INFINITY;
 }
 
 __device__ __forceinline__ float attn_tile_max(const f32x16 (&s)[2]) {
