@@ -66,6 +66,11 @@ def parse():
     ap.add_argument("--skip-rollout", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="instead of the step: read two rocprofv3 --pmc --output-format csv runs "
+                         "of this script (FETCH_SIZE, then WRITE_SIZE), scale them by the copy "
+                         "calibration's known bytes, write profiles/traffic.json and print a "
+                         "table (no GPU needed)")
     ap.add_argument("--sweep-read", action="store_true",
                     help="instead of the step: time the fused read (arl2_read_prepared) across "
                          "frame lengths, heads and videos, one JSON line per shape")
@@ -255,22 +260,29 @@ class Bench:
         return res
 
     def copy_calibration(self, nbytes=1 << 30):
-        """A plain device copy of known size, so rocprofv3 counter runs of this
-        script can scale FETCH_SIZE / WRITE_SIZE against known bytes."""
+        """Two device kernels of known traffic, so that rocprofv3 counter runs
+        of this script can scale FETCH_SIZE / WRITE_SIZE against known bytes
+        (the copy) and check the scale on a kernel of another shape (the add:
+        two inputs read, one output written)."""
         torch = self.torch
         a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        a2 = torch.empty_like(a).fill_(2.0)
         b = torch.empty_like(a)
+        torch.add(a[:1024], a2[:1024], out=b[:1024])      # the add's kernel loaded
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
         b.copy_(a)
-        e1.record()
+        ev[1].record()
+        torch.add(a, a2, out=b)
+        ev[2].record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        del a, b
+        ms_copy, ms_add = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+        del a, a2, b
         return {"bytes_read": nbytes, "bytes_written": nbytes,
-                "GBps": 2 * nbytes / (ms / 1e3) / 1e9}
+                "GBps": 2 * nbytes / (ms_copy / 1e3) / 1e9,
+                "add_bytes_read": 2 * nbytes, "add_bytes_written": nbytes,
+                "add_GBps": 3 * nbytes / (ms_add / 1e3) / 1e9}
 
     def rollout_flatness(self, n_frames, warm_frames=120):
         """Per-frame time and device memory over a long rollout of the layer,
@@ -477,8 +489,130 @@ def cpu_baseline(seconds: float):
     }
 
 
+CALIB_BYTES = 1 << 30
+
+
+def _short_kernel(name: str) -> str:
+    """rocprofv3 kernel name -> the short name used in profiles/traffic.json."""
+    import re
+    if name.startswith("_Z"):
+        # mangled (rocprofv3 leaves names with __bf16 parameters mangled):
+        # <len><name>[I<template args>E]..., bool arguments as Lb0E / Lb1E,
+        # int arguments as Li<n>E
+        i = name.find("N", 2) + 1 if name.startswith("_ZN") else 2
+        ident = ""
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            ident, i = name[j:j + n], j + n
+        m = re.match(r"I((?:L[bi]\d+E)+)E", name[i:])
+        if ident:
+            args = ["true" if a == "b1" else "false" if a == "b0" else a[1:]
+                    for a in re.findall(r"L([bi]\d+)E", m.group(1) if m else "")]
+            name = f"{ident}<{', '.join(args)}>(" if args else f"{ident}("
+    m = re.search(r"(\w+_k)(<([^()]*)>)?\(", name)
+    if m:
+        base, targs = m.group(1), (m.group(3) or "")
+        args = [a.strip() for a in targs.split(",")] if targs else []
+        if base == "attn_mfma_k" and args:
+            return f"attn_mfma_k<{args[0]}>" + (" (LSE)" if len(args) > 1 and args[1] == "true"
+                                                 else "")
+        if base == "rowmap_mfma_k" and args:
+            return {"0": "rowmap_mfma_k<MAP_PHI> (feature map)",
+                    "1": "rowmap_mfma_k<MAP_STATE>"}.get(args[0], name)
+        return base
+    if "copyBuffer" in name:
+        return "copyBuffer"
+    if "elementwise" in name and "add" in name.lower():
+        return "elementwise_add"
+    return name[:60]
+
+
+def _read_counter_csv(d: str, counter: str):
+    """(short kernel name, grid size, value) per dispatch from the
+    counter_collection csv files under d."""
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(d):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(dirpath, fn), newline="") as f:
+                for r in csv.DictReader(f):
+                    low = {k.lower(): v for k, v in r.items()}
+                    if low.get("counter_name") != counter:
+                        continue
+                    rows.append((_short_kernel(low["kernel_name"]), int(low["grid_size"]),
+                                 float(low["counter_value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return rows
+
+
+def traffic_from(fetch_dir: str, write_dir: str):
+    """HBM bytes per launch of each kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (KiB per dispatch), scaled so that the calibration copy
+    reads and writes its known 1 GiB; the calibration add (2 GiB read, 1 GiB
+    written) checks the scale on a kernel of another shape. Per kernel: the
+    median dispatch of its largest grid. Writes profiles/traffic.json."""
+    import re
+    import statistics
+    fetch = _read_counter_csv(fetch_dir, "FETCH_SIZE")
+    write = _read_counter_csv(write_dir, "WRITE_SIZE")
+
+    def largest(rows, kernel):
+        sel = [(g, v) for k, g, v in rows if k == kernel]
+        if not sel:
+            return None, None
+        gmax = max(g for g, _ in sel)
+        return gmax, statistics.median(v for g, v in sel if g == gmax)
+
+    _, f_copy = largest(fetch, "copyBuffer")
+    _, w_copy = largest(write, "copyBuffer")
+    ff = CALIB_BYTES / (f_copy * 1024.0)
+    fw = CALIB_BYTES / (w_copy * 1024.0)
+    _, f_add = largest(fetch, "elementwise_add")
+    _, w_add = largest(write, "elementwise_add")
+    check = None
+    if f_add and w_add:
+        check = {"add_read_ratio": f_add * 1024.0 * ff / (2 * CALIB_BYTES),
+                 "add_write_ratio": w_add * 1024.0 * fw / CALIB_BYTES}
+    src_hash = kernel_source_hash()
+    out = {}
+    names = sorted({k for k, _, _ in fetch} & {k for k, _, _ in write})
+    for k in names:
+        if k in ("copyBuffer", "elementwise_add") or not re.match(r"^\w+_k\b", k):
+            continue
+        g, fv = largest(fetch, k)
+        g2, wv = largest(write, k)
+        if g != g2:
+            continue
+        out[k] = {"bytes_per_launch": fv * 1024.0 * ff + wv * 1024.0 * fw, "grid": g,
+                  "fetch_bytes": fv * 1024.0 * ff, "write_bytes": wv * 1024.0 * fw,
+                  "source_hash": src_hash,
+                  "note": f"FETCH_SIZE*{ff:.3f} + WRITE_SIZE*{fw:.3f} (KiB x 1024), median "
+                          "dispatch of the largest grid"}
+    out["_calibration"] = {"fetch_scale": ff, "write_scale": fw, "add_check": check,
+                           "copy_bytes": CALIB_BYTES}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(f"scales: FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {fw:.3f}; add check {check}")
+    print("| kernel | grid | read MB | written MB | total MB |")
+    print("|---|---|---|---|---|")
+    for k, e in sorted(out.items()):
+        if k.startswith("_"):
+            continue
+        print(f"| {k} | {e['grid']} | {e['fetch_bytes'] / 1e6:.2f} | {e['write_bytes'] / 1e6:.2f} "
+              f"| {e['bytes_per_launch'] / 1e6:.2f} |")
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer shards "
               "by (video, head) with no exchange inside the step, and this program measures "
