@@ -1070,8 +1070,8 @@ static_assert(4 * CC_KP_B <= AKV && 2 * CC_RED_B <= AKV && HD * HD * 2 <= AKV &&
 // S columns); the K' buffers of waves 0-3 and of waves 4-7; then the per-wave
 // U sums (two waves per array).
 // Token halves: the frame's 32-token slices are split into two halves, one
-// workgroup each (logical blocks 2 c and 2 c + 1 of column block c = 4 bh +
-// cb). Each publishes its fp32 sum U_half[:, cols] (16 KB, lane order e = tid +
+// workgroup each (logical blocks 8 bh + cb and 8 bh + 4 + cb of column block
+// 4 bh + cb). Each publishes its fp32 sum U_half[:, cols] (16 KB, lane order e = tid +
 // 512 i) in its slot of the workspace with device-scope stores, waits for
 // them to complete and counts its arrival on the column block's counter
 // (pair_arrive); the second to arrive loads the other's sum with device-scope
@@ -1097,8 +1097,11 @@ __device__ __forceinline__ void commit_col_block(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  const int half = pair ? (blk & 1) : 0;
-  const int cblk = pair ? (blk >> 1) : blk;             // 4 bh + cb
+  // logical block 8 bh + 4 half + cb: the four column blocks that read the
+  // same token half of K and V are consecutive, so the XCD-aware block order
+  // keeps them on one XCD (one L2 fetch of that half)
+  const int half = pair ? ((blk >> 2) & 1) : 0;
+  const int cblk = pair ? (((blk >> 3) << 2) | (blk & 3)) : blk;   // 4 bh + cb
   const long bh = cblk >> 2;
   const int cb = cblk & 3;
   const int h = (int)(bh % H);
