@@ -452,29 +452,45 @@ __device__ __forceinline__ void attn_block(
   const float lsum = halves_sum(l * fa + lb * fb);
   // Writes this wave's 32 queries x 64 output columns: intra(b2, r) is the
   // normalised softmax branch of accumulator register r of column block b2.
+  // Each requested output goes through LDS (the K buffers are idle now): the
+  // workgroup's 128 x 128 bf16 tile, row-major with 16-byte chunks under the
+  // swz_r swizzle, then whole rows to memory (each store instruction writes
+  // four 256-byte rows, where a lane's registers hold 8-byte pieces of 32).
   auto store = [&](auto intra_of) __attribute__((always_inline)) {
-    if (t >= T) return;
-    const size_t row = ((size_t)bh * T + t) * HD + 4 * h2;
+    char* st = lk0;
+    const int ql = (wave & 3) * 32 + n;
+    const size_t row0 = (size_t)bh * T + (size_t)qblk * AQ;
+    const int n_rows = min(AQ, T - qblk * AQ);
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
-      const int db = 2 * stream + b2;
+    for (int kind = 0; kind < 3; ++kind) {
+      __bf16* out = kind == 0 ? o : kind == 1 ? o_intra : o_inter;
+      if (!out) continue;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 w, wi, we;
+      for (int b2 = 0; b2 < 2; ++b2) {
+        const int db = 2 * stream + b2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * jj + i;
-          const float intra = intra_of(b2, r);
-          const float inter = INTER ? oi[b2][r] : 0.f;
-          w[i] = (__bf16)(intra + inter);
-          wi[i] = (__bf16)intra;
-          we[i] = (__bf16)inter;
+        for (int jj = 0; jj < 4; ++jj) {
+          bf16x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * jj + i;
+            const float intra = kind == 2 ? 0.f : intra_of(b2, r);
+            const float inter = INTER && kind != 1 ? oi[b2][r] : 0.f;
+            w[i] = (__bf16)(intra + inter);
+          }
+          const int c = 4 * db + jj;          // 16-byte chunk of the row
+          *reinterpret_cast<bf16x4*>(st + ql * 256 + ((c ^ swz_r(ql)) << 4) + 8 * h2) = w;
         }
-        const size_t off_o = row + 32 * db + 8 * jj;
-        *reinterpret_cast<bf16x4*>(o + off_o) = w;
-        if (o_intra) *reinterpret_cast<bf16x4*>(o_intra + off_o) = wi;
-        if (o_inter) *reinterpret_cast<bf16x4*>(o_inter + off_o) = we;
       }
+      __syncthreads();
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int g = tid + 512 * k2, r = g >> 4, c = g & 15;
+        if (r < n_rows)
+          *reinterpret_cast<bf16x8*>(out + (row0 + r) * HD + 8 * c) =
+              *reinterpret_cast<const bf16x8*>(st + r * 256 + ((c ^ swz_r(r)) << 4));
+      }
+      __syncthreads();                    // the tile is read before the next output
     }
   };
   if (SK && sk->nseg > 1) {
