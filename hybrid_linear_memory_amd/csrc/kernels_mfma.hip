@@ -272,12 +272,31 @@ __device__ __forceinline__ void attn_block(
   const int stream = wave >> 2;
   const int t = qblk * AQ + (wave & 3) * 32 + n;
 
+  // The block's Q rows go to LDS (lk1, whose first use is the first
+  // iteration's loads) by direct loads of whole 256-byte rows, wave w taking
+  // rows [16 w, 16 w + 16) under the swz_r swizzle (rows past T arrive as
+  // zeros); each wave takes its operand registers from there once they have
+  // landed (run_pass, mode 0).
   bf16x8 qreg[8];
   {
-    const __bf16* qrow = q + ((size_t)bh * T + min(t, T - 1)) * HD + 8 * h2;
+    const int n_rows = min(AQ, T - qblk * AQ);
+    const __amdgpu_buffer_rsrc_t qr =
+        buffer_rsrc(q + ((size_t)bh * T + (size_t)qblk * AQ) * HD, (uint32_t)n_rows * HD * 2);
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) qreg[kc] = t < T ? ld8(qrow + 16 * kc) : zero8();
+    for (int qi = 0; qi < 4; ++qi) {
+      const int r = 16 * wave + 4 * qi + (lane >> 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void_t*)(lk1 + (16 * wave + 4 * qi) * 256),
+                                               16, r * 256 + (((lane & 15) ^ swz_r(r)) << 4), 0,
+                                               0, 0);
+    }
   }
+  auto read_q = [&]() __attribute__((always_inline)) {
+    const int ql = (wave & 3) * 32 + n;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+      qreg[kc] = *reinterpret_cast<const bf16x8*>(lk1 + ql * 256 +
+                                                 (((2 * kc + h2) ^ swz_r(ql)) << 4));
+  };
   const AttnOffsets off = attn_offsets(lane);
 
   // stream s owns global tiles s, s + 2, s + 4, ...: local tile j -> 2j + s.
@@ -388,12 +407,24 @@ __device__ __forceinline__ void attn_block(
     if (stream == 0) {
       load_k(lk0, 0);
       load_v(lv0, 0);
+      if (mode == 0) {
+        // Q landed for every wave (the 8 tile loads just issued may still fly)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        read_q();
+      }
       for (int it = 0; it < n_iter; it += 2) {
         step_a(it, lk0, lv0, lk1, lv1);
         if (it + 1 < n_iter) step_a(it + 1, lk1, lv1, lk0, lv0);
       }
     } else {
       if (my_cnt > 0) load_k(lk0 + TILE_B, 0);
+      if (mode == 0) {
+        if (my_cnt > 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        read_q();
+      }
       for (int it = 0; it < n_iter; it += 2) {
         step_b(it, lk0, lv0, lk1, lv1);
         if (it + 1 < n_iter) step_b(it + 1, lk1, lv1, lk0, lv0);
