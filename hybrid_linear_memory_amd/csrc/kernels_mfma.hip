@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "arl2_internal.h"
 #include "mfma_common.h"
@@ -70,13 +71,17 @@ constexpr int AKV = 2 * TILE_B;
 // tile past the last key) arrive as zeros: their scores are masked and their
 // values meet p = 0.
 template <bool IS_V>
+__device__ __forceinline__ void tile_row4(char* dst, __amdgpu_buffer_rsrc_t src, int tile_off,
+                                          int qoff, const int (&off)[2], int ii) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + qoff + ii * 1024), 16,
+                                           IS_V ? off[0] : off[ii & 1],
+                                           tile_off + qoff + ii * 1024, 0, 0);
+}
+template <bool IS_V>
 __device__ __forceinline__ void tile_quarter(char* dst, __amdgpu_buffer_rsrc_t src, int tile_off,
                                              int qoff, const int (&off)[2]) {
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + qoff + ii * 1024), 16,
-                                             IS_V ? off[0] : off[ii & 1],
-                                             tile_off + qoff + ii * 1024, 0, 0);
+  for (int ii = 0; ii < 4; ++ii) tile_row4<IS_V>(dst, src, tile_off, qoff, off, ii);
 }
 
 
@@ -135,6 +140,32 @@ __device__ __forceinline__ void attn_qk(f32x16 (&s)[2], const char* Kb, const At
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+}
+
+// The same products with the caller's next-tile loads spread over them: after
+// every second product, issue(n) sends load instruction n (n < n_ld, at most
+// 8), so that the loads leave one at a time while the matrix unit works
+// instead of in one burst that holds the wave. The order is fixed step by
+// step (K operand reads three products ahead).
+template <int N_LD, typename Issue>
+__device__ __forceinline__ void attn_qk_ld(f32x16 (&s)[2], const char* Kb,
+                                           const AttnOffsets& off, const bf16x8 (&qreg)[8],
+                                           Issue&& issue) {
+  bf16x8 ka[4];
+  auto kread = [&](int i) __attribute__((always_inline)) {
+    ka[i & 3] = *reinterpret_cast<const bf16x8*>(Kb + (i & 1) * 8192 + off.k[i >> 1]);
+  };
+  kread(0);
+  kread(1);
+  kread(2);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + 3 < 16) kread(i + 3);
+    const int kc = i >> 1, kb = i & 1;
+    s[kb] = mfma32(ka[i & 3], qreg[kc], kc == 0 ? zero16() : s[kb]);
+    if ((i & 1) && (i >> 1) < N_LD) issue(i >> 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 __device__ __forceinline__ void attn_mask(f32x16 (&s)[2], int valid, int lane) {
@@ -327,6 +358,17 @@ __device__ __forceinline__ void attn_block(
     asm volatile("" : "+s"(qoff));
     tile_quarter<true>(dst, v_src, (t0 + 2 * j + stream) * TILE_B, qoff, v_off);
   };
+  // instruction ii (0-3) of load_k / load_v
+  auto load_k1 = [&](char* dst, int j, int ii) __attribute__((always_inline)) {
+    int qoff = (wave & 3) * 4096;
+    asm volatile("" : "+s"(qoff));
+    tile_row4<false>(dst, k_src, (t0 + 2 * j + stream) * TILE_B, qoff, k_off, ii);
+  };
+  auto load_v1 = [&](char* dst, int j, int ii) __attribute__((always_inline)) {
+    int qoff = (wave & 3) * 4096;
+    asm volatile("" : "+s"(qoff));
+    tile_row4<true>(dst, v_src, (t0 + 2 * j + stream) * TILE_B, qoff, v_off, ii);
+  };
   // M^T (the inter-frame map, 32 KB) is loaded during the last iteration into
   // the K buffers that iteration leaves idle (rows under the swz_r swizzle),
   // wave w taking rows [16w, 16w + 16).
@@ -372,6 +414,18 @@ __device__ __forceinline__ void attn_block(
     if (mode == 1) m_ref = -INFINITY;
     if (tid == 0) redo_flag = 0;
     f32x16 s[2];
+    auto scores_tail = [&](int j) __attribute__((always_inline)) {
+      const int valid = n_kv - (t0 + 2 * j + stream) * AKT;
+      if (valid < AKT) attn_mask(s, valid, lane);
+      if (mode == 1) m_ref = fmaxf(m_ref, attn_tile_max(s));
+      if (mode == 0 && j == 0) m_ref = attn_tile_max(s);
+    };
+    // the scores of local tile j with load instructions spread over them
+    auto scores_ld = [&](int j, const char* Kb, auto n_ld, auto&& issue)
+        __attribute__((always_inline)) {
+      attn_qk_ld<decltype(n_ld)::value>(s, Kb, off, qreg, issue);
+      scores_tail(j);
+    };
     auto scores = [&](int j, const char* Kb) __attribute__((always_inline)) {
       attn_qk(s, Kb, off, qreg);
       const int valid = n_kv - (t0 + 2 * j + stream) * AKT;
@@ -385,14 +439,23 @@ __device__ __forceinline__ void attn_block(
         __attribute__((always_inline)) {
       sync();
       if (it == n_iter - 1) load_m(kn);
-      if (it + 1 < my_cnt) {
-        load_k(kn, it + 1);
-        load_v(vn, it + 1);
+      if constexpr (SK) {
+        // (split-key segments: the loads in one burst measured faster)
+        if (it + 1 < my_cnt) {
+          load_k(kn, it + 1);
+          load_v(vn, it + 1);
+        }
+        if (it < my_cnt) scores(it, kc);
+      } else if (it < my_cnt) {
+        if (it + 1 < my_cnt)
+          scores_ld(it, kc, std::integral_constant<int, 8>(), [&](int n2) {
+            if (n2 < 4) load_k1(kn, it + 1, n2);
+            else load_v1(vn, it + 1, n2 - 4);
+          });
+        else
+          scores(it, kc);
       }
-      if (it < my_cnt) {
-        scores(it, kc);
-        if (mode != 1) attn_softmax_pv(acc, l, m_ref, s, vc, off, sl2);
-      }
+      if (mode != 1 && it < my_cnt) attn_softmax_pv(acc, l, m_ref, s, vc, off, sl2);
     };
     auto step_b = [&](int it, char* kc, char* vc, char* kn, char* vn)
         __attribute__((always_inline)) {
@@ -400,9 +463,19 @@ __device__ __forceinline__ void attn_block(
       if (it == n_iter - 1) load_m(kn);
       if (mode != 1 && it >= 1 && it <= my_cnt)
         attn_softmax_pv(acc, l, m_ref, s, vc + TILE_B, off, sl2);
-      if (it < my_cnt) load_v(vn + TILE_B, it);
-      if (it + 1 < my_cnt) load_k(kn + TILE_B, it + 1);
-      if (it < my_cnt) scores(it, kc + TILE_B);
+      if constexpr (SK) {
+        if (it < my_cnt) load_v(vn + TILE_B, it);
+        if (it + 1 < my_cnt) load_k(kn + TILE_B, it + 1);
+        if (it < my_cnt) scores(it, kc + TILE_B);
+      } else if (it + 1 < my_cnt) {
+        scores_ld(it, kc + TILE_B, std::integral_constant<int, 8>(), [&](int n2) {
+          if (n2 < 4) load_v1(vn + TILE_B, it, n2);
+          else load_k1(kn + TILE_B, it + 1, n2 - 4);
+        });
+      } else if (it < my_cnt) {
+        scores_ld(it, kc + TILE_B, std::integral_constant<int, 4>(),
+                  [&](int n2) { load_v1(vn + TILE_B, it, n2); });
+      }
     };
     if (stream == 0) {
       load_k(lk0, 0);
