@@ -461,6 +461,11 @@ __device__ __forceinline__ void attn_block(
         __attribute__((always_inline)) {
       sync();
       if (it == n_iter - 1) load_m(kn);
+      if constexpr (!SK) {
+        // the V tile this stream needs next iteration, right after the barrier
+        // (its buffer is free since then), a full iteration ahead of its wait
+        if (it < my_cnt) load_v(vn + TILE_B, it);
+      }
       if (mode != 1 && it >= 1 && it <= my_cnt)
         attn_softmax_pv(acc, l, m_ref, s, vc + TILE_B, off, sl2);
       if constexpr (SK) {
@@ -468,13 +473,10 @@ __device__ __forceinline__ void attn_block(
         if (it + 1 < my_cnt) load_k(kn + TILE_B, it + 1);
         if (it < my_cnt) scores(it, kc + TILE_B);
       } else if (it + 1 < my_cnt) {
-        scores_ld(it, kc + TILE_B, std::integral_constant<int, 8>(), [&](int n2) {
-          if (n2 < 4) load_v1(vn + TILE_B, it, n2);
-          else load_k1(kn + TILE_B, it + 1, n2 - 4);
-        });
-      } else if (it < my_cnt) {
         scores_ld(it, kc + TILE_B, std::integral_constant<int, 4>(),
-                  [&](int n2) { load_v1(vn + TILE_B, it, n2); });
+                  [&](int n2) { load_k1(kn + TILE_B, it + 1, n2); });
+      } else if (it < my_cnt) {
+        scores(it, kc + TILE_B);
       }
     };
     if (stream == 0) {
