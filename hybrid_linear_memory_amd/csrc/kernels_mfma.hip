@@ -188,12 +188,11 @@ __device__ __forceinline__ float attn_tile_max(const f32x16 (&s)[2]) {
   return halves_max(m);
 }
 
-// p = 2^((s - m_ref) * sl2), row sums in fp32, then O^T += V^T P^T.
-__device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, float m_ref,
-                                                const f32x16 (&s)[2], const char* Vb,
-                                                const AttnOffsets& off, float sl2) {
+// p = 2^((s - m_ref) * sl2) rounded to bf16, and the row sums of the rounded
+// p in fp32.
+__device__ __forceinline__ void attn_softmax(bf16x8 (&pb)[2][2], float& l, float m_ref,
+                                             const f32x16 (&s)[2], float sl2) {
   const float mc = m_ref * sl2;
-  bf16x8 pb[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -214,7 +213,11 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
       ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, ls1, false);
     }
   l += ls0 + ls1;
-  // four independent accumulation chains advance together
+}
+
+// O^T += V^T P^T: four independent accumulation chains advance together.
+__device__ __forceinline__ void attn_pv(f32x16 (&acc)[4], const bf16x8 (&pb)[2][2],
+                                        const char* Vb, const AttnOffsets& off) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -233,6 +236,14 @@ __device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, floa
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+}
+
+__device__ __forceinline__ void attn_softmax_pv(f32x16 (&acc)[4], float& l, float m_ref,
+                                                const f32x16 (&s)[2], const char* Vb,
+                                                const AttnOffsets& off, float sl2) {
+  bf16x8 pb[2][2];
+  attn_softmax(pb, l, m_ref, s, sl2);
+  attn_pv(acc, pb, Vb, off);
 }
 
 // Split key ranges ("stream-K"): when a shape's query blocks are too few to
@@ -395,11 +406,15 @@ __device__ __forceinline__ void attn_block(
   };
 
   // The two streams run half an iteration apart so that the two waves sharing
-  // a SIMD alternate between matrix products and the softmax: after barrier
-  // it, stream A computes the scores of its tile it, their softmax and P V,
-  // while stream B first finishes its tile it-1 (softmax, P V, started from
-  // scores kept in registers) and then computes the scores of its tile it.
-  const int n_iter = max((n_tiles + 1) / 2, n_tiles / 2 + 1);   // same for every wave
+  // a SIMD alternate between matrix products and the softmax, each wave's
+  // products forming one block per iteration: after barrier it, stream A
+  // computes P V of its tile it-1 (P kept in registers) and the scores of its
+  // tile it, then their softmax; stream B first takes the softmax of its tile
+  // it-1 (scores kept in registers), then P V of that tile and the scores of
+  // its tile it. So while one wave of a SIMD runs its softmax the other runs
+  // its products. Tile j's V sits in the V buffers of parity j + 1 for both
+  // streams (loaded during iteration j, read during iteration j + 1).
+  const int n_iter = (n_tiles + 1) / 2 + 1;   // same for every wave
   f32x16 acc[4];
   float l = 0.f, m_ref = -INFINITY;
   // One pass over the keys. Mode 0: reference maximum from the stream's first
@@ -414,6 +429,7 @@ __device__ __forceinline__ void attn_block(
     if (mode == 1) m_ref = -INFINITY;
     if (tid == 0) redo_flag = 0;
     f32x16 s[2];
+    bf16x8 pa[2][2];      // stream A: P of its previous tile
     auto scores_tail = [&](int j) __attribute__((always_inline)) {
       const int valid = n_kv - (t0 + 2 * j + stream) * AKT;
       if (valid < AKT) attn_mask(s, valid, lane);
@@ -439,23 +455,24 @@ __device__ __forceinline__ void attn_block(
         __attribute__((always_inline)) {
       sync();
       if (it == n_iter - 1) load_m(kn);
-      if constexpr (SK) {
-        // (split-key segments: the loads in one burst measured faster)
-        if (it + 1 < my_cnt) {
-          load_k(kn, it + 1);
-          load_v(vn, it + 1);
-        }
-        if (it < my_cnt) scores(it, kc);
-      } else if (it < my_cnt) {
-        if (it + 1 < my_cnt)
+      if (mode != 1 && it >= 1 && it <= my_cnt) attn_pv(acc, pa, vc, off);
+      if (it < my_cnt) {
+        if constexpr (SK) {
+          // (split-key segments: the loads in one burst measured faster)
+          if (it + 1 < my_cnt) load_k(kn, it + 1);
+          load_v(vn, it);
+          scores(it, kc);
+        } else if (it + 1 < my_cnt) {
           scores_ld(it, kc, std::integral_constant<int, 8>(), [&](int n2) {
             if (n2 < 4) load_k1(kn, it + 1, n2);
-            else load_v1(vn, it + 1, n2 - 4);
+            else load_v1(vn, it, n2 - 4);
           });
-        else
-          scores(it, kc);
+        } else {
+          scores_ld(it, kc, std::integral_constant<int, 4>(),
+                    [&](int n2) { load_v1(vn, it, n2); });
+        }
+        if (mode != 1) attn_softmax(pa, l, m_ref, s, sl2);
       }
-      if (mode != 1 && it < my_cnt) attn_softmax_pv(acc, l, m_ref, s, vc, off, sl2);
     };
     auto step_b = [&](int it, char* kc, char* vc, char* kn, char* vn)
         __attribute__((always_inline)) {
@@ -480,11 +497,11 @@ __device__ __forceinline__ void attn_block(
       }
     };
     if (stream == 0) {
-      load_k(lk0, 0);
-      load_v(lv0, 0);
+      if (my_cnt > 0) load_k(lk0, 0);
       if (mode == 0) {
-        // Q landed for every wave (the 8 tile loads just issued may still fly)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        // Q landed for every wave (the 4 tile loads just issued may still fly)
+        if (my_cnt > 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         read_q();
       }
@@ -500,10 +517,14 @@ __device__ __forceinline__ void attn_block(
         __builtin_amdgcn_s_barrier();
         read_q();
       }
+      // Stream B's chain (softmax, P V, scores) is the longer one after each
+      // barrier: its instructions go first when both waves of a SIMD can issue.
+      __builtin_amdgcn_s_setprio(2);
       for (int it = 0; it < n_iter; it += 2) {
         step_b(it, lk0, lv0, lk1, lv1);
         if (it + 1 < n_iter) step_b(it + 1, lk1, lv1, lk0, lv0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (mode == 0 && __any(l > kRedoSum)) redo_flag = 1;     // every writer stores 1
     __builtin_amdgcn_s_waitcnt(0);
