@@ -120,7 +120,8 @@ size_t ws_commit(const arl2::Dims& d) {
 // bf16: the commit partials of the one-launch clean pass; otherwise the read
 // and the commit run one after the other in the same workspace.
 size_t ws_clean_pass_prepared(const arl2::Dims& d) {
-  return arl2::use_mfma(d) ? ws_commit(d) : std::max(ws_read_prepared(d), ws_commit(d));
+  return arl2::use_mfma(d) ? arl2::round_up(arl2::mfma_clean_commit_ws_bytes(d), 256)
+                           : std::max(ws_read_prepared(d), ws_commit(d));
 }
 
 // Token-level access: Q', K', V', an o_intra buffer, then the scan's own.

@@ -88,8 +88,11 @@ hipError_t mfma_read(const Dims& d, const void* q, const void* k, const void* v,
                      void* ws, hipStream_t s);
 // Fused commit (bf16, D = 128) from the raw K, V: feature maps, row norm and
 // the gated delta update in one launch, one workgroup per (b, h, 32 state
-// columns); needs no workspace (mfma_commit_ws_bytes is 0).
+// columns, token part); the workspace holds each part's fp32 sum and one
+// counter per column block (mfma_commit_ws_bytes; the clean pass, whose commit
+// takes two token parts, needs mfma_clean_commit_ws_bytes).
 size_t mfma_commit_ws_bytes(const Dims& d);
+size_t mfma_clean_commit_ws_bytes(const Dims& d);
 hipError_t mfma_commit(const Dims& d, const void* k, const void* v, const void* phi_k,
                        const void* phi_v, const float* beta, const float* alpha,
                        const float* S_prev, float* S_next, void* ws, hipStream_t s);

@@ -275,11 +275,13 @@ struct SkSeg {
 // The counter holds (tag << 16 | count) while a call is under way and is left
 // at 0 by the last arrival; a value from another call (or any other content of
 // the workspace) carries a different tag and counts as 0, so the workspace
-// needs no clearing between calls. Each failed exchange means another arrival
-// succeeded, so the loop ends after at most nseg attempts.
+// needs no clearing between calls. The first exchange assumes the 0 that a
+// completed call leaves (no load first); a failed exchange returns the actual
+// content, and each failure means another arrival succeeded, so the loop ends
+// after at most nseg + 1 attempts.
 __device__ __forceinline__ bool sk_arrive(unsigned long long* ctr, unsigned long long tag,
                                           int nseg) {
-  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long old = 0;
   for (;;) {
     const unsigned c = (old >> 16) == (tag >> 16) ? (unsigned)(old & 0xFFFFu) : 0u;
     const bool last = (int)c + 1 == nseg;
@@ -1212,22 +1214,72 @@ static_assert(4 * CC_KP_B <= AKV && 2 * CC_RED_B <= AKV && HD * HD * 2 <= AKV &&
 // The LDS arrays l0..l3 (32 KB each): Phi_k; the fixed B operands (Phi_v and
 // S columns); the K' buffers of waves 0-3 and of waves 4-7; then the per-wave
 // U sums (two waves per array).
-// Token halves: the frame's 32-token slices are split into two halves, one
-// workgroup each (logical blocks 8 bh + cb and 8 bh + 4 + cb of column block
-// 4 bh + cb). Each publishes its fp32 sum U_half[:, cols] (16 KB, lane order e = tid +
-// 512 i) in its slot of the workspace with device-scope stores, waits for
-// them to complete and counts its arrival on the column block's counter
-// (pair_arrive); the second to arrive loads the other's sum with device-scope
-// loads and finishes the column block with U = U_0 + U_1 (the same sum
-// whichever half arrives second). Device-scope accesses are served at the
-// point where the XCDs' L2 caches are coherent, so neither side can see a
-// stale copy of the slot.
+// Token parts: the frame's 32-token slices are split into n_parts parts (two
+// in the clean pass, up to eight in the commit alone), one workgroup each
+// (logical block (n_parts bh + part) 4 + cb of column block 4 bh + cb; part p
+// takes slices [ceil(p n / n_parts), ceil((p + 1) n / n_parts)) of the n).
+// Each publishes its fp32 sum U_p[:, cols] (16 KB, lane order e = tid + 512 i)
+// in its slot of the workspace with device-scope stores, waits for them to
+// complete and counts its arrival on the column block's counter (two parts:
+// pair_arrive, one exchange; more: commit_arrive, a compare-and-swap loop);
+// the last to arrive loads the others' sums with device-scope loads and
+// finishes the column block with U = U_0 + U_1 + ... in part order (the same
+// sum whichever part arrives last). Device-scope accesses are served at the
+// point where the XCDs' L2 caches are coherent, so no part can see a stale
+// copy of a slot.
 struct CommitPair {
-  float* slots;                  // [4 B H][2][4096] floats
+  float* slots;                  // [4 B H][n_parts][4096] floats
   unsigned long long* ctr;       // one per (b, h, column block)
-  unsigned long long tag;        // this call's tag (bit 63 set)
+  unsigned long long tag;        // this call's tag, in bits 16..63 (never 0)
+  int n_parts;                   // 2..8
 };
+
+// Counts one arrival at a column block's counter; true for the last of the
+// n_parts parts. The counter holds (tag | count) while a call is under way and
+// is left at 0 by the last arrival; a value carrying another tag (a completed
+// call leaves 0; a fresh workspace holds anything) counts as no arrival, so
+// the workspace needs no clearing between calls. The first exchange assumes
+// the 0 that a completed call leaves (no load first); a failed exchange
+// returns the actual content, and each failure means another arrival
+// succeeded, so the loop ends after at most n_parts + 1 attempts.
+__device__ __forceinline__ bool commit_arrive(unsigned long long* ctr, unsigned long long tag,
+                                              int n_parts) {
+  unsigned long long old = 0;
+  for (;;) {
+    const unsigned c = (old >> 16) == (tag >> 16) ? (unsigned)(old & 0xFFFFu) : 0u;
+    const bool last = (int)c + 1 == n_parts;
+    const unsigned long long nw = last ? 0ull : (tag | (c + 1u));
+    if (__hip_atomic_compare_exchange_strong(ctr, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return last;
+  }
+}
 constexpr int kScopeDevice = 16;   // cache policy bits: device scope (sc1)
+
+// The last part's merge: every other part's sum (device-scope loads, all in
+// flight at once), then U = U_0 + U_1 + ... in part order, this part's own
+// sum (sv, lane order e = tid + 512 i) taking its place.
+template <int NP>
+__device__ __forceinline__ void commit_merge(float (&sv)[8], const float* cslots, int part,
+                                             int tid) {
+  float pv[NP][8];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const __amdgpu_buffer_rsrc_t other = buffer_rsrc(cslots + (size_t)j * 4096, 4096 * 4);
+    if (j == part) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pv[j][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               other, (tid + 512 * i) * 4, 0, kScopeDevice));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float acc = part == 0 ? sv[i] : pv[0][i];
+#pragma unroll
+    for (int j = 1; j < NP; ++j) acc += j == part ? sv[i] : pv[j][i];
+    sv[i] = acc;
+  }
+}
 
 __device__ __forceinline__ void commit_col_block(
     int blk, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -1240,11 +1292,12 @@ __device__ __forceinline__ void commit_col_block(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h2 = lane >> 5;
-  // logical block 8 bh + 4 half + cb: the four column blocks that read the
-  // same token half of K and V are consecutive, so the XCD-aware block order
-  // keeps them on one XCD (one L2 fetch of that half)
-  const int half = pair ? ((blk >> 2) & 1) : 0;
-  const int cblk = pair ? (((blk >> 3) << 2) | (blk & 3)) : blk;   // 4 bh + cb
+  // logical block (n_parts bh + part) 4 + cb: the four column blocks that
+  // read the same token part of K and V are consecutive, so the XCD-aware
+  // block order keeps them on one XCD (one L2 fetch of that part)
+  const int n_parts = pair ? pair->n_parts : 1;
+  const int part = pair ? (blk >> 2) % n_parts : 0;
+  const int cblk = pair ? (blk / (4 * n_parts)) * 4 + (blk & 3) : blk;   // 4 bh + cb
   const long bh = cblk >> 2;
   const int cb = cblk & 3;
   const int h = (int)(bh % H);
@@ -1293,8 +1346,8 @@ __device__ __forceinline__ void commit_col_block(
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) uacc[ib] = zero16();
   const int n_all = (T + CC_SLICE - 1) / CC_SLICE;
-  const int s_begin = pair && half ? (n_all + 1) / 2 : 0;
-  const int n_slices = pair && !half ? (n_all + 1) / 2 : n_all;
+  const int s_begin = (part * n_all + n_parts - 1) / n_parts;
+  const int n_slices = ((part + 1) * n_all + n_parts - 1) / n_parts;   // end of the range
   // Operands of slice sl: lane n holds token 32 sl + perm32(n) of K and V,
   // lane n < 32 the beta of token 32 sl + n, each a load of its own (rows past
   // T read as zeros; a slice past the last reads zeros only). The next slice's
@@ -1409,26 +1462,30 @@ __device__ __forceinline__ void commit_col_block(
     sv[i] = acc;
   }
   if (pair) {
-    const __amdgpu_buffer_rsrc_t mine =
-        buffer_rsrc(pair->slots + ((size_t)cblk * 2 + half) * 4096, 4096 * 4);
+    float* cslots = pair->slots + (size_t)cblk * n_parts * 4096;
+    const __amdgpu_buffer_rsrc_t mine = buffer_rsrc(cslots + (size_t)part * 4096, 4096 * 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, sv[i]), mine,
                                             (tid + 512 * i) * 4, 0, kScopeDevice);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) *flag = pair_arrive(pair->ctr + cblk, pair->tag) ? 1 : 0;
+    if (tid == 0)
+      *flag = (n_parts == 2 ? pair_arrive(pair->ctr + cblk, pair->tag)
+                            : commit_arrive(pair->ctr + cblk, pair->tag, n_parts))
+                  ? 1
+                  : 0;
     __syncthreads();
     if (*flag == 0) return;
-    const __amdgpu_buffer_rsrc_t other =
-        buffer_rsrc(pair->slots + ((size_t)cblk * 2 + (1 - half)) * 4096, 4096 * 4);
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            other, (tid + 512 * i) * 4, 0, kScopeDevice));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = half ? pv[i] + sv[i] : sv[i] + pv[i];
+    switch (n_parts) {
+      case 2: commit_merge<2>(sv, cslots, part, tid); break;
+      case 3: commit_merge<3>(sv, cslots, part, tid); break;
+      case 4: commit_merge<4>(sv, cslots, part, tid); break;
+      case 5: commit_merge<5>(sv, cslots, part, tid); break;
+      case 6: commit_merge<6>(sv, cslots, part, tid); break;
+      case 7: commit_merge<7>(sv, cslots, part, tid); break;
+      default: commit_merge<8>(sv, cslots, part, tid); break;
+    }
   }
   const float a = alpha[bh];
   float* Sn = S_next + (size_t)bh * HD * HD;
@@ -1708,16 +1765,17 @@ hipError_t mfma_read_prepared(const Dims& d, const void* q, const void* k, const
   return hipGetLastError();
 }
 
-// The commit's pair-split workspace (mfma_commit_ws_bytes): the two halves'
-// slots per column block, then one counter per column block; each call gets
-// its own tag.
-static CommitPair commit_pair(const Dims& d, void* ws) {
+// The commit's token-split workspace: n_parts slots per column block, then one
+// counter per column block; each call gets its own tag.
+static CommitPair commit_pair(const Dims& d, void* ws, int n_parts) {
   static std::atomic<unsigned long long> g_commit_tag{0};
   const size_t n_cb = (size_t)4 * d.B * d.H;
   char* w = static_cast<char*>(ws);
+  unsigned long long tag = 0;
+  while (tag == 0) tag = (++g_commit_tag) & 0xFFFFFFFFFFFFull;
   return CommitPair{reinterpret_cast<float*>(w),
-                    reinterpret_cast<unsigned long long*>(w + n_cb * 2 * 4096 * sizeof(float)),
-                    (++g_commit_tag) | (1ull << 63)};
+                    reinterpret_cast<unsigned long long*>(w + n_cb * n_parts * 4096 * sizeof(float)),
+                    tag << 16, n_parts};
 }
 
 hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k, const void* v,
@@ -1745,7 +1803,7 @@ hipError_t mfma_clean_pass_prepared(const Dims& d, const void* q, const void* k,
       static_cast<__bf16*>(o_intra), static_cast<__bf16*>(o_inter), (int)n_attn, (int)n_pad,
       (int)n_commit, (int)n_commit_pad, (int)n_warm, static_cast<const __bf16*>(phi_k),
       static_cast<const __bf16*>(phi_v), static_cast<const __bf16*>(phi_q), beta, alpha, S_prev,
-      S_next, static_cast<__bf16*>(mt_next), d.H, commit_pair(d, ws));
+      S_next, static_cast<__bf16*>(mt_next), d.H, commit_pair(d, ws, 2));
   return hipGetLastError();
 }
 
@@ -1800,7 +1858,22 @@ hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
   return hipGetLastError();
 }
 
+// Token parts of the commit alone: as many as fill 256 compute units with the
+// 4 B H column blocks (at least two, at most eight), each part at least eight
+// 32-token slices (one per wave) when the frame has them.
+static int commit_parts(const Dims& d) {
+  const long n_cb = 4L * d.B * d.H;
+  const int n_all = (d.T + CC_SLICE - 1) / CC_SLICE;
+  long p = std::min<long>(256 / n_cb, n_all / CC_WAVES);
+  return (int)std::max<long>(2, std::min<long>(8, p));
+}
+
 size_t mfma_commit_ws_bytes(const Dims& d) {
+  const size_t n_cb = (size_t)4 * d.B * d.H;
+  return n_cb * commit_parts(d) * 4096 * sizeof(float) + round_up(n_cb * 8, 256);
+}
+
+size_t mfma_clean_commit_ws_bytes(const Dims& d) {
   const size_t n_cb = (size_t)4 * d.B * d.H;
   return n_cb * 2 * 4096 * sizeof(float) + round_up(n_cb * 8, 256);
 }
@@ -1808,10 +1881,11 @@ size_t mfma_commit_ws_bytes(const Dims& d) {
 hipError_t mfma_commit(const Dims& d, const void* k, const void* v, const void* phi_k,
                        const void* phi_v, const float* beta, const float* alpha,
                        const float* S_prev, float* S_next, void* ws, hipStream_t s) {
-  commit_col_k<<<(unsigned)(8 * (long)d.B * d.H), 512, 0, s>>>(
+  const int n_parts = commit_parts(d);
+  commit_col_k<<<(unsigned)(4L * n_parts * d.B * d.H), 512, 0, s>>>(
       static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(phi_k), static_cast<const __bf16*>(phi_v), nullptr, beta, alpha,
-      S_prev, S_next, nullptr, d.H, d.T, commit_pair(d, ws));
+      S_prev, S_next, nullptr, d.H, d.T, commit_pair(d, ws, n_parts));
   return hipGetLastError();
 }
 

@@ -215,12 +215,13 @@ arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q,
 /* Commit only (the clean pass's state write without its read):
  * K' = rownorm(K Phi_k[h]), V' = V Phi_v[h], then arl2_state_commit.
  * Needs arl2_workspace_bytes(shape, ARL2_OP_COMMIT). On bf16 shapes (D = 128)
- * one launch: each (video, head, 32 state columns) is split over two token
- * halves whose fp32 products the second half to finish adds in a fixed order
- * (the first half's first), so results are deterministic. The workspace holds
- * those products and one counter per column block; the counters carry a
- * per-call tag and are left at zero, so the workspace needs no clearing, and
- * calls that share a workspace must not overlap in time. */
+ * one launch: each (video, head, 32 state columns) is split over 2 to 8 token
+ * parts (as many as fill 256 compute units; 5 at 1 video x 12 heads x 1560
+ * tokens) whose fp32 products the last part to finish adds in part order, so
+ * results are deterministic. The workspace holds those products and one
+ * counter per column block; the counters carry a per-call tag and are left at
+ * zero, so the workspace needs no clearing, and calls that share a workspace
+ * must not overlap in time. */
 arl2_status arl2_commit(const arl2_shape* shape, const void* k, const void* v,
                         const void* phi_k, const void* phi_v,
                         const float* beta, const float* alpha,

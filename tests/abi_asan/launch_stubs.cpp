@@ -77,6 +77,7 @@ hipError_t mfma_read(const Dims&, const void*, const void*, const void*, const v
   return reached();
 }
 size_t mfma_commit_ws_bytes(const Dims& d) { return sized(d, 65536); }
+size_t mfma_clean_commit_ws_bytes(const Dims& d) { return sized(d, 32768); }
 hipError_t mfma_commit(const Dims&, const void*, const void*, const void*, const void*,
                        const float*, const float*, const float*, float*, void*, hipStream_t) {
   return reached();

@@ -129,6 +129,36 @@ def test_state_commit(case):
     assert_close(host(Sn), ref, TOL[w.dtype], "S_next")
 
 
+# The fused commit from the raw K, V over its token-part splits: 2 parts (513
+# tokens; 8 videos; one token), 3 (3 heads x 777), 5 (12 heads x 1560), 6 (one
+# head x 1560) and 8 (one head x 4000).
+COMMIT_CASES = [("bf16", 1, 2, 513, 128), ("bf16", 2, 3, 1, 128), ("bf16", 1, 3, 777, 128),
+                ("bf16", 1, 12, 1560, 128), ("bf16", 1, 1, 1560, 128), ("bf16", 1, 1, 4000, 128),
+                ("bf16", 8, 12, 200, 128)]
+
+
+@pytest.mark.parametrize("case", COMMIT_CASES, ids=_ids)
+def test_commit(case):
+    """arl2_commit against the oracle's commit, twice on one workspace with
+    different inputs (every part's slot and the counters reused)."""
+    from hybrid_linear_memory_amd import arl2
+    w = _w(*case)
+    log(f"commit {_ids(case)}")
+    sh = shape_of(w)
+    phis = synth.phi_maps(w)
+    ws = arl2.alloc_workspace(sh, arl2.OP_COMMIT)
+    g = np.random.default_rng(9)
+    for call in range(2):
+        k, v = synth.kv(w, call, 0)
+        beta, alpha = synth.gates(w, call)
+        S = (g.standard_normal((w.B, w.H, w.D, w.D)) * 0.05).astype(np.float32)
+        Sn = dev32(np.zeros_like(S))
+        arl2.commit(sh, dev(k, w.dtype), dev(v, w.dtype), dev(phis[1], w.dtype),
+                    dev(phis[2], w.dtype), dev32(beta), dev32(alpha), dev32(S), Sn, ws)
+        assert_close(host(Sn), oracle.commit(k, v, phis[1], phis[2], beta, alpha, S),
+                     TOL[w.dtype], f"S_next (call {call})")
+
+
 @pytest.mark.parametrize("case", STEP_CASES, ids=_ids)
 def test_clean_pass_prepared(case):
     """The one-call clean pass from a prepared map: every output and S_next
