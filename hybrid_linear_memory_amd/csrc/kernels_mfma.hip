@@ -54,12 +54,11 @@ constexpr int TILE_B = AKT * HD * 2;        // one 64 x 128 bf16 tile (16 KB)
 constexpr float kRedoSum = 18446744073709551616.0f;   // 2^64: largest accepted l
 constexpr float kLn2 = 0.6931471805599453f;
 // LDS: the tiles of parity p (local tile index & 1) sit in arrays of their
-// own: lk[p] = [stream A K, stream B K] of parity p and lv[p] = [stream A V of
-// parity p, stream B V of parity 1-p] (stream B's V tiles are loaded one
-// iteration after its K tiles). At an iteration of parity p every read is from
-// lk[p] / lv[p] and every load in flight targets lk[1-p] / lv[1-p]: distinct
-// objects, which lets the compiler see that the reads need not wait for the
-// prefetch.
+// own: lk[p] = [stream A K, stream B K] of parity p and lv[p] = [stream A V,
+// stream B V] of parity 1-p (each stream's V tiles are loaded one iteration
+// after its K tiles). At an iteration of parity p every read is from lk[p] /
+// lv[p] and every load in flight targets lk[1-p] / lv[1-p]: distinct objects,
+// which lets the compiler see that the reads need not wait for the prefetch.
 constexpr int AKV = 2 * TILE_B;
 
 
