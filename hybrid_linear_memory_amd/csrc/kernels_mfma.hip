@@ -1857,14 +1857,20 @@ hipError_t mfma_inter_read(const Dims& d, const void* q_prime, const float* S,
   return hipGetLastError();
 }
 
-// Token parts of the commit alone: as many as fill 256 compute units with the
-// 4 B H column blocks (at least two, at most eight), each part at least eight
-// 32-token slices (one per wave) when the frame has them.
+// Token parts of the commit alone: at most as many as fill 256 compute units
+// with the 4 B H column blocks (at least two, at most eight), each part at
+// least eight 32-token slices (one per wave) when the frame has them; then the
+// fewest parts that give each wave the same number of slices (fewer sums to
+// publish and merge for the same time).
 static int commit_parts(const Dims& d) {
   const long n_cb = 4L * d.B * d.H;
   const int n_all = (d.T + CC_SLICE - 1) / CC_SLICE;
   long p = std::min<long>(256 / n_cb, n_all / CC_WAVES);
-  return (int)std::max<long>(2, std::min<long>(8, p));
+  p = std::max<long>(2, std::min<long>(8, p));
+  auto rounds = [&](long q) { return ((n_all + q - 1) / q + CC_WAVES - 1) / CC_WAVES; };
+  const long r = rounds(p);
+  while (p > 2 && rounds(p - 1) == r) --p;
+  return (int)p;
 }
 
 size_t mfma_commit_ws_bytes(const Dims& d) {

@@ -216,7 +216,8 @@ arl2_status arl2_read_prepared(const arl2_shape* shape, const void* q,
  * K' = rownorm(K Phi_k[h]), V' = V Phi_v[h], then arl2_state_commit.
  * Needs arl2_workspace_bytes(shape, ARL2_OP_COMMIT). On bf16 shapes (D = 128)
  * one launch: each (video, head, 32 state columns) is split over 2 to 8 token
- * parts (as many as fill 256 compute units; 5 at 1 video x 12 heads x 1560
+ * parts (at most as many as fill 256 compute units, then the fewest that give
+ * each wave the same number of 32-token slices; 4 at 1 video x 12 heads x 1560
  * tokens) whose fp32 products the last part to finish adds in part order, so
  * results are deterministic. The workspace holds those products and one
  * counter per column block; the counters carry a per-call tag and are left at

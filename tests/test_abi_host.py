@@ -48,21 +48,25 @@ def test_workspace_sizes(arl2):
     assert arl2.workspace_bytes(s, arl2.OP_READ) >= 12 * 128 * 128 * 2
     # the bf16 commit and the one-launch clean pass: per (video, head, 32 state
     # columns) one fp32 sum of 128 x 32 per token part and one 8-byte counter.
-    # The clean pass takes two parts; the commit alone as many as fill 256
-    # compute units (here 256 // 48 = 5; at least 2, at most 8, and at least
-    # eight 32-token slices per part where the frame has them); the commit
-    # from given K', V' sums fp32 partials of its token chunks
+    # The clean pass takes two parts; the commit alone at most as many as fill
+    # 256 compute units (at least 2, at most 8, and at least eight 32-token
+    # slices per part where the frame has them), then the fewest that keep
+    # each wave's slice count (here 49 slices: 5 parts of <= 10 slices and 4
+    # of <= 13 both give two per wave, so 4); the commit from given K', V' sums
+    # fp32 partials of its token chunks
     def parts_ws(cblocks, parts):
         return cblocks * parts * 4096 * 4 + (cblocks * 8 + 255) // 256 * 256
     cblocks = 1 * 12 * 4
-    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) == parts_ws(cblocks, 5)
+    assert arl2.workspace_bytes(s, arl2.OP_COMMIT) == parts_ws(cblocks, 4)
     assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS_PREPARED) == parts_ws(cblocks, 2)
     eight = arl2.Shape(8, 12, 1560, 128, arl2.BF16)
     assert arl2.workspace_bytes(eight, arl2.OP_COMMIT) == parts_ws(8 * 12 * 4, 2)
     short = arl2.Shape(1, 2, 100, 128, arl2.BF16)         # 4 slices: two parts
     assert arl2.workspace_bytes(short, arl2.OP_COMMIT) == parts_ws(2 * 4, 2)
-    few = arl2.Shape(1, 1, 1560, 128, arl2.BF16)          # 49 slices: at most 8 parts
-    assert arl2.workspace_bytes(few, arl2.OP_COMMIT) == parts_ws(4, 6)
+    three = arl2.Shape(1, 1, 768, 128, arl2.BF16)         # 24 slices: 3 parts of 8
+    assert arl2.workspace_bytes(three, arl2.OP_COMMIT) == parts_ws(4, 3)
+    most = arl2.Shape(1, 1, 4000, 128, arl2.BF16)         # 125 slices: 8 parts of <= 16
+    assert arl2.workspace_bytes(most, arl2.OP_COMMIT) == parts_ws(4, 8)
     assert arl2.workspace_bytes(s, arl2.OP_STATE_COMMIT) > 0
     assert arl2.workspace_bytes(s, arl2.OP_CLEAN_PASS) == max(
         arl2.workspace_bytes(s, arl2.OP_READ), arl2.workspace_bytes(s, arl2.OP_COMMIT))

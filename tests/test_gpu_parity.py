@@ -130,11 +130,11 @@ def test_state_commit(case):
 
 
 # The fused commit from the raw K, V over its token-part splits: 2 parts (513
-# tokens; 8 videos; one token), 3 (3 heads x 777), 5 (12 heads x 1560), 6 (one
-# head x 1560) and 8 (one head x 4000).
+# tokens; 3 heads x 777; 8 videos; one token), 3 (one head x 768), 4 (12 heads
+# x 1560; one head x 1560, ragged parts) and 8 (one head x 4000).
 COMMIT_CASES = [("bf16", 1, 2, 513, 128), ("bf16", 2, 3, 1, 128), ("bf16", 1, 3, 777, 128),
-                ("bf16", 1, 12, 1560, 128), ("bf16", 1, 1, 1560, 128), ("bf16", 1, 1, 4000, 128),
-                ("bf16", 8, 12, 200, 128)]
+                ("bf16", 1, 1, 768, 128), ("bf16", 1, 12, 1560, 128), ("bf16", 1, 1, 1560, 128),
+                ("bf16", 1, 1, 4000, 128), ("bf16", 8, 12, 200, 128)]
 
 
 @pytest.mark.parametrize("case", COMMIT_CASES, ids=_ids)
