@@ -139,14 +139,20 @@ COMMIT_CASES = [("bf16", 1, 2, 513, 128), ("bf16", 2, 3, 1, 128), ("bf16", 1, 3,
 
 @pytest.mark.parametrize("case", COMMIT_CASES, ids=_ids)
 def test_commit(case):
-    """arl2_commit against the oracle's commit, twice on one workspace with
-    different inputs (every part's slot and the counters reused)."""
+    """arl2_commit against the oracle's commit on a workspace first filled with
+    arbitrary bytes (no clearing needed: the counters carry a per-call tag),
+    then again on the same workspace with different inputs (every part's slot
+    and the counters reused)."""
+    import torch
     from hybrid_linear_memory_amd import arl2
     w = _w(*case)
     log(f"commit {_ids(case)}")
     sh = shape_of(w)
     phis = synth.phi_maps(w)
     ws = arl2.alloc_workspace(sh, arl2.OP_COMMIT)
+    tg = torch.Generator(device="cuda").manual_seed(11)
+    ws.copy_(torch.randint(0, 256, ws.shape, generator=tg, device="cuda", dtype=torch.int32)
+             .to(torch.uint8))
     g = np.random.default_rng(9)
     for call in range(2):
         k, v = synth.kv(w, call, 0)
