@@ -32,6 +32,7 @@ STEP_CASES = [
     ("f32", 1, 1, 64, 16), ("f32", 2, 3, 100, 32), ("f32", 1, 2, 37, 64), ("f32", 1, 2, 130, 128),
     ("f32", 1, 1, 1, 16),
     ("bf16", 1, 2, 200, 128), ("bf16", 2, 3, 1, 128), ("bf16", 1, 1, 37, 128),
+    ("bf16", 1, 2, 100, 128), ("bf16", 1, 2, 150, 128),
     ("bf16", 1, 2, 513, 128), ("bf16", 1, 12, 1560, 128),
     ("bf16", 1, 2, 200, 64), ("bf16", 2, 1, 77, 16), ("bf16", 1, 3, 1560, 64),
     ("bf16", 1, 1, 1, 16),
