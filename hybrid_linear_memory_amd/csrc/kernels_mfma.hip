@@ -56,7 +56,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 // LDS: the tiles of parity p (local tile index & 1) sit in arrays of their
 // own: lk[p] = [stream A K, stream B K] of parity p and lv[p] = [stream A V,
 // stream B V] of parity 1-p (each stream's V tiles are loaded one iteration
-// after its K tiles). At an iteration of parity p every read is from lk[p] /
+// after its K tiles; in split-key segments stream A's V tiles are of parity p,
+// loaded with its K tiles). At an iteration of parity p every read is from lk[p] /
 // lv[p] and every load in flight targets lk[1-p] / lv[1-p]: distinct objects,
 // which lets the compiler see that the reads need not wait for the prefetch.
 constexpr int AKV = 2 * TILE_B;
@@ -415,7 +416,12 @@ __device__ __forceinline__ void attn_block(
   // its tile it. So while one wave of a SIMD runs its softmax the other runs
   // its products. Tile j's V sits in the V buffers of parity j + 1 for both
   // streams (loaded during iteration j, read during iteration j + 1).
-  const int n_iter = (n_tiles + 1) / 2 + 1;   // same for every wave
+  // (Split-key segments keep the earlier order of stream A, which finishes
+  // each of its tiles within its iteration: their short key ranges would pay
+  // the extra iteration once per segment. There tile j's V of stream A sits in
+  // the V buffers of parity j.)
+  const int n_iter = SK ? max((n_tiles + 1) / 2, n_tiles / 2 + 1)
+                        : (n_tiles + 1) / 2 + 1;   // same for every wave
   f32x16 acc[4];
   float l = 0.f, m_ref = -INFINITY;
   // One pass over the keys. Mode 0: reference maximum from the stream's first
@@ -456,23 +462,27 @@ __device__ __forceinline__ void attn_block(
         __attribute__((always_inline)) {
       sync();
       if (it == n_iter - 1) load_m(kn);
-      if (mode != 1 && it >= 1 && it <= my_cnt) attn_pv(acc, pa, vc, off);
-      if (it < my_cnt) {
-        if constexpr (SK) {
-          // (split-key segments: the loads in one burst measured faster)
-          if (it + 1 < my_cnt) load_k(kn, it + 1);
-          load_v(vn, it);
-          scores(it, kc);
-        } else if (it + 1 < my_cnt) {
-          scores_ld(it, kc, std::integral_constant<int, 8>(), [&](int n2) {
-            if (n2 < 4) load_k1(kn, it + 1, n2);
-            else load_v1(vn, it, n2 - 4);
-          });
-        } else {
-          scores_ld(it, kc, std::integral_constant<int, 4>(),
-                    [&](int n2) { load_v1(vn, it, n2); });
+      if constexpr (SK) {
+        // (split-key segments: the loads in one burst measured faster)
+        if (it + 1 < my_cnt) {
+          load_k(kn, it + 1);
+          load_v(vn, it + 1);
         }
-        if (mode != 1) attn_softmax(pa, l, m_ref, s, sl2);
+        if (it < my_cnt) scores(it, kc);
+        if (mode != 1 && it < my_cnt) attn_softmax_pv(acc, l, m_ref, s, vc, off, sl2);
+      } else {
+        if (mode != 1 && it >= 1 && it <= my_cnt) attn_pv(acc, pa, vc, off);
+        if (it < my_cnt) {
+          if (it + 1 < my_cnt)
+            scores_ld(it, kc, std::integral_constant<int, 8>(), [&](int n2) {
+              if (n2 < 4) load_k1(kn, it + 1, n2);
+              else load_v1(vn, it, n2 - 4);
+            });
+          else
+            scores_ld(it, kc, std::integral_constant<int, 4>(),
+                      [&](int n2) { load_v1(vn, it, n2); });
+          if (mode != 1) attn_softmax(pa, l, m_ref, s, sl2);
+        }
       }
     };
     auto step_b = [&](int it, char* kc, char* vc, char* kn, char* vn)
@@ -499,9 +509,11 @@ __device__ __forceinline__ void attn_block(
     };
     if (stream == 0) {
       if (my_cnt > 0) load_k(lk0, 0);
+      if (SK && my_cnt > 0) load_v(lv0, 0);
       if (mode == 0) {
-        // Q landed for every wave (the 4 tile loads just issued may still fly)
-        if (my_cnt > 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        // Q landed for every wave (the 4 or 8 tile loads just issued may still fly)
+        if (SK && my_cnt > 0) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (my_cnt > 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         read_q();
